@@ -1,0 +1,224 @@
+"""Benchmark of the fused Dr. GRPO loss forward + backward on one MI355X.
+
+One step = one drgrpo_loss_fwd_bwd call (completion mask, group advantage,
+log-prob sweep over the vocabulary, clipped surrogate, token sum, dlogits)
+over one synthetic rollout batch resident in HBM.  Prints ONE JSON line.
+
+Default workload: B=8 prompts x G=8 completions x C=256 tokens over the
+151,936-entry vocabulary in bfloat16 (the Qwen2.5-0.5B-Instruct-shaped
+batch), synthetic seeded inputs.  logp_old is the library's own forward
+log-prob plus N(0, 0.02^2) noise, as an update step would receive it.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "loss fwd+bwd completion tokens/s and HBM GB/s (% of peak), V=151936 bf16"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+
+
+def _alg_bytes(cfg, adv, lens):
+    """Algorithmic HBM bytes of the per-row kernel for this batch: an active
+    token row reads and writes V elements plus its token id, logp_old (and
+    logp_ref); an inactive row writes V zeros and reads its token id."""
+    import numpy as np
+
+    esz = 2 if cfg.dtype == "bf16" else 4
+    mask = np.arange(cfg.C)[None, :] < lens[:, None]
+    active = mask & ((adv[:, None] != 0) | (cfg.beta != 0))
+    n_act = int(active.sum())
+    n_inact = cfg.T - n_act
+    per_act = 2 * esz * cfg.V + 8 + 4 + (4 if cfg.beta != 0 else 0)
+    per_inact = esz * cfg.V + 8
+    return n_act, n_inact, n_act * per_act + n_inact * per_inact, per_act, per_inact
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    for p in ("rl_post_loss_dr_amd/csrc/drgrpo.hip",):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), if the
+    committed measurement was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"k_rows_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("src_hash") != _src_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, case, target_s: float = 15.0):
+    """The CPU oracle, as it stands, on a strided sample of the workload's token
+    rows (whole rows, every group represented)."""
+    import numpy as np
+
+    import oracle
+
+    T = cfg.T
+    n_rows = 256
+    step = max(1, T // n_rows)
+    rows = np.arange(0, T, step)[:n_rows]
+    tok = case.tokens.reshape(-1)[rows]
+    x = case.logits_rows(rows)
+    # inputs of the sample (not timed): logp_old from the oracle's own log-probs
+    _, lp, _ = oracle.row_logprob(x, tok)
+    old = synth_perturb(lp, case.old_noise.reshape(-1)[rows])
+    ref = None if case.ref_noise is None else synth_perturb(lp, case.ref_noise.reshape(-1)[rows])
+    lens = oracle.completion_len(case.tokens, cfg.eos_id)
+    adv_all = oracle.group_advantage(case.rewards, cfg.G)
+    i_idx = rows // cfg.C
+    t_idx = rows % cfg.C
+    adv_s = adv_all[i_idx]
+    # each sampled token is its own length-1 "completion" carrying its mask
+    lens_s = (t_idx < lens[i_idx]).astype(np.int32)
+    eps, beta, kappa = (float(np.float32(v)) for v in (cfg.eps, cfg.beta, cfg.norm_const))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.completion_len(case.tokens, cfg.eos_id)
+        oracle.group_advantage(case.rewards, cfg.G)
+        lse, logp, _ = oracle.row_logprob(x, tok)
+        lam, coef, _ = oracle.token_terms(logp[:, None], old[:, None],
+                                          None if ref is None else ref[:, None], adv_s, lens_s,
+                                          eps, beta, kappa)
+        oracle.loss_sum(lam, kappa)
+        oracle.dlogits_rows(x, tok, lse, coef.reshape(-1))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    tok_s = reps * len(rows) / el
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": tok_s, "unit": "completion tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} token rows (every {step}th of {T}) x V={cfg.V}, "
+                      f"{reps} passes in {el:.1f} s; mask and advantage over the whole batch"}
+
+
+def synth_perturb(lp, noise):
+    import synth
+
+    return synth.perturb(lp, noise)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen_b8g8c256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import rl_post_loss_dr_amd as dr
+
+    cfg = synth.get_config(args.workload)
+    case = synth.make_case(cfg)
+    dev = torch.device("cuda:0")
+    torch_dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    logits = torch.empty((cfg.N, cfg.C, cfg.V), dtype=torch_dt, device=dev)
+    synth.gpu_normal_fill(logits, cfg.seed, synth.S_LOGITS, 0, cfg.logit_std)
+    tokens = torch.from_numpy(case.tokens).to(dev)
+    rewards = torch.from_numpy(case.rewards).to(dev)
+    lp = dr.logprobs(logits, tokens).double().cpu().numpy()
+    old = torch.from_numpy(synth.perturb(lp, case.old_noise)).to(dev)
+    ref = None if case.ref_noise is None else torch.from_numpy(
+        synth.perturb(lp, case.ref_noise)).to(dev)
+    dlogits = torch.empty_like(logits)
+    ws = dr.make_workspace(cfg.N, cfg.C, cfg.V, cfg.G, dev)
+    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const,
+              out_dlogits=dlogits, workspace=ws)
+    aux = {}
+    dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, aux=aux, **kw)
+    torch.cuda.synchronize()
+    lens = aux["len"].cpu().numpy()
+    adv = aux["adv"].cpu().numpy()
+    n_act, n_inact, alg_bytes, per_act, per_inact = _alg_bytes(cfg, adv, lens)
+
+    for _ in range(args.warmup):
+        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, **kw)
+    torch.cuda.synchronize()
+
+    # per-row-kernel events on the stream the library launches on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:  # create the underlying HIP events
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(args.steps):
+        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, rows_events=evs[k], **kw)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    rows_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    rows_ms_avg = float(np.mean(rows_ms))
+    if dr.device_status(ws) != dr.OK:
+        raise SystemExit("device status not OK")
+
+    tok_s = cfg.T / (ms_step / 1e3)
+    achieved = alg_bytes / (rows_ms_avg / 1e3) / 1e9
+    traffic = _traffic(args.workload)
+    rec = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "completion tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded generator; no dataset or weights)",
+        "config": {"workload": cfg.name, "B": cfg.B, "G": cfg.G, "C": cfg.C, "V": cfg.V,
+                   "token_rows": cfg.T, "beta": cfg.beta, "eps": cfg.eps,
+                   "norm_const": cfg.norm_const, "active_rows": n_act, "inactive_rows": n_inact},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "k_rows", "kernel_ms": rows_ms_avg,
+                     "alg_bytes_per_launch": alg_bytes, "bytes_per_active_row": per_act,
+                     "bytes_per_inactive_row": per_inact},
+        "step_gbps_alg": alg_bytes / (ms_step / 1e3) / 1e9,
+        "wall_s_timed": wall,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, case)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

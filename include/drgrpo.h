@@ -1,0 +1,162 @@
+/*
+ * drgrpo.h - C ABI of the fused Dr. GRPO update loss for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The library computes, for a rollout batch of N = B*G completions of C
+ * tokens each (G completions per prompt, stored as G consecutive rows), the
+ * Dr. GRPO loss and its gradient with respect to the policy logits, in one
+ * stream-ordered call, without materialising log_softmax.
+ *
+ * Definitions ("Making Dr GRPO go brrr", sections named per call below):
+ *   len_i   = index of the first EOS in row i, plus one; C if the row has no
+ *             EOS ("The completion mask": first EOS inclusive, a row without
+ *             EOS counts every token).  mask[i,t] = t < len_i.
+ *   A_i     = R_i - mean of R over row i's group, no division by the group
+ *             standard deviation ("Dr. GRPO"); binary32, sequential group sum.
+ *   logp    = x[y] - logsumexp(x), where x = logits[i,t,:] and y = tokens[i,t]
+ *             ("compute_logprobs"): the logits passed in are the completion
+ *             slice, so logits row t scores token t.
+ *   r       = exp(logp - logp_old)                                  ("PPO")
+ *   s       = min(r*A, clip(r, 1-eps, 1+eps)*A)        ("PPO", "The loss")
+ *   k3      = exp(d) - d - 1 with d = logp_ref - logp   (KL term, beta > 0)
+ *   lambda  = -s + beta*k3 per token; the mask multiplies lambda ("The loss")
+ *   L       = (sum over mask=1 tokens of lambda) / norm_const  ("Dr. GRPO":
+ *             token sum divided by a fixed constant)
+ *   dlogits = dL/dlogits = coef*(softmax(x) - onehot(y)), coef = -g/norm_const
+ *             with g = dlambda/dlogp = -A*r*chi + beta*(1 - exp(d)), chi = 0
+ *             when the clip cuts the surrogate ((A>0 and r>1+eps) or (A<0 and
+ *             r<1-eps)), 1 otherwise.
+ * A token is "active" when mask = 1 and (A != 0 or beta != 0).  Inactive
+ * tokens contribute exactly 0 to L and to dlogits; their logits are not read.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller unless stated.  The
+ *     library keeps no global state and allocates no device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it; no call synchronises except
+ *     drgrpo_device_status.  Results are valid once the stream has reached
+ *     the end of the call.
+ *   - Host-side argument errors are returned before anything is enqueued.
+ *   - Layouts are dense row-major: logits/dlogits [N, C, V]; tokens, logp_old,
+ *     logp_ref [N, C]; rewards [N].
+ */
+#ifndef DRGRPO_H
+#define DRGRPO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logits and dlogits. */
+typedef enum { DRGRPO_F32 = 0, DRGRPO_BF16 = 1 } drgrpo_dtype_t;
+
+/* Status codes (0 = success, negative = error). */
+enum {
+  DRGRPO_OK = 0,
+  DRGRPO_ERR_NULL = -1,        /* a required pointer is NULL */
+  DRGRPO_ERR_SHAPE = -2,       /* N, C, V, G <= 0, N % G != 0, or a size overflows */
+  DRGRPO_ERR_PARAM = -3,       /* eps, beta or norm_const invalid (see each call) */
+  DRGRPO_ERR_DTYPE = -4,       /* unknown drgrpo_dtype_t */
+  DRGRPO_ERR_WORKSPACE = -5,   /* workspace NULL, too small or not 256-byte aligned */
+  DRGRPO_ERR_ALIAS = -6,       /* out_dlogits partially overlaps logits */
+  DRGRPO_ERR_HIP = -7,         /* a HIP launch failed */
+  DRGRPO_ERR_TOKEN_RANGE = -8  /* device-side: a token at a mask=1 position is outside [0, V) */
+};
+
+/* Bytes of device workspace drgrpo_loss_fwd_bwd needs for these sizes (0 if
+ * the sizes are invalid).  The workspace is caller-owned, 256-byte aligned,
+ * needs no initialisation, and holds the device status word read by
+ * drgrpo_device_status.  One workspace must not be used by two calls that
+ * can run concurrently. */
+size_t drgrpo_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t G);
+
+/* Dr. GRPO loss forward and backward over raw logits.
+ *
+ *   logits      [N, C, V] of `dtype`; row t scores tokens[:, t].
+ *   tokens      [N, C] int64 completion ids; positions after the first EOS
+ *               are never read as vocabulary indices.
+ *   eos_id      EOS id; a value outside [0, V) means no row ends early.
+ *   rewards     [N] float; group b is rows [b*G, (b+1)*G).
+ *   logp_old    [N, C] float log-probs of the policy that sampled the batch.
+ *   logp_ref    [N, C] float reference-policy log-probs; may be NULL iff
+ *               beta == 0.
+ *   G           completions per prompt (N % G == 0).
+ *   eps         clip half-width, finite and >= 0.
+ *   beta        KL weight, finite and >= 0.
+ *   norm_const  the aggregation constant, finite and > 0 (G*C reproduces a
+ *               per-group token sum divided by C; B*G a mean over completions).
+ *   out_loss    [1] float on the device: L rounded to binary32 (NaN when a
+ *               device-side error occurred).
+ *   out_dlogits [N, C, V] of `dtype`, fully overwritten; may be exactly
+ *               `logits` (in place), any other overlap is DRGRPO_ERR_ALIAS.
+ *               bfloat16 results are rounded to nearest even from binary32.
+ *   workspace   device buffer of drgrpo_workspace_bytes(N, C, V, G) bytes.
+ *
+ * The logits may have any V; rows whose byte size is a multiple of 16 with
+ * 16-byte aligned bases take the vector path, others the element path.
+ * Device-side errors (a token outside [0, V) at a mask=1 position) make the
+ * loss and that token's dlogits row NaN and set the status word. */
+int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_id,
+                        const float* rewards, const float* logp_old, const float* logp_ref,
+                        int64_t G, float eps, float beta, float norm_const, float* out_loss,
+                        void* out_dlogits, int64_t N, int64_t C, int64_t V,
+                        drgrpo_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Optional per-call diagnostics; every field may be NULL. */
+typedef struct drgrpo_aux {
+  int32_t* len;     /* [N] completion lengths */
+  uint8_t* mask;    /* [N, C] completion mask (1 = counted) */
+  float* adv;       /* [N] advantages */
+  float* logp;      /* [N, C] log-probs of active tokens, 0 elsewhere */
+  float* tok_loss;  /* [N, C] per-token lambda, 0 for inactive tokens */
+  int64_t* stats;   /* [4] groups without reward contrast, rows without EOS,
+                       active tokens with r outside [1-eps, 1+eps], active
+                       tokens whose surrogate gradient the clip cuts */
+  void* rows_event_begin; /* hipEvent_t stamped when the per-row kernel's
+                             dispatch starts (NULL: none), to time it alone */
+  void* rows_event_end;   /* hipEvent_t stamped when it ends (NULL: none) */
+} drgrpo_aux_t;
+
+/* drgrpo_loss_fwd_bwd plus the diagnostics `aux` asks for (aux may be NULL). */
+int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
+                           const float* rewards, const float* logp_old, const float* logp_ref,
+                           int64_t G, float eps, float beta, float norm_const, float* out_loss,
+                           void* out_dlogits, int64_t N, int64_t C, int64_t V,
+                           drgrpo_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                           void* stream, const drgrpo_aux_t* aux);
+
+/* Completion mask alone ("The completion mask"): out_len [N] int32 (required),
+ * out_mask [N, C] uint8 (may be NULL). */
+int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t C, int64_t eos_id,
+                           int32_t* out_len, uint8_t* out_mask, void* stream);
+
+/* Group advantages alone ("Dr. GRPO"): out_adv [N] float (required);
+ * out_nocontrast [1] int32 (may be NULL) receives the number of groups whose
+ * rewards are all equal ("The sparse-reward bottleneck" of "The Quiet
+ * Library"). */
+int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, float* out_adv,
+                           int32_t* out_nocontrast, void* stream);
+
+/* Forward-only log-probs of every token ("compute_logprobs"), the no-gradient
+ * pass that produces logp_old / logp_ref: out_logp [N, C] float.  A token
+ * outside [0, V) gives NaN. */
+int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_t C, int64_t V,
+                    drgrpo_dtype_t dtype, float* out_logp, void* stream);
+
+/* Synchronises `stream`, then reads the status word the last
+ * drgrpo_loss_fwd_bwd call on `workspace` left: DRGRPO_OK or
+ * DRGRPO_ERR_TOKEN_RANGE (DRGRPO_ERR_HIP if the read fails). */
+int drgrpo_device_status(const void* workspace, void* stream);
+
+/* Static, human-readable text of a status code. */
+const char* drgrpo_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRGRPO_H */

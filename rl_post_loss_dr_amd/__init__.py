@@ -1,0 +1,245 @@
+"""Fused Dr. GRPO update loss (forward + backward) on AMD Instinct MI355X.
+
+Thin Python binding over the C ABI of ``libdrgrpo.so`` (declared in
+``include/drgrpo.h``).  This module only checks and marshals arguments:
+every step of the loss runs in the library's HIP kernels.  PyTorch provides
+device memory and the current stream.  There is no CPU fallback: if the
+library is missing, every call raises.
+
+Definitions follow "Making Dr GRPO go brrr" ("The completion mask",
+"compute_logprobs", "PPO", "Dr. GRPO", "The loss"); see ``drgrpo.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB, build  # noqa: F401
+
+F32, BF16 = 0, 1
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE = -1, -2, -3, -4
+ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOKEN_RANGE = -5, -6, -7, -8
+
+
+class DrGRPOError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} (status {code})")
+
+
+class _Aux(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("adv", ctypes.c_void_p),
+                ("logp", ctypes.c_void_p), ("tok_loss", ctypes.c_void_p),
+                ("stats", ctypes.c_void_p), ("rows_event_begin", ctypes.c_void_p),
+                ("rows_event_end", ctypes.c_void_p)]
+
+
+_lib = None
+_P, _I64, _F, _SZ, _I = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t,
+                         ctypes.c_int)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(
+                f"{LIB} is missing: the fused Dr. GRPO loss needs its HIP library "
+                "(build it with rl_post_loss_dr_amd.build()); there is no CPU fallback")
+        L = ctypes.CDLL(LIB)
+        L.drgrpo_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+        L.drgrpo_workspace_bytes.restype = _SZ
+        common = [_P, _P, _I64, _P, _P, _P, _I64, _F, _F, _F, _P, _P, _I64, _I64, _I64, _I, _P,
+                  _SZ, _P]
+        L.drgrpo_loss_fwd_bwd.argtypes = common
+        L.drgrpo_loss_fwd_bwd.restype = _I
+        L.drgrpo_loss_fwd_bwd_ex.argtypes = common + [ctypes.POINTER(_Aux)]
+        L.drgrpo_loss_fwd_bwd_ex.restype = _I
+        L.drgrpo_completion_mask.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
+        L.drgrpo_completion_mask.restype = _I
+        L.drgrpo_group_advantage.argtypes = [_P, _I64, _I64, _P, _P, _P]
+        L.drgrpo_group_advantage.restype = _I
+        L.drgrpo_logprobs.argtypes = [_P, _P, _I64, _I64, _I64, _I, _P, _P]
+        L.drgrpo_logprobs.restype = _I
+        L.drgrpo_device_status.argtypes = [_P, _P]
+        L.drgrpo_device_status.restype = _I
+        L.drgrpo_status_string.argtypes = [_I]
+        L.drgrpo_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().drgrpo_status_string(code).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != OK:
+        raise DrGRPOError(code, where)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def workspace_bytes(N: int, C: int, V: int, G: int) -> int:
+    return int(lib().drgrpo_workspace_bytes(N, C, V, G))
+
+
+def make_workspace(N: int, C: int, V: int, G: int, device) -> torch.Tensor:
+    n = workspace_bytes(N, C, V, G)
+    if n == 0:
+        raise DrGRPOError(ERR_SHAPE, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, rewards: torch.Tensor,
+                 logp_old: torch.Tensor, logp_ref: torch.Tensor | None = None, *, G: int,
+                 eps: float = 0.2, beta: float = 0.0, norm_const: float | None = None,
+                 out_dlogits: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 aux: dict | None = None, rows_events=None):
+    """Loss and dlogits of the Dr. GRPO update for one rollout batch.
+
+    logits [N, C, V] float32/bfloat16 (the completion slice: row t scores
+    tokens[:, t]); tokens [N, C] int64; rewards [N] float32; logp_old,
+    logp_ref [N, C] float32.  norm_const defaults to G*C.  Returns
+    (loss [] float32 device tensor, dlogits like logits).  `out_dlogits` may
+    be `logits` itself (in place).  `aux` (a dict) receives device tensors
+    len, mask, adv, logp, tok_loss, stats when given.  `rows_events` is an
+    optional pair of recorded torch.cuda.Event (enable_timing=True) that the
+    library records around its per-row kernel on the current stream.
+    """
+    if logits.dim() != 3:
+        raise ValueError("logits must be [N, C, V]")
+    N, C, V = logits.shape
+    dt = _dtype_code(logits)
+    _dev(logits, "logits", logits.dtype)
+    dev = logits.device
+    _dev(tokens, "tokens", torch.int64, (N, C))
+    _dev(rewards, "rewards", torch.float32, (N,))
+    _dev(logp_old, "logp_old", torch.float32, (N, C))
+    if logp_ref is not None:
+        _dev(logp_ref, "logp_ref", torch.float32, (N, C))
+    if norm_const is None:
+        norm_const = float(G * C)
+    if out_dlogits is None:
+        out_dlogits = torch.empty_like(logits)
+    else:
+        _dev(out_dlogits, "out_dlogits", logits.dtype, (N, C, V))
+    if workspace is None:
+        workspace = make_workspace(N, C, V, G, dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    args = (logits.data_ptr(), tokens.data_ptr(), int(eos_id), rewards.data_ptr(),
+            logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta),
+            float(norm_const), loss.data_ptr(), out_dlogits.data_ptr(), N, C, V, dt,
+            workspace.data_ptr(), workspace.numel(), _stream(dev))
+    if aux is None and rows_events is None:
+        _check(lib().drgrpo_loss_fwd_bwd(*args), "drgrpo_loss_fwd_bwd")
+        return loss, out_dlogits
+    s = _Aux()
+    if aux is not None:
+        aux["len"] = torch.empty(N, dtype=torch.int32, device=dev)
+        aux["mask"] = torch.empty((N, C), dtype=torch.uint8, device=dev)
+        aux["adv"] = torch.empty(N, dtype=torch.float32, device=dev)
+        aux["logp"] = torch.empty((N, C), dtype=torch.float32, device=dev)
+        aux["tok_loss"] = torch.empty((N, C), dtype=torch.float32, device=dev)
+        aux["stats"] = torch.empty(4, dtype=torch.int64, device=dev)
+        for k in ("len", "mask", "adv", "logp", "tok_loss", "stats"):
+            setattr(s, k, aux[k].data_ptr())
+    if rows_events is not None:
+        s.rows_event_begin = rows_events[0].cuda_event
+        s.rows_event_end = rows_events[1].cuda_event
+    _check(lib().drgrpo_loss_fwd_bwd_ex(*args, ctypes.byref(s)), "drgrpo_loss_fwd_bwd_ex")
+    return loss, out_dlogits
+
+
+def logprobs(logits: torch.Tensor, tokens: torch.Tensor) -> torch.Tensor:
+    """Forward-only log-probs [N, C] float32 of every token (no mask)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [N, C, V]")
+    N, C, V = logits.shape
+    dt = _dtype_code(logits)
+    _dev(logits, "logits", logits.dtype)
+    _dev(tokens, "tokens", torch.int64, (N, C))
+    out = torch.empty((N, C), dtype=torch.float32, device=logits.device)
+    _check(lib().drgrpo_logprobs(logits.data_ptr(), tokens.data_ptr(), N, C, V, dt,
+                                 out.data_ptr(), _stream(logits.device)), "drgrpo_logprobs")
+    return out
+
+
+def completion_mask(tokens: torch.Tensor, eos_id: int):
+    """(len int32 [N], mask uint8 [N, C]) of the first-EOS-inclusive mask."""
+    _dev(tokens, "tokens", torch.int64)
+    N, C = tokens.shape
+    ln = torch.empty(N, dtype=torch.int32, device=tokens.device)
+    mk = torch.empty((N, C), dtype=torch.uint8, device=tokens.device)
+    _check(lib().drgrpo_completion_mask(tokens.data_ptr(), N, C, int(eos_id), ln.data_ptr(),
+                                        mk.data_ptr(), _stream(tokens.device)),
+           "drgrpo_completion_mask")
+    return ln, mk
+
+
+def group_advantage(rewards: torch.Tensor, G: int):
+    """(advantages float32 [N], no-contrast group count int32 [1])."""
+    _dev(rewards, "rewards", torch.float32)
+    N = rewards.numel()
+    adv = torch.empty(N, dtype=torch.float32, device=rewards.device)
+    cnt = torch.empty(1, dtype=torch.int32, device=rewards.device)
+    _check(lib().drgrpo_group_advantage(rewards.data_ptr(), N, int(G), adv.data_ptr(),
+                                        cnt.data_ptr(), _stream(rewards.device)),
+           "drgrpo_group_advantage")
+    return adv, cnt
+
+
+def device_status(workspace: torch.Tensor) -> int:
+    """Synchronises the current stream and returns the status word of the last
+    loss call that used `workspace` (OK or ERR_TOKEN_RANGE)."""
+    return int(lib().drgrpo_device_status(workspace.data_ptr(), _stream(workspace.device)))
+
+
+class DrGRPOLoss(torch.autograd.Function):
+    """Autograd wrapper: forward returns the loss, backward returns
+    grad_out * dlogits for the logits (no gradient to any other input)."""
+
+    @staticmethod
+    def forward(ctx, logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
+                norm_const):
+        loss, dlogits = loss_fwd_bwd(logits.detach(), tokens, eos_id, rewards, logp_old,
+                                     logp_ref, G=G, eps=eps, beta=beta, norm_const=norm_const)
+        ctx.save_for_backward(dlogits)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (dlogits,) = ctx.saved_tensors
+        g = dlogits * grad_out.to(dlogits.dtype)
+        return g, None, None, None, None, None, None, None, None, None

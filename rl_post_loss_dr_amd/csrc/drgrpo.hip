@@ -1,0 +1,741 @@
+/*
+ * drgrpo.hip - fused Dr. GRPO update loss, forward and backward, for gfx950.
+ *
+ * Definitions are those of include/drgrpo.h ("Making Dr GRPO go brrr":
+ * "The completion mask", "compute_logprobs", "PPO", "Dr. GRPO", "The loss").
+ *
+ * One call is three stream-ordered launches:
+ *   k_prep    one wavefront per completion: first-EOS length (ballot over 64
+ *             tokens at a time), group advantage, per-row flags.
+ *   k_rows    one 1024-thread workgroup per token row: streams the row's V
+ *             logits from HBM once with 16-byte loads, keeps them in
+ *             registers (19 chunks of 16 B per lane covers a bf16 row of up
+ *             to 155,648 entries), reduces max / sum-of-exp with wavefront
+ *             shuffles and one LDS exchange, evaluates the per-token surrogate
+ *             and KL in binary64, then writes dlogits = coef*(softmax - onehot)
+ *             from the same registers.  Rows longer than one register tile
+ *             are swept tile by tile and re-read for the write pass.  Tokens
+ *             whose loss term is identically zero only write zeros.
+ *   k_finish  one workgroup: fixed-order binary64 sum of the per-token terms,
+ *             divide by norm_const, counters and the status word.
+ * No floating-point atomics: results are bitwise reproducible.
+ */
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "drgrpo.h"
+
+namespace {
+
+constexpr int kThreads = 1024;          // threads per token-row workgroup
+constexpr int kWaves = kThreads / 64;   // wavefronts per workgroup
+constexpr int kNch = 19;                // register-resident 16-byte chunks per lane
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2eD = 1.4426950408889634074;
+
+// per-token flags
+constexpr uint8_t TF_OUTSIDE = 1;  // ratio outside [1-eps, 1+eps]
+constexpr uint8_t TF_CUT = 2;      // clip cuts the surrogate gradient (A != 0)
+constexpr uint8_t TF_BADTOK = 4;   // token outside [0, V) at a mask=1 position
+// per-row flags
+constexpr uint8_t RF_NOEOS = 1;      // row has no EOS
+constexpr uint8_t RF_NOCONTRAST = 2; // first row of a group whose rewards are all equal
+
+constexpr int32_t kStatusTokenRange = 1;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace carve-up (offsets from a 256-byte aligned base).
+struct Ws {
+  int32_t* status;     // [64]: [0] status word
+  int32_t* len;        // [N]
+  float* adv;          // [N]
+  uint8_t* row_flags;  // [N]
+  double* tok_loss;    // [T]
+  uint8_t* tok_flags;  // [T]
+};
+
+size_t ws_carve(void* base, int64_t N, int64_t T, Ws* ws) {
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  Ws w;
+  w.status = reinterpret_cast<int32_t*>(take(256));
+  w.len = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * N));
+  w.adv = reinterpret_cast<float*>(take(sizeof(float) * N));
+  w.row_flags = reinterpret_cast<uint8_t*>(take(N));
+  w.tok_loss = reinterpret_cast<double*>(take(sizeof(double) * T));
+  w.tok_flags = reinterpret_cast<uint8_t*>(take(T));
+  if (ws) *ws = w;
+  return off;
+}
+
+// ----------------------------------------------------------------- element IO
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 ha = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
+  const __bf16 hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int DT, int VEC>
+struct Io;
+
+// bfloat16, 8 per 16-byte chunk
+template <>
+struct Io<DRGRPO_BF16, 8> {
+  using chunk = uint4;
+  static constexpr int kBytes = 2;
+  __device__ static chunk load(const char* row, int64_t c) {
+    return reinterpret_cast<const uint4*>(row)[c];
+  }
+  __device__ static void unpack(const chunk& v, float (&f)[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  }
+  __device__ static void store(char* row, int64_t c, const float (&f)[8]) {
+    uint4 o;
+    o.x = pack_bf16x2(f[0], f[1]);
+    o.y = pack_bf16x2(f[2], f[3]);
+    o.z = pack_bf16x2(f[4], f[5]);
+    o.w = pack_bf16x2(f[6], f[7]);
+    reinterpret_cast<uint4*>(row)[c] = o;
+  }
+  __device__ static void fill(char* row, int64_t c, float val) {
+    const uint32_t w = pack_bf16x2(val, val);
+    reinterpret_cast<uint4*>(row)[c] = make_uint4(w, w, w, w);
+  }
+  __device__ static float elem(const char* row, int64_t v) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[v] << 16);
+  }
+};
+
+// binary32, 4 per 16-byte chunk
+template <>
+struct Io<DRGRPO_F32, 4> {
+  using chunk = uint4;
+  static constexpr int kBytes = 4;
+  __device__ static chunk load(const char* row, int64_t c) {
+    return reinterpret_cast<const uint4*>(row)[c];
+  }
+  __device__ static void unpack(const chunk& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  __device__ static void store(char* row, int64_t c, const float (&f)[4]) {
+    reinterpret_cast<uint4*>(row)[c] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                  __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+  __device__ static void fill(char* row, int64_t c, float val) {
+    const uint32_t w = __float_as_uint(val);
+    reinterpret_cast<uint4*>(row)[c] = make_uint4(w, w, w, w);
+  }
+  __device__ static float elem(const char* row, int64_t v) {
+    return reinterpret_cast<const float*>(row)[v];
+  }
+};
+
+// bfloat16, one element per access (rows not 16-byte aligned)
+template <>
+struct Io<DRGRPO_BF16, 1> {
+  using chunk = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static chunk load(const char* row, int64_t c) {
+    return reinterpret_cast<const uint16_t*>(row)[c];
+  }
+  __device__ static void unpack(const chunk& v, float (&f)[1]) {
+    f[0] = __uint_as_float((uint32_t)v << 16);
+  }
+  __device__ static void store(char* row, int64_t c, const float (&f)[1]) {
+    const __bf16 h = (__bf16)f[0];
+    reinterpret_cast<uint16_t*>(row)[c] = __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static void fill(char* row, int64_t c, float val) {
+    const __bf16 h = (__bf16)val;
+    reinterpret_cast<uint16_t*>(row)[c] = __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static float elem(const char* row, int64_t v) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[v] << 16);
+  }
+};
+
+// binary32, one element per access (rows not 16-byte aligned)
+template <>
+struct Io<DRGRPO_F32, 1> {
+  using chunk = float;
+  static constexpr int kBytes = 4;
+  __device__ static chunk load(const char* row, int64_t c) {
+    return reinterpret_cast<const float*>(row)[c];
+  }
+  __device__ static void unpack(const chunk& v, float (&f)[1]) { f[0] = v; }
+  __device__ static void store(char* row, int64_t c, const float (&f)[1]) {
+    reinterpret_cast<float*>(row)[c] = f[0];
+  }
+  __device__ static void fill(char* row, int64_t c, float val) {
+    reinterpret_cast<float*>(row)[c] = val;
+  }
+  __device__ static float elem(const char* row, int64_t v) {
+    return reinterpret_cast<const float*>(row)[v];
+  }
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (max, sum of exp(x - max)) pair merge; empty sides have max = -inf, sum = 0.
+__device__ inline void lse_merge(float& m, float& s, float m2, float s2) {
+  const float nm = fmaxf(m, m2);
+  if (nm == -INFINITY) return;
+  s = s * fast_exp2((m - nm) * kLog2e) + s2 * fast_exp2((m2 - nm) * kLog2e);
+  m = nm;
+}
+
+// ------------------------------------------------------------------- k_prep
+// One wavefront per completion row i.
+__global__ void __launch_bounds__(64)
+k_prep(const int64_t* __restrict__ tokens, int64_t C, int64_t eos_id,
+       const float* __restrict__ rewards, int64_t G, int32_t* __restrict__ len,
+       float* __restrict__ adv, uint8_t* __restrict__ row_flags, int32_t* __restrict__ aux_len,
+       uint8_t* __restrict__ aux_mask, float* __restrict__ aux_adv,
+       int32_t* __restrict__ nocontrast_count) {
+  const int64_t i = blockIdx.x;
+  const int lane = threadIdx.x;
+  int64_t first = C;
+  if (tokens) {
+    const int64_t* row = tokens + i * C;
+    for (int64_t base = 0; base < C; base += 64) {
+      const int64_t t = base + lane;
+      const bool hit = t < C && row[t] == eos_id;
+      const unsigned long long b = __ballot(hit);
+      if (b) {
+        first = base + __ffsll(b) - 1;
+        break;
+      }
+    }
+    const int32_t L = first < C ? (int32_t)(first + 1) : (int32_t)C;
+    if (aux_mask)
+      for (int64_t t = lane; t < C; t += 64) aux_mask[i * C + t] = t < L ? 1 : 0;
+    if (lane == 0) {
+      if (len) len[i] = L;
+      if (aux_len) aux_len[i] = L;
+    }
+  }
+  if (rewards && lane == 0) {
+    // A_i = R_i - (sequential binary32 group sum) / G
+    const int64_t g0 = (i / G) * G;
+    const float r0 = rewards[g0];
+    float s = 0.0f;
+    bool same = true;
+    for (int64_t j = 0; j < G; ++j) {
+      const float r = rewards[g0 + j];
+      s = s + r;
+      same = same && (r == r0);
+    }
+    const float mu = s / (float)G;
+    const float a = rewards[i] - mu;
+    if (adv) adv[i] = a;
+    if (aux_adv) aux_adv[i] = a;
+    const bool group_head = (i == g0) && same;
+    if (row_flags)
+      row_flags[i] = (uint8_t)((tokens && first == C ? RF_NOEOS : 0) |
+                               (group_head ? RF_NOCONTRAST : 0));
+    if (nocontrast_count && group_head) atomicAdd(nocontrast_count, 1);
+  }
+}
+
+__global__ void k_zero_i32(int32_t* p) { *p = 0; }
+
+// ------------------------------------------------------------------- k_rows
+struct RowArgs {
+  const void* logits;
+  void* dlogits;
+  const int64_t* tokens;
+  const float* logp_old;
+  const float* logp_ref;
+  const int32_t* len;
+  const float* adv;
+  int64_t C;
+  int64_t V;
+  float eps;
+  float beta;
+  double kappa;
+  double* tok_loss;
+  uint8_t* tok_flags;
+  float* aux_logp;
+  float* aux_tok_loss;
+  float* out_logp;  // forward-only mode: log-prob of every token
+};
+
+template <int DT, int VEC, bool kFwdOnly>
+__global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
+  using IO = Io<DT, VEC>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t i = row / a.C;
+  const int64_t t = row - i * a.C;
+  const int64_t V = a.V;
+  const int64_t nchunks = V / VEC;
+  const char* in = static_cast<const char*>(a.logits) + row * V * IO::kBytes;
+  char* out = kFwdOnly ? nullptr : static_cast<char*>(a.dlogits) + row * V * IO::kBytes;
+  const int64_t y = a.tokens[row];
+
+  bool in_mask = true;
+  bool active = true;
+  float A = 0.0f;
+  if (!kFwdOnly) {
+    in_mask = t < a.len[i];
+    A = a.adv[i];
+    active = in_mask && (A != 0.0f || a.beta != 0.0f);
+  }
+  const bool bad = in_mask && (y < 0 || y >= V);
+  if (bad || !active) {
+    if (kFwdOnly) {
+      if (tid == 0) a.out_logp[row] = NAN;
+      return;
+    }
+    const float fillv = bad ? NAN : 0.0f;
+    for (int64_t c = tid; c < nchunks; c += kThreads) IO::fill(out, c, fillv);
+    if (tid == 0) {
+      a.tok_loss[row] = bad ? (double)NAN : 0.0;
+      a.tok_flags[row] = bad ? TF_BADTOK : 0;
+      if (a.aux_logp) a.aux_logp[row] = bad ? NAN : 0.0f;
+      if (a.aux_tok_loss) a.aux_tok_loss[row] = bad ? NAN : 0.0f;
+    }
+    return;
+  }
+
+  // ---- pass 1: running max / sum of exp per lane over register tiles
+  typename IO::chunk buf[kNch];
+  const int64_t tile = (int64_t)kNch * kThreads;
+  const int ntiles = (int)((nchunks + tile - 1) / tile);
+  float m = -INFINITY;
+  float s = 0.0f;
+  for (int k = 0; k < ntiles; ++k) {
+    const int64_t c0 = (int64_t)k * tile + tid;
+#pragma unroll
+    for (int j = 0; j < kNch; ++j) {
+      const int64_t c = c0 + (int64_t)j * kThreads;
+      if (c < nchunks) buf[j] = IO::load(in, c);
+    }
+    float tm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kNch; ++j) {
+      const int64_t c = c0 + (int64_t)j * kThreads;
+      if (c < nchunks) {
+        float f[VEC];
+        IO::unpack(buf[j], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) tm = fmaxf(tm, f[e]);
+      }
+    }
+    const float nm = fmaxf(m, tm);
+    if (nm != -INFINITY) {
+      const float nm2 = nm * kLog2e;
+      float ts = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kNch; ++j) {
+        const int64_t c = c0 + (int64_t)j * kThreads;
+        if (c < nchunks) {
+          float f[VEC];
+          IO::unpack(buf[j], f);
+          float cs = 0.0f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) cs += fast_exp2(fmaf(f[e], kLog2e, -nm2));
+          ts += cs;
+        }
+      }
+      s = s * fast_exp2((m - nm) * kLog2e) + ts;
+      m = nm;
+    }
+  }
+  // wavefront merge (fixed butterfly order)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float s2 = __shfl_xor(s, off);
+    lse_merge(m, s, m2, s2);
+  }
+  __shared__ float sh_m[kWaves];
+  __shared__ float sh_s[kWaves];
+  __shared__ float sh_coef, sh_nlse2, sh_dy;
+  if (lane == 0) {
+    sh_m[wave] = m;
+    sh_s[wave] = s;
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // merge the 16 wavefront partials in binary64
+    const float mw = lane < kWaves ? sh_m[lane] : -INFINITY;
+    const float sw = lane < kWaves ? sh_s[lane] : 0.0f;
+    float M = mw;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    double term = 0.0;
+    if (lane < kWaves && sw != 0.0f) term = (double)sw * exp2(((double)mw - (double)M) * kLog2eD);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) term += __shfl_xor(term, off);
+    const double lse = (double)M + log(term);
+    const double logp = (double)IO::elem(in, y) - lse;
+    if (kFwdOnly) {
+      if (lane == 0) a.out_logp[row] = (float)logp;
+    } else if (lane == 0) {
+      const double Ad = (double)A;
+      const double eps = (double)a.eps;
+      const double beta = (double)a.beta;
+      const double r = exp(logp - (double)a.logp_old[row]);
+      const double lo = 1.0 - eps, hi = 1.0 + eps;
+      const double c = r < lo ? lo : (r > hi ? hi : r);
+      const double u = r * Ad;
+      const double v = c * Ad;
+      const double sur = (u < v || isnan(u)) ? u : v;
+      double k3 = 0.0, dk3 = 0.0;
+      if (beta != 0.0) {
+        const double d = (double)a.logp_ref[row] - logp;
+        const double ed = exp(d);
+        k3 = ed - d - 1.0;
+        dk3 = 1.0 - ed;
+      }
+      const bool cut = (Ad > 0.0 && r > hi) || (Ad < 0.0 && r < lo);
+      const double g = -Ad * r * (cut ? 0.0 : 1.0) + beta * dk3;
+      const double lam = -sur + beta * k3;
+      const double coef = -g / a.kappa;
+      a.tok_loss[row] = lam;
+      a.tok_flags[row] = (uint8_t)(((r < lo || r > hi) ? TF_OUTSIDE : 0) |
+                                   ((cut && Ad != 0.0) ? TF_CUT : 0));
+      if (a.aux_logp) a.aux_logp[row] = (float)logp;
+      if (a.aux_tok_loss) a.aux_tok_loss[row] = (float)lam;
+      sh_coef = (float)coef;
+      sh_nlse2 = (float)(lse * kLog2eD);
+      sh_dy = (float)(coef * (exp(logp) - 1.0));
+    }
+  }
+  if (kFwdOnly) return;
+  __syncthreads();
+
+  // ---- pass 2: dlogits = coef * (softmax - onehot)
+  const float coef = sh_coef;
+  const float nlse2 = sh_nlse2;
+  const float dy = sh_dy;
+  const int64_t cy = y / VEC;
+  const int ey = (int)(y - cy * VEC);
+  for (int k = 0; k < ntiles; ++k) {
+    const int64_t c0 = (int64_t)k * tile + tid;
+    if (ntiles > 1) {
+#pragma unroll
+      for (int j = 0; j < kNch; ++j) {
+        const int64_t c = c0 + (int64_t)j * kThreads;
+        if (c < nchunks) buf[j] = IO::load(in, c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kNch; ++j) {
+      const int64_t c = c0 + (int64_t)j * kThreads;
+      if (c < nchunks) {
+        float f[VEC];
+        IO::unpack(buf[j], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) f[e] = coef * fast_exp2(fmaf(f[e], kLog2e, -nlse2));
+        if (c == cy) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            if (e == ey) f[e] = dy;
+        }
+        IO::store(out, c, f);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- k_finish
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__global__ void __launch_bounds__(1024)
+k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_flags, int64_t T,
+         const uint8_t* __restrict__ row_flags, int64_t N, double kappa,
+         float* __restrict__ out_loss, int32_t* __restrict__ status,
+         int64_t* __restrict__ aux_stats) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double s = 0.0;
+  int n_out = 0, n_cut = 0, n_bad = 0, n_trunc = 0, n_noc = 0;
+  for (int64_t k = tid; k < T; k += 1024) {
+    s += tok_loss[k];
+    const uint8_t f = tok_flags[k];
+    n_out += (f & TF_OUTSIDE) ? 1 : 0;
+    n_cut += (f & TF_CUT) ? 1 : 0;
+    n_bad += (f & TF_BADTOK) ? 1 : 0;
+  }
+  for (int64_t k = tid; k < N; k += 1024) {
+    const uint8_t f = row_flags[k];
+    n_trunc += (f & RF_NOEOS) ? 1 : 0;
+    n_noc += (f & RF_NOCONTRAST) ? 1 : 0;
+  }
+  s = wave_sum_d(s);
+  n_out = wave_sum_i(n_out);
+  n_cut = wave_sum_i(n_cut);
+  n_bad = wave_sum_i(n_bad);
+  n_trunc = wave_sum_i(n_trunc);
+  n_noc = wave_sum_i(n_noc);
+  __shared__ double sh_s[16];
+  __shared__ int sh_i[5][16];
+  if (lane == 0) {
+    sh_s[wave] = s;
+    sh_i[0][wave] = n_out;
+    sh_i[1][wave] = n_cut;
+    sh_i[2][wave] = n_bad;
+    sh_i[3][wave] = n_trunc;
+    sh_i[4][wave] = n_noc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+    int64_t c[5] = {0, 0, 0, 0, 0};
+    for (int w = 0; w < 16; ++w) {
+      tot += sh_s[w];
+      for (int q = 0; q < 5; ++q) c[q] += sh_i[q][w];
+    }
+    *out_loss = (float)(tot / kappa);
+    status[0] = c[2] ? kStatusTokenRange : 0;
+    status[1] = (int32_t)c[3];
+    status[2] = (int32_t)c[4];
+    if (aux_stats) {
+      aux_stats[0] = c[4];
+      aux_stats[1] = c[3];
+      aux_stats[2] = c[0];
+      aux_stats[3] = c[1];
+    }
+  }
+}
+
+__global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int64_t n) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n) dst[k] = src[k];
+}
+
+// ------------------------------------------------------------ host helpers
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool finite_f(float x) { return x == x && x - x == 0.0f; }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? DRGRPO_OK : DRGRPO_ERR_HIP; }
+
+template <bool kFwdOnly>
+int launch_rows(const RowArgs& a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
+                hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
+  const size_t esz = dtype == DRGRPO_BF16 ? 2 : 4;
+  const bool vec = ((size_t)a.V * esz) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 &&
+                   (kFwdOnly || reinterpret_cast<uintptr_t>(a.dlogits) % 16 == 0);
+  const dim3 grid((unsigned)T), block(kThreads);
+  auto go = [&](auto kernel) {
+    if (ev_begin || ev_end)  // events stamped by the dispatch itself
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev_begin, ev_end, 0, a);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+  };
+  if (dtype == DRGRPO_BF16) {
+    if (vec)
+      go(k_rows<DRGRPO_BF16, 8, kFwdOnly>);
+    else
+      go(k_rows<DRGRPO_BF16, 1, kFwdOnly>);
+  } else {
+    if (vec)
+      go(k_rows<DRGRPO_F32, 4, kFwdOnly>);
+    else
+      go(k_rows<DRGRPO_F32, 1, kFwdOnly>);
+  }
+  return launch_status();
+}
+
+int check_shape(int64_t N, int64_t C, int64_t V, int64_t G, int64_t* T, int64_t* elems) {
+  if (N <= 0 || C <= 0 || V <= 0 || G <= 0 || N % G != 0) return DRGRPO_ERR_SHAPE;
+  if (!mul_ok(N, C, T)) return DRGRPO_ERR_SHAPE;
+  if (*T > INT32_MAX) return DRGRPO_ERR_SHAPE;  // one workgroup per token row
+  if (!mul_ok(*T, V, elems)) return DRGRPO_ERR_SHAPE;
+  int64_t bytes;
+  if (!mul_ok(*elems, 4, &bytes)) return DRGRPO_ERR_SHAPE;
+  return DRGRPO_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" size_t drgrpo_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t G) {
+  int64_t T, elems;
+  if (check_shape(N, C, V, G, &T, &elems) != DRGRPO_OK) return 0;
+  return ws_carve(nullptr, N, T, nullptr);
+}
+
+extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
+                                      const float* rewards, const float* logp_old,
+                                      const float* logp_ref, int64_t G, float eps, float beta,
+                                      float norm_const, float* out_loss, void* out_dlogits,
+                                      int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      const drgrpo_aux_t* aux) {
+  if (!logits || !tokens || !rewards || !logp_old || !out_loss || !out_dlogits)
+    return DRGRPO_ERR_NULL;
+  if (dtype != DRGRPO_F32 && dtype != DRGRPO_BF16) return DRGRPO_ERR_DTYPE;
+  int64_t T, elems;
+  const int sh = check_shape(N, C, V, G, &T, &elems);
+  if (sh != DRGRPO_OK) return sh;
+  if (!finite_f(eps) || eps < 0.0f || !finite_f(beta) || beta < 0.0f || !finite_f(norm_const) ||
+      norm_const <= 0.0f)
+    return DRGRPO_ERR_PARAM;
+  if (beta > 0.0f && !logp_ref) return DRGRPO_ERR_NULL;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < ws_carve(nullptr, N, T, nullptr))
+    return DRGRPO_ERR_WORKSPACE;
+  const size_t esz = dtype == DRGRPO_BF16 ? 2 : 4;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(logits);
+  const uintptr_t dl = reinterpret_cast<uintptr_t>(out_dlogits);
+  const uintptr_t nbytes = (uintptr_t)elems * esz;
+  if (lo != dl && lo < dl + nbytes && dl < lo + nbytes) return DRGRPO_ERR_ALIAS;
+
+  Ws ws;
+  ws_carve(workspace, N, T, &ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const drgrpo_aux_t none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr};
+  const drgrpo_aux_t& x = aux ? *aux : none;
+
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
+                     ws.len, ws.adv, ws.row_flags, x.len, x.mask, x.adv, (int32_t*)nullptr);
+  int rc = launch_status();
+  if (rc != DRGRPO_OK) return rc;
+
+  RowArgs a;
+  a.logits = logits;
+  a.dlogits = out_dlogits;
+  a.tokens = tokens;
+  a.logp_old = logp_old;
+  a.logp_ref = logp_ref;
+  a.len = ws.len;
+  a.adv = ws.adv;
+  a.C = C;
+  a.V = V;
+  a.eps = eps;
+  a.beta = beta;
+  a.kappa = (double)norm_const;
+  a.tok_loss = ws.tok_loss;
+  a.tok_flags = ws.tok_flags;
+  a.aux_logp = x.logp;
+  a.aux_tok_loss = x.tok_loss;
+  a.out_logp = nullptr;
+  rc = launch_rows<false>(a, T, dtype, st, static_cast<hipEvent_t>(x.rows_event_begin),
+                         static_cast<hipEvent_t>(x.rows_event_end));
+  if (rc != DRGRPO_OK) return rc;
+
+  hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, ws.tok_loss, ws.tok_flags, T,
+                     ws.row_flags, N, (double)norm_const, out_loss, ws.status, x.stats);
+  return launch_status();
+}
+
+extern "C" int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_id,
+                                   const float* rewards, const float* logp_old,
+                                   const float* logp_ref, int64_t G, float eps, float beta,
+                                   float norm_const, float* out_loss, void* out_dlogits,
+                                   int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return drgrpo_loss_fwd_bwd_ex(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
+                                norm_const, out_loss, out_dlogits, N, C, V, dtype, workspace,
+                                workspace_bytes, stream, nullptr);
+}
+
+extern "C" int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t C,
+                                      int64_t eos_id, int32_t* out_len, uint8_t* out_mask,
+                                      void* stream) {
+  if (!tokens || !out_len) return DRGRPO_ERR_NULL;
+  int64_t T;
+  if (N <= 0 || C <= 0 || !mul_ok(N, C, &T) || N > INT32_MAX) return DRGRPO_ERR_SHAPE;
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     tokens, C, eos_id, (const float*)nullptr, (int64_t)1, (int32_t*)nullptr,
+                     (float*)nullptr, (uint8_t*)nullptr, out_len, out_mask, (float*)nullptr,
+                     (int32_t*)nullptr);
+  return launch_status();
+}
+
+extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, float* out_adv,
+                                      int32_t* out_nocontrast, void* stream) {
+  if (!rewards || !out_adv) return DRGRPO_ERR_NULL;
+  if (N <= 0 || G <= 0 || N % G != 0 || N > INT32_MAX) return DRGRPO_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (out_nocontrast) {
+    hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(1), 0, st, out_nocontrast);
+    const int rc = launch_status();
+    if (rc != DRGRPO_OK) return rc;
+  }
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, (const int64_t*)nullptr,
+                     (int64_t)1, (int64_t)0, rewards, G, (int32_t*)nullptr, (float*)nullptr,
+                     (uint8_t*)nullptr, (int32_t*)nullptr, (uint8_t*)nullptr, out_adv,
+                     out_nocontrast);
+  return launch_status();
+}
+
+extern "C" int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_t C,
+                               int64_t V, drgrpo_dtype_t dtype, float* out_logp, void* stream) {
+  if (!logits || !tokens || !out_logp) return DRGRPO_ERR_NULL;
+  if (dtype != DRGRPO_F32 && dtype != DRGRPO_BF16) return DRGRPO_ERR_DTYPE;
+  int64_t T, elems;
+  const int sh = check_shape(N, C, V, 1, &T, &elems);
+  if (sh != DRGRPO_OK) return sh;
+  RowArgs a = {};
+  a.logits = logits;
+  a.tokens = tokens;
+  a.C = C;
+  a.V = V;
+  a.kappa = 1.0;
+  a.out_logp = out_logp;
+  return launch_rows<true>(a, T, dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int drgrpo_device_status(const void* workspace, void* stream) {
+  if (!workspace) return DRGRPO_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return DRGRPO_ERR_HIP;
+  int32_t word = 0;
+  if (hipMemcpy(&word, workspace, sizeof word, hipMemcpyDeviceToHost) != hipSuccess)
+    return DRGRPO_ERR_HIP;
+  return word & kStatusTokenRange ? DRGRPO_ERR_TOKEN_RANGE : DRGRPO_OK;
+}
+
+extern "C" const char* drgrpo_status_string(int status) {
+  switch (status) {
+    case DRGRPO_OK: return "ok";
+    case DRGRPO_ERR_NULL: return "a required pointer is NULL";
+    case DRGRPO_ERR_SHAPE: return "invalid shape (N, C, V, G must be > 0, N % G == 0, sizes in range)";
+    case DRGRPO_ERR_PARAM: return "invalid parameter (eps, beta finite and >= 0; norm_const finite and > 0)";
+    case DRGRPO_ERR_DTYPE: return "unknown element type";
+    case DRGRPO_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
+    case DRGRPO_ERR_ALIAS: return "out_dlogits partially overlaps logits";
+    case DRGRPO_ERR_HIP: return "HIP launch or runtime error";
+    case DRGRPO_ERR_TOKEN_RANGE: return "a token at a mask=1 position is outside [0, V)";
+    default: return "unknown status";
+  }
+}

@@ -132,11 +132,11 @@ _add(Config(name="clip_heavy_f32", B=2, G=4, C=16, V=200, dtype="f32", logit_std
 _add(Config(name="clip_heavy_bf16", B=2, G=4, C=16, V=4096, logit_std=2.0, eos_id=3,
             tok_lo=0, tok_hi=4096, eos_rows=4, reward="graded", old_noise=0.3, ref_noise=0.2,
             beta=0.04, seed=7007))
-_add(Config(name="big_v_f32", B=1, G=2, C=3, V=200003, dtype="f32", logit_std=2.0,
-            eos_id=QWEN_EOS, tok_lo=0, tok_hi=200003, eos_rows=1, reward="tiny", p=0.5,
+_add(Config(name="big_v_f32", B=2, G=2, C=3, V=200003, dtype="f32", logit_std=2.0,
+            eos_id=QWEN_EOS, tok_lo=0, tok_hi=200003, eos_rows=2, reward="tiny", p=0.5,
             old_noise=0.05, seed=7008))
-_add(Config(name="big_v_bf16", B=1, G=2, C=3, V=262144, logit_std=2.0, eos_id=QWEN_EOS,
-            tok_lo=0, tok_hi=262144, eos_rows=1, reward="tiny", p=0.5, old_noise=0.05,
+_add(Config(name="big_v_bf16", B=2, G=2, C=3, V=262144, logit_std=2.0, eos_id=QWEN_EOS,
+            tok_lo=0, tok_hi=262144, eos_rows=2, reward="tiny", p=0.5, old_noise=0.05,
             seed=7009))
 _add(Config(name="no_eos_id", B=2, G=2, C=5, V=640, logit_std=1.0, eos_id=-1, tok_lo=0,
             tok_hi=640, eos_rows=0, reward="tiny", p=0.5, old_noise=0.05, seed=7010))

@@ -1,0 +1,111 @@
+"""Boundary tests that need no GPU: the C-ABI library loads, exports every
+symbol include/drgrpo.h declares, and rejects bad arguments before launching
+anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rl_post_loss_dr_amd as dr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "drgrpo.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(drgrpo_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dr.LIB):
+        dr.build()
+    return dr.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert "drgrpo_loss_fwd_bwd" in names and len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_workspace_bytes(L):
+    assert L.drgrpo_workspace_bytes(64, 256, 151936, 8) > 64 * 256 * 8
+    assert L.drgrpo_workspace_bytes(0, 256, 151936, 8) == 0
+    assert L.drgrpo_workspace_bytes(64, 256, 151936, 7) == 0
+    assert L.drgrpo_workspace_bytes(64, 0, 10, 8) == 0
+
+
+def test_status_strings(L):
+    for code in range(-8, 1):
+        assert dr.status_string(code)
+    assert "unknown" in dr.status_string(-99)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _call(L, **kw):
+    a = dict(logits=FAKE, tokens=FAKE, eos=0, rewards=FAKE, old=FAKE, ref=None, G=8, eps=0.2,
+             beta=0.0, kappa=2048.0, loss=FAKE, dl=FAKE * 1000000, N=64, C=256, V=151936,
+             dtype=1, ws=FAKE * 4096, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return L.drgrpo_loss_fwd_bwd(a["logits"], a["tokens"], a["eos"], a["rewards"], a["old"],
+                                 a["ref"], a["G"], a["eps"], a["beta"], a["kappa"], a["loss"],
+                                 a["dl"], a["N"], a["C"], a["V"], a["dtype"], a["ws"], a["wsb"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), dr.ERR_NULL),
+    (dict(tokens=None), dr.ERR_NULL),
+    (dict(rewards=None), dr.ERR_NULL),
+    (dict(old=None), dr.ERR_NULL),
+    (dict(loss=None), dr.ERR_NULL),
+    (dict(dl=None), dr.ERR_NULL),
+    (dict(beta=0.04, ref=None), dr.ERR_NULL),
+    (dict(N=0), dr.ERR_SHAPE),
+    (dict(C=-1), dr.ERR_SHAPE),
+    (dict(V=0), dr.ERR_SHAPE),
+    (dict(G=0), dr.ERR_SHAPE),
+    (dict(G=7), dr.ERR_SHAPE),
+    (dict(N=1 << 40, C=1 << 30), dr.ERR_SHAPE),
+    (dict(eps=-0.1), dr.ERR_PARAM),
+    (dict(eps=float("nan")), dr.ERR_PARAM),
+    (dict(beta=-1.0, ref=FAKE), dr.ERR_PARAM),
+    (dict(beta=float("inf"), ref=FAKE), dr.ERR_PARAM),
+    (dict(kappa=0.0), dr.ERR_PARAM),
+    (dict(kappa=-3.0), dr.ERR_PARAM),
+    (dict(kappa=float("inf")), dr.ERR_PARAM),
+    (dict(dtype=5), dr.ERR_DTYPE),
+    (dict(ws=None), dr.ERR_WORKSPACE),
+    (dict(wsb=16), dr.ERR_WORKSPACE),
+    (dict(ws=FAKE * 4096 + 8), dr.ERR_WORKSPACE),
+    (dict(dl=FAKE + 64), dr.ERR_ALIAS),
+])
+def test_argument_validation(L, kw, code):
+    assert _call(L, **kw) == code
+
+
+def test_other_entry_points_validate(L):
+    assert L.drgrpo_completion_mask(None, 4, 4, 0, FAKE, None, None) == dr.ERR_NULL
+    assert L.drgrpo_completion_mask(FAKE, 0, 4, 0, FAKE, None, None) == dr.ERR_SHAPE
+    assert L.drgrpo_group_advantage(FAKE, 8, 3, FAKE, None, None) == dr.ERR_SHAPE
+    assert L.drgrpo_group_advantage(None, 8, 4, FAKE, None, None) == dr.ERR_NULL
+    assert L.drgrpo_logprobs(FAKE, FAKE, 2, 2, 10, 9, FAKE, None) == dr.ERR_DTYPE
+    assert L.drgrpo_logprobs(FAKE, FAKE, 2, 0, 10, 1, FAKE, None) == dr.ERR_SHAPE
+    assert L.drgrpo_device_status(None, None) == dr.ERR_NULL
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports the oracle and has no CPU fallback."""
+    pkg = os.path.join(ROOT, "rl_post_loss_dr_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "drgrpo_oracle" not in txt, f

@@ -1,0 +1,137 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  The oracle computes every token's log-prob and loss term
+(so the scalar loss is checked exactly as at small sizes) and full gradient
+rows for a sample of token rows; properties that hold at any size are
+checked on every row (inactive rows exactly zero, each row summing to zero,
+the gathered entry equal to coef*(p_y - 1))."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import rl_post_loss_dr_amd as dr
+from _cases import compare_dlogits, compare_loss, f32, oracle_logp_all, tol
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+FULL = ["qwen_b8g8c256", "qwen_b8g16c512", "qwen_kl_b16g8c1024"]
+
+
+def _sample_rows(cfg, res, k=48):
+    coef = res.coef.reshape(-1)
+    rng = np.random.default_rng(cfg.seed)
+    act_pos = np.flatnonzero(coef > 0)
+    act_neg = np.flatnonzero(coef < 0)
+    inact = np.flatnonzero(coef == 0)
+    picks = [0, cfg.T - 1]
+    for pool, n in ((act_pos, k // 3), (act_neg, k // 3), (inact, k // 6)):
+        if pool.size:
+            picks += rng.choice(pool, size=min(n, pool.size), replace=False).tolist()
+    # rows whose surrogate gradient the clip cuts, if any
+    r = np.exp(res.logp - res_old_cache[cfg.name].astype(np.float64))
+    A = np.repeat(res.adv[:, None], cfg.C, axis=1)
+    mask = np.arange(cfg.C)[None, :] < res.len[:, None]
+    cut = np.flatnonzero(((((A > 0) & (r > 1 + f32(cfg.eps))) |
+                           ((A < 0) & (r < 1 - f32(cfg.eps)))) & mask).reshape(-1))
+    picks += cut[:4].tolist()
+    return np.unique(np.array(picks, dtype=np.int64))
+
+
+res_old_cache = {}
+
+
+class _Res:
+    pass
+
+
+@pytest.fixture(scope="module", params=FULL)
+def full(request):
+    name = request.param
+    cfg = synth.get_config(name)
+    case = synth.make_case(cfg)
+    print(f"[{name}] oracle log-probs of {cfg.T} rows x {cfg.V}", flush=True)
+    lse, logp = oracle_logp_all(case)
+    old = synth.perturb(logp, case.old_noise)
+    ref = None if case.ref_noise is None else synth.perturb(logp, case.ref_noise)
+    res_old_cache[name] = old
+    eps, beta, kappa = f32(cfg.eps), f32(cfg.beta), f32(cfg.norm_const)
+    res = _Res()
+    res.len = oracle.completion_len(case.tokens, cfg.eos_id)
+    res.adv = oracle.group_advantage(case.rewards, cfg.G)
+    res.lse, res.logp = lse, logp
+    res.lam, res.coef, res.stats = oracle.token_terms(logp, old, ref, res.adv, res.len, eps, beta,
+                                                      kappa)
+    res.loss = oracle.loss_sum(res.lam, kappa)
+    res.abs_sum = float(np.abs(res.lam).sum())
+    res.nocontrast = oracle.nocontrast_groups(case.rewards, cfg.G)
+    res.truncated = int((~(case.tokens == cfg.eos_id).any(axis=1)).sum())
+
+    print(f"[{name}] device inputs", flush=True)
+    logits = torch.empty((cfg.N, cfg.C, cfg.V), dtype=torch.bfloat16, device=DEV)
+    synth.gpu_normal_fill(logits, cfg.seed, synth.S_LOGITS, 0, cfg.logit_std)
+    tokens = torch.from_numpy(case.tokens).to(DEV)
+    aux = {}
+    loss, d = dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, torch.from_numpy(case.rewards).to(DEV),
+                              torch.from_numpy(old).to(DEV),
+                              None if ref is None else torch.from_numpy(ref).to(DEV), G=cfg.G,
+                              eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const, aux=aux)
+    torch.cuda.synchronize()
+    print(f"[{name}] gpu loss {float(loss.item())!r} oracle {res.loss!r}", flush=True)
+    yield cfg, case, res, logits, float(loss.item()), d, aux
+    del logits, d
+    torch.cuda.empty_cache()
+
+
+def test_full_integer_outputs(full):
+    cfg, case, res, logits, loss, d, aux = full
+    assert np.array_equal(aux["len"].cpu().numpy(), res.len)
+    assert np.array_equal(aux["adv"].cpu().numpy().view(np.uint32), res.adv.view(np.uint32))
+    st = aux["stats"].cpu().numpy()
+    assert st[0] == res.nocontrast and st[1] == res.truncated
+    # ratio-outside / clip-cut counts may differ only by tokens on a boundary
+    assert abs(int(st[2]) - int(res.stats[0])) <= 2 and abs(int(st[3]) - int(res.stats[1])) <= 2
+
+
+def test_full_loss(full):
+    cfg, case, res, logits, loss, d, aux = full
+    compare_loss(cfg, loss, res)
+
+
+def test_full_sampled_rows(full):
+    cfg, case, res, logits, loss, d, aux = full
+    rows = _sample_rows(cfg, res)
+    x = case.logits_rows(rows)
+    # the device generator wrote the same inputs the host regenerates
+    got_x = logits.view(-1, cfg.V)[torch.from_numpy(rows).to(DEV)].view(torch.int16).cpu().numpy()
+    assert np.array_equal(got_x.view(np.uint16), x)
+    want = oracle.dlogits_rows(x, case.tokens.reshape(-1)[rows], res.lse.reshape(-1)[rows],
+                               res.coef.reshape(-1)[rows])
+    got = d.view(-1, cfg.V)[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    compare_dlogits(cfg, got, want)
+
+
+def test_full_row_properties(full):
+    """Every row: inactive rows are exactly zero; active rows sum to zero within
+    bf16 rounding and hold coef*(p_y - 1) at the sampled token."""
+    cfg, case, res, logits, loss, d, aux = full
+    coef = torch.from_numpy(res.coef.reshape(-1)).to(DEV)
+    p_y = torch.from_numpy(np.exp(res.logp.reshape(-1))).to(DEV)
+    tok = torch.from_numpy(case.tokens.reshape(-1)).to(DEV)
+    D = d.view(-1, cfg.V)
+    step = 2048
+    for r0 in range(0, cfg.T, step):
+        blk = D[r0:r0 + step].float()
+        c = coef[r0:r0 + step]
+        inactive = c == 0
+        assert float(blk[inactive].abs().max()) == 0.0 if bool(inactive.any()) else True
+        act = ~inactive
+        if bool(act.any()):
+            s = blk[act].double().sum(dim=1)
+            bound = 2.0 ** -7 * 2 * c[act].abs() + 1e-12
+            assert bool((s.abs() <= bound).all()), float((s.abs() / bound).max())
+            dy = blk[act].gather(1, tok[r0:r0 + step][act][:, None])[:, 0].double()
+            want = c[act] * (p_y[r0:r0 + step][act] - 1)
+            assert bool(((dy - want).abs() <= 2.0 ** -7 * want.abs() + 1e-12).all())
+    assert tol(cfg)
