@@ -77,6 +77,10 @@ size_t ws_carve(void* base, int64_t N, int64_t T, Ws* ws) {
 }
 
 // ----------------------------------------------------------------- element IO
+// Row data moves in 16-byte chunks (bf16 x 8 or f32 x 4) with nontemporal
+// loads and stores: every byte is touched once, so nothing is kept in cache.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   const __bf16 ha = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
   const __bf16 hb = (__bf16)b;
@@ -93,10 +97,10 @@ struct Io;
 // bfloat16, 8 per 16-byte chunk
 template <>
 struct Io<DRGRPO_BF16, 8> {
-  using chunk = uint4;
+  using chunk = u32x4;
   static constexpr int kBytes = 2;
-  __device__ static chunk load(const char* row, int64_t c) {
-    return reinterpret_cast<const uint4*>(row)[c];
+  __device__ static chunk load(const char* row, uint32_t c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + c);
   }
   __device__ static void unpack(const chunk& v, float (&f)[8]) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
@@ -104,45 +108,43 @@ struct Io<DRGRPO_BF16, 8> {
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
     f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
   }
-  __device__ static void store(char* row, int64_t c, const float (&f)[8]) {
-    uint4 o;
-    o.x = pack_bf16x2(f[0], f[1]);
-    o.y = pack_bf16x2(f[2], f[3]);
-    o.z = pack_bf16x2(f[4], f[5]);
-    o.w = pack_bf16x2(f[6], f[7]);
-    reinterpret_cast<uint4*>(row)[c] = o;
+  // `sign` (0 or all ones) flips the sign bit of every stored value
+  __device__ static void store(char* row, uint32_t c, const float (&f)[8], uint32_t sign = 0) {
+    const uint32_t m = sign & 0x80008000u;
+    u32x4 o;
+    o.x = pack_bf16x2(f[0], f[1]) ^ m;
+    o.y = pack_bf16x2(f[2], f[3]) ^ m;
+    o.z = pack_bf16x2(f[4], f[5]) ^ m;
+    o.w = pack_bf16x2(f[6], f[7]) ^ m;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(row) + c);
   }
-  __device__ static void fill(char* row, int64_t c, float val) {
+  __device__ static void fill(char* row, uint32_t c, float val) {
     const uint32_t w = pack_bf16x2(val, val);
-    reinterpret_cast<uint4*>(row)[c] = make_uint4(w, w, w, w);
-  }
-  __device__ static float elem(const char* row, int64_t v) {
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[v] << 16);
+    __builtin_nontemporal_store(u32x4{w, w, w, w}, reinterpret_cast<u32x4*>(row) + c);
   }
 };
 
 // binary32, 4 per 16-byte chunk
 template <>
 struct Io<DRGRPO_F32, 4> {
-  using chunk = uint4;
+  using chunk = u32x4;
   static constexpr int kBytes = 4;
-  __device__ static chunk load(const char* row, int64_t c) {
-    return reinterpret_cast<const uint4*>(row)[c];
+  __device__ static chunk load(const char* row, uint32_t c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + c);
   }
   __device__ static void unpack(const chunk& v, float (&f)[4]) {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
-  __device__ static void store(char* row, int64_t c, const float (&f)[4]) {
-    reinterpret_cast<uint4*>(row)[c] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
-                                                  __float_as_uint(f[2]), __float_as_uint(f[3]));
+  __device__ static void store(char* row, uint32_t c, const float (&f)[4], uint32_t sign = 0) {
+    const uint32_t m = sign & 0x80000000u;
+    const u32x4 o{__float_as_uint(f[0]) ^ m, __float_as_uint(f[1]) ^ m,
+                  __float_as_uint(f[2]) ^ m, __float_as_uint(f[3]) ^ m};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(row) + c);
   }
-  __device__ static void fill(char* row, int64_t c, float val) {
+  __device__ static void fill(char* row, uint32_t c, float val) {
     const uint32_t w = __float_as_uint(val);
-    reinterpret_cast<uint4*>(row)[c] = make_uint4(w, w, w, w);
-  }
-  __device__ static float elem(const char* row, int64_t v) {
-    return reinterpret_cast<const float*>(row)[v];
+    __builtin_nontemporal_store(u32x4{w, w, w, w}, reinterpret_cast<u32x4*>(row) + c);
   }
 };
 
@@ -151,22 +153,21 @@ template <>
 struct Io<DRGRPO_BF16, 1> {
   using chunk = uint16_t;
   static constexpr int kBytes = 2;
-  __device__ static chunk load(const char* row, int64_t c) {
-    return reinterpret_cast<const uint16_t*>(row)[c];
+  __device__ static chunk load(const char* row, uint32_t c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(row) + c);
   }
   __device__ static void unpack(const chunk& v, float (&f)[1]) {
     f[0] = __uint_as_float((uint32_t)v << 16);
   }
-  __device__ static void store(char* row, int64_t c, const float (&f)[1]) {
+  __device__ static void store(char* row, uint32_t c, const float (&f)[1], uint32_t sign = 0) {
     const __bf16 h = (__bf16)f[0];
-    reinterpret_cast<uint16_t*>(row)[c] = __builtin_bit_cast(uint16_t, h);
+    __builtin_nontemporal_store((uint16_t)(__builtin_bit_cast(uint16_t, h) ^ (sign & 0x8000u)),
+                                reinterpret_cast<uint16_t*>(row) + c);
   }
-  __device__ static void fill(char* row, int64_t c, float val) {
+  __device__ static void fill(char* row, uint32_t c, float val) {
     const __bf16 h = (__bf16)val;
-    reinterpret_cast<uint16_t*>(row)[c] = __builtin_bit_cast(uint16_t, h);
-  }
-  __device__ static float elem(const char* row, int64_t v) {
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[v] << 16);
+    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, h),
+                                reinterpret_cast<uint16_t*>(row) + c);
   }
 };
 
@@ -175,18 +176,16 @@ template <>
 struct Io<DRGRPO_F32, 1> {
   using chunk = float;
   static constexpr int kBytes = 4;
-  __device__ static chunk load(const char* row, int64_t c) {
-    return reinterpret_cast<const float*>(row)[c];
+  __device__ static chunk load(const char* row, uint32_t c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const float*>(row) + c);
   }
   __device__ static void unpack(const chunk& v, float (&f)[1]) { f[0] = v; }
-  __device__ static void store(char* row, int64_t c, const float (&f)[1]) {
-    reinterpret_cast<float*>(row)[c] = f[0];
+  __device__ static void store(char* row, uint32_t c, const float (&f)[1], uint32_t sign = 0) {
+    __builtin_nontemporal_store(__uint_as_float(__float_as_uint(f[0]) ^ (sign & 0x80000000u)),
+                                reinterpret_cast<float*>(row) + c);
   }
-  __device__ static void fill(char* row, int64_t c, float val) {
-    reinterpret_cast<float*>(row)[c] = val;
-  }
-  __device__ static float elem(const char* row, int64_t v) {
-    return reinterpret_cast<const float*>(row)[v];
+  __device__ static void fill(char* row, uint32_t c, float val) {
+    __builtin_nontemporal_store(val, reinterpret_cast<float*>(row) + c);
   }
 };
 
@@ -274,19 +273,88 @@ struct RowArgs {
   float* aux_logp;
   float* aux_tok_loss;
   float* out_logp;  // forward-only mode: log-prob of every token
+  uint32_t row_stride;  // workgroup b handles row (b * row_stride) mod T; gcd(row_stride, T) = 1
+  uint32_t T;
 };
 
+// Merge one chunk of values into a lane's running (max, sum of exp(x - max)).
+template <int VEC>
+__device__ inline void lse_chunk(float& m, float& s, const float (&f)[VEC]) {
+  float cm = f[0];
+#pragma unroll
+  for (int e = 1; e < VEC; ++e) cm = fmaxf(cm, f[e]);
+  const float nm = fmaxf(m, cm);
+  const float base = nm == -INFINITY ? 0.0f : nm;  // nothing finite seen yet
+  const float b2 = base * kLog2e;
+  float cs = 0.0f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) cs += fast_exp2(fmaf(f[e], kLog2e, -b2));
+  s = s * fast_exp2((m - base) * kLog2e) + cs;
+  m = nm;
+}
+
+// Pass 2 of a row: dlogits = coef * (softmax - onehot), with |coef| folded
+// into the exponent (|coef| * exp(x - lse) = exp2(x*log2e - off2)) and the
+// sign of coef applied to the packed result bits.
+template <typename IO, int VEC>
+__device__ __attribute__((always_inline)) inline void write_dlogits(
+    typename IO::chunk (&buf)[kNch], const char* in, char* out, uint32_t nchunks,
+    uint32_t ntiles, int tid, float off2, float dy, bool neg, int64_t y) {
+  const uint32_t tile = (uint32_t)kNch * kThreads;
+  const uint32_t last = nchunks - 1;
+  const uint32_t cy = (uint32_t)(y / VEC);
+  const int ey = (int)(y - (int64_t)cy * VEC);
+  const float dy_pre = neg ? -dy : dy;  // the sign flip below restores it
+  const uint32_t sign = neg ? 0xFFFFFFFFu : 0u;
+  for (uint32_t k = 0; k < ntiles; ++k) {
+    const uint32_t tb = k * tile;
+    if (ntiles > 1) {
+#pragma unroll
+      for (int j = 0; j < kNch; ++j) {
+        const uint32_t c = tb + (uint32_t)j * kThreads + tid;
+        buf[j] = IO::load(in, c < nchunks ? c : last);
+      }
+    }
+    // slot and lane holding the sampled token's chunk in this tile
+    const bool here = cy >= tb && cy - tb < tile;
+    const int js = here ? (int)((cy - tb) / kThreads) : -1;
+    const int owner = here ? (int)((cy - tb) % kThreads) : -1;
+#pragma unroll
+    for (int j = 0; j < kNch; ++j) {
+      const uint32_t sb = tb + (uint32_t)j * kThreads;
+      if (sb < nchunks) {
+        float f[VEC];
+        IO::unpack(buf[j], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) f[e] = fast_exp2(fmaf(f[e], kLog2e, -off2));
+        if (j == js && tid == owner) {  // the sampled token: coef * (p_y - 1)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) f[e] = e == ey ? dy_pre : f[e];
+        }
+        if (sb + kThreads <= nchunks || sb + tid < nchunks) IO::store(out, sb + tid, f, sign);
+      }
+    }
+  }
+}
+
+// One workgroup per token row.  Every lane issues all of its kNch 16-byte
+// loads of a tile before touching any of them (tail lanes re-read the last
+// chunk and mask it), so a row's 297 KB are in flight at once; each chunk is
+// merged into the lane's running (max, sum) as it arrives.
 template <int DT, int VEC, bool kFwdOnly>
 __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
   using IO = Io<DT, VEC>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t row = blockIdx.x;
+  // consecutive workgroups take rows far apart, so the workgroups in flight
+  // mix rows of every reward group (active rows and zero rows interleave)
+  const int64_t row = (int64_t)(((uint64_t)blockIdx.x * a.row_stride) % a.T);
   const int64_t i = row / a.C;
   const int64_t t = row - i * a.C;
   const int64_t V = a.V;
-  const int64_t nchunks = V / VEC;
+  const uint32_t nchunks = (uint32_t)(V / VEC);  // < 2^31 (checked on the host)
+  const uint32_t last = nchunks - 1;
   const char* in = static_cast<const char*>(a.logits) + row * V * IO::kBytes;
   char* out = kFwdOnly ? nullptr : static_cast<char*>(a.dlogits) + row * V * IO::kBytes;
   const int64_t y = a.tokens[row];
@@ -306,7 +374,7 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
       return;
     }
     const float fillv = bad ? NAN : 0.0f;
-    for (int64_t c = tid; c < nchunks; c += kThreads) IO::fill(out, c, fillv);
+    for (uint32_t c = tid; c < nchunks; c += kThreads) IO::fill(out, c, fillv);
     if (tid == 0) {
       a.tok_loss[row] = bad ? (double)NAN : 0.0;
       a.tok_flags[row] = bad ? TF_BADTOK : 0;
@@ -316,48 +384,39 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
     return;
   }
 
+  // the sampled token's logit and the per-token inputs, fetched early by the
+  // wavefront that evaluates the epilogue (read before any store of the row)
+  // (every wavefront issues the same few loads: no divergent branch, so the
+  // compiler need not drain the load counter before the row loads)
+  const typename IO::chunk xy_chunk = IO::load(in, (uint32_t)(y / VEC));
+  const float old = kFwdOnly ? 0.0f : a.logp_old[row];
+  const float ref = (!kFwdOnly && a.beta != 0.0f) ? a.logp_ref[row] : 0.0f;
+
   // ---- pass 1: running max / sum of exp per lane over register tiles
   typename IO::chunk buf[kNch];
-  const int64_t tile = (int64_t)kNch * kThreads;
-  const int ntiles = (int)((nchunks + tile - 1) / tile);
+  const uint32_t tile = (uint32_t)kNch * kThreads;
+  const uint32_t ntiles = (nchunks + tile - 1) / tile;
   float m = -INFINITY;
   float s = 0.0f;
-  for (int k = 0; k < ntiles; ++k) {
-    const int64_t c0 = (int64_t)k * tile + tid;
+  for (uint32_t k = 0; k < ntiles; ++k) {
+    const uint32_t tb = k * tile;
 #pragma unroll
     for (int j = 0; j < kNch; ++j) {
-      const int64_t c = c0 + (int64_t)j * kThreads;
-      if (c < nchunks) buf[j] = IO::load(in, c);
+      const uint32_t c = tb + (uint32_t)j * kThreads + tid;
+      buf[j] = IO::load(in, c < nchunks ? c : last);
     }
-    float tm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kNch; ++j) {
-      const int64_t c = c0 + (int64_t)j * kThreads;
-      if (c < nchunks) {
+      const uint32_t sb = tb + (uint32_t)j * kThreads;  // first chunk of the slot (uniform)
+      if (sb < nchunks) {
         float f[VEC];
         IO::unpack(buf[j], f);
+        if (sb + kThreads > nchunks && sb + tid >= nchunks) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) tm = fmaxf(tm, f[e]);
-      }
-    }
-    const float nm = fmaxf(m, tm);
-    if (nm != -INFINITY) {
-      const float nm2 = nm * kLog2e;
-      float ts = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kNch; ++j) {
-        const int64_t c = c0 + (int64_t)j * kThreads;
-        if (c < nchunks) {
-          float f[VEC];
-          IO::unpack(buf[j], f);
-          float cs = 0.0f;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) cs += fast_exp2(fmaf(f[e], kLog2e, -nm2));
-          ts += cs;
+          for (int e = 0; e < VEC; ++e) f[e] = -INFINITY;
         }
+        lse_chunk<VEC>(m, s, f);
       }
-      s = s * fast_exp2((m - nm) * kLog2e) + ts;
-      m = nm;
     }
   }
   // wavefront merge (fixed butterfly order)
@@ -369,7 +428,8 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
   }
   __shared__ float sh_m[kWaves];
   __shared__ float sh_s[kWaves];
-  __shared__ float sh_coef, sh_nlse2, sh_dy;
+  __shared__ float sh_coef, sh_off2, sh_dy;
+  __shared__ bool sh_neg;
   if (lane == 0) {
     sh_m[wave] = m;
     sh_s[wave] = s;
@@ -388,14 +448,23 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) term += __shfl_xor(term, off);
     const double lse = (double)M + log(term);
-    const double logp = (double)IO::elem(in, y) - lse;
+    float xy;
+    {
+      float f[VEC];
+      IO::unpack(xy_chunk, f);
+      const int ey = (int)(y % VEC);
+      xy = f[0];
+#pragma unroll
+      for (int e = 1; e < VEC; ++e) xy = e == ey ? f[e] : xy;
+    }
+    const double logp = (double)xy - lse;
     if (kFwdOnly) {
       if (lane == 0) a.out_logp[row] = (float)logp;
     } else if (lane == 0) {
       const double Ad = (double)A;
       const double eps = (double)a.eps;
       const double beta = (double)a.beta;
-      const double r = exp(logp - (double)a.logp_old[row]);
+      const double r = exp(logp - (double)old);
       const double lo = 1.0 - eps, hi = 1.0 + eps;
       const double c = r < lo ? lo : (r > hi ? hi : r);
       const double u = r * Ad;
@@ -403,7 +472,7 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
       const double sur = (u < v || isnan(u)) ? u : v;
       double k3 = 0.0, dk3 = 0.0;
       if (beta != 0.0) {
-        const double d = (double)a.logp_ref[row] - logp;
+        const double d = (double)ref - logp;
         const double ed = exp(d);
         k3 = ed - d - 1.0;
         dk3 = 1.0 - ed;
@@ -418,7 +487,8 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
       if (a.aux_logp) a.aux_logp[row] = (float)logp;
       if (a.aux_tok_loss) a.aux_tok_loss[row] = (float)lam;
       sh_coef = (float)coef;
-      sh_nlse2 = (float)(lse * kLog2eD);
+      sh_neg = coef < 0.0;
+      sh_off2 = (float)(lse * kLog2eD - log2(fabs(coef)));
       sh_dy = (float)(coef * (exp(logp) - 1.0));
     }
   }
@@ -427,36 +497,11 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
 
   // ---- pass 2: dlogits = coef * (softmax - onehot)
   const float coef = sh_coef;
-  const float nlse2 = sh_nlse2;
-  const float dy = sh_dy;
-  const int64_t cy = y / VEC;
-  const int ey = (int)(y - cy * VEC);
-  for (int k = 0; k < ntiles; ++k) {
-    const int64_t c0 = (int64_t)k * tile + tid;
-    if (ntiles > 1) {
-#pragma unroll
-      for (int j = 0; j < kNch; ++j) {
-        const int64_t c = c0 + (int64_t)j * kThreads;
-        if (c < nchunks) buf[j] = IO::load(in, c);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kNch; ++j) {
-      const int64_t c = c0 + (int64_t)j * kThreads;
-      if (c < nchunks) {
-        float f[VEC];
-        IO::unpack(buf[j], f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) f[e] = coef * fast_exp2(fmaf(f[e], kLog2e, -nlse2));
-        if (c == cy) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if (e == ey) f[e] = dy;
-        }
-        IO::store(out, c, f);
-      }
-    }
+  if (coef == 0.0f) {  // the clip cut the only gradient term: an exact zero row
+    for (uint32_t c = tid; c < nchunks; c += kThreads) IO::fill(out, c, 0.0f);
+    return;
   }
+  write_dlogits<IO, VEC>(buf, in, out, nchunks, ntiles, tid, sh_off2, sh_dy, sh_neg, y);
 }
 
 // ----------------------------------------------------------------- k_finish
@@ -545,9 +590,28 @@ bool finite_f(float x) { return x == x && x - x == 0.0f; }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? DRGRPO_OK : DRGRPO_ERR_HIP; }
 
+uint64_t gcd_u64(uint64_t a, uint64_t b) {
+  while (b) {
+    const uint64_t r = a % b;
+    a = b;
+    b = r;
+  }
+  return a;
+}
+
+// A stride coprime with T of about T/256: the ~256 workgroups in flight at
+// once then cover the whole batch.
+uint32_t row_stride_for(int64_t T) {
+  uint64_t s = (uint64_t)T / 256 + 1;
+  while (gcd_u64(s, (uint64_t)T) != 1) ++s;
+  return (uint32_t)s;
+}
+
 template <bool kFwdOnly>
-int launch_rows(const RowArgs& a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
+int launch_rows(RowArgs a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
                 hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
+  a.T = (uint32_t)T;
+  a.row_stride = row_stride_for(T);
   const size_t esz = dtype == DRGRPO_BF16 ? 2 : 4;
   const bool vec = ((size_t)a.V * esz) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 &&
@@ -575,6 +639,7 @@ int launch_rows(const RowArgs& a, int64_t T, drgrpo_dtype_t dtype, hipStream_t s
 
 int check_shape(int64_t N, int64_t C, int64_t V, int64_t G, int64_t* T, int64_t* elems) {
   if (N <= 0 || C <= 0 || V <= 0 || G <= 0 || N % G != 0) return DRGRPO_ERR_SHAPE;
+  if (V > (int64_t(1) << 28)) return DRGRPO_ERR_SHAPE;  // per-row offsets are 32-bit
   if (!mul_ok(N, C, T)) return DRGRPO_ERR_SHAPE;
   if (*T > INT32_MAX) return DRGRPO_ERR_SHAPE;  // one workgroup per token row
   if (!mul_ok(*T, V, elems)) return DRGRPO_ERR_SHAPE;
