@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen_b8g8c256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 4 GiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -136,6 +138,18 @@ def main():
 
     import synth
     import rl_post_loss_dr_amd as dr
+
+    if args.calibrate_copy:
+        # a plain copy kernel of known size: 4 GiB read + 4 GiB written per call
+        n = 1 << 31
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 2 * n, "calibrate_copy_bytes_written": 2 * n,
+                          "calls": 3}), flush=True)
+        return
 
     cfg = synth.get_config(args.workload)
     case = synth.make_case(cfg)
