@@ -147,6 +147,32 @@ int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, float* ou
 int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_t C, int64_t V,
                     drgrpo_dtype_t dtype, float* out_logp, void* stream);
 
+/* Fused lm_head variant: the same loss with logits = hidden . W^T computed
+ * on the fly ("compute_logprobs" of "Making Dr GRPO go brrr": the model's
+ * final projection feeds the log-softmax), never stored as a [N*C, V] tensor.
+ *
+ *   hidden      [N*C, H] bfloat16: the policy's final hidden state at the
+ *               position that scores completion token t (row i*C + t).
+ *   W           [V, H] bfloat16 unembedding (lm_head weight).
+ *   out_dhidden [N*C, H] bfloat16 = dL/dhidden = dlogits . W (zero rows for
+ *               tokens without gradient; NaN rows for a bad token id).
+ *   out_dW      [V, H] bfloat16 = dL/dW = dlogits^T . hidden.
+ *   H must be a multiple of 32 and V of 8; hidden, W and the outputs
+ *   16-byte aligned (else DRGRPO_ERR_ALIAS).  Other arguments as for
+ *   drgrpo_loss_fwd_bwd.  Logits accumulate in binary32 on the matrix cores;
+ *   dlogits enter the two gradient products rounded to bfloat16, one
+ *   vocabulary chunk at a time.
+ * The workspace (drgrpo_lmhead_workspace_bytes) holds transposed copies of W
+ * and of the active tokens' hidden rows and one chunk of dlogits. */
+size_t drgrpo_lmhead_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G);
+
+int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,
+                               int64_t eos_id, const float* rewards, const float* logp_old,
+                               const float* logp_ref, int64_t G, float eps, float beta,
+                               float norm_const, float* out_loss, void* out_dhidden,
+                               void* out_dW, int64_t N, int64_t C, int64_t V, int64_t H,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then reads the status word the last
  * drgrpo_loss_fwd_bwd call on `workspace` left: DRGRPO_OK or
  * DRGRPO_ERR_TOKEN_RANGE (DRGRPO_ERR_HIP if the read fails). */

@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.drgrpo_group_advantage.restype = _I
         L.drgrpo_logprobs.argtypes = [_P, _P, _I64, _I64, _I64, _I, _P, _P]
         L.drgrpo_logprobs.restype = _I
+        L.drgrpo_lmhead_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64]
+        L.drgrpo_lmhead_workspace_bytes.restype = _SZ
+        L.drgrpo_lmhead_loss_fwd_bwd.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _I64, _F, _F, _F,
+                                                 _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]
+        L.drgrpo_lmhead_loss_fwd_bwd.restype = _I
         L.drgrpo_device_status.argtypes = [_P, _P]
         L.drgrpo_device_status.restype = _I
         L.drgrpo_status_string.argtypes = [_I]
@@ -224,6 +229,56 @@ def device_status(workspace: torch.Tensor) -> int:
     """Synchronises the current stream and returns the status word of the last
     loss call that used `workspace` (OK or ERR_TOKEN_RANGE)."""
     return int(lib().drgrpo_device_status(workspace.data_ptr(), _stream(workspace.device)))
+
+
+def lmhead_workspace_bytes(N: int, C: int, V: int, H: int, G: int) -> int:
+    return int(lib().drgrpo_lmhead_workspace_bytes(N, C, V, H, G))
+
+
+def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Tensor, eos_id: int,
+                        rewards: torch.Tensor, logp_old: torch.Tensor,
+                        logp_ref: torch.Tensor | None = None, *, G: int, eps: float = 0.2,
+                        beta: float = 0.0, norm_const: float | None = None,
+                        out_dhidden: torch.Tensor | None = None,
+                        out_dW: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None):
+    """Fused lm_head variant: logits = hidden . W^T are never stored.
+
+    hidden [N*C, H] (or [N, C, H]) bfloat16, W [V, H] bfloat16, tokens [N, C]
+    int64.  Returns (loss [] float32, dhidden like hidden, dW like W).
+    """
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [N, C]")
+    N, C = tokens.shape
+    V, H = W.shape
+    _dev(W, "W", torch.bfloat16)
+    _dev(hidden, "hidden", torch.bfloat16)
+    if hidden.numel() != N * C * H:
+        raise ValueError(f"hidden must hold N*C rows of H={H}")
+    dev = hidden.device
+    _dev(tokens, "tokens", torch.int64)
+    _dev(rewards, "rewards", torch.float32, (N,))
+    _dev(logp_old, "logp_old", torch.float32, (N, C))
+    if logp_ref is not None:
+        _dev(logp_ref, "logp_ref", torch.float32, (N, C))
+    if norm_const is None:
+        norm_const = float(G * C)
+    if out_dhidden is None:
+        out_dhidden = torch.empty_like(hidden)
+    if out_dW is None:
+        out_dW = torch.empty_like(W)
+    if workspace is None:
+        n = lmhead_workspace_bytes(N, C, V, H, G)
+        if n == 0:
+            raise DrGRPOError(ERR_SHAPE, "drgrpo_lmhead_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    _check(lib().drgrpo_lmhead_loss_fwd_bwd(
+        hidden.data_ptr(), W.data_ptr(), tokens.data_ptr(), int(eos_id), rewards.data_ptr(),
+        logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta), float(norm_const),
+        loss.data_ptr(), out_dhidden.data_ptr(), out_dW.data_ptr(), N, C, V, H,
+        workspace.data_ptr(), workspace.numel(), _stream(dev)), "drgrpo_lmhead_loss_fwd_bwd")
+    return loss, out_dhidden, out_dW
 
 
 class DrGRPOLoss(torch.autograd.Function):

@@ -1,0 +1,673 @@
+/*
+ * lmhead.hip - fused lm_head variant of the Dr. GRPO loss for gfx950: the
+ * policy's last hidden states and the unembedding W go in, the loss, dhidden
+ * and dW come out; the [tokens, V] logits are never stored.
+ *
+ * Definitions are those of include/drgrpo.h with logits = hidden . W^T.
+ * Only "active" tokens (counted, with a non-zero advantage or beta > 0)
+ * have a non-zero gradient; they are compacted first and every GEMM runs over
+ * them alone.  All products are C = A . B^T with both operands stored with
+ * the reduction dimension contiguous ("NT"), computed by one MFMA kernel
+ * (v_mfma_f32_16x16x32_bf16, binary32 accumulation) with four epilogues:
+ *
+ *   GM_LSE    logits tile of H_a . W^T -> per-token (max, sum exp) over the
+ *             tile's vocabulary columns, plus the sampled token's logit
+ *   GM_D      logits tile recomputed for one vocabulary chunk ->
+ *             dlogits = coef*(softmax - onehot) in bfloat16, stored for the
+ *             chunk only, row-major and transposed
+ *   GM_ACC    dhidden += dlogits_chunk . W_chunk   (binary32 accumulator)
+ *   GM_STORE  dW_chunk = dlogits_chunk^T . H_a     (bfloat16 result)
+ *
+ * Transposed copies of W and of the compacted hidden states give every
+ * product its reduction dimension contiguous.  No floating-point atomics:
+ * results are bitwise reproducible.
+ */
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "drgrpo.h"
+#include "common.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int GBM = 256;                   // workgroup tile rows (A rows)
+constexpr int GBN = 128;                   // workgroup tile columns (B rows)
+constexpr int GBK = 32;                    // reduction depth per step: one MFMA
+constexpr int GT = 256;                    // 4 wavefronts as 2 (rows) x 2 (columns)
+constexpr int WM = 128, WN = 64;           // wavefront tile
+constexpr int FM = WM / 16, FN = WN / 16;  // 8 x 4 MFMA blocks per wavefront
+constexpr int kChunkV = 16384;             // vocabulary columns per backward chunk
+constexpr float kL2E = 1.4426950408889634f;
+constexpr double kL2ED = 1.4426950408889634074;
+
+enum { GM_LSE = 0, GM_D = 1, GM_ACC = 2, GM_STORE = 3 };
+
+struct GemmArgs {
+  const uint16_t* A;  // [M, K] bfloat16, row stride lda
+  const uint16_t* B;  // [N, K] bfloat16, row stride ldb
+  int64_t lda, ldb;
+  int64_t M, N, K;    // static bounds (grid); K a multiple of 8
+  const int32_t* M_dev;  // if set: M = *M_dev (active-token count)
+  const int32_t* K_dev;  // if set: K = *K_dev (padded active-token count)
+  // GM_LSE
+  float2* part;          // [rows, ntn] per-token (max, sum exp) of each column tile
+  int64_t ntn;
+  float* xy;             // [rows] sampled token's logit
+  const int32_t* ycol;   // [rows] sampled token id
+  int64_t col_base;      // vocabulary id of column 0 (GM_LSE, GM_D)
+  // GM_D
+  const float* lse2;     // [rows] lse * log2(e)
+  const float* coef;     // [rows]
+  uint16_t* D;           // [Mpad, ldd] chunk of dlogits, row-major
+  int64_t ldd;
+  uint16_t* Dt;          // [N, ldt] the same chunk transposed
+  int64_t ldt;
+  // GM_ACC / GM_STORE
+  float* Cf;             // [M, ldc] binary32 accumulator
+  uint16_t* Cb;          // [M, ldc] bfloat16 result
+  int64_t ldc;
+  int accumulate;        // GM_ACC: add to Cf (else overwrite)
+};
+
+__device__ inline uint16_t bf16_bits(float x) {
+  const __bf16 h = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// max / sum over the 16 lanes of a DPP row (lanes sharing l / 16)
+__device__ inline float row16_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
+  return v;
+}
+__device__ inline float row16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 16);
+  return v;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GBN * GBK];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t M = g.M_dev ? (int64_t)*g.M_dev : g.M;
+  const int64_t K = g.K_dev ? (int64_t)*g.K_dev : g.K;
+  // row tiles vary fastest: workgroups resident together share a B tile
+  const int64_t ntm = (g.M + GBM - 1) / GBM;
+  const int64_t tm = blockIdx.x % ntm;
+  const int64_t tn = blockIdx.x / ntm;
+  const int64_t m0 = tm * GBM;
+  const int64_t n0 = tn * GBN;
+  if (m0 >= M) {
+    // GM_STORE writes every (static) row; the others have nothing to do
+    if (MODE != GM_STORE) return;
+  }
+
+  // global -> LDS: A tile 256 x 32 (4 x 16 B per thread), B tile 128 x 32 (2 per thread)
+  u32x4 ra[4], rb[2];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int q = tid + GT * p;
+      const int64_t row = m0 + (q >> 2);
+      const int64_t k = k0 + 8 * (q & 3);
+      const int64_t rc = row < M ? row : (M > 0 ? M - 1 : 0);
+      ra[p] = (k < K && M > 0)
+                  ? *reinterpret_cast<const u32x4*>(g.A + rc * g.lda + k)
+                  : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int q = tid + GT * p;
+      const int64_t row = n0 + (q >> 2);
+      const int64_t k = k0 + 8 * (q & 3);
+      const int64_t rc = row < g.N ? row : g.N - 1;
+      rb[p] = k < K ? *reinterpret_cast<const u32x4*>(g.B + rc * g.ldb + k)
+                    : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<u32x4*>(&As[buf][(tid + GT * p) * 8]) = ra[p];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      *reinterpret_cast<u32x4*>(&Bs[buf][(tid + GT * p) * 8]) = rb[p];
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nk = (K + GBK - 1) / GBK;
+  if (nk > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  const int fr = lane & 15;        // row (A) / column (B) within a 16 x 16 block
+  const int fk = 8 * (lane >> 4);  // first of the lane's 8 reduction indices
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt & 1);
+    if (kt + 1 < nk) gload((kt + 1) * GBK);
+    bf16x8 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * WM + i * 16 + fr) * GBK + fk]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn * WN + j * 16 + fr) * GBK + fk]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    if (kt + 1 < nk) swrite(cur ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator layout: acc[i][j][r] = C[m0 + wm*WM + i*16 + 4*(lane/16) + r]
+  //                                    [n0 + wn*WN + j*16 + lane%16]
+  const int rq = 4 * (lane >> 4);
+
+  if constexpr (MODE == GM_LSE) {
+    __shared__ float2 red[2][GBM];
+    __shared__ int32_t ys[GBM];
+    for (int r = tid; r < GBM; r += GT) {
+      const int64_t row = m0 + r;
+      ys[r] = row < M ? g.ycol[row] : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rt = wm * WM + i * 16 + rq + r;
+        float v[FN];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t col = n0 + wn * WN + j * 16 + fr;
+          v[j] = col < g.N ? acc[i][j][r] : -INFINITY;
+          mx = fmaxf(mx, v[j]);
+          if (col + g.col_base == (int64_t)ys[rt]) g.xy[m0 + rt] = v[j];
+        }
+        mx = row16_max(mx);
+        // a half tile past the last vocabulary column holds no value at all
+        const float base = mx == -INFINITY ? 0.0f : mx;
+        float sm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f((v[j] - base) * kL2E);
+        sm = row16_sum(sm);
+        if (fr == 0) red[wn][rt] = make_float2(mx, sm);
+      }
+    }
+    __syncthreads();
+    for (int r = tid; r < GBM; r += GT) {
+      const int64_t row = m0 + r;
+      if (row >= M) continue;
+      const float2 a = red[0][r], b = red[1][r];
+      const float mx = fmaxf(a.x, b.x);
+      float sm = 0.0f;
+      if (mx != -INFINITY)
+        sm = a.y * __builtin_amdgcn_exp2f((a.x - mx) * kL2E) +
+             b.y * __builtin_amdgcn_exp2f((b.x - mx) * kL2E);
+      g.part[row * g.ntn + tn] = make_float2(mx, sm);
+    }
+  } else if constexpr (MODE == GM_D) {
+    __shared__ float sl[GBM], sc[GBM];
+    __shared__ int32_t ys[GBM];
+    for (int r = tid; r < GBM; r += GT) {
+      const int64_t row = m0 + r;
+      const bool ok = row < M;
+      sl[r] = ok ? g.lse2[row] : INFINITY;  // rows past the active count: exact zeros
+      sc[r] = ok ? g.coef[row] : 0.0f;
+      ys[r] = ok ? g.ycol[row] : -1;
+    }
+    __syncthreads();
+    const int64_t mpad = (M + 7) & ~int64_t(7);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rt0 = wm * WM + i * 16 + rq;
+      const int64_t row0 = m0 + rt0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + wn * WN + j * 16 + fr;
+        uint16_t d[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rt = rt0 + r;
+          const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -sl[rt]));
+          const float hit = (col + g.col_base == (int64_t)ys[rt]) ? 1.0f : 0.0f;
+          d[r] = bf16_bits(sc[rt] * (p - hit));
+        }
+        if (col < g.N) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (row0 + r < mpad) g.D[(row0 + r) * g.ldd + col] = d[r];
+          if (row0 < mpad) {  // 4 consecutive rows: all below mpad (a multiple of 8) or none
+            const uint32_t lo = (uint32_t)d[0] | ((uint32_t)d[1] << 16);
+            const uint32_t hi = (uint32_t)d[2] | ((uint32_t)d[3] << 16);
+            *reinterpret_cast<uint2*>(g.Dt + col * g.ldt + row0) = make_uint2(lo, hi);
+          }
+        }
+      }
+    }
+  } else {
+    const int64_t Mst = MODE == GM_STORE ? g.M : M;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + wn * WN + j * 16 + fr;
+        if (col >= g.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = m0 + wm * WM + i * 16 + rq + r;
+          if (row >= Mst) continue;
+          if constexpr (MODE == GM_ACC) {
+            float* c = g.Cf + row * g.ldc + col;
+            *c = g.accumulate ? *c + acc[i][j][r] : acc[i][j][r];
+          } else {
+            g.Cb[row * g.ldc + col] = bf16_bits(acc[i][j][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ small kernels
+// Active-token count per completion and exclusive offsets (one workgroup).
+// A token is active when counted (t < len_i, token id in range) and
+// (A_i != 0 or beta != 0); bad ids are handled separately.
+__global__ void __launch_bounds__(1024)
+k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int64_t N,
+             float beta, int32_t* __restrict__ offs, int32_t* __restrict__ counts) {
+  __shared__ int32_t sh[1024];
+  const int tid = threadIdx.x;
+  int32_t base = 0;
+  for (int64_t c0 = 0; c0 < N; c0 += 1024) {
+    const int64_t i = c0 + tid;
+    const int32_t a = (i < N && (adv[i] != 0.0f || beta != 0.0f)) ? len[i] : 0;
+    sh[tid] = a;
+    __syncthreads();
+    // inclusive Hillis-Steele scan (fixed order, integers)
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int32_t v = tid >= o ? sh[tid - o] : 0;
+      __syncthreads();
+      sh[tid] += v;
+      __syncthreads();
+    }
+    if (i < N) offs[i] = base + sh[tid] - a;
+    base += sh[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    offs[N] = base;
+    counts[0] = base;                // active tokens
+    counts[1] = (base + 7) & ~7;     // padded to a multiple of 8
+  }
+}
+
+// One workgroup per completion: list its active tokens, gather their hidden
+// rows, and zero the loss terms of its other tokens.
+__global__ void __launch_bounds__(256)
+k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __restrict__ tokens,
+            int64_t C, int64_t V, const int32_t* __restrict__ len,
+            const int32_t* __restrict__ offs, int32_t* __restrict__ act_pos,
+            int32_t* __restrict__ ycol, uint16_t* __restrict__ Ha, double* __restrict__ tok_loss,
+            uint8_t* __restrict__ tok_flags) {
+  const int64_t i = blockIdx.x;
+  const int32_t n_act = offs[i + 1] - offs[i];
+  const int32_t k0 = offs[i];
+  const int32_t L = len[i];
+  for (int64_t t = threadIdx.x; t < C; t += blockDim.x) {
+    const int64_t pos = i * C + t;
+    const int64_t y = tokens[pos];
+    const bool bad = t < L && (y < 0 || y >= V);
+    if (t < n_act) {
+      act_pos[k0 + t] = (int32_t)pos;
+      ycol[k0 + t] = bad ? -1 : (int32_t)y;
+    }
+    if (t >= n_act || bad) {
+      tok_loss[pos] = bad ? (double)NAN : 0.0;
+      tok_flags[pos] = bad ? TF_BADTOK : 0;
+    }
+  }
+  // hidden rows of the active tokens: 16-byte copies
+  const int64_t per_row = H / 8;
+  for (int64_t q = threadIdx.x; q < (int64_t)n_act * per_row; q += blockDim.x) {
+    const int64_t t = q / per_row, c = q - t * per_row;
+    *reinterpret_cast<u32x4*>(Ha + (k0 + t) * H + 8 * c) =
+        *reinterpret_cast<const u32x4*>(hidden + (i * C + t) * H + 8 * c);
+  }
+}
+
+// dst[c, r] = src[r, c] for r < rows (device count if rows_dev) and zeros for
+// rows_dev <= r < its multiple of 8; 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(256)
+k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int64_t cols,
+            const int32_t* __restrict__ rows_dev, uint16_t* __restrict__ dst, int64_t ld_dst) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t R = rows_dev ? (int64_t)*rows_dev : rows;
+  const int64_t Rpad = rows_dev ? ((R + 7) & ~int64_t(7)) : R;
+  const int64_t ntr = (rows + 63) / 64;
+  const int64_t r0 = (blockIdx.x % ntr) * 64;
+  const int64_t c0 = (blockIdx.x / ntr) * 64;
+  if (r0 >= Rpad) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < R && c < cols) ? src[r * ld_src + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t c = c0 + k, r = r0 + tx;
+    if (c < cols && r < Rpad) dst[c * ld_dst + r] = tile[tx][k];
+  }
+}
+
+// One wavefront per active token: merge the per-tile (max, sum exp), then
+// the per-token loss term and gradient coefficient.
+__global__ void __launch_bounds__(256)
+k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restrict__ xy,
+             const int32_t* __restrict__ counts, const int32_t* __restrict__ act_pos,
+             const int32_t* __restrict__ ycol, int64_t C, const float* __restrict__ adv,
+             const float* __restrict__ logp_old, const float* __restrict__ logp_ref, float eps,
+             float beta, double kappa, float* __restrict__ lse2, float* __restrict__ coef,
+             double* __restrict__ tok_loss, uint8_t* __restrict__ tok_flags) {
+  const int lane = threadIdx.x & 63;
+  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= counts[0]) return;
+  float m = -INFINITY, s = 0.0f;
+  for (int64_t j = lane; j < ntn; j += 64) {
+    const float2 p = part[k * ntn + j];
+    const float nm = fmaxf(m, p.x);
+    if (nm == -INFINITY) continue;
+    s = s * __builtin_amdgcn_exp2f((m - nm) * kL2E) + p.y * __builtin_amdgcn_exp2f((p.x - nm) * kL2E);
+    m = nm;
+  }
+  float M = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  double term = s != 0.0f ? (double)s * exp2(((double)m - (double)M) * kL2ED) : 0.0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) term += __shfl_xor(term, o);
+  if (lane != 0) return;
+  const int64_t pos = act_pos[k];
+  const int64_t i = pos / C;
+  if (ycol[k] < 0) {  // bad token id: excluded from the gradient, poisons the loss
+    lse2[k] = INFINITY;
+    coef[k] = 0.0f;
+    return;
+  }
+  const double lse = (double)M + log(term);
+  const double logp = (double)xy[k] - lse;
+  const TokenTerms tt = token_terms(logp, logp_old[pos], beta != 0.0f ? logp_ref[pos] : 0.0f,
+                                    adv[i], eps, beta, kappa);
+  tok_loss[pos] = tt.lam;
+  tok_flags[pos] = tt.flags;
+  lse2[k] = (float)(lse * kL2ED);
+  coef[k] = (float)tt.coef;
+}
+
+// dhidden rows: active tokens get their accumulator, others zero (NaN for a
+// bad token id at a counted position).
+__global__ void __launch_bounds__(256)
+k_lm_dh_out(const float* __restrict__ dHacc, int64_t H, const int32_t* __restrict__ offs,
+            const int32_t* __restrict__ len, const int64_t* __restrict__ tokens, int64_t C,
+            int64_t V, uint16_t* __restrict__ dhidden) {
+  const int64_t pos = blockIdx.x;
+  const int64_t i = pos / C, t = pos - i * C;
+  const int32_t n_act = offs[i + 1] - offs[i];
+  const int64_t y = tokens[pos];
+  const bool bad = t < len[i] && (y < 0 || y >= V);
+  const int64_t k = offs[i] + t;
+  for (int64_t h = threadIdx.x; h < H; h += blockDim.x) {
+    float v = 0.0f;
+    if (bad) v = NAN;
+    else if (t < n_act) v = dHacc[k * H + h];
+    dhidden[pos * H + h] = bf16_bits(v);
+  }
+}
+
+// ------------------------------------------------------------ host side
+struct LmWs {
+  int32_t* status;
+  int32_t* len;
+  float* adv;
+  uint8_t* row_flags;
+  int32_t* offs;     // [N + 1]
+  int32_t* counts;   // [2]: active tokens, padded to 8
+  int32_t* act_pos;  // [T]
+  int32_t* ycol;     // [T]
+  double* tok_loss;  // [T]
+  uint8_t* tok_flags;
+  float2* part;      // [T, ntn]
+  float* xy;         // [T]
+  float* lse2;       // [T]
+  float* coef;       // [T]
+  uint16_t* Ha;      // [T, H]
+  uint16_t* Hat;     // [H, Tcap]
+  uint16_t* Wt;      // [H, V]
+  uint16_t* Dc;      // [Tcap, kChunkV]
+  uint16_t* Dtc;     // [kChunkV, Tcap]
+  float* dH;         // [Tcap, H]
+};
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws) {
+  const int64_t Tcap = round_up(T, 8);
+  const int64_t ntn = (V + GBN - 1) / GBN;
+  const int64_t vc = V < kChunkV ? round_up(V, 8) : kChunkV;
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  LmWs w;
+  w.status = reinterpret_cast<int32_t*>(take(256));
+  w.len = reinterpret_cast<int32_t*>(take(4 * N));
+  w.adv = reinterpret_cast<float*>(take(4 * N));
+  w.row_flags = reinterpret_cast<uint8_t*>(take(N));
+  w.offs = reinterpret_cast<int32_t*>(take(4 * (N + 1)));
+  w.counts = reinterpret_cast<int32_t*>(take(16));
+  w.act_pos = reinterpret_cast<int32_t*>(take(4 * T));
+  w.ycol = reinterpret_cast<int32_t*>(take(4 * T));
+  w.tok_loss = reinterpret_cast<double*>(take(8 * T));
+  w.tok_flags = reinterpret_cast<uint8_t*>(take(T));
+  w.part = reinterpret_cast<float2*>(take(8 * (size_t)T * ntn));
+  w.xy = reinterpret_cast<float*>(take(4 * T));
+  w.lse2 = reinterpret_cast<float*>(take(4 * T));
+  w.coef = reinterpret_cast<float*>(take(4 * T));
+  w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
+  w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
+  w.Wt = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * V));
+  w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
+  w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
+  w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
+  if (ws) *ws = w;
+  return off;
+}
+
+int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_t* T) {
+  if (N <= 0 || C <= 0 || V <= 0 || H <= 0 || G <= 0 || N % G != 0) return DRGRPO_ERR_SHAPE;
+  if (V % 8 != 0 || H % 32 != 0 || V > (int64_t(1) << 30) || H > 65536) return DRGRPO_ERR_SHAPE;
+  if (!mul_ok(N, C, T) || *T > (int64_t(1) << 30)) return DRGRPO_ERR_SHAPE;
+  int64_t tmp;
+  if (!mul_ok(*T, (V + GBN - 1) / GBN * 8, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
+      !mul_ok(V, H * 2, &tmp))
+    return DRGRPO_ERR_SHAPE;
+  return DRGRPO_OK;
+}
+
+template <int MODE>
+int launch_gemm(const GemmArgs& g, hipStream_t st) {
+  const int64_t ntm = (g.M + GBM - 1) / GBM;
+  const int64_t ntn = (g.N + GBN - 1) / GBN;
+  const int64_t blocks = ntm * ntn;
+  if (blocks <= 0) return DRGRPO_OK;
+  if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
+  hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), 0, st, g);
+  return launch_status();
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" size_t drgrpo_lmhead_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t H,
+                                                int64_t G) {
+  int64_t T;
+  if (lm_check_shape(N, C, V, H, G, &T) != DRGRPO_OK) return 0;
+  return lm_carve(nullptr, N, T, V, H, nullptr);
+}
+
+extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,
+                                          int64_t eos_id, const float* rewards,
+                                          const float* logp_old, const float* logp_ref, int64_t G,
+                                          float eps, float beta, float norm_const,
+                                          float* out_loss, void* out_dhidden, void* out_dW,
+                                          int64_t N, int64_t C, int64_t V, int64_t H,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (!hidden || !W || !tokens || !rewards || !logp_old || !out_loss || !out_dhidden || !out_dW)
+    return DRGRPO_ERR_NULL;
+  int64_t T;
+  const int sh = lm_check_shape(N, C, V, H, G, &T);
+  if (sh != DRGRPO_OK) return sh;
+  if (!finite_f(eps) || eps < 0.0f || !finite_f(beta) || beta < 0.0f || !finite_f(norm_const) ||
+      norm_const <= 0.0f)
+    return DRGRPO_ERR_PARAM;
+  if (beta > 0.0f && !logp_ref) return DRGRPO_ERR_NULL;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W) |
+                       reinterpret_cast<uintptr_t>(out_dhidden) |
+                       reinterpret_cast<uintptr_t>(out_dW);
+  if (al % 16 != 0) return DRGRPO_ERR_ALIAS;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < lm_carve(nullptr, N, T, V, H, nullptr))
+    return DRGRPO_ERR_WORKSPACE;
+  LmWs w;
+  lm_carve(workspace, N, T, V, H, &w);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t Tcap = round_up(T, 8);
+  const int64_t ntn = (V + GBN - 1) / GBN;
+  const uint16_t* hid = static_cast<const uint16_t*>(hidden);
+  const uint16_t* Wb = static_cast<const uint16_t*>(W);
+  int rc;
+
+  // mask, advantage, active-token list, gathered hidden rows and transposes
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
+                     w.len, w.adv, w.row_flags, (int32_t*)nullptr, (uint8_t*)nullptr,
+                     (float*)nullptr, (int32_t*)nullptr);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, w.adv, N, beta, w.offs,
+                     w.counts);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st, hid, H, tokens, C, V, w.len,
+                     w.offs, w.act_pos, w.ycol, w.Ha, w.tok_loss, w.tok_flags);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  {
+    const int64_t blocks = ((V + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks), dim3(256), 0, st, Wb, H, V, H,
+                       (const int32_t*)nullptr, w.Wt, V);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+    const int64_t blocks2 = ((T + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, H, Tcap, H,
+                       w.counts, w.Hat, Tcap);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  }
+
+  // forward: per-token log-sum-exp over the vocabulary, logits never stored
+  GemmArgs g = {};
+  g.A = w.Ha;
+  g.lda = H;
+  g.B = Wb;
+  g.ldb = H;
+  g.M = T;
+  g.N = V;
+  g.K = H;
+  g.M_dev = w.counts;
+  g.part = w.part;
+  g.ntn = ntn;
+  g.xy = w.xy;
+  g.ycol = w.ycol;
+  g.col_base = 0;
+  if ((rc = launch_gemm<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
+                     w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, logp_old, logp_ref, eps, beta,
+                     (double)norm_const, w.lse2, w.coef, w.tok_loss, w.tok_flags);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+
+  // backward, one vocabulary chunk at a time
+  const int64_t vc_cap = V < kChunkV ? round_up(V, 8) : kChunkV;
+  for (int64_t v0 = 0; v0 < V; v0 += kChunkV) {
+    const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
+    GemmArgs d = {};
+    d.A = w.Ha;
+    d.lda = H;
+    d.B = Wb + v0 * H;
+    d.ldb = H;
+    d.M = T;
+    d.N = wv;
+    d.K = H;
+    d.M_dev = w.counts;
+    d.ycol = w.ycol;
+    d.col_base = v0;
+    d.lse2 = w.lse2;
+    d.coef = w.coef;
+    d.D = w.Dc;
+    d.ldd = vc_cap;
+    d.Dt = w.Dtc;
+    d.ldt = Tcap;
+    if ((rc = launch_gemm<GM_D>(d, st)) != DRGRPO_OK) return rc;
+
+    GemmArgs a = {};  // dhidden += D_chunk . W_chunk
+    a.A = w.Dc;
+    a.lda = vc_cap;
+    a.B = w.Wt + v0;
+    a.ldb = V;
+    a.M = T;
+    a.N = H;
+    a.K = wv;
+    a.M_dev = w.counts;
+    a.Cf = w.dH;
+    a.ldc = H;
+    a.accumulate = v0 > 0;
+    if ((rc = launch_gemm<GM_ACC>(a, st)) != DRGRPO_OK) return rc;
+
+    GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a
+    s.A = w.Dtc;
+    s.lda = Tcap;
+    s.B = w.Hat;
+    s.ldb = Tcap;
+    s.M = wv;
+    s.N = H;
+    s.K = Tcap;
+    s.K_dev = w.counts + 1;
+    s.Cb = static_cast<uint16_t*>(out_dW) + v0 * H;
+    s.ldc = H;
+    if ((rc = launch_gemm<GM_STORE>(s, st)) != DRGRPO_OK) return rc;
+  }
+
+  hipLaunchKernelGGL(k_lm_dh_out, dim3((unsigned)T), dim3(256), 0, st, w.dH, H, w.offs, w.len,
+                     tokens, C, V, static_cast<uint16_t*>(out_dhidden));
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, w.tok_loss, w.tok_flags, T,
+                     w.row_flags, N, (double)norm_const, out_loss, w.status, (int64_t*)nullptr);
+  return launch_status();
+}

@@ -143,6 +143,14 @@ _add(Config(name="no_eos_id", B=2, G=2, C=5, V=640, logit_std=1.0, eos_id=-1, to
 _add(Config(name="lmhead_mini", B=2, G=4, C=32, V=4096, H=QWEN_H, eos_id=3, tok_lo=0,
             tok_hi=4096, eos_rows=5, eos_t0_rows=1, p=0.5, reward="tiny", old_noise=0.02,
             seed=7011))
+# two backward vocabulary chunks, a ragged last column tile, a KL term
+_add(Config(name="lmhead_multi", B=2, G=2, C=7, V=20488, H=96, eos_id=3, tok_lo=0,
+            tok_hi=20488, eos_rows=2, reward="tiny", p=0.5, old_noise=0.05, ref_noise=0.1,
+            beta=0.04, w_std=0.1, seed=7012))
+# tiny fp64-checkable shape for finite differences of the lm_head oracle
+_add(Config(name="lmhead_fd", B=2, G=2, C=3, V=48, H=32, eos_id=3, tok_lo=0, tok_hi=48,
+            eos_rows=1, reward="tiny", p=0.5, old_noise=0.3, ref_noise=0.2, beta=0.04,
+            w_std=0.3, seed=7013))
 
 
 def get_config(name: str) -> Config:

@@ -112,3 +112,24 @@ def compare_loss(cfg, got: float, res):
     else:
         assert abs(got - ref) <= t["loss_rel"] * abs(ref), (got, ref, abs(got - ref) / abs(ref))
     return cond
+
+
+@functools.lru_cache(maxsize=None)
+def lm_case(name: str):
+    """(cfg, case, hidden bits [T,H], W bits [V,H], logp_old, logp_ref, oracle terms)
+    for a fused lm_head case small enough for the oracle's full gradients."""
+    from oracle import lmhead
+
+    cfg = synth.get_config(name)
+    case = synth.make_case(cfg)
+    hb = case.hidden()
+    Wb = case.weight()
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    _, logp = lmhead.token_rows(h64, W64, case.tokens.reshape(-1), np.arange(cfg.T))
+    logp = logp.reshape(cfg.N, cfg.C)
+    old = synth.perturb(logp, case.old_noise)
+    ref = None if case.ref_noise is None else synth.perturb(logp, case.ref_noise)
+    terms = lmhead.full(hb, Wb, case.tokens, cfg.eos_id, case.rewards, old, ref, cfg.G,
+                        f32(cfg.eps), f32(cfg.beta), f32(cfg.norm_const))
+    return cfg, case, hb, Wb, old, ref, terms

@@ -1,0 +1,115 @@
+"""GPU parity of the fused lm_head variant against the CPU oracle.
+
+Small cases: loss, every dhidden and dW entry.  Full size (B=8, G=8, C=512,
+H=896, V=151936): loss over every token, sampled dhidden rows and dW rows.
+Tolerances: loss rel <= 2e-3; dhidden, dW max|diff| <= 1e-2 * max|ref| (bf16
+outputs from binary32 accumulation, dlogits entering the products in bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import rl_post_loss_dr_amd as dr
+from oracle import lmhead
+from _cases import f32, lm_case
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _bits_to_dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _dev_to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _run(cfg, case, hb, Wb, old, ref):
+    loss, dh, dW = dr.lmhead_loss_fwd_bwd(
+        _bits_to_dev(hb), _bits_to_dev(Wb), torch.from_numpy(case.tokens).to(DEV), cfg.eos_id,
+        torch.from_numpy(case.rewards).to(DEV), torch.from_numpy(old).to(DEV),
+        None if ref is None else torch.from_numpy(ref).to(DEV), G=cfg.G, eps=cfg.eps,
+        beta=cfg.beta, norm_const=cfg.norm_const)
+    torch.cuda.synchronize()
+    return float(loss.item()), dh, dW
+
+
+def _close(got, want, frac=1e-2):
+    scale = float(np.abs(want).max())
+    err = float(np.abs(got - want).max())
+    assert err <= frac * scale, (err, scale)
+    return err, scale
+
+
+@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi"])
+def test_lmhead_small(name):
+    print(f"case {name}", flush=True)
+    cfg, case, hb, Wb, old, ref, t = lm_case(name)
+    loss, dh, dW = _run(cfg, case, hb, Wb, old, ref)
+    assert abs(loss - t["loss"]) <= 2e-3 * abs(t["loss"]), (loss, t["loss"])
+    _close(_dev_to_f64(dh), t["dhidden"])
+    _close(_dev_to_f64(dW), t["dW"])
+    # tokens without gradient have exactly zero dhidden rows
+    zero = t["coef"] == 0
+    assert (_dev_to_f64(dh)[zero] == 0).all()
+
+
+def test_lmhead_deterministic():
+    cfg, case, hb, Wb, old, ref, t = lm_case("lmhead_multi")
+    l1, dh1, dW1 = _run(cfg, case, hb, Wb, old, ref)
+    l2, dh2, dW2 = _run(cfg, case, hb, Wb, old, ref)
+    assert l1 == l2 and torch.equal(dh1, dh2) and torch.equal(dW1, dW2)
+
+
+def test_lmhead_no_active_tokens():
+    """All groups uniform and beta = 0: zero loss, zero gradients."""
+    cfg, case, hb, Wb, old, ref, t = lm_case("lmhead_mini")
+    rewards = np.ones_like(case.rewards)
+    loss, dh, dW = dr.lmhead_loss_fwd_bwd(
+        _bits_to_dev(hb), _bits_to_dev(Wb), torch.from_numpy(case.tokens).to(DEV), cfg.eos_id,
+        torch.from_numpy(rewards).to(DEV), torch.from_numpy(old).to(DEV), None, G=cfg.G)
+    torch.cuda.synchronize()
+    assert float(loss.item()) == 0.0
+    assert float(dh.float().abs().max()) == 0.0 and float(dW.float().abs().max()) == 0.0
+
+
+def test_lmhead_full_size_sampled():
+    cfg = synth.get_config("lmhead_b8g8c512")
+    case = synth.make_case(cfg)
+    print(f"[{cfg.name}] host inputs", flush=True)
+    hb = case.hidden()
+    Wb = case.weight()
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    lens = oracle.completion_len(case.tokens, cfg.eos_id)
+    adv = oracle.group_advantage(case.rewards, cfg.G)
+    mask = np.arange(cfg.C)[None, :] < lens[:, None]
+    active = np.flatnonzero((mask & (adv[:, None] != 0)).reshape(-1))
+    # logp_old only matters at active tokens; elsewhere any finite value
+    print(f"[{cfg.name}] oracle log-probs of {active.size} active tokens", flush=True)
+    _, lp_act = lmhead.token_rows(h64, W64, case.tokens.reshape(-1), active)
+    lp = np.zeros(cfg.T)
+    lp[active] = lp_act
+    old = synth.perturb(lp.reshape(cfg.N, cfg.C), case.old_noise)
+    t = lmhead.loss_and_terms(h64, W64, case.tokens, cfg.eos_id, case.rewards, old, None, cfg.G,
+                              f32(cfg.eps), f32(cfg.beta), f32(cfg.norm_const))
+    print(f"[{cfg.name}] device run", flush=True)
+    loss, dh, dW = _run(cfg, case, hb, Wb, old, None)
+    print(f"[{cfg.name}] loss gpu {loss!r} oracle {t['loss']!r}", flush=True)
+    assert abs(loss - t["loss"]) <= 2e-3 * abs(t["loss"])
+    rng = np.random.default_rng(cfg.seed)
+    rows = np.unique(np.concatenate([rng.choice(active, 12, replace=False), active[:2],
+                                     active[-2:], [0]]))
+    want_h = lmhead.dhidden_rows(h64, W64, case.tokens.reshape(-1), t, rows)
+    got_h = _dev_to_f64(dh[torch.from_numpy(rows).to(DEV)])
+    _close(got_h, want_h)
+    vs = np.unique(np.concatenate([rng.choice(cfg.V, 10, replace=False),
+                                   case.tokens.reshape(-1)[active[:4]], [0, cfg.V - 1]]))
+    want_w = lmhead.dW_rows(h64, W64, case.tokens.reshape(-1), t, vs)
+    got_w = _dev_to_f64(dW[torch.from_numpy(vs).to(DEV)])
+    _close(got_w, want_w)
+    # every inactive token's dhidden row is exactly zero
+    inactive = np.setdiff1d(np.arange(cfg.T), active)
+    assert float(dh[torch.from_numpy(inactive).to(DEV)].float().abs().max()) == 0.0
