@@ -112,6 +112,64 @@ def cpu_baseline(cfg, case, target_s: float = 15.0):
                       f"{reps} passes in {el:.1f} s; mask and advantage over the whole batch"}
 
 
+def run_lmhead(cfg, case, args):
+    """Fused lm_head workload: hidden [T, H] and W [V, H] in, loss, dhidden, dW out."""
+    import numpy as np
+    import torch
+
+    import synth
+    import rl_post_loss_dr_amd as dr
+
+    dev = torch.device("cuda:0")
+    hidden = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    W = torch.empty((cfg.V, cfg.H), dtype=torch.bfloat16, device=dev)
+    synth.gpu_normal_fill(hidden, cfg.seed, synth.S_HIDDEN, 0, cfg.hidden_std)
+    synth.gpu_normal_fill(W, cfg.seed, synth.S_WEIGHT, 0, cfg.w_std)
+    tokens = torch.from_numpy(case.tokens).to(dev)
+    rewards = torch.from_numpy(case.rewards).to(dev)
+    # logp_old: the policy's own log-probs (logits formed once, outside the timed region)
+    logits = torch.mm(hidden, W.t().contiguous()).view(cfg.N, cfg.C, cfg.V)
+    lp = dr.logprobs(logits, tokens).double().cpu().numpy()
+    del logits
+    torch.cuda.empty_cache()
+    old = torch.from_numpy(synth.perturb(lp, case.old_noise)).to(dev)
+    dh = torch.empty_like(hidden)
+    dW = torch.empty_like(W)
+    ws = torch.empty(dr.lmhead_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H, cfg.G),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const, out_dhidden=dh,
+              out_dW=dW, workspace=ws)
+    _, mask_rows = dr.completion_mask(tokens, cfg.eos_id)
+    adv, _ = dr.group_advantage(rewards, cfg.G)
+    n_act = int(((mask_rows != 0) & (adv[:, None] != 0)).sum().item())
+    for _ in range(args.warmup):
+        dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None, **kw)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = 3 * 2.0 * n_act * cfg.V * cfg.H
+    achieved = flops / (ms / 1e3) / 1e12
+    return {
+        "metric": METRIC, "value": cfg.T / (ms / 1e3), "unit": "completion tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generator; no dataset or weights)",
+        "config": {"workload": cfg.name, "B": cfg.B, "G": cfg.G, "C": cfg.C, "V": cfg.V,
+                   "H": cfg.H, "token_rows": cfg.T, "active_tokens": n_act},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": achieved / 2500.0, "traffic": None, "kernel": "whole call",
+                     "alg_flops_per_call": flops,
+                     "note": "3 x 2*T_active*V*H (logits, dhidden, dW); recompute not counted"},
+        "device": torch.cuda.get_device_name(0),
+    }
+
+
 def synth_perturb(lp, noise):
     import synth
 
@@ -153,6 +211,9 @@ def main():
 
     cfg = synth.get_config(args.workload)
     case = synth.make_case(cfg)
+    if cfg.H is not None:
+        print(json.dumps(run_lmhead(cfg, case, args)), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch_dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     logits = torch.empty((cfg.N, cfg.C, cfg.V), dtype=torch_dt, device=dev)

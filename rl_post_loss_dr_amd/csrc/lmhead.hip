@@ -36,11 +36,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256;                   // workgroup tile rows (A rows)
-constexpr int GBN = 128;                   // workgroup tile columns (B rows)
-constexpr int GBK = 32;                    // reduction depth per step: one MFMA
-constexpr int GT = 256;                    // 4 wavefronts as 2 (rows) x 2 (columns)
+constexpr int GBN = 256;                   // workgroup tile columns (B rows)
+constexpr int GBK = 64;                    // reduction depth per LDS stage (two MFMAs)
 constexpr int WM = 128, WN = 64;           // wavefront tile
+constexpr int NWM = GBM / WM, NWN = GBN / WN;  // wavefront grid: 2 (rows) x 4 (columns)
+constexpr int GT = 64 * NWM * NWN;         // 8 wavefronts, 2 per SIMD
 constexpr int FM = WM / 16, FN = WN / 16;  // 8 x 4 MFMA blocks per wavefront
+constexpr int kLoadsPerThread = GBM * GBK / 8 / GT;  // 16-byte chunks of A (and of B) per stage
+constexpr int kStageElems = (GBM + GBN) * GBK;          // bfloat16 per LDS stage
+constexpr size_t kGemmLds = 2 * kStageElems * sizeof(uint16_t);  // 128 KB
 constexpr int kChunkV = 16384;             // vocabulary columns per backward chunk
 constexpr float kL2E = 1.4426950408889634f;
 constexpr double kL2ED = 1.4426950408889634074;
@@ -93,18 +97,30 @@ __device__ inline float row16_sum(float v) {
 
 template <int MODE>
 __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GBN * GBK];
+  // two LDS stages of [A 256 x 64 | B 256 x 64] bfloat16; 16-byte chunk c of
+  // row r sits at chunk position c ^ (r & 7) so the 16 rows an MFMA operand
+  // read touches spread over the banks
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int64_t M = g.M_dev ? (int64_t)*g.M_dev : g.M;
   const int64_t K = g.K_dev ? (int64_t)*g.K_dev : g.K;
-  // row tiles vary fastest: workgroups resident together share a B tile
+  // tile order: each XCD (workgroup id mod 8) takes a contiguous run of one
+  // linear order, so the workgroups sharing its L2 share operand tiles.  The
+  // order runs along the operand that is small: row tiles fastest when B is
+  // the large operand (the vocabulary-wide products), column tiles fastest
+  // when A is (the products reducing over a dlogits chunk)
   const int64_t ntm = (g.M + GBM - 1) / GBM;
-  const int64_t tm = blockIdx.x % ntm;
-  const int64_t tn = blockIdx.x / ntm;
+  const int64_t ntn_t = (g.N + GBN - 1) / GBN;
+  const int64_t total = ntm * ntn_t;
+  const int64_t b = blockIdx.x;
+  const int64_t q8 = total / 8;
+  const int64_t v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
+  constexpr bool kColsFastest = MODE == GM_ACC || MODE == GM_STORE;
+  const int64_t tm = kColsFastest ? v / ntn_t : v % ntm;
+  const int64_t tn = kColsFastest ? v % ntn_t : v / ntm;
   const int64_t m0 = tm * GBM;
   const int64_t n0 = tn * GBN;
   if (m0 >= M) {
@@ -112,36 +128,36 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     if (MODE != GM_STORE) return;
   }
 
-  // global -> LDS: A tile 256 x 32 (4 x 16 B per thread), B tile 128 x 32 (2 per thread)
-  u32x4 ra[4], rb[2];
+  // global -> registers -> LDS, kLoadsPerThread chunks of 16 B of A and of B
+  // per thread per stage.  Each load writes its register directly (a chunk
+  // past K stays zero): the registers are read only when the stage is copied
+  // to LDS, so the loads stay in flight across the whole MFMA phase.
+  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
   auto gload = [&](int64_t k0) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < kLoadsPerThread; ++p) {
       const int q = tid + GT * p;
-      const int64_t row = m0 + (q >> 2);
-      const int64_t k = k0 + 8 * (q & 3);
+      const int64_t k = k0 + 8 * (q & 7);
+      const int64_t row = m0 + (q >> 3);
       const int64_t rc = row < M ? row : (M > 0 ? M - 1 : 0);
-      ra[p] = (k < K && M > 0)
-                  ? *reinterpret_cast<const u32x4*>(g.A + rc * g.lda + k)
-                  : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int q = tid + GT * p;
-      const int64_t row = n0 + (q >> 2);
-      const int64_t k = k0 + 8 * (q & 3);
-      const int64_t rc = row < g.N ? row : g.N - 1;
-      rb[p] = k < K ? *reinterpret_cast<const u32x4*>(g.B + rc * g.ldb + k)
-                    : u32x4{0, 0, 0, 0};
+      ra[p] = (k < K && M > 0) ? *reinterpret_cast<const u32x4*>(g.A + rc * g.lda + k)
+                               : u32x4{0, 0, 0, 0};
+      const int64_t col = n0 + (q >> 3);
+      const int64_t cc = col < g.N ? col : g.N - 1;
+      rb[p] = k < K ? *reinterpret_cast<const u32x4*>(g.B + cc * g.ldb + k) : u32x4{0, 0, 0, 0};
     }
   };
   auto swrite = [&](int buf) {
+    uint16_t* As = smem + buf * kStageElems;
+    uint16_t* Bs = As + GBM * GBK;
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<u32x4*>(&As[buf][(tid + GT * p) * 8]) = ra[p];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      *reinterpret_cast<u32x4*>(&Bs[buf][(tid + GT * p) * 8]) = rb[p];
+    for (int p = 0; p < kLoadsPerThread; ++p) {
+      const int q = tid + GT * p;
+      const int r = q >> 3, c = q & 7;
+      const int off = r * GBK + 8 * (c ^ (r & 7));
+      *reinterpret_cast<u32x4*>(As + off) = ra[p];
+      *reinterpret_cast<u32x4*>(Bs + off) = rb[p];
+    }
   };
 
   f32x4 acc[FM][FN];
@@ -156,34 +172,45 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     swrite(0);
   }
   __syncthreads();
-  const int fr = lane & 15;        // row (A) / column (B) within a 16 x 16 block
-  const int fk = 8 * (lane >> 4);  // first of the lane's 8 reduction indices
+  const int fr = lane & 15;  // row (A) / column (B) within a 16 x 16 block
+  const int fc = lane >> 4;  // which 8 of the MFMA's 32 reduction indices
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int cur = (int)(kt & 1);
     if (kt + 1 < nk) gload((kt + 1) * GBK);
-    bf16x8 af[FM], bfr[FN];
+    const uint16_t* As = smem + cur * kStageElems;
+    const uint16_t* Bs = As + GBM * GBK;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * WM + i * 16 + fr) * GBK + fk]);
+    for (int s = 0; s < GBK / 32; ++s) {
+      const int c = 4 * s + fc;
+      bf16x8 af[FM], bfr[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn * WN + j * 16 + fr) * GBK + fk]);
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WM + i * 16 + fr;
+        af[i] = *reinterpret_cast<const bf16x8*>(As + r * GBK + 8 * (c ^ (r & 7)));
+      }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WN + j * 16 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + r * GBK + 8 * (c ^ (r & 7)));
+      }
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
     if (kt + 1 < nk) swrite(cur ^ 1);
     __syncthreads();
   }
 
   // accumulator layout: acc[i][j][r] = C[m0 + wm*WM + i*16 + 4*(lane/16) + r]
   //                                    [n0 + wn*WN + j*16 + lane%16]
+  // (the LDS stages are free from here on and hold the epilogue's tables)
   const int rq = 4 * (lane >> 4);
 
   if constexpr (MODE == GM_LSE) {
-    __shared__ float2 red[2][GBM];
-    __shared__ int32_t ys[GBM];
+    float2* red = reinterpret_cast<float2*>(smem);              // [NWN][GBM]
+    int32_t* ys = reinterpret_cast<int32_t*>(red + NWN * GBM);  // [GBM]
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       ys[r] = row < M ? g.ycol[row] : -1;
@@ -194,40 +221,46 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int rt = wm * WM + i * 16 + rq + r;
-        float v[FN];
+        float vv[FN];
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int64_t col = n0 + wn * WN + j * 16 + fr;
-          v[j] = col < g.N ? acc[i][j][r] : -INFINITY;
-          mx = fmaxf(mx, v[j]);
-          if (col + g.col_base == (int64_t)ys[rt]) g.xy[m0 + rt] = v[j];
+          vv[j] = col < g.N ? acc[i][j][r] : -INFINITY;
+          mx = fmaxf(mx, vv[j]);
+          if (col + g.col_base == (int64_t)ys[rt]) g.xy[m0 + rt] = vv[j];
         }
         mx = row16_max(mx);
-        // a half tile past the last vocabulary column holds no value at all
+        // a quarter tile past the last vocabulary column holds no value at all
         const float base = mx == -INFINITY ? 0.0f : mx;
         float sm = 0.0f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f((v[j] - base) * kL2E);
+        for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f((vv[j] - base) * kL2E);
         sm = row16_sum(sm);
-        if (fr == 0) red[wn][rt] = make_float2(mx, sm);
+        if (fr == 0) red[wn * GBM + rt] = make_float2(mx, sm);
       }
     }
     __syncthreads();
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       if (row >= M) continue;
-      const float2 a = red[0][r], b = red[1][r];
-      const float mx = fmaxf(a.x, b.x);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWN; ++w) mx = fmaxf(mx, red[w * GBM + r].x);
       float sm = 0.0f;
-      if (mx != -INFINITY)
-        sm = a.y * __builtin_amdgcn_exp2f((a.x - mx) * kL2E) +
-             b.y * __builtin_amdgcn_exp2f((b.x - mx) * kL2E);
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NWN; ++w) {
+          const float2 p = red[w * GBM + r];
+          sm += p.y * __builtin_amdgcn_exp2f((p.x - mx) * kL2E);
+        }
+      }
       g.part[row * g.ntn + tn] = make_float2(mx, sm);
     }
   } else if constexpr (MODE == GM_D) {
-    __shared__ float sl[GBM], sc[GBM];
-    __shared__ int32_t ys[GBM];
+    float* sl = reinterpret_cast<float*>(smem);  // [GBM] lse * log2(e)
+    float* sc = sl + GBM;                        // [GBM] coef
+    int32_t* ys = reinterpret_cast<int32_t*>(sc + GBM);
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       const bool ok = row < M;
@@ -523,7 +556,11 @@ int launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t blocks = ntm * ntn;
   if (blocks <= 0) return DRGRPO_OK;
   if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
-  hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), 0, st, g);
+  // 128 KB of LDS per workgroup (gfx950 has 160 KB per CU)
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds) != hipSuccess)
+    return DRGRPO_ERR_HIP;
+  hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), kGemmLds, st, g);
   return launch_status();
 }
 
