@@ -37,14 +37,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256;                   // workgroup tile rows (A rows)
 constexpr int GBN = 256;                   // workgroup tile columns (B rows)
-constexpr int GBK = 64;                    // reduction depth per LDS stage (two MFMAs)
+constexpr int GBK = 32;                    // reduction depth per LDS stage: one MFMA
 constexpr int WM = 128, WN = 64;           // wavefront tile
 constexpr int NWM = GBM / WM, NWN = GBN / WN;  // wavefront grid: 2 (rows) x 4 (columns)
 constexpr int GT = 64 * NWM * NWN;         // 8 wavefronts, 2 per SIMD
 constexpr int FM = WM / 16, FN = WN / 16;  // 8 x 4 MFMA blocks per wavefront
-constexpr int kLoadsPerThread = GBM * GBK / 8 / GT;  // 16-byte chunks of A (and of B) per stage
-constexpr int kStageElems = (GBM + GBN) * GBK;          // bfloat16 per LDS stage
-constexpr size_t kGemmLds = 2 * kStageElems * sizeof(uint16_t);  // 128 KB
+constexpr int kStages = 4;                 // LDS ring depth
+constexpr int kStageElems = (GBM + GBN) * GBK;  // bfloat16 per LDS stage (32 KB)
+constexpr int kDmaPerThread = kStageElems / 8 / GT;  // 16-byte direct loads per thread per stage
+constexpr size_t kGemmLds = kStages * kStageElems * sizeof(uint16_t);  // 128 KB
+constexpr int kPad = 32;                   // token counts and vocabulary chunks are padded to this
 constexpr int kChunkV = 16384;             // vocabulary columns per backward chunk
 constexpr float kL2E = 1.4426950408889634f;
 constexpr double kL2ED = 1.4426950408889634074;
@@ -78,6 +80,15 @@ struct GemmArgs {
   int accumulate;        // GM_ACC: add to Cf (else overwrite)
 };
 
+// Workgroup barrier for the LDS ring: the hardware barrier alone (the waits
+// before it are explicit), fenced for the compiler so no memory access moves
+// across it.
+__device__ inline void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ inline uint16_t bf16_bits(float x) {
   const __bf16 h = (__bf16)x;  // round to nearest even
   return __builtin_bit_cast(uint16_t, h);
@@ -97,9 +108,6 @@ __device__ inline float row16_sum(float v) {
 
 template <int MODE>
 __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
-  // two LDS stages of [A 256 x 64 | B 256 x 64] bfloat16; 16-byte chunk c of
-  // row r sits at chunk position c ^ (r & 7) so the 16 rows an MFMA operand
-  // read touches spread over the banks
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,36 +136,46 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     if (MODE != GM_STORE) return;
   }
 
-  // global -> registers -> LDS, kLoadsPerThread chunks of 16 B of A and of B
-  // per thread per stage.  Each load writes its register directly (a chunk
-  // past K stays zero): the registers are read only when the stage is copied
-  // to LDS, so the loads stay in flight across the whole MFMA phase.
-  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto gload = [&](int64_t k0) {
+  // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
+  // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled
+  // by direct global -> LDS loads issued kStages-1 stages ahead.  Each wave
+  // instruction moves 16 rows x 64 B (lane l: row l/4, 16-byte chunk l%4);
+  // wavefronts 0-3 load A, 4-7 load B.  Rows past M or N re-read the last
+  // valid row (their results are never used).  K is a multiple of 32.
+  const int64_t nk = K / GBK;
+  const int64_t mlast = M > 0 ? M - 1 : 0;
+  auto dma = [&](int64_t kt) {
+    uint16_t* slot = smem + (kt % kStages) * kStageElems;
 #pragma unroll
-    for (int p = 0; p < kLoadsPerThread; ++p) {
-      const int q = tid + GT * p;
-      const int64_t k = k0 + 8 * (q & 7);
-      const int64_t row = m0 + (q >> 3);
-      const int64_t rc = row < M ? row : (M > 0 ? M - 1 : 0);
-      ra[p] = (k < K && M > 0) ? *reinterpret_cast<const u32x4*>(g.A + rc * g.lda + k)
-                               : u32x4{0, 0, 0, 0};
-      const int64_t col = n0 + (q >> 3);
-      const int64_t cc = col < g.N ? col : g.N - 1;
-      rb[p] = k < K ? *reinterpret_cast<const u32x4*>(g.B + cc * g.ldb + k) : u32x4{0, 0, 0, 0};
+    for (int p = 0; p < kDmaPerThread; ++p) {
+      const int blk = wave * kDmaPerThread + p;  // 16-row block of the stage
+      const int r = blk * 16 + (lane >> 2);
+      const int64_t k = kt * GBK + 8 * (lane & 3);
+      const uint16_t* src;
+      if (blk < GBM / 16) {
+        const int64_t row = m0 + r;
+        src = g.A + (row < M ? row : mlast) * g.lda + k;
+      } else {
+        const int64_t col = n0 + (r - GBM);
+        src = g.B + (col < g.N ? col : g.N - 1) * g.ldb + k;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)src,
+          (__attribute__((address_space(3))) void*)(slot + blk * 16 * GBK), 16, 0, 0);
     }
   };
-  auto swrite = [&](int buf) {
-    uint16_t* As = smem + buf * kStageElems;
-    uint16_t* Bs = As + GBM * GBK;
+  const int fr = lane & 15;       // row (A) / column (B) within a 16 x 16 block
+  const int fk = 8 * (lane >> 4);  // first of the lane's 8 reduction indices
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto frags = [&](int64_t kt, int buf) {
+    const uint16_t* As = smem + (kt % kStages) * kStageElems;
+    const uint16_t* Bs = As + GBM * GBK;
 #pragma unroll
-    for (int p = 0; p < kLoadsPerThread; ++p) {
-      const int q = tid + GT * p;
-      const int r = q >> 3, c = q & 7;
-      const int off = r * GBK + 8 * (c ^ (r & 7));
-      *reinterpret_cast<u32x4*>(As + off) = ra[p];
-      *reinterpret_cast<u32x4*>(Bs + off) = rb[p];
-    }
+    for (int i = 0; i < FM; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
   };
 
   f32x4 acc[FM][FN];
@@ -166,42 +184,50 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t nk = (K + GBK - 1) / GBK;
+  // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+  // operations are outstanding, leave the other counters alone
+  constexpr int kWaitVm0 = 0x0F70;              // vmcnt(0)
+  constexpr int kWaitVmStage = 0x0F70 | kDmaPerThread;  // one stage still in flight
+  constexpr int kWaitVm2Stages = 0x0F70 | (2 * kDmaPerThread);
   if (nk > 0) {
-    gload(0);
-    swrite(0);
+    for (int64_t s = 0; s < kStages - 1 && s < nk; ++s) dma(s);
+    // stage 0 complete: the loads of stages 1 and 2 may still be in flight
+    if (nk >= 3)
+      __builtin_amdgcn_s_waitcnt(kWaitVm2Stages);
+    else if (nk == 2)
+      __builtin_amdgcn_s_waitcnt(kWaitVmStage);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    ring_barrier();
+    frags(0, 0);
   }
-  __syncthreads();
-  const int fr = lane & 15;  // row (A) / column (B) within a 16 x 16 block
-  const int fc = lane >> 4;  // which 8 of the MFMA's 32 reduction indices
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nk) gload((kt + 1) * GBK);
-    const uint16_t* As = smem + cur * kStageElems;
-    const uint16_t* Bs = As + GBM * GBK;
+  // one step: stage kt's operands are in registers `cur`; make stage kt+1
+  // visible, refill the slot stage kt-1 used, read stage kt+1's operands into
+  // the other registers while stage kt's MFMAs run
+  auto step = [&](int64_t kt, int cur) {
+    if (kt + 2 < nk)
+      __builtin_amdgcn_s_waitcnt(kWaitVmStage);  // stage kt+1 done, kt+2 in flight
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    ring_barrier();
+    if (kt + kStages - 1 < nk) dma(kt + kStages - 1);
+    // unconditional, so the LDS-read count is the same on every path (after
+    // the last stage it reads a stale slot, in bounds, never used)
+    frags(kt + 1, cur ^ 1);
 #pragma unroll
-    for (int s = 0; s < GBK / 32; ++s) {
-      const int c = 4 * s + fc;
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM + i * 16 + fr;
-        af[i] = *reinterpret_cast<const bf16x8*>(As + r * GBK + 8 * (c ^ (r & 7)));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WN + j * 16 + fr;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + r * GBK + 8 * (c ^ (r & 7)));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) swrite(cur ^ 1);
-    __syncthreads();
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0,
+                                                            0, 0);
+  };
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
   }
+  if (kt < nk) step(kt, 0);
+  __syncthreads();  // every wavefront is done with the ring before the epilogue reuses it
 
   // accumulator layout: acc[i][j][r] = C[m0 + wm*WM + i*16 + 4*(lane/16) + r]
   //                                    [n0 + wn*WN + j*16 + lane%16]
@@ -269,7 +295,8 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       ys[r] = ok ? g.ycol[row] : -1;
     }
     __syncthreads();
-    const int64_t mpad = (M + 7) & ~int64_t(7);
+    const int64_t mpad = (M + kPad - 1) / kPad * kPad;
+    const int64_t npad = (g.N + kPad - 1) / kPad * kPad;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rt0 = wm * WM + i * 16 + rq;
@@ -283,13 +310,13 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
           const int rt = rt0 + r;
           const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -sl[rt]));
           const float hit = (col + g.col_base == (int64_t)ys[rt]) ? 1.0f : 0.0f;
-          d[r] = bf16_bits(sc[rt] * (p - hit));
+          d[r] = col < g.N ? bf16_bits(sc[rt] * (p - hit)) : (uint16_t)0;
         }
-        if (col < g.N) {
+        if (col < npad) {  // columns past the chunk: zeros, so the products can read them
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (row0 + r < mpad) g.D[(row0 + r) * g.ldd + col] = d[r];
-          if (row0 < mpad) {  // 4 consecutive rows: all below mpad (a multiple of 8) or none
+          if (row0 < mpad) {  // 4 consecutive rows: all below mpad (a multiple of 32) or none
             const uint32_t lo = (uint32_t)d[0] | ((uint32_t)d[1] << 16);
             const uint32_t hi = (uint32_t)d[2] | ((uint32_t)d[3] << 16);
             *reinterpret_cast<uint2*>(g.Dt + col * g.ldt + row0) = make_uint2(lo, hi);
@@ -350,7 +377,7 @@ k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int
   if (tid == 0) {
     offs[N] = base;
     counts[0] = base;                // active tokens
-    counts[1] = (base + 7) & ~7;     // padded to a multiple of 8
+    counts[1] = (base + kPad - 1) / kPad * kPad;  // padded for the products over tokens
   }
 }
 
@@ -388,15 +415,17 @@ k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __res
   }
 }
 
-// dst[c, r] = src[r, c] for r < rows (device count if rows_dev) and zeros for
-// rows_dev <= r < its multiple of 8; 64 x 64 tiles through LDS.
+// dst[c, r] = src[r, c] for r < rows (or the device count rows_dev) and zeros
+// for r up to rows_pad (or rows_dev rounded up to kPad); 64 x 64 tiles through
+// LDS.  The grid covers ceil(rows_pad / 64) x ceil(cols / 64) tiles.
 __global__ void __launch_bounds__(256)
-k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int64_t cols,
-            const int32_t* __restrict__ rows_dev, uint16_t* __restrict__ dst, int64_t ld_dst) {
+k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int64_t rows_pad,
+            int64_t cols, const int32_t* __restrict__ rows_dev, uint16_t* __restrict__ dst,
+            int64_t ld_dst) {
   __shared__ uint16_t tile[64][65];
   const int64_t R = rows_dev ? (int64_t)*rows_dev : rows;
-  const int64_t Rpad = rows_dev ? ((R + 7) & ~int64_t(7)) : R;
-  const int64_t ntr = (rows + 63) / 64;
+  const int64_t Rpad = rows_dev ? (R + kPad - 1) / kPad * kPad : rows_pad;
+  const int64_t ntr = (rows_pad + 63) / 64;
   const int64_t r0 = (blockIdx.x % ntr) * 64;
   const int64_t c0 = (blockIdx.x / ntr) * 64;
   if (r0 >= Rpad) return;
@@ -494,7 +523,7 @@ struct LmWs {
   float* coef;       // [T]
   uint16_t* Ha;      // [T, H]
   uint16_t* Hat;     // [H, Tcap]
-  uint16_t* Wt;      // [H, V]
+  uint16_t* Wt;      // [H, Vpad] (zero columns past V)
   uint16_t* Dc;      // [Tcap, kChunkV]
   uint16_t* Dtc;     // [kChunkV, Tcap]
   float* dH;         // [Tcap, H]
@@ -503,9 +532,10 @@ struct LmWs {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws) {
-  const int64_t Tcap = round_up(T, 8);
+  const int64_t Tcap = round_up(T, kPad);
   const int64_t ntn = (V + GBN - 1) / GBN;
-  const int64_t vc = V < kChunkV ? round_up(V, 8) : kChunkV;
+  const int64_t vc = V < kChunkV ? round_up(V, kPad) : kChunkV;
+  const int64_t Vpad = round_up(V, kPad);
   size_t off = 0;
   char* b = static_cast<char*>(base);
   auto take = [&](size_t bytes) {
@@ -530,7 +560,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.coef = reinterpret_cast<float*>(take(4 * T));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
   w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
-  w.Wt = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * V));
+  w.Wt = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Vpad));
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
   w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
@@ -540,7 +570,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
 
 int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_t* T) {
   if (N <= 0 || C <= 0 || V <= 0 || H <= 0 || G <= 0 || N % G != 0) return DRGRPO_ERR_SHAPE;
-  if (V % 8 != 0 || H % 32 != 0 || V > (int64_t(1) << 30) || H > 65536) return DRGRPO_ERR_SHAPE;
+  if (V % 8 != 0 || H % kPad != 0 || V > (int64_t(1) << 30) || H > 65536) return DRGRPO_ERR_SHAPE;
   if (!mul_ok(N, C, T) || *T > (int64_t(1) << 30)) return DRGRPO_ERR_SHAPE;
   int64_t tmp;
   if (!mul_ok(*T, (V + GBN - 1) / GBN * 8, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
@@ -601,7 +631,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
   LmWs w;
   lm_carve(workspace, N, T, V, H, &w);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t Tcap = round_up(T, 8);
+  const int64_t Tcap = round_up(T, kPad);
+  const int64_t Vpad = round_up(V, kPad);
   const int64_t ntn = (V + GBN - 1) / GBN;
   const uint16_t* hid = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
@@ -619,12 +650,12 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
                      w.offs, w.act_pos, w.ycol, w.Ha, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   {
-    const int64_t blocks = ((V + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks), dim3(256), 0, st, Wb, H, V, H,
-                       (const int32_t*)nullptr, w.Wt, V);
+    const int64_t blocks = ((Vpad + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks), dim3(256), 0, st, Wb, H, V, Vpad, H,
+                       (const int32_t*)nullptr, w.Wt, Vpad);
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
-    const int64_t blocks2 = ((T + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, H, Tcap, H,
+    const int64_t blocks2 = ((Tcap + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, H, T, Tcap, H,
                        w.counts, w.Hat, Tcap);
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
   }
@@ -651,7 +682,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
   // backward, one vocabulary chunk at a time
-  const int64_t vc_cap = V < kChunkV ? round_up(V, 8) : kChunkV;
+  const int64_t vc_cap = V < kChunkV ? round_up(V, kPad) : kChunkV;
   for (int64_t v0 = 0; v0 < V; v0 += kChunkV) {
     const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
     GemmArgs d = {};
@@ -677,10 +708,10 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
     a.A = w.Dc;
     a.lda = vc_cap;
     a.B = w.Wt + v0;
-    a.ldb = V;
+    a.ldb = Vpad;
     a.M = T;
     a.N = H;
-    a.K = wv;
+    a.K = round_up(wv, kPad);
     a.M_dev = w.counts;
     a.Cf = w.dH;
     a.ldc = H;
