@@ -157,7 +157,8 @@ int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_
  *   out_dhidden [N*C, H] bfloat16 = dL/dhidden = dlogits . W (zero rows for
  *               tokens without gradient; NaN rows for a bad token id).
  *   out_dW      [V, H] bfloat16 = dL/dW = dlogits^T . hidden.
- *   H must be a multiple of 32 and V of 8; hidden, W and the outputs
+ *   H must be a multiple of 32 and at most 65536, V a multiple of 8 and
+ *   N*C at most 2^24 (else DRGRPO_ERR_SHAPE); hidden, W and the outputs
  *   16-byte aligned (else DRGRPO_ERR_ALIAS).  Other arguments as for
  *   drgrpo_loss_fwd_bwd.  Logits accumulate in binary32 on the matrix cores;
  *   dlogits enter the two gradient products rounded to bfloat16, one

@@ -80,6 +80,11 @@ struct GemmArgs {
   int accumulate;        // GM_ACC: add to Cf (else overwrite)
 };
 
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // Workgroup barrier for the LDS ring: the hardware barrier alone (the waits
 // before it are explicit), fenced for the compiler so no memory access moves
 // across it.
@@ -94,17 +99,19 @@ __device__ inline uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// max / sum over the 16 lanes of a DPP row (lanes sharing l / 16)
-__device__ inline float row16_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
-  return v;
+// Cross-lane moves within a DPP row of 16 lanes (lanes sharing l / 16).  A
+// max or sum over the row takes four steps: swaps within quads (xor 1, xor 2),
+// then across quad pairs (half-row mirror) and row halves (row mirror); every
+// lane of the row ends with the result.
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-__device__ inline float row16_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 16);
-  return v;
-}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
 
 template <int MODE>
 __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
@@ -234,38 +241,78 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // (the LDS stages are free from here on and hold the epilogue's tables)
   const int rq = 4 * (lane >> 4);
 
+  // columns of this tile that exist (the rest of the tile is padding)
+  const int ncols = (int)(g.N - n0 < GBN ? g.N - n0 : GBN);
+  const int lc0 = wn * WN + fr;  // tile-local column of acc[.][0]
   if constexpr (MODE == GM_LSE) {
     float2* red = reinterpret_cast<float2*>(smem);              // [NWN][GBM]
-    int32_t* ys = reinterpret_cast<int32_t*>(red + NWN * GBM);  // [GBM]
+    int32_t* yl = reinterpret_cast<int32_t*>(red + NWN * GBM);  // [GBM] tile-local target column
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
-      ys[r] = row < M ? g.ycol[row] : -1;
+      // -1 (no target) or a column of another tile never equals a local column
+      yl[r] = row < M ? (int32_t)(g.ycol[row] < 0 ? -1 : g.ycol[row] - (g.col_base + n0)) : -1;
     }
     __syncthreads();
+    // full tiles (the common case) compile without the column checks
+    auto body = [&](auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;
+      // the four rows of a lane run in lockstep so the cross-lane steps of
+      // one row fill the others' DPP wait states
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
+        const int rt0 = wm * WM + i * 16 + rq;
+        const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
+        const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+        float mx[4], sm[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rt = wm * WM + i * 16 + rq + r;
-        float vv[FN];
-        float mx = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          float xv = 0.0f;
+          bool hit = false;
+          mx[r] = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t col = n0 + wn * WN + j * 16 + fr;
-          vv[j] = col < g.N ? acc[i][j][r] : -INFINITY;
-          mx = fmaxf(mx, vv[j]);
-          if (col + g.col_base == (int64_t)ys[rt]) g.xy[m0 + rt] = vv[j];
+          for (int j = 0; j < FN; ++j) {
+            const int lc = lc0 + j * 16;
+            if (!kFull && lc >= ncols) acc[i][j][r] = -INFINITY;
+            mx[r] = fmaxf(mx[r], acc[i][j][r]);
+            xv = lc == yv[r] ? acc[i][j][r] : xv;
+            hit = hit || lc == yv[r];
+          }
+          if (hit) g.xy[m0 + rt0 + r] = xv;
         }
-        mx = row16_max(mx);
-        // a quarter tile past the last vocabulary column holds no value at all
-        const float base = mx == -INFINITY ? 0.0f : mx;
-        float sm = 0.0f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sm += __builtin_amdgcn_exp2f((vv[j] - base) * kL2E);
-        sm = row16_sum(sm);
-        if (fr == 0) red[wn * GBM + rt] = make_float2(mx, sm);
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppXor1>(mx[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppXor2>(mx[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppHalfMirror>(mx[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppMirror>(mx[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // a quarter tile past the last vocabulary column holds no value at all
+          const float nb = mx[r] == -INFINITY ? 0.0f : -mx[r] * kL2E;
+          sm[r] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) sm[r] += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, nb));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor1>(sm[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor2>(sm[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppHalfMirror>(sm[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppMirror>(sm[r]);
+        if (fr == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[wn * GBM + rt0 + r] = make_float2(mx[r], sm[r]);
+        }
       }
-    }
+    };
+    if (ncols == GBN)
+      body(BoolC<true>{});
+    else
+      body(BoolC<false>{});
     __syncthreads();
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
@@ -286,65 +333,103 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   } else if constexpr (MODE == GM_D) {
     float* sl = reinterpret_cast<float*>(smem);  // [GBM] lse * log2(e)
     float* sc = sl + GBM;                        // [GBM] coef
-    int32_t* ys = reinterpret_cast<int32_t*>(sc + GBM);
+    int32_t* yl = reinterpret_cast<int32_t*>(sc + GBM);  // [GBM] tile-local target column
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       const bool ok = row < M;
       sl[r] = ok ? g.lse2[row] : INFINITY;  // rows past the active count: exact zeros
       sc[r] = ok ? g.coef[row] : 0.0f;
-      ys[r] = ok ? g.ycol[row] : -1;
+      yl[r] = ok ? (int32_t)(g.ycol[row] < 0 ? -1 : g.ycol[row] - (g.col_base + n0)) : -1;
     }
     __syncthreads();
+    // rows up to the active count rounded up to kPad, columns up to the
+    // chunk width rounded up to kPad are written (zeros past the data), so
+    // the products over the chunk may read whole kPad blocks
     const int64_t mpad = (M + kPad - 1) / kPad * kPad;
     const int64_t npad = (g.N + kPad - 1) / kPad * kPad;
+    const int nrows_w = (int)(mpad - m0 < GBM ? mpad - m0 : GBM);
+    const int ncols_w = (int)(npad - n0 < GBN ? npad - n0 : GBN);
+    uint16_t* Dw = g.D + (m0 + wm * WM + rq) * g.ldd + n0 + lc0;
+    uint16_t* Dtw = g.Dt + (n0 + lc0) * g.ldt + m0 + wm * WM + rq;
+    const int ldd = (int)g.ldd, ldt = (int)g.ldt;
+    auto body = [&](auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rt0 = wm * WM + i * 16 + rq;
-      const int64_t row0 = m0 + rt0;
+      const float4 l4 = *reinterpret_cast<const float4*>(sl + rt0);
+      const float4 c4 = *reinterpret_cast<const float4*>(sc + rt0);
+      const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+      const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+      // 4 consecutive rows: all below mpad (a multiple of 32) or none
+      const bool row_ok = rt0 < nrows_w;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int64_t col = n0 + wn * WN + j * 16 + fr;
+        const int lc = lc0 + j * 16;
         uint16_t d[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int rt = rt0 + r;
-          const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -sl[rt]));
-          const float hit = (col + g.col_base == (int64_t)ys[rt]) ? 1.0f : 0.0f;
-          d[r] = col < g.N ? bf16_bits(sc[rt] * (p - hit)) : (uint16_t)0;
+          const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -lv[r]));
+          const float hit = lc == yv[r] ? 1.0f : 0.0f;
+          d[r] = (kFull || lc < ncols) ? bf16_bits(cv[r] * (p - hit)) : (uint16_t)0;
         }
-        if (col < npad) {  // columns past the chunk: zeros, so the products can read them
+        if (kFull || (row_ok && lc < ncols_w)) {
+          const int off = i * 16 * ldd + j * 16;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (row0 + r < mpad) g.D[(row0 + r) * g.ldd + col] = d[r];
-          if (row0 < mpad) {  // 4 consecutive rows: all below mpad (a multiple of 32) or none
-            const uint32_t lo = (uint32_t)d[0] | ((uint32_t)d[1] << 16);
-            const uint32_t hi = (uint32_t)d[2] | ((uint32_t)d[3] << 16);
-            *reinterpret_cast<uint2*>(g.Dt + col * g.ldt + row0) = make_uint2(lo, hi);
-          }
+          for (int r = 0; r < 4; ++r) Dw[off + r * ldd] = d[r];
+          const uint32_t lo = (uint32_t)d[0] | ((uint32_t)d[1] << 16);
+          const uint32_t hi = (uint32_t)d[2] | ((uint32_t)d[3] << 16);
+          *reinterpret_cast<uint2*>(Dtw + j * 16 * ldt + i * 16) = make_uint2(lo, hi);
         }
       }
     }
+    };
+    if (ncols == GBN && nrows_w == GBM)
+      body(BoolC<true>{});
+    else
+      body(BoolC<false>{});
   } else {
     const int64_t Mst = MODE == GM_STORE ? g.M : M;
+    const int nrows = (int)(Mst - m0 < GBM ? Mst - m0 : GBM);
+    const int ldc = (int)g.ldc;
+    const int64_t base = (m0 + wm * WM + rq) * g.ldc + n0 + lc0;
+    auto body = [&](auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
+        const int rt0 = wm * WM + i * 16 + rq;
+        auto ok = [&](int j, int r) { return kFull || (lc0 + j * 16 < ncols && rt0 + r < nrows); };
+        if constexpr (MODE == GM_ACC) {
+          float* c = g.Cf + base + i * 16 * ldc;
+          float old[FN][4] = {};
+          if (g.accumulate) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t col = n0 + wn * WN + j * 16 + fr;
-        if (col >= g.N) continue;
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = m0 + wm * WM + i * 16 + rq + r;
-          if (row >= Mst) continue;
-          if constexpr (MODE == GM_ACC) {
-            float* c = g.Cf + row * g.ldc + col;
-            *c = g.accumulate ? *c + acc[i][j][r] : acc[i][j][r];
-          } else {
-            g.Cb[row * g.ldc + col] = bf16_bits(acc[i][j][r]);
+              for (int r = 0; r < 4; ++r)
+                if (ok(j, r)) old[j][r] = c[r * ldc + j * 16];
           }
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (ok(j, r)) c[r * ldc + j * 16] = old[j][r] + acc[i][j][r];
+        } else {
+          uint16_t* c = g.Cb + base + i * 16 * ldc;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (ok(j, r)) c[r * ldc + j * 16] = bf16_bits(acc[i][j][r]);
         }
       }
-    }
+    };
+    if (ncols == GBN && nrows == GBM)
+      body(BoolC<true>{});
+    else
+      body(BoolC<false>{});
   }
 }
 
@@ -571,7 +656,8 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
 int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_t* T) {
   if (N <= 0 || C <= 0 || V <= 0 || H <= 0 || G <= 0 || N % G != 0) return DRGRPO_ERR_SHAPE;
   if (V % 8 != 0 || H % kPad != 0 || V > (int64_t(1) << 30) || H > 65536) return DRGRPO_ERR_SHAPE;
-  if (!mul_ok(N, C, T) || *T > (int64_t(1) << 30)) return DRGRPO_ERR_SHAPE;
+  // token rows up to 2^24 keep every in-tile offset of the epilogues in 32 bits
+  if (!mul_ok(N, C, T) || *T > (int64_t(1) << 24)) return DRGRPO_ERR_SHAPE;
   int64_t tmp;
   if (!mul_ok(*T, (V + GBN - 1) / GBN * 8, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
       !mul_ok(V, H * 2, &tmp))
