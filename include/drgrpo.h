@@ -163,8 +163,9 @@ int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_
  *   drgrpo_loss_fwd_bwd.  Logits accumulate in binary32 on the matrix cores;
  *   dlogits enter the two gradient products rounded to bfloat16, one
  *   vocabulary chunk at a time.
- * The workspace (drgrpo_lmhead_workspace_bytes) holds transposed copies of W
- * and of the active tokens' hidden rows and one chunk of dlogits. */
+ * The workspace (drgrpo_lmhead_workspace_bytes) holds the active tokens'
+ * hidden rows (and their transpose), one vocabulary chunk of W transposed and
+ * one chunk of dlogits. */
 size_t drgrpo_lmhead_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G);
 
 int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,

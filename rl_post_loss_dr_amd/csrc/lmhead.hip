@@ -18,9 +18,9 @@
  *   GM_ACC    dhidden += dlogits_chunk . W_chunk   (binary32 accumulator)
  *   GM_STORE  dW_chunk = dlogits_chunk^T . H_a     (bfloat16 result)
  *
- * Transposed copies of W and of the compacted hidden states give every
- * product its reduction dimension contiguous.  No floating-point atomics:
- * results are bitwise reproducible.
+ * Transposed copies of the compacted hidden states and of each vocabulary
+ * chunk of W give every product its reduction dimension contiguous.  No
+ * floating-point atomics: results are bitwise reproducible.
  */
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -113,6 +113,10 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// chunk permutation of LDS row r (see the main loop): rows of one parity
+// among 8 consecutive, and rows equal mod 4 among 16, get distinct values
+__device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
 template <int MODE>
 __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -127,10 +131,13 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // order runs along the operand that is small: row tiles fastest when B is
   // the large operand (the vocabulary-wide products), column tiles fastest
   // when A is (the products reducing over a dlogits chunk)
-  const int64_t ntm = (g.M + GBM - 1) / GBM;
+  // The grid covers the static row bound; only the tiles of the first M rows
+  // (M read on the device) take part, spread evenly over the XCDs.
+  const int64_t ntm = (M + GBM - 1) / GBM;
   const int64_t ntn_t = (g.N + GBN - 1) / GBN;
   const int64_t total = ntm * ntn_t;
   const int64_t b = blockIdx.x;
+  if (b >= total) return;
   const int64_t q8 = total / 8;
   const int64_t v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
   constexpr bool kColsFastest = MODE == GM_ACC || MODE == GM_STORE;
@@ -138,17 +145,15 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   const int64_t tn = kColsFastest ? v % ntn_t : v / ntm;
   const int64_t m0 = tm * GBM;
   const int64_t n0 = tn * GBN;
-  if (m0 >= M) {
-    // GM_STORE writes every (static) row; the others have nothing to do
-    if (MODE != GM_STORE) return;
-  }
 
   // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
   // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled
   // by direct global -> LDS loads issued kStages-1 stages ahead.  Each wave
-  // instruction moves 16 rows x 64 B (lane l: row l/4, 16-byte chunk l%4);
+  // instruction moves 16 rows x 64 B (lane l: row l/4, LDS chunk l%4);
   // wavefronts 0-3 load A, 4-7 load B.  Rows past M or N re-read the last
   // valid row (their results are never used).  K is a multiple of 32.
+  // The four 16-byte chunks of a row are stored XOR-permuted by swz(row % 16),
+  // so the fragment reads (16 rows, one chunk) spread over all LDS banks.
   const int64_t nk = K / GBK;
   const int64_t mlast = M > 0 ? M - 1 : 0;
   auto dma = [&](int64_t kt) {
@@ -157,7 +162,7 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     for (int p = 0; p < kDmaPerThread; ++p) {
       const int blk = wave * kDmaPerThread + p;  // 16-row block of the stage
       const int r = blk * 16 + (lane >> 2);
-      const int64_t k = kt * GBK + 8 * (lane & 3);
+      const int64_t k = kt * GBK + 8 * ((lane & 3) ^ swz(lane >> 2));
       const uint16_t* src;
       if (blk < GBM / 16) {
         const int64_t row = m0 + r;
@@ -171,8 +176,9 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
           (__attribute__((address_space(3))) void*)(slot + blk * 16 * GBK), 16, 0, 0);
     }
   };
-  const int fr = lane & 15;       // row (A) / column (B) within a 16 x 16 block
-  const int fk = 8 * (lane >> 4);  // first of the lane's 8 reduction indices
+  const int fr = lane & 15;  // row (A) / column (B) within a 16 x 16 block
+  // LDS position of the lane's 8 reduction indices 8*(lane/16) .. +7
+  const int fk = 8 * ((lane >> 4) ^ swz(fr));
   bf16x8 fa[2][FM], fb[2][FN];
   auto frags = [&](int64_t kt, int buf) {
     const uint16_t* As = smem + (kt % kStages) * kStageElems;
@@ -391,8 +397,7 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     else
       body(BoolC<false>{});
   } else {
-    const int64_t Mst = MODE == GM_STORE ? g.M : M;
-    const int nrows = (int)(Mst - m0 < GBM ? Mst - m0 : GBM);
+    const int nrows = (int)(M - m0 < GBM ? M - m0 : GBM);
     const int ldc = (int)g.ldc;
     const int64_t base = (m0 + wm * WM + rq) * g.ldc + n0 + lc0;
     auto body = [&](auto full_tag) {
@@ -608,7 +613,7 @@ struct LmWs {
   float* coef;       // [T]
   uint16_t* Ha;      // [T, H]
   uint16_t* Hat;     // [H, Tcap]
-  uint16_t* Wt;      // [H, Vpad] (zero columns past V)
+  uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W, transposed
   uint16_t* Dc;      // [Tcap, kChunkV]
   uint16_t* Dtc;     // [kChunkV, Tcap]
   float* dH;         // [Tcap, H]
@@ -620,7 +625,6 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   const int64_t Tcap = round_up(T, kPad);
   const int64_t ntn = (V + GBN - 1) / GBN;
   const int64_t vc = V < kChunkV ? round_up(V, kPad) : kChunkV;
-  const int64_t Vpad = round_up(V, kPad);
   size_t off = 0;
   char* b = static_cast<char*>(base);
   auto take = [&](size_t bytes) {
@@ -645,7 +649,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.coef = reinterpret_cast<float*>(take(4 * T));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
   w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
-  w.Wt = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Vpad));
+  w.Wtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * vc));
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
   w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
@@ -718,7 +722,6 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
   lm_carve(workspace, N, T, V, H, &w);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t Tcap = round_up(T, kPad);
-  const int64_t Vpad = round_up(V, kPad);
   const int64_t ntn = (V + GBN - 1) / GBN;
   const uint16_t* hid = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
@@ -736,10 +739,6 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
                      w.offs, w.act_pos, w.ycol, w.Ha, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   {
-    const int64_t blocks = ((Vpad + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks), dim3(256), 0, st, Wb, H, V, Vpad, H,
-                       (const int32_t*)nullptr, w.Wt, Vpad);
-    if ((rc = launch_status()) != DRGRPO_OK) return rc;
     const int64_t blocks2 = ((Tcap + 63) / 64) * ((H + 63) / 64);
     hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, H, T, Tcap, H,
                        w.counts, w.Hat, Tcap);
@@ -790,11 +789,18 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
     d.ldt = Tcap;
     if ((rc = launch_gemm<GM_D>(d, st)) != DRGRPO_OK) return rc;
 
+    // the chunk of W transposed, [H, vc_cap] with zero columns past wv
+    const int64_t wv_pad = round_up(wv, kPad);
+    const int64_t tblocks = ((wv_pad + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb + v0 * H, H, wv,
+                       wv_pad, H, (const int32_t*)nullptr, w.Wtc, vc_cap);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+
     GemmArgs a = {};  // dhidden += D_chunk . W_chunk
     a.A = w.Dc;
     a.lda = vc_cap;
-    a.B = w.Wt + v0;
-    a.ldb = Vpad;
+    a.B = w.Wtc;
+    a.ldb = vc_cap;
     a.M = T;
     a.N = H;
     a.K = round_up(wv, kPad);
