@@ -34,6 +34,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256;                   // workgroup tile rows (A rows)
 constexpr int GBN = 256;                   // workgroup tile columns (B rows)
@@ -45,7 +46,9 @@ constexpr int FM = WM / 16, FN = WN / 16;  // 8 x 4 MFMA blocks per wavefront
 constexpr int kStages = 4;                 // LDS ring depth
 constexpr int kStageElems = (GBM + GBN) * GBK;  // bfloat16 per LDS stage (32 KB)
 constexpr int kDmaPerThread = kStageElems / 8 / GT;  // 16-byte direct loads per thread per stage
-constexpr size_t kGemmLds = kStages * kStageElems * sizeof(uint16_t);  // 128 KB
+constexpr int kRingElems = kStages * kStageElems;  // 128 KB ring
+constexpr int kTableBytes = 4096;          // per-row epilogue tables, past the ring
+constexpr size_t kGemmLds = kRingElems * sizeof(uint16_t) + kTableBytes;
 constexpr int kPad = 32;                   // token counts and vocabulary chunks are padded to this
 constexpr int kChunkV = 16384;             // vocabulary columns per backward chunk
 constexpr float kL2E = 1.4426950408889634f;
@@ -116,6 +119,13 @@ constexpr int kDppMirror = 0x140;
 // chunk permutation of LDS row r (see the main loop): rows of one parity
 // among 8 consecutive, and rows equal mod 4 among 16, get distinct values
 __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// quad permutation of row c of an epilogue stage: an even value, so 16-byte
+// pairs of quads stay in order; 16 consecutive rows get distinct values, and
+// 4 rows from a multiple of 4 distinct bits 2-3 (the transposing reads)
+__device__ inline int stage_swz(int c) {
+  return 2 * (((c & 3) << 1) | ((c >> 2) & 1) | (((c >> 3) & 1) << 3));
+}
 
 template <int MODE>
 __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
@@ -337,9 +347,9 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       g.part[row * g.ntn + tn] = make_float2(mx, sm);
     }
   } else if constexpr (MODE == GM_D) {
-    float* sl = reinterpret_cast<float*>(smem);  // [GBM] lse * log2(e)
-    float* sc = sl + GBM;                        // [GBM] coef
-    int32_t* yl = reinterpret_cast<int32_t*>(sc + GBM);  // [GBM] tile-local target column
+    float* sl = reinterpret_cast<float*>(smem + kRingElems);  // [GBM] lse * log2(e)
+    float* sc = sl + GBM;                                     // [GBM] coef
+    int32_t* yl = reinterpret_cast<int32_t*>(sc + GBM);       // [GBM] tile-local target column
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       const bool ok = row < M;
@@ -347,7 +357,6 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       sc[r] = ok ? g.coef[row] : 0.0f;
       yl[r] = ok ? (int32_t)(g.ycol[row] < 0 ? -1 : g.ycol[row] - (g.col_base + n0)) : -1;
     }
-    __syncthreads();
     // rows up to the active count rounded up to kPad, columns up to the
     // chunk width rounded up to kPad are written (zeros past the data), so
     // the products over the chunk may read whole kPad blocks
@@ -355,42 +364,72 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     const int64_t npad = (g.N + kPad - 1) / kPad * kPad;
     const int nrows_w = (int)(mpad - m0 < GBM ? mpad - m0 : GBM);
     const int ncols_w = (int)(npad - n0 < GBN ? npad - n0 : GBN);
-    uint16_t* Dw = g.D + (m0 + wm * WM + rq) * g.ldd + n0 + lc0;
-    uint16_t* Dtw = g.Dt + (n0 + lc0) * g.ldt + m0 + wm * WM + rq;
-    const int ldd = (int)g.ldd, ldt = (int)g.ldt;
+    // Each wavefront stages its 128 x 64 block of dlogits in its own 16 KB of
+    // the (now idle) ring, column-major: row c of the stage holds column c of
+    // the block, 128 bfloat16 in 32 eight-byte quads, quad q stored at
+    // q ^ stage_swz(c).  Both stores then leave with 16-byte accesses.
+    uint16_t* stg = smem + wave * (WM * WN);
+    __syncthreads();
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int rt0 = wm * WM + i * 16 + rq;
-      const float4 l4 = *reinterpret_cast<const float4*>(sl + rt0);
-      const float4 c4 = *reinterpret_cast<const float4*>(sc + rt0);
-      const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-      const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
-      // 4 consecutive rows: all below mpad (a multiple of 32) or none
-      const bool row_ok = rt0 < nrows_w;
+      for (int i = 0; i < FM; ++i) {
+        const int rt0 = wm * WM + i * 16 + rq;
+        const float4 l4 = *reinterpret_cast<const float4*>(sl + rt0);
+        const float4 c4 = *reinterpret_cast<const float4*>(sc + rt0);
+        const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+        const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+        const int q = i * 4 + (lane >> 4);  // quad of the lane's 4 rows
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int lc = lc0 + j * 16;
-        uint16_t d[4];
+        for (int j = 0; j < FN; ++j) {
+          const int lc = lc0 + j * 16;
+          uint16_t d[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -lv[r]));
-          const float hit = lc == yv[r] ? 1.0f : 0.0f;
-          d[r] = (kFull || lc < ncols) ? bf16_bits(cv[r] * (p - hit)) : (uint16_t)0;
-        }
-        if (kFull || (row_ok && lc < ncols_w)) {
-          const int off = i * 16 * ldd + j * 16;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Dw[off + r * ldd] = d[r];
-          const uint32_t lo = (uint32_t)d[0] | ((uint32_t)d[1] << 16);
-          const uint32_t hi = (uint32_t)d[2] | ((uint32_t)d[3] << 16);
-          *reinterpret_cast<uint2*>(Dtw + j * 16 * ldt + i * 16) = make_uint2(lo, hi);
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -lv[r]));
+            const float hit = lc == yv[r] ? 1.0f : 0.0f;
+            d[r] = (kFull || lc < ncols) ? bf16_bits(cv[r] * (p - hit)) : (uint16_t)0;
+          }
+          const int c = j * 16 + fr;  // column within the wavefront block
+          *reinterpret_cast<uint2*>(stg + c * WM + 4 * (q ^ stage_swz(c))) =
+              make_uint2((uint32_t)d[0] | ((uint32_t)d[1] << 16),
+                         (uint32_t)d[2] | ((uint32_t)d[3] << 16));
         }
       }
-    }
+      __syncthreads();
+      const int grp = lane >> 4, li = lane & 15;
+      const int rw0 = wm * WM, cw0 = wn * WN;  // wavefront block within the tile
+      // dlogits rows: the transposing LDS read gives lane li of a 16-lane
+      // group 4 consecutive columns of row tb + li, when lane 4e + q4 of the
+      // group points at quad tb/4 + q4 of stage row (first column + e)
+      const int e = li >> 2, q4 = li & 3;
+#pragma unroll
+      for (int sidx = 0; sidx < 2 * (WM / 16); ++sidx) {
+        const int tb = 16 * (sidx % (WM / 16));
+        const int cb = 32 * (sidx / (WM / 16)) + 8 * grp;  // 8 columns of this group
+        const int qq = (tb >> 2) + q4;
+        const int ca = cb + e, cc = cb + 4 + e;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(stg + ca * WM + 4 * (qq ^ stage_swz(ca))));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(stg + cc * WM + 4 * (qq ^ stage_swz(cc))));
+        const int t = rw0 + tb + li;
+        if (kFull || (t < nrows_w && cw0 + cb < ncols_w)) {
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          *reinterpret_cast<u32x4*>(g.D + (m0 + t) * g.ldd + n0 + cw0 + cb) =
+              u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+      }
+      // transposed rows: 16 bytes (8 rows of one column) per lane
+#pragma unroll
+      for (int sidx = 0; sidx < WN / 4; ++sidx) {
+        const int c = 4 * sidx + grp;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + c * WM + 4 * ((2 * li) ^ stage_swz(c)));
+        if (kFull || (cw0 + c < ncols_w && rw0 + 8 * li < nrows_w))
+          *reinterpret_cast<u32x4*>(g.Dt + (n0 + cw0 + c) * g.ldt + m0 + rw0 + 8 * li) = v;
+      }
     };
     if (ncols == GBN && nrows_w == GBM)
       body(BoolC<true>{});
