@@ -127,6 +127,43 @@ __device__ inline int stage_swz(int c) {
   return 2 * (((c & 3) << 1) | ((c >> 2) & 1) | (((c >> 3) & 1) << 3));
 }
 
+// Row-major 16-byte stores of a wavefront's staged 128 x 64 bfloat16 block:
+// out[t * ld + c] for rows t < rows_lim and 8-column groups c < cols_lim
+// (cols_lim a multiple of 8).  The transposing LDS read gives lane li of a
+// 16-lane group 4 consecutive columns of row tb + li when lane 4e + q4 of the
+// group points at quad tb/4 + q4 of stage row (first column + e).
+template <bool kFull>
+__device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t* out, int64_t ld,
+                                         int rows_lim, int cols_lim) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int e = li >> 2, q4 = li & 3;
+#pragma unroll
+  for (int sidx = 0; sidx < 2 * (WM / 16); ++sidx) {
+    const int tb = 16 * (sidx % (WM / 16));
+    const int cb = 32 * (sidx / (WM / 16)) + 8 * grp;  // 8 columns of this group
+    const int qq = (tb >> 2) + q4;
+    const int ca = cb + e, cc = cb + 4 + e;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(stg + ca * WM + 4 * (qq ^ stage_swz(ca))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(stg + cc * WM + 4 * (qq ^ stage_swz(cc))));
+    const int t = tb + li;
+    if (kFull || (t < rows_lim && cb < cols_lim)) {
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      *reinterpret_cast<u32x4*>(out + t * ld + cb) = u32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+}
+
+// Stage column c = j*16 + (lane % 16) of the wavefront block, rows
+// i*16 + 4*(lane/16) .. +3 (one MFMA accumulator quad, as bfloat16 bits).
+__device__ inline void stage_quad(uint16_t* stg, int lane, int i, int j, const uint16_t d[4]) {
+  const int q = i * 4 + (lane >> 4);
+  const int c = j * 16 + (lane & 15);
+  *reinterpret_cast<uint2*>(stg + c * WM + 4 * (q ^ stage_swz(c))) =
+      make_uint2((uint32_t)d[0] | ((uint32_t)d[1] << 16), (uint32_t)d[2] | ((uint32_t)d[3] << 16));
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -381,7 +418,6 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
         const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
-        const int q = i * 4 + (lane >> 4);  // quad of the lane's 4 rows
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int lc = lc0 + j * 16;
@@ -392,36 +428,14 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
             const float hit = lc == yv[r] ? 1.0f : 0.0f;
             d[r] = (kFull || lc < ncols) ? bf16_bits(cv[r] * (p - hit)) : (uint16_t)0;
           }
-          const int c = j * 16 + fr;  // column within the wavefront block
-          *reinterpret_cast<uint2*>(stg + c * WM + 4 * (q ^ stage_swz(c))) =
-              make_uint2((uint32_t)d[0] | ((uint32_t)d[1] << 16),
-                         (uint32_t)d[2] | ((uint32_t)d[3] << 16));
+          stage_quad(stg, lane, i, j, d);
         }
       }
       __syncthreads();
       const int grp = lane >> 4, li = lane & 15;
       const int rw0 = wm * WM, cw0 = wn * WN;  // wavefront block within the tile
-      // dlogits rows: the transposing LDS read gives lane li of a 16-lane
-      // group 4 consecutive columns of row tb + li, when lane 4e + q4 of the
-      // group points at quad tb/4 + q4 of stage row (first column + e)
-      const int e = li >> 2, q4 = li & 3;
-#pragma unroll
-      for (int sidx = 0; sidx < 2 * (WM / 16); ++sidx) {
-        const int tb = 16 * (sidx % (WM / 16));
-        const int cb = 32 * (sidx / (WM / 16)) + 8 * grp;  // 8 columns of this group
-        const int qq = (tb >> 2) + q4;
-        const int ca = cb + e, cc = cb + 4 + e;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(stg + ca * WM + 4 * (qq ^ stage_swz(ca))));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(stg + cc * WM + 4 * (qq ^ stage_swz(cc))));
-        const int t = rw0 + tb + li;
-        if (kFull || (t < nrows_w && cw0 + cb < ncols_w)) {
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          *reinterpret_cast<u32x4*>(g.D + (m0 + t) * g.ldd + n0 + cw0 + cb) =
-              u32x4{l2.x, l2.y, h2.x, h2.y};
-        }
-      }
+      store_staged_rows<kFull>(stg, lane, g.D + (m0 + rw0) * g.ldd + n0 + cw0, g.ldd,
+                               nrows_w - rw0, ncols_w - cw0);
       // transposed rows: 16 bytes (8 rows of one column) per lane
 #pragma unroll
       for (int sidx = 0; sidx < WN / 4; ++sidx) {
@@ -438,6 +452,8 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   } else {
     const int nrows = (int)(M - m0 < GBM ? M - m0 : GBM);
     const int ldc = (int)g.ldc;
+    // GM_STORE stages its bfloat16 block like the dlogits (see GM_D)
+    uint16_t* stg = smem + wave * (WM * WN);
     const int64_t base = (m0 + wm * WM + rq) * g.ldc + n0 + lc0;
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
@@ -461,13 +477,18 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
             for (int r = 0; r < 4; ++r)
               if (ok(j, r)) c[r * ldc + j * 16] = old[j][r] + acc[i][j][r];
         } else {
-          uint16_t* c = g.Cb + base + i * 16 * ldc;
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (ok(j, r)) c[r * ldc + j * 16] = bf16_bits(acc[i][j][r]);
+          for (int j = 0; j < FN; ++j) {
+            const uint16_t d[4] = {bf16_bits(acc[i][j][0]), bf16_bits(acc[i][j][1]),
+                                   bf16_bits(acc[i][j][2]), bf16_bits(acc[i][j][3])};
+            stage_quad(stg, lane, i, j, d);
+          }
         }
+      }
+      if constexpr (MODE == GM_STORE) {
+        __syncthreads();
+        store_staged_rows<kFull>(stg, lane, g.Cb + (m0 + wm * WM) * g.ldc + n0 + wn * WN, g.ldc,
+                                 nrows - wm * WM, ncols - wn * WN);
       }
     };
     if (ncols == GBN && nrows == GBM)

@@ -109,3 +109,12 @@ def test_product_path_has_no_oracle_dependency():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "drgrpo_oracle" not in txt, f
+
+
+def test_graft_entry_build_compiles_and_imports():
+    """The top-level build() entry compiles every native piece in-tree (HIP
+    library, generators, oracle) and imports the package."""
+    import __graft_entry__
+
+    __graft_entry__.build()
+    assert os.path.exists(dr.LIB)
