@@ -127,11 +127,9 @@ def run_lmhead(cfg, case, args):
     synth.gpu_normal_fill(W, cfg.seed, synth.S_WEIGHT, 0, cfg.w_std)
     tokens = torch.from_numpy(case.tokens).to(dev)
     rewards = torch.from_numpy(case.rewards).to(dev)
-    # logp_old: the policy's own log-probs (logits formed once, outside the timed region)
-    logits = torch.mm(hidden, W.t().contiguous()).view(cfg.N, cfg.C, cfg.V)
-    lp = dr.logprobs(logits, tokens).double().cpu().numpy()
-    del logits
-    torch.cuda.empty_cache()
+    # logp_old: the policy's own log-probs from the forward-only fused pass
+    # (outside the timed region)
+    lp = dr.lmhead_logprobs(hidden, W, tokens, cfg.eos_id).double().cpu().numpy()
     old = torch.from_numpy(synth.perturb(lp, case.old_noise)).to(dev)
     dh = torch.empty_like(hidden)
     dW = torch.empty_like(W)

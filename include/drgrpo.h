@@ -175,6 +175,30 @@ int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t*
                                void* out_dW, int64_t N, int64_t C, int64_t V, int64_t H,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward-only log-probs through the fused lm_head, for the no-gradient
+ * old-policy and reference-policy passes of the "Dr. GRPO" pseudo-code
+ * ("compute_logprobs": log_softmax of the final projection, gathered at the
+ * sampled token), without storing the [N*C, V] logits.
+ *
+ *   hidden   [N*C, H] bfloat16 (row i*C + t scores tokens[i, t]); W [V, H]
+ *            bfloat16; both 16-byte aligned (else DRGRPO_ERR_ALIAS).
+ *   tokens   [N, C] int64; eos_id as for drgrpo_loss_fwd_bwd: log-probs are
+ *            computed for the counted tokens (up to and including the first
+ *            EOS; every token when eos_id is outside [0, V)).
+ *   out_logp [N, C] float: x[y] - logsumexp(x) with x = hidden_row . W^T in
+ *            binary32 MFMA accumulation; 0 at positions after the first EOS;
+ *            NaN for a counted token outside [0, V).
+ *   Shape limits as for drgrpo_lmhead_loss_fwd_bwd.  The workspace
+ *   (drgrpo_lmhead_logprobs_workspace_bytes, 256-byte aligned, no
+ *   initialisation) holds the counted tokens' hidden rows and per-tile
+ *   partial sums. */
+size_t drgrpo_lmhead_logprobs_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t H);
+
+int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const int64_t* tokens,
+                           int64_t eos_id, int64_t N, int64_t C, int64_t V, int64_t H,
+                           float* out_logp, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Synchronises `stream`, then reads the status word the last
  * drgrpo_loss_fwd_bwd call on `workspace` left: DRGRPO_OK or
  * DRGRPO_ERR_TOKEN_RANGE (DRGRPO_ERR_HIP if the read fails). */

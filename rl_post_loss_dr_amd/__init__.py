@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.drgrpo_lmhead_loss_fwd_bwd.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _I64, _F, _F, _F,
                                                  _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]
         L.drgrpo_lmhead_loss_fwd_bwd.restype = _I
+        L.drgrpo_lmhead_logprobs_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+        L.drgrpo_lmhead_logprobs_workspace_bytes.restype = _SZ
+        L.drgrpo_lmhead_logprobs.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P,
+                                             _SZ, _P]
+        L.drgrpo_lmhead_logprobs.restype = _I
         L.drgrpo_device_status.argtypes = [_P, _P]
         L.drgrpo_device_status.restype = _I
         L.drgrpo_status_string.argtypes = [_I]
@@ -279,6 +284,38 @@ def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Ten
         loss.data_ptr(), out_dhidden.data_ptr(), out_dW.data_ptr(), N, C, V, H,
         workspace.data_ptr(), workspace.numel(), _stream(dev)), "drgrpo_lmhead_loss_fwd_bwd")
     return loss, out_dhidden, out_dW
+
+
+def lmhead_logprobs_workspace_bytes(N: int, C: int, V: int, H: int) -> int:
+    return int(lib().drgrpo_lmhead_logprobs_workspace_bytes(N, C, V, H))
+
+
+def lmhead_logprobs(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Tensor,
+                    eos_id: int = -1, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Forward-only log-probs [N, C] float32 through the fused lm_head (logits
+    = hidden . W^T never stored): counted tokens get log_softmax(x)[y], positions
+    after the first EOS get 0 (eos_id = -1: every token is counted)."""
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [N, C]")
+    N, C = tokens.shape
+    V, H = W.shape
+    _dev(W, "W", torch.bfloat16)
+    _dev(hidden, "hidden", torch.bfloat16)
+    if hidden.numel() != N * C * H:
+        raise ValueError(f"hidden must hold N*C rows of H={H}")
+    _dev(tokens, "tokens", torch.int64)
+    dev = hidden.device
+    if workspace is None:
+        n = lmhead_logprobs_workspace_bytes(N, C, V, H)
+        if n == 0:
+            raise DrGRPOError(ERR_SHAPE, "drgrpo_lmhead_logprobs_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = torch.empty((N, C), dtype=torch.float32, device=dev)
+    _check(lib().drgrpo_lmhead_logprobs(
+        hidden.data_ptr(), W.data_ptr(), tokens.data_ptr(), int(eos_id), N, C, V, H,
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)),
+        "drgrpo_lmhead_logprobs")
+    return out
 
 
 class DrGRPOLoss(torch.autograd.Function):

@@ -501,7 +501,8 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 // ------------------------------------------------------------ small kernels
 // Active-token count per completion and exclusive offsets (one workgroup).
 // A token is active when counted (t < len_i, token id in range) and
-// (A_i != 0 or beta != 0); bad ids are handled separately.
+// (A_i != 0 or beta != 0); with adv == NULL every counted token is active
+// (the forward-only log-prob pass).  Bad ids are handled separately.
 __global__ void __launch_bounds__(1024)
 k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int64_t N,
              float beta, int32_t* __restrict__ offs, int32_t* __restrict__ counts) {
@@ -510,7 +511,8 @@ k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int
   int32_t base = 0;
   for (int64_t c0 = 0; c0 < N; c0 += 1024) {
     const int64_t i = c0 + tid;
-    const int32_t a = (i < N && (adv[i] != 0.0f || beta != 0.0f)) ? len[i] : 0;
+    const int32_t a =
+        (i < N && (adv == nullptr || adv[i] != 0.0f || beta != 0.0f)) ? len[i] : 0;
     sh[tid] = a;
     __syncthreads();
     // inclusive Hillis-Steele scan (fixed order, integers)
@@ -532,7 +534,8 @@ k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int
 }
 
 // One workgroup per completion: list its active tokens, gather their hidden
-// rows, and zero the loss terms of its other tokens.
+// rows, and zero the loss terms of its other tokens (tok_loss == NULL: no
+// loss terms, the forward-only pass).
 __global__ void __launch_bounds__(256)
 k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __restrict__ tokens,
             int64_t C, int64_t V, const int32_t* __restrict__ len,
@@ -551,7 +554,7 @@ k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __res
       act_pos[k0 + t] = (int32_t)pos;
       ycol[k0 + t] = bad ? -1 : (int32_t)y;
     }
-    if (t >= n_act || bad) {
+    if (tok_loss && (t >= n_act || bad)) {
       tok_loss[pos] = bad ? (double)NAN : 0.0;
       tok_flags[pos] = bad ? TF_BADTOK : 0;
     }
@@ -591,18 +594,11 @@ k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int6
   }
 }
 
-// One wavefront per active token: merge the per-tile (max, sum exp), then
-// the per-token loss term and gradient coefficient.
-__global__ void __launch_bounds__(256)
-k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restrict__ xy,
-             const int32_t* __restrict__ counts, const int32_t* __restrict__ act_pos,
-             const int32_t* __restrict__ ycol, int64_t C, const float* __restrict__ adv,
-             const float* __restrict__ logp_old, const float* __restrict__ logp_ref, float eps,
-             float beta, double kappa, float* __restrict__ lse2, float* __restrict__ coef,
-             double* __restrict__ tok_loss, uint8_t* __restrict__ tok_flags) {
-  const int lane = threadIdx.x & 63;
-  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (k >= counts[0]) return;
+// log-sum-exp of active token k from its per-column-tile (max, sum exp)
+// pairs, merged by one wavefront (binary32 per lane, binary64 across lanes);
+// every lane returns the result.
+__device__ inline double merge_lse(const float2* __restrict__ part, int64_t ntn, int64_t k,
+                                   int lane) {
   float m = -INFINITY, s = 0.0f;
   for (int64_t j = lane; j < ntn; j += 64) {
     const float2 p = part[k * ntn + j];
@@ -617,6 +613,22 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
   double term = s != 0.0f ? (double)s * exp2(((double)m - (double)M) * kL2ED) : 0.0;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) term += __shfl_xor(term, o);
+  return (double)M + log(term);
+}
+
+// One wavefront per active token: merge the per-tile (max, sum exp), then
+// the per-token loss term and gradient coefficient.
+__global__ void __launch_bounds__(256)
+k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restrict__ xy,
+             const int32_t* __restrict__ counts, const int32_t* __restrict__ act_pos,
+             const int32_t* __restrict__ ycol, int64_t C, const float* __restrict__ adv,
+             const float* __restrict__ logp_old, const float* __restrict__ logp_ref, float eps,
+             float beta, double kappa, float* __restrict__ lse2, float* __restrict__ coef,
+             double* __restrict__ tok_loss, uint8_t* __restrict__ tok_flags) {
+  const int lane = threadIdx.x & 63;
+  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= counts[0]) return;
+  const double lse = merge_lse(part, ntn, k, lane);
   if (lane != 0) return;
   const int64_t pos = act_pos[k];
   const int64_t i = pos / C;
@@ -625,7 +637,6 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
     coef[k] = 0.0f;
     return;
   }
-  const double lse = (double)M + log(term);
   const double logp = (double)xy[k] - lse;
   const TokenTerms tt = token_terms(logp, logp_old[pos], beta != 0.0f ? logp_ref[pos] : 0.0f,
                                     adv[i], eps, beta, kappa);
@@ -653,6 +664,26 @@ k_lm_dh_out(const float* __restrict__ dHacc, int64_t H, const int32_t* __restric
     else if (t < n_act) v = dHacc[k * H + h];
     dhidden[pos * H + h] = bf16_bits(v);
   }
+}
+
+// Forward-only pass: log-prob of active token k (every counted token), one
+// wavefront per token; NaN for a token id outside [0, V).
+__global__ void __launch_bounds__(256)
+k_lm_logp(const float2* __restrict__ part, int64_t ntn, const float* __restrict__ xy,
+          const int32_t* __restrict__ counts, const int32_t* __restrict__ act_pos,
+          const int32_t* __restrict__ ycol, float* __restrict__ out_logp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= counts[0]) return;
+  const double lse = merge_lse(part, ntn, k, lane);
+  if (lane == 0) out_logp[act_pos[k]] = ycol[k] < 0 ? NAN : (float)((double)xy[k] - lse);
+}
+
+// Forward-only pass: positions after a completion's first EOS get 0.
+__global__ void __launch_bounds__(256)
+k_lm_logp_tail(const int32_t* __restrict__ len, int64_t C, float* __restrict__ out_logp) {
+  const int64_t i = blockIdx.x;
+  for (int64_t t = len[i] + (int64_t)threadIdx.x; t < C; t += blockDim.x) out_logp[i * C + t] = 0.0f;
 }
 
 // ------------------------------------------------------------ host side
@@ -713,6 +744,41 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
   w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
+  if (ws) *ws = w;
+  return off;
+}
+
+// Workspace of the forward-only log-prob pass: the loss pass's lists and
+// per-tile partials, without the backward buffers.
+struct LpWs {
+  int32_t* len;      // [N]
+  int32_t* offs;     // [N + 1]
+  int32_t* counts;   // [2]
+  int32_t* act_pos;  // [T]
+  int32_t* ycol;     // [T]
+  float2* part;      // [T, ntn]
+  float* xy;         // [T]
+  uint16_t* Ha;      // [T, H]
+};
+
+size_t lp_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LpWs* ws) {
+  const int64_t ntn = (V + GBN - 1) / GBN;
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  LpWs w;
+  w.len = reinterpret_cast<int32_t*>(take(4 * N));
+  w.offs = reinterpret_cast<int32_t*>(take(4 * (N + 1)));
+  w.counts = reinterpret_cast<int32_t*>(take(16));
+  w.act_pos = reinterpret_cast<int32_t*>(take(4 * T));
+  w.ycol = reinterpret_cast<int32_t*>(take(4 * T));
+  w.part = reinterpret_cast<float2*>(take(8 * (size_t)T * ntn));
+  w.xy = reinterpret_cast<float*>(take(4 * T));
+  w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
   if (ws) *ws = w;
   return off;
 }
@@ -889,5 +955,64 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, w.tok_loss, w.tok_flags, T,
                      w.row_flags, N, (double)norm_const, out_loss, w.status, (int64_t*)nullptr);
+  return launch_status();
+}
+
+extern "C" size_t drgrpo_lmhead_logprobs_workspace_bytes(int64_t N, int64_t C, int64_t V,
+                                                         int64_t H) {
+  int64_t T;
+  if (lm_check_shape(N, C, V, H, 1, &T) != DRGRPO_OK) return 0;
+  return lp_carve(nullptr, N, T, V, H, nullptr);
+}
+
+extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const int64_t* tokens,
+                                      int64_t eos_id, int64_t N, int64_t C, int64_t V, int64_t H,
+                                      float* out_logp, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!hidden || !W || !tokens || !out_logp) return DRGRPO_ERR_NULL;
+  int64_t T;
+  const int sh = lm_check_shape(N, C, V, H, 1, &T);
+  if (sh != DRGRPO_OK) return sh;
+  if ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W)) % 16 != 0)
+    return DRGRPO_ERR_ALIAS;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < lp_carve(nullptr, N, T, V, H, nullptr))
+    return DRGRPO_ERR_WORKSPACE;
+  LpWs w;
+  lp_carve(workspace, N, T, V, H, &w);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t ntn = (V + GBN - 1) / GBN;
+  int rc;
+  // counted tokens (first EOS inclusive), listed and gathered like the loss pass
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id,
+                     (const float*)nullptr, (int64_t)1, w.len, (float*)nullptr, (uint8_t*)nullptr,
+                     (int32_t*)nullptr, (uint8_t*)nullptr, (float*)nullptr, (int32_t*)nullptr);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, (const float*)nullptr, N,
+                     0.0f, w.offs, w.counts);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(hidden), H, tokens, C, V, w.len, w.offs,
+                     w.act_pos, w.ycol, w.Ha, (double*)nullptr, (uint8_t*)nullptr);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_logp_tail, dim3((unsigned)N), dim3(256), 0, st, w.len, C, out_logp);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  GemmArgs g = {};
+  g.A = w.Ha;
+  g.lda = H;
+  g.B = static_cast<const uint16_t*>(W);
+  g.ldb = H;
+  g.M = T;
+  g.N = V;
+  g.K = H;
+  g.M_dev = w.counts;
+  g.part = w.part;
+  g.ntn = ntn;
+  g.xy = w.xy;
+  g.ycol = w.ycol;
+  g.col_base = 0;
+  if ((rc = launch_gemm<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_logp, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
+                     w.xy, w.counts, w.act_pos, w.ycol, out_logp);
   return launch_status();
 }

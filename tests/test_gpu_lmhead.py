@@ -113,3 +113,78 @@ def test_lmhead_full_size_sampled():
     # every inactive token's dhidden row is exactly zero
     inactive = np.setdiff1d(np.arange(cfg.T), active)
     assert float(dh[torch.from_numpy(inactive).to(DEV)].float().abs().max()) == 0.0
+
+
+def _logp_bound(h64, W64, rows):
+    """Tolerance of a log-prob from binary32 MFMA logits: each logit's
+    accumulation error is at most gamma_H * sum_k |h_k||w_k| (gamma_H =
+    H u / (1 - H u), u = 2^-24), and log_softmax moves by at most twice the
+    largest logit error; 1e-5 covers the binary32 exp / sum over V."""
+    H = h64.shape[1]
+    u = 2.0 ** -24
+    gamma = H * u / (1 - H * u)
+    a = np.abs(h64[rows]) @ np.abs(W64).T
+    return 2 * gamma * a.max(axis=1) + 1e-5
+
+
+@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi"])
+def test_lmhead_logprobs_small(name):
+    """Forward-only fused log-probs: every counted token against the oracle,
+    zeros after the first EOS, and every token when no EOS id is given."""
+    print(f"case {name}", flush=True)
+    cfg, case, hb, Wb, old, ref, t = lm_case(name)
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    tok = case.tokens.reshape(-1)
+    _, want = lmhead.token_rows(h64, W64, tok, np.arange(cfg.T))
+    bound = _logp_bound(h64, W64, np.arange(cfg.T))
+    hd, Wd, td = _bits_to_dev(hb), _bits_to_dev(Wb), torch.from_numpy(case.tokens).to(DEV)
+    got = dr.lmhead_logprobs(hd, Wd, td, cfg.eos_id).cpu().numpy().astype(np.float64).reshape(-1)
+    lens = oracle.completion_len(case.tokens, cfg.eos_id)
+    counted = (np.arange(cfg.C)[None, :] < lens[:, None]).reshape(-1)
+    assert (np.abs(got - want)[counted] <= bound[counted]).all(), float(
+        np.abs(got - want)[counted].max())
+    assert (got[~counted] == 0.0).all()
+    got_all = dr.lmhead_logprobs(hd, Wd, td, -1).cpu().numpy().astype(np.float64).reshape(-1)
+    assert (np.abs(got_all - want) <= bound).all()
+    # the counted tokens are the same computation either way
+    assert np.array_equal(got_all[counted], got[counted])
+
+
+def test_lmhead_logprobs_bad_token_is_nan():
+    cfg, case, hb, Wb, old, ref, t = lm_case("lmhead_mini")
+    tokens = case.tokens.copy()
+    tokens[1, 0] = cfg.V + 5  # counted: no EOS id is given below
+    got = dr.lmhead_logprobs(_bits_to_dev(hb), _bits_to_dev(Wb), torch.from_numpy(tokens).to(DEV),
+                             -1).cpu().numpy()
+    assert np.isnan(got[1, 0])
+    assert np.isfinite(np.delete(got.reshape(-1), cfg.C)).all()
+
+
+def test_lmhead_logprobs_full_size_sampled():
+    """Full Qwen2.5-0.5B-shaped lm_head (T = 32,768 rows, V = 151,936, H = 896):
+    sampled counted rows against the oracle, zeros after each first EOS."""
+    cfg = synth.get_config("lmhead_b8g8c512")
+    case = synth.make_case(cfg)
+    print(f"[{cfg.name}] host inputs", flush=True)
+    hb = case.hidden()
+    Wb = case.weight()
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    lens = oracle.completion_len(case.tokens, cfg.eos_id)
+    counted = (np.arange(cfg.C)[None, :] < lens[:, None]).reshape(-1)
+    print(f"[{cfg.name}] device run", flush=True)
+    got = dr.lmhead_logprobs(_bits_to_dev(hb), _bits_to_dev(Wb),
+                             torch.from_numpy(case.tokens).to(DEV), cfg.eos_id)
+    got = got.cpu().numpy().astype(np.float64).reshape(-1)
+    assert (got[~counted] == 0.0).all()
+    rng = np.random.default_rng(cfg.seed + 1)
+    idx = np.flatnonzero(counted)
+    rows = np.unique(np.concatenate([rng.choice(idx, 24, replace=False), idx[:2], idx[-2:]]))
+    print(f"[{cfg.name}] oracle log-probs of {rows.size} sampled rows", flush=True)
+    _, want = lmhead.token_rows(h64, W64, case.tokens.reshape(-1), rows)
+    bound = _logp_bound(h64, W64, rows)
+    err = np.abs(got[rows] - want)
+    print(f"[{cfg.name}] max |logp err| {err.max():.3g} (bound min {bound.min():.3g})", flush=True)
+    assert (err <= bound).all()
+    assert np.isfinite(got[counted]).all()
