@@ -8,7 +8,9 @@ HIP library is missing.
 The arithmetic lives in ``drgrpo_oracle.c`` (compiled with gcc, no HIP); this
 module only marshals numpy arrays and composes its steps in the pages' order:
 completion mask -> group advantage -> log-softmax + gather -> clipped
-surrogate (+ k3 KL) -> token sum / kappa -> gradient rows.  The fused lm_head
+surrogate (+ k3 KL) -> token sum / kappa -> gradient rows.  The GRPO
+normalisations (group-std advantage, per-response mean) and the token mean are
+selected by ``adv_mode`` / ``agg``.  The fused lm_head
 variant (logits = hidden @ W^T) is in ``lmhead.py``.
 """
 from __future__ import annotations
@@ -52,13 +54,17 @@ def lib():
         L.oracle_completion_len.restype = ctypes.c_int
         L.oracle_group_advantage.argtypes = [_P, _I64, _I64, _P]
         L.oracle_group_advantage.restype = ctypes.c_int
+        L.oracle_group_advantage_zscore.argtypes = [_P, _I64, _I64, _P]
+        L.oracle_group_advantage_zscore.restype = ctypes.c_int
+        L.oracle_row_divisor.argtypes = [_P, _I64, ctypes.c_int, _D, _P]
+        L.oracle_row_divisor.restype = ctypes.c_int
         L.oracle_nocontrast_groups.argtypes = [_P, _I64, _I64]
         L.oracle_nocontrast_groups.restype = _I64
         L.oracle_row_logprob.argtypes = [_P, ctypes.c_int, _I64, _P, _I64, _P, _P]
         L.oracle_row_logprob.restype = _I64
-        L.oracle_token_terms.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _D, _P, _P, _P]
+        L.oracle_token_terms.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _P, _P, _P]
         L.oracle_token_terms.restype = ctypes.c_int
-        L.oracle_loss.argtypes = [_P, _I64, _D]
+        L.oracle_loss.argtypes = [_P, _P, _I64, _I64]
         L.oracle_loss.restype = _D
         L.oracle_dlogits_rows.argtypes = [_P, ctypes.c_int, _I64, _P, _P, _P, _I64, _P]
         L.oracle_dlogits_rows.restype = ctypes.c_int
@@ -96,10 +102,26 @@ def completion_mask(tokens: np.ndarray, eos_id: int) -> np.ndarray:
     return (np.arange(tokens.shape[1])[None, :] < L[:, None]).astype(np.uint8)
 
 
-def group_advantage(rewards: np.ndarray, G: int) -> np.ndarray:
+ADV_CENTER, ADV_ZSCORE = 0, 1                      # Dr. GRPO, GRPO advantages
+AGG_TOKEN_SUM, AGG_SEQ_MEAN, AGG_TOKEN_MEAN = 0, 1, 2  # aggregation divisors
+
+
+def group_advantage(rewards: np.ndarray, G: int, mode: int = ADV_CENTER) -> np.ndarray:
     rewards = _c(rewards, np.float32)
     out = np.empty_like(rewards)
-    if lib().oracle_group_advantage(rewards.ctypes.data, rewards.size, G, out.ctypes.data) != 0:
+    fn = lib().oracle_group_advantage if mode == ADV_CENTER else \
+        lib().oracle_group_advantage_zscore
+    if mode not in (ADV_CENTER, ADV_ZSCORE) or \
+            fn(rewards.ctypes.data, rewards.size, G, out.ctypes.data) != 0:
+        raise ValueError("bad arguments")
+    return out
+
+
+def row_divisor(lens: np.ndarray, kappa: float, agg: int = AGG_TOKEN_SUM) -> np.ndarray:
+    """Per-completion divisor of the token sums (see oracle_row_divisor)."""
+    lens = _c(lens, np.int32).reshape(-1)
+    out = np.empty(lens.size, dtype=np.float64)
+    if lib().oracle_row_divisor(lens.ctypes.data, lens.size, agg, kappa, out.ctypes.data) != 0:
         raise ValueError("bad arguments")
     return out
 
@@ -127,7 +149,7 @@ def row_logprob(logits2d: np.ndarray, tokens_flat: np.ndarray) -> tuple[np.ndarr
     return lse, logp, int(bad)
 
 
-def token_terms(logp, logp_old, logp_ref, adv, lens, eps, beta, kappa):
+def token_terms(logp, logp_old, logp_ref, adv, lens, eps, beta, kappa, agg=AGG_TOKEN_SUM):
     """(lambda, coef, stats[2]) per token of a [N, C] batch."""
     logp = _c(logp, np.float64)
     N, C = logp.shape
@@ -138,18 +160,28 @@ def token_terms(logp, logp_old, logp_ref, adv, lens, eps, beta, kappa):
     lam = np.empty((N, C), dtype=np.float64)
     coef = np.empty((N, C), dtype=np.float64)
     stats = np.zeros(2, dtype=np.int64)
+    div = row_divisor(lens, kappa, agg)
     rc = lib().oracle_token_terms(logp.ctypes.data, old.ctypes.data,
                                   None if ref is None else ref.ctypes.data, adv.ctypes.data,
-                                  lens.ctypes.data, N, C, eps, beta, kappa, lam.ctypes.data,
-                                  coef.ctypes.data, stats.ctypes.data)
+                                  lens.ctypes.data, N, C, eps, beta, div.ctypes.data,
+                                  lam.ctypes.data, coef.ctypes.data, stats.ctypes.data)
     if rc != 0:
         raise ValueError("bad arguments")
     return lam, coef, stats
 
 
-def loss_sum(lam: np.ndarray, kappa: float) -> float:
+def loss_sum(lam: np.ndarray, kappa: float, lens=None, agg: int = AGG_TOKEN_SUM) -> float:
+    """L from the per-token terms lam [N, C] (a flat array is one row per
+    entry); lens is needed for the per-response and token-mean divisors."""
     lam = _c(lam, np.float64)
-    return float(lib().oracle_loss(lam.ctypes.data, lam.size, kappa))
+    lam2 = lam.reshape(lam.shape[0], -1) if lam.ndim > 1 else lam.reshape(-1, 1)
+    N, C = lam2.shape
+    if lens is None:
+        if agg != AGG_TOKEN_SUM:
+            raise ValueError("lens is needed for this aggregation")
+        lens = np.ones(N, dtype=np.int32)
+    div = row_divisor(lens, kappa, agg)
+    return float(lib().oracle_loss(lam2.ctypes.data, div.ctypes.data, N, C))
 
 
 def dlogits_rows(logits2d, tokens_flat, lse, coef) -> np.ndarray:
@@ -188,7 +220,8 @@ class Result:
 
 
 def loss_fwd_bwd(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa,
-                 want_dlogits: bool = True) -> Result:
+                 want_dlogits: bool = True, adv_mode: int = ADV_CENTER,
+                 agg: int = AGG_TOKEN_SUM) -> Result:
     """Whole oracle pass for a batch small enough to hold [N*C, V] in memory.
 
     logits: [N*C, V] (or [N, C, V]) float32 / float64 / bf16 bits as uint16.
@@ -197,14 +230,14 @@ def loss_fwd_bwd(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, be
     N, C = tokens.shape
     x = logits.reshape(N * C, -1)
     lens = completion_len(tokens, eos_id)
-    adv = group_advantage(rewards, G)
+    adv = group_advantage(rewards, G, adv_mode)
     mask = np.arange(C)[None, :] < lens[:, None]
     lse, logp, _ = row_logprob(x, tokens.reshape(-1))
     bad = int(((tokens < 0) | (tokens >= x.shape[1]))[mask].sum())
     lse = lse.reshape(N, C)
     logp = logp.reshape(N, C)
-    lam, coef, stats = token_terms(logp, logp_old, logp_ref, adv, lens, eps, beta, kappa)
-    L = loss_sum(lam, kappa)
+    lam, coef, stats = token_terms(logp, logp_old, logp_ref, adv, lens, eps, beta, kappa, agg)
+    L = loss_sum(lam, kappa, lens, agg)
     if bad:
         L = float("nan")
     D = dlogits_rows(x, tokens.reshape(-1), lse.reshape(-1), coef.reshape(-1)) \

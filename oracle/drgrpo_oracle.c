@@ -20,7 +20,9 @@
  *     token t of the completion ([DG] "compute_logprobs": the slice that
  *     starts one position before the completion);
  *   - the token sum is divided by a caller-supplied constant kappa ([DG]
- *     "Dr. GRPO": a sum, optionally divided by a fixed constant);
+ *     "Dr. GRPO": a sum, optionally divided by a fixed constant); the GRPO
+ *     normalisations the same section removes (group standard deviation,
+ *     per-response mean) and the token mean are kept as variants;
  *   - the KL term is the k3 estimator exp(d) - d - 1, d = logp_ref - logp,
  *     summed into the same masked token sum (the pages name the penalty but
  *     not its estimator);
@@ -79,6 +81,64 @@ int oracle_group_advantage(const float* rewards, int64_t N, int64_t G, float* ad
     for (int64_t j = 0; j < G; ++j) s = s + rewards[b * G + j];
     volatile float mu = s / (float)G;
     for (int64_t j = 0; j < G; ++j) adv[b * G + j] = rewards[b * G + j] - mu;
+  }
+  return 0;
+}
+
+/* [DG] "GRPO": the advantage is the reward minus the group mean, divided by
+ * the group's standard deviation.  Readings: the standard deviation is the
+ * sample one (divisor G - 1, what torch's Tensor.std computes), and a group
+ * whose rewards are all equal has advantage 0 (it carries no contrast and the
+ * quotient would be 0/0).  Binary32 throughout: the mean as in
+ * oracle_group_advantage, then the sequential sum of squared deviations
+ * (each square rounded, then added), one division by G - 1, a correctly
+ * rounded square root, and one division per completion. */
+int oracle_group_advantage_zscore(const float* rewards, int64_t N, int64_t G, float* adv) {
+  if (!rewards || !adv || G <= 0 || N < 0 || N % G != 0) return -1;
+  for (int64_t b = 0; b < N / G; ++b) {
+    int same = 1;
+    for (int64_t j = 1; j < G; ++j)
+      if (!(rewards[b * G + j] == rewards[b * G])) same = 0;
+    if (same) {
+      for (int64_t j = 0; j < G; ++j) adv[b * G + j] = 0.0f;
+      continue;
+    }
+    volatile float s = 0.0f;
+    for (int64_t j = 0; j < G; ++j) s = s + rewards[b * G + j];
+    volatile float mu = s / (float)G;
+    volatile float q = 0.0f;
+    for (int64_t j = 0; j < G; ++j) {
+      volatile float d = rewards[b * G + j] - mu;
+      volatile float d2 = d * d;
+      q = q + d2;
+    }
+    volatile float var = q / (float)(G - 1);
+    volatile float sd = sqrtf(var);
+    for (int64_t j = 0; j < G; ++j) {
+      volatile float d = rewards[b * G + j] - mu;
+      adv[b * G + j] = d / sd;
+    }
+  }
+  return 0;
+}
+
+/* Aggregation: the loss is L = sum_i (sum_t lambda[i,t]) / div_i, with one
+ * divisor per completion:
+ *   agg 0, [DG] "Dr. GRPO": the token sum over the batch divided by a fixed
+ *          constant, div_i = kappa;
+ *   agg 1, [DG] "Dr. GRPO" (length bias): the original GRPO loss averages each
+ *          response's token sum over its |o_i| tokens, div_i = kappa * len_i
+ *          (kappa = N gives the mean over completions);
+ *   agg 2, [DG] "Dr. GRPO" pseudo-code ("not token_mean"): the mean over
+ *          every counted token of the batch, div_i = kappa * sum_j len_j. */
+int oracle_row_divisor(const int32_t* len, int64_t N, int agg, double kappa, double* div) {
+  if (!len || !div || N < 0 || agg < 0 || agg > 2) return -1;
+  double total = 0.0;
+  for (int64_t i = 0; i < N; ++i) total += (double)len[i];
+  for (int64_t i = 0; i < N; ++i) {
+    if (agg == 0) div[i] = kappa;
+    else if (agg == 1) div[i] = kappa * (double)len[i];
+    else div[i] = kappa * total;
   }
   return 0;
 }
@@ -149,10 +209,11 @@ int64_t oracle_row_logprob(const void* logits, int dtype, int64_t V, const int64
  * surrogates splits it evenly, which sums to the unclipped branch):
  *   chi = 0 if (A > 0 and r > 1+eps) or (A < 0 and r < 1-eps), else 1
  *   g   = -A*r*chi + beta*(1 - exp(d)).
- * The loss is L = (sum over mask=1 tokens of lambda) / kappa, so the gradient
- * of L with respect to the logits of token (i,t) is
- *   dL/dx_v = (g/kappa) * ([v = y] - softmax_v) = coef * (softmax_v - [v = y])
- * with coef = -g / kappa.
+ * The loss is L = sum_i (sum over mask=1 tokens of row i of lambda) / div_i
+ * (div from oracle_row_divisor; div_i = kappa for the Dr. GRPO token sum), so
+ * the gradient of L with respect to the logits of token (i,t) is
+ *   dL/dx_v = (g/div_i) * ([v = y] - softmax_v) = coef * (softmax_v - [v = y])
+ * with coef = -g / div_i.
  *
  * Inactive tokens (t >= len_i, or A_i = 0 with beta = 0) get lambda = 0 and
  * coef = 0 without reading logp.  stats (nullable, int64[2]) receives the
@@ -161,8 +222,10 @@ int64_t oracle_row_logprob(const void* logits, int dtype, int64_t V, const int64
  * logp_ref may be NULL only when beta == 0. */
 int oracle_token_terms(const double* logp, const float* logp_old, const float* logp_ref,
                        const float* adv, const int32_t* len, int64_t N, int64_t C, double eps,
-                       double beta, double kappa, double* lambda, double* coef, int64_t* stats) {
-  if (!logp || !logp_old || !adv || !len || !lambda || !coef || N < 0 || C < 0) return -1;
+                       double beta, const double* div, double* lambda, double* coef,
+                       int64_t* stats) {
+  if (!logp || !logp_old || !adv || !len || !div || !lambda || !coef || N < 0 || C < 0)
+    return -1;
   if (beta != 0.0 && !logp_ref) return -1;
   int64_t n_out = 0, n_cut = 0;
   for (int64_t i = 0; i < N; ++i) {
@@ -189,7 +252,7 @@ int oracle_token_terms(const double* logp, const float* logp_old, const float* l
       const int cut = (A > 0.0 && r > 1.0 + eps) || (A < 0.0 && r < 1.0 - eps);
       const double g = -A * r * (cut ? 0.0 : 1.0) + beta * dk3;
       lambda[k] = -s + beta * k3;
-      coef[k] = -g / kappa;
+      coef[k] = -g / div[i];
       if (r < 1.0 - eps || r > 1.0 + eps) n_out += 1;
       if (cut && A != 0.0) n_cut += 1;
     }
@@ -201,13 +264,18 @@ int oracle_token_terms(const double* logp, const float* logp_old, const float* l
   return 0;
 }
 
-/* [DG] "Dr. GRPO": token-sum aggregation, divided by the constant kappa.
- * lambda is zero at masked positions, so the plain sum over all T entries is
- * the masked sum. */
-double oracle_loss(const double* lambda, int64_t T, double kappa) {
+/* [DG] "Dr. GRPO": token-sum aggregation; each completion's token sum is
+ * divided by its divisor (oracle_row_divisor) and the quotients are added.
+ * lambda is zero at masked positions, so the plain sum over a row is the
+ * masked sum. */
+double oracle_loss(const double* lambda, const double* div, int64_t N, int64_t C) {
   double s = 0.0;
-  for (int64_t k = 0; k < T; ++k) s += lambda[k];
-  return s / kappa;
+  for (int64_t i = 0; i < N; ++i) {
+    double row = 0.0;
+    for (int64_t t = 0; t < C; ++t) row += lambda[i * C + t];
+    s += row / div[i];
+  }
+  return s;
 }
 
 /* Gradient rows: out[r, v] = coef_r * (exp(x_v - lse_r) - [v = y_r]); a row

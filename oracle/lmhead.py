@@ -34,11 +34,11 @@ def token_rows(hidden64, W64, tokens_flat, rows, block=256):
 
 
 def loss_and_terms(hidden64, W64, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
-                   kappa):
+                   kappa, adv_mode=0, agg=0):
     """Loss over every token and the per-token pieces the gradients need."""
     N, C = tokens.shape
     lens = completion_len(tokens, eos_id)
-    adv = group_advantage(rewards, G)
+    adv = group_advantage(rewards, G, adv_mode)
     mask = np.arange(C)[None, :] < lens[:, None]
     active = mask & ((adv[:, None] != 0) | (beta != 0))
     rows = np.flatnonzero(active.reshape(-1))
@@ -49,8 +49,8 @@ def loss_and_terms(hidden64, W64, tokens, eos_id, rewards, logp_old, logp_ref, G
         lse[rows] = l
         logp[rows] = p
     lam, coef, stats = token_terms(logp.reshape(N, C), logp_old, logp_ref, adv, lens, eps, beta,
-                                   kappa)
-    return dict(loss=loss_sum(lam, kappa), lse=lse, logp=logp.reshape(N, C), lam=lam,
+                                   kappa, agg)
+    return dict(loss=loss_sum(lam, kappa, lens, agg), lse=lse, logp=logp.reshape(N, C), lam=lam,
                 coef=coef.reshape(-1), active_rows=rows, len=lens, adv=adv, stats=stats)
 
 
@@ -85,11 +85,13 @@ def dW_rows(hidden64, W64, tokens_flat, terms, vocab_rows):
     return out
 
 
-def full(hidden_bits, W_bits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa):
+def full(hidden_bits, W_bits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa,
+         adv_mode=0, agg=0):
     """Loss, full dhidden [T, H] and dW [V, H] for a case small enough to hold [T, V]."""
     h = bf16_to_f64(hidden_bits)
     W = bf16_to_f64(W_bits)
-    terms = loss_and_terms(h, W, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa)
+    terms = loss_and_terms(h, W, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa,
+                           adv_mode, agg)
     logits = h @ W.T
     D = dlogits_rows(logits, tokens.reshape(-1), terms["lse"], terms["coef"])
     terms["dhidden"] = D @ W
