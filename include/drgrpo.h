@@ -106,6 +106,26 @@ int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_i
                         drgrpo_dtype_t dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* Normalisation variants ("Making Dr GRPO go brrr", sections "GRPO" and
+ * "Dr. GRPO": Dr. GRPO deletes GRPO's division by the group standard
+ * deviation and its per-response 1/|o_i| average).  NULL = Dr. GRPO. */
+typedef enum {
+  DRGRPO_ADV_CENTER = 0,  /* A_i = R_i - mean of the group                 (Dr. GRPO) */
+  DRGRPO_ADV_ZSCORE = 1   /* A_i = (R_i - mean) / sample std of the group, divisor G-1;
+                             0 for a group whose rewards are all equal     (GRPO) */
+} drgrpo_adv_mode_t;
+typedef enum {
+  DRGRPO_AGG_TOKEN_SUM = 0,  /* L = sum_i sum_t lambda / norm_const                (Dr. GRPO) */
+  DRGRPO_AGG_SEQ_MEAN = 1,   /* L = sum_i (sum_t lambda / |o_i|) / norm_const      (GRPO;
+                                norm_const = N is the mean over completions) */
+  DRGRPO_AGG_TOKEN_MEAN = 2  /* L = sum_i sum_t lambda / (norm_const * sum_i |o_i|)
+                                (norm_const = 1 is the mean over counted tokens) */
+} drgrpo_agg_mode_t;
+typedef struct drgrpo_variant {
+  int32_t adv_mode;  /* drgrpo_adv_mode_t */
+  int32_t agg_mode;  /* drgrpo_agg_mode_t; |o_i| = len_i, the counted tokens of row i */
+} drgrpo_variant_t;
+
 /* Optional per-call diagnostics; every field may be NULL. */
 typedef struct drgrpo_aux {
   int32_t* len;     /* [N] completion lengths */
@@ -113,33 +133,41 @@ typedef struct drgrpo_aux {
   float* adv;       /* [N] advantages */
   float* logp;      /* [N, C] log-probs of active tokens, 0 elsewhere */
   float* tok_loss;  /* [N, C] per-token lambda, 0 for inactive tokens */
-  int64_t* stats;   /* [4] groups without reward contrast, rows without EOS,
+  int64_t* stats;   /* [6] groups without reward contrast, rows without EOS,
                        active tokens with r outside [1-eps, 1+eps], active
-                       tokens whose surrogate gradient the clip cuts */
+                       tokens whose surrogate gradient the clip cuts, counted
+                       tokens (sum of len), active tokens (counted tokens of
+                       rows with A != 0, or all counted tokens if beta > 0) */
   void* rows_event_begin; /* hipEvent_t stamped when the per-row kernel's
                              dispatch starts (NULL: none), to time it alone */
   void* rows_event_end;   /* hipEvent_t stamped when it ends (NULL: none) */
 } drgrpo_aux_t;
 
-/* drgrpo_loss_fwd_bwd plus the diagnostics `aux` asks for (aux may be NULL). */
+/* drgrpo_loss_fwd_bwd plus the diagnostics `aux` asks for (aux may be NULL)
+ * and a normalisation variant (variant may be NULL: Dr. GRPO; an unknown
+ * mode is DRGRPO_ERR_PARAM).  With a variant, coef = -g / div_i where div_i
+ * is row i's divisor above (norm_const, norm_const*len_i or
+ * norm_const*sum len). */
 int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
                            const float* rewards, const float* logp_old, const float* logp_ref,
                            int64_t G, float eps, float beta, float norm_const, float* out_loss,
                            void* out_dlogits, int64_t N, int64_t C, int64_t V,
                            drgrpo_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                           void* stream, const drgrpo_aux_t* aux);
+                           void* stream, const drgrpo_aux_t* aux,
+                           const drgrpo_variant_t* variant);
 
 /* Completion mask alone ("The completion mask"): out_len [N] int32 (required),
  * out_mask [N, C] uint8 (may be NULL). */
 int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t C, int64_t eos_id,
                            int32_t* out_len, uint8_t* out_mask, void* stream);
 
-/* Group advantages alone ("Dr. GRPO"): out_adv [N] float (required);
- * out_nocontrast [1] int32 (may be NULL) receives the number of groups whose
- * rewards are all equal ("The sparse-reward bottleneck" of "The Quiet
- * Library"). */
-int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, float* out_adv,
-                           int32_t* out_nocontrast, void* stream);
+/* Group advantages alone ("Dr. GRPO", or "GRPO" with adv_mode =
+ * DRGRPO_ADV_ZSCORE; another value is DRGRPO_ERR_PARAM): out_adv [N] float
+ * (required); out_nocontrast [1] int32 (may be NULL) receives the number of
+ * groups whose rewards are all equal ("The sparse-reward bottleneck" of "The
+ * Quiet Library"). */
+int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, int32_t adv_mode,
+                           float* out_adv, int32_t* out_nocontrast, void* stream);
 
 /* Forward-only log-probs of every token ("compute_logprobs"), the no-gradient
  * pass that produces logp_old / logp_ref: out_logp [N, C] float.  A token
@@ -174,6 +202,16 @@ int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t*
                                float norm_const, float* out_loss, void* out_dhidden,
                                void* out_dW, int64_t N, int64_t C, int64_t V, int64_t H,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* drgrpo_lmhead_loss_fwd_bwd with a normalisation variant (NULL: Dr. GRPO),
+ * as for drgrpo_loss_fwd_bwd_ex. */
+int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W, const int64_t* tokens,
+                                  int64_t eos_id, const float* rewards, const float* logp_old,
+                                  const float* logp_ref, int64_t G, float eps, float beta,
+                                  float norm_const, float* out_loss, void* out_dhidden,
+                                  void* out_dW, int64_t N, int64_t C, int64_t V, int64_t H,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const drgrpo_variant_t* variant);
 
 /* Forward-only log-probs through the fused lm_head, for the no-gradient
  * old-policy and reference-policy passes of the "Dr. GRPO" pseudo-code

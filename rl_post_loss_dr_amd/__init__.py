@@ -31,6 +31,14 @@ class DrGRPOError(RuntimeError):
         super().__init__(f"{where}: {status_string(code)} (status {code})")
 
 
+ADV_CENTER, ADV_ZSCORE = 0, 1                          # Dr. GRPO, GRPO advantages
+AGG_TOKEN_SUM, AGG_SEQ_MEAN, AGG_TOKEN_MEAN = 0, 1, 2  # aggregation (drgrpo_agg_mode_t)
+
+
+class _Variant(ctypes.Structure):
+    _fields_ = [("adv_mode", ctypes.c_int32), ("agg_mode", ctypes.c_int32)]
+
+
 class _Aux(ctypes.Structure):
     _fields_ = [("len", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("adv", ctypes.c_void_p),
                 ("logp", ctypes.c_void_p), ("tok_loss", ctypes.c_void_p),
@@ -58,11 +66,12 @@ def lib() -> ctypes.CDLL:
                   _SZ, _P]
         L.drgrpo_loss_fwd_bwd.argtypes = common
         L.drgrpo_loss_fwd_bwd.restype = _I
-        L.drgrpo_loss_fwd_bwd_ex.argtypes = common + [ctypes.POINTER(_Aux)]
+        L.drgrpo_loss_fwd_bwd_ex.argtypes = common + [ctypes.POINTER(_Aux),
+                                                      ctypes.POINTER(_Variant)]
         L.drgrpo_loss_fwd_bwd_ex.restype = _I
         L.drgrpo_completion_mask.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
         L.drgrpo_completion_mask.restype = _I
-        L.drgrpo_group_advantage.argtypes = [_P, _I64, _I64, _P, _P, _P]
+        L.drgrpo_group_advantage.argtypes = [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P]
         L.drgrpo_group_advantage.restype = _I
         L.drgrpo_logprobs.argtypes = [_P, _P, _I64, _I64, _I64, _I, _P, _P]
         L.drgrpo_logprobs.restype = _I
@@ -71,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.drgrpo_lmhead_loss_fwd_bwd.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _I64, _F, _F, _F,
                                                  _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]
         L.drgrpo_lmhead_loss_fwd_bwd.restype = _I
+        L.drgrpo_lmhead_loss_fwd_bwd_ex.argtypes = L.drgrpo_lmhead_loss_fwd_bwd.argtypes + [
+            ctypes.POINTER(_Variant)]
+        L.drgrpo_lmhead_loss_fwd_bwd_ex.restype = _I
         L.drgrpo_lmhead_logprobs_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
         L.drgrpo_lmhead_logprobs_workspace_bytes.restype = _SZ
         L.drgrpo_lmhead_logprobs.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P,
@@ -136,7 +148,8 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
                  logp_old: torch.Tensor, logp_ref: torch.Tensor | None = None, *, G: int,
                  eps: float = 0.2, beta: float = 0.0, norm_const: float | None = None,
                  out_dlogits: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                 aux: dict | None = None, rows_events=None):
+                 aux: dict | None = None, rows_events=None, adv_mode: int = ADV_CENTER,
+                 agg: int = AGG_TOKEN_SUM):
     """Loss and dlogits of the Dr. GRPO update for one rollout batch.
 
     logits [N, C, V] float32/bfloat16 (the completion slice: row t scores
@@ -147,6 +160,8 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
     len, mask, adv, logp, tok_loss, stats when given.  `rows_events` is an
     optional pair of recorded torch.cuda.Event (enable_timing=True) that the
     library records around its per-row kernel on the current stream.
+    adv_mode / agg select GRPO's normalisations (ADV_ZSCORE, AGG_SEQ_MEAN) or
+    the token mean (AGG_TOKEN_MEAN) instead of Dr. GRPO's.
     """
     if logits.dim() != 3:
         raise ValueError("logits must be [N, C, V]")
@@ -172,7 +187,8 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
             logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta),
             float(norm_const), loss.data_ptr(), out_dlogits.data_ptr(), N, C, V, dt,
             workspace.data_ptr(), workspace.numel(), _stream(dev))
-    if aux is None and rows_events is None:
+    variant = (adv_mode, agg) != (ADV_CENTER, AGG_TOKEN_SUM)
+    if aux is None and rows_events is None and not variant:
         _check(lib().drgrpo_loss_fwd_bwd(*args), "drgrpo_loss_fwd_bwd")
         return loss, out_dlogits
     s = _Aux()
@@ -182,13 +198,15 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
         aux["adv"] = torch.empty(N, dtype=torch.float32, device=dev)
         aux["logp"] = torch.empty((N, C), dtype=torch.float32, device=dev)
         aux["tok_loss"] = torch.empty((N, C), dtype=torch.float32, device=dev)
-        aux["stats"] = torch.empty(4, dtype=torch.int64, device=dev)
+        aux["stats"] = torch.empty(6, dtype=torch.int64, device=dev)
         for k in ("len", "mask", "adv", "logp", "tok_loss", "stats"):
             setattr(s, k, aux[k].data_ptr())
     if rows_events is not None:
         s.rows_event_begin = rows_events[0].cuda_event
         s.rows_event_end = rows_events[1].cuda_event
-    _check(lib().drgrpo_loss_fwd_bwd_ex(*args, ctypes.byref(s)), "drgrpo_loss_fwd_bwd_ex")
+    var = _Variant(int(adv_mode), int(agg))
+    _check(lib().drgrpo_loss_fwd_bwd_ex(*args, ctypes.byref(s), ctypes.byref(var)),
+           "drgrpo_loss_fwd_bwd_ex")
     return loss, out_dlogits
 
 
@@ -218,13 +236,13 @@ def completion_mask(tokens: torch.Tensor, eos_id: int):
     return ln, mk
 
 
-def group_advantage(rewards: torch.Tensor, G: int):
+def group_advantage(rewards: torch.Tensor, G: int, mode: int = ADV_CENTER):
     """(advantages float32 [N], no-contrast group count int32 [1])."""
     _dev(rewards, "rewards", torch.float32)
     N = rewards.numel()
     adv = torch.empty(N, dtype=torch.float32, device=rewards.device)
     cnt = torch.empty(1, dtype=torch.int32, device=rewards.device)
-    _check(lib().drgrpo_group_advantage(rewards.data_ptr(), N, int(G), adv.data_ptr(),
+    _check(lib().drgrpo_group_advantage(rewards.data_ptr(), N, int(G), int(mode), adv.data_ptr(),
                                         cnt.data_ptr(), _stream(rewards.device)),
            "drgrpo_group_advantage")
     return adv, cnt
@@ -246,7 +264,8 @@ def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Ten
                         beta: float = 0.0, norm_const: float | None = None,
                         out_dhidden: torch.Tensor | None = None,
                         out_dW: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None):
+                        workspace: torch.Tensor | None = None, adv_mode: int = ADV_CENTER,
+                        agg: int = AGG_TOKEN_SUM):
     """Fused lm_head variant: logits = hidden . W^T are never stored.
 
     hidden [N*C, H] (or [N, C, H]) bfloat16, W [V, H] bfloat16, tokens [N, C]
@@ -278,11 +297,13 @@ def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Ten
             raise DrGRPOError(ERR_SHAPE, "drgrpo_lmhead_workspace_bytes")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
-    _check(lib().drgrpo_lmhead_loss_fwd_bwd(
+    var = _Variant(int(adv_mode), int(agg))
+    _check(lib().drgrpo_lmhead_loss_fwd_bwd_ex(
         hidden.data_ptr(), W.data_ptr(), tokens.data_ptr(), int(eos_id), rewards.data_ptr(),
         logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta), float(norm_const),
         loss.data_ptr(), out_dhidden.data_ptr(), out_dW.data_ptr(), N, C, V, H,
-        workspace.data_ptr(), workspace.numel(), _stream(dev)), "drgrpo_lmhead_loss_fwd_bwd")
+        workspace.data_ptr(), workspace.numel(), _stream(dev), ctypes.byref(var)),
+        "drgrpo_lmhead_loss_fwd_bwd_ex")
     return loss, out_dhidden, out_dW
 
 

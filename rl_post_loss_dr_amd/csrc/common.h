@@ -70,9 +70,10 @@ __device__ inline TokenTerms token_terms(double logp, float old, float ref, floa
 
 // ------------------------------------------------------------------- k_prep
 // One wavefront per completion row i.
+// adv_mode: DRGRPO_ADV_CENTER or DRGRPO_ADV_ZSCORE (include/drgrpo.h).
 __global__ void __launch_bounds__(64)
 k_prep(const int64_t* __restrict__ tokens, int64_t C, int64_t eos_id,
-       const float* __restrict__ rewards, int64_t G, int32_t* __restrict__ len,
+       const float* __restrict__ rewards, int64_t G, int adv_mode, int32_t* __restrict__ len,
        float* __restrict__ adv, uint8_t* __restrict__ row_flags, int32_t* __restrict__ aux_len,
        uint8_t* __restrict__ aux_mask, float* __restrict__ aux_adv,
        int32_t* __restrict__ nocontrast_count) {
@@ -99,7 +100,13 @@ k_prep(const int64_t* __restrict__ tokens, int64_t C, int64_t eos_id,
     }
   }
   if (rewards && lane == 0) {
-    // A_i = R_i - (sequential binary32 group sum) / G
+    // A_i = R_i - (sequential binary32 group sum) / G ("Dr. GRPO"); the GRPO
+    // variant divides by the group's sample standard deviation (sequential
+    // sum of rounded squares, / (G-1), correctly rounded sqrt and division),
+    // and gives 0 to a group whose rewards are all equal.  No contraction:
+    // every product and sum is rounded on its own, bit-identical to a plain
+    // binary32 evaluation in this order.
+#pragma clang fp contract(off)
     const int64_t g0 = (i / G) * G;
     const float r0 = rewards[g0];
     float s = 0.0f;
@@ -110,7 +117,21 @@ k_prep(const int64_t* __restrict__ tokens, int64_t C, int64_t eos_id,
       same = same && (r == r0);
     }
     const float mu = s / (float)G;
-    const float a = rewards[i] - mu;
+    float a = rewards[i] - mu;
+    if (adv_mode == DRGRPO_ADV_ZSCORE) {
+      if (same) {
+        a = 0.0f;
+      } else {
+        float q = 0.0f;
+        for (int64_t j = 0; j < G; ++j) {
+          const float d = rewards[g0 + j] - mu;
+          const float d2 = d * d;
+          q = q + d2;
+        }
+        const float sd = sqrtf(q / (float)(G - 1));
+        a = a / sd;
+      }
+    }
     if (adv) adv[i] = a;
     if (aux_adv) aux_adv[i] = a;
     const bool group_head = (i == g0) && same;
@@ -122,6 +143,34 @@ k_prep(const int64_t* __restrict__ tokens, int64_t C, int64_t eos_id,
 }
 
 __global__ void k_zero_i32(int32_t* p) { *p = 0; }
+
+// Divisor of completion i's token sum for the aggregation `agg`
+// (include/drgrpo.h, drgrpo_variant_t): kappa (token sum), kappa*len_i
+// (per-response mean), kappa * total counted tokens (token mean).
+__device__ inline double row_divisor(int agg, double kappa, int32_t len_i,
+                                     const int64_t* total_len) {
+  if (agg == DRGRPO_AGG_SEQ_MEAN) return kappa * (double)len_i;
+  if (agg == DRGRPO_AGG_TOKEN_MEAN) return kappa * (double)*total_len;
+  return kappa;
+}
+
+// Total counted tokens (sum of len) for the token mean: one workgroup,
+// integer sum (exact, order-free).
+__global__ void __launch_bounds__(1024)
+k_total_len(const int32_t* __restrict__ len, int64_t N, int64_t* __restrict__ total) {
+  __shared__ long long sh[16];
+  long long s = 0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) s += len[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long t = 0;
+    for (int w = 0; w < 16; ++w) t += sh[w];
+    *total = (int64_t)t;
+  }
+}
 
 // ----------------------------------------------------------------- k_finish
 __device__ inline double wave_sum_d(double v) {
@@ -135,14 +184,17 @@ __device__ inline int wave_sum_i(int v) {
   return v;
 }
 
+// tok_loss holds each token's term already divided by its row divisor, so
+// the loss is their plain sum (fixed order).  Counters: see drgrpo_aux_t.
 __global__ void __launch_bounds__(1024)
 k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_flags, int64_t T,
-         const uint8_t* __restrict__ row_flags, int64_t N, double kappa,
-         float* __restrict__ out_loss, int32_t* __restrict__ status,
-         int64_t* __restrict__ aux_stats) {
+         const uint8_t* __restrict__ row_flags, const int32_t* __restrict__ len,
+         const float* __restrict__ adv, float beta, int64_t N, float* __restrict__ out_loss,
+         int32_t* __restrict__ status, int64_t* __restrict__ aux_stats) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   double s = 0.0;
   int n_out = 0, n_cut = 0, n_bad = 0, n_trunc = 0, n_noc = 0;
+  long long n_len = 0, n_act = 0;
   for (int64_t k = tid; k < T; k += 1024) {
     s += tok_loss[k];
     const uint8_t f = tok_flags[k];
@@ -154,6 +206,8 @@ k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_fl
     const uint8_t f = row_flags[k];
     n_trunc += (f & RF_NOEOS) ? 1 : 0;
     n_noc += (f & RF_NOCONTRAST) ? 1 : 0;
+    n_len += len[k];
+    n_act += (adv[k] != 0.0f || beta != 0.0f) ? len[k] : 0;
   }
   s = wave_sum_d(s);
   n_out = wave_sum_i(n_out);
@@ -161,8 +215,14 @@ k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_fl
   n_bad = wave_sum_i(n_bad);
   n_trunc = wave_sum_i(n_trunc);
   n_noc = wave_sum_i(n_noc);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    n_len += __shfl_xor(n_len, off);
+    n_act += __shfl_xor(n_act, off);
+  }
   __shared__ double sh_s[16];
   __shared__ int sh_i[5][16];
+  __shared__ long long sh_l[2][16];
   if (lane == 0) {
     sh_s[wave] = s;
     sh_i[0][wave] = n_out;
@@ -170,16 +230,21 @@ k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_fl
     sh_i[2][wave] = n_bad;
     sh_i[3][wave] = n_trunc;
     sh_i[4][wave] = n_noc;
+    sh_l[0][wave] = n_len;
+    sh_l[1][wave] = n_act;
   }
   __syncthreads();
   if (tid == 0) {
     double tot = 0.0;
     int64_t c[5] = {0, 0, 0, 0, 0};
+    int64_t nl = 0, na = 0;
     for (int w = 0; w < 16; ++w) {
       tot += sh_s[w];
       for (int q = 0; q < 5; ++q) c[q] += sh_i[q][w];
+      nl += sh_l[0][w];
+      na += sh_l[1][w];
     }
-    *out_loss = (float)(tot / kappa);
+    *out_loss = (float)tot;
     status[0] = c[2] ? kStatusTokenRange : 0;
     status[1] = (int32_t)c[3];
     status[2] = (int32_t)c[4];
@@ -188,6 +253,8 @@ k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_fl
       aux_stats[1] = c[3];
       aux_stats[2] = c[0];
       aux_stats[3] = c[1];
+      aux_stats[4] = nl;
+      aux_stats[5] = na;
     }
   }
 }
@@ -201,6 +268,15 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 }
 
 bool finite_f(float x) { return x == x && x - x == 0.0f; }
+
+// Validated variant (NULL = Dr. GRPO: centred advantage, token sum).
+bool read_variant(const drgrpo_variant_t* v, int* adv_mode, int* agg) {
+  *adv_mode = v ? v->adv_mode : DRGRPO_ADV_CENTER;
+  *agg = v ? v->agg_mode : DRGRPO_AGG_TOKEN_SUM;
+  return (*adv_mode == DRGRPO_ADV_CENTER || *adv_mode == DRGRPO_ADV_ZSCORE) &&
+         (*agg == DRGRPO_AGG_TOKEN_SUM || *agg == DRGRPO_AGG_SEQ_MEAN ||
+          *agg == DRGRPO_AGG_TOKEN_MEAN);
+}
 
 int launch_status() { return hipGetLastError() == hipSuccess ? DRGRPO_OK : DRGRPO_ERR_HIP; }
 

@@ -16,8 +16,10 @@
  *             from the same registers.  Rows longer than one register tile
  *             are swept tile by tile and re-read for the write pass.  Tokens
  *             whose loss term is identically zero only write zeros.
- *   k_finish  one workgroup: fixed-order binary64 sum of the per-token terms,
- *             divide by norm_const, counters and the status word.
+ *   k_finish  one workgroup: fixed-order binary64 sum of the per-token terms
+ *             (each already divided by its completion's aggregation divisor:
+ *             norm_const for the Dr. GRPO token sum), counters and the
+ *             status word.
  * No floating-point atomics: results are bitwise reproducible.
  */
 #include <hip/hip_ext.h>
@@ -42,7 +44,8 @@ struct Ws {
   int32_t* len;        // [N]
   float* adv;          // [N]
   uint8_t* row_flags;  // [N]
-  double* tok_loss;    // [T]
+  int64_t* total_len;  // [1] counted tokens (token-mean aggregation)
+  double* tok_loss;    // [T] per-token term / row divisor
   uint8_t* tok_flags;  // [T]
 };
 
@@ -59,6 +62,7 @@ size_t ws_carve(void* base, int64_t N, int64_t T, Ws* ws) {
   w.len = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * N));
   w.adv = reinterpret_cast<float*>(take(sizeof(float) * N));
   w.row_flags = reinterpret_cast<uint8_t*>(take(N));
+  w.total_len = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.tok_loss = reinterpret_cast<double*>(take(sizeof(double) * T));
   w.tok_flags = reinterpret_cast<uint8_t*>(take(T));
   if (ws) *ws = w;
@@ -202,6 +206,8 @@ struct RowArgs {
   float eps;
   float beta;
   double kappa;
+  int agg;                   // drgrpo_agg_mode_t
+  const int64_t* total_len;  // counted tokens of the batch (token mean only)
   double* tok_loss;
   uint8_t* tok_flags;
   float* aux_logp;
@@ -395,10 +401,11 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
     if (kFwdOnly) {
       if (lane == 0) a.out_logp[row] = (float)logp;
     } else if (lane == 0) {
-      const TokenTerms tt = token_terms(logp, old, ref, A, a.eps, a.beta, a.kappa);
+      const double div = row_divisor(a.agg, a.kappa, a.len[i], a.total_len);
+      const TokenTerms tt = token_terms(logp, old, ref, A, a.eps, a.beta, div);
       const double lam = tt.lam;
       const double coef = tt.coef;
-      a.tok_loss[row] = lam;
+      a.tok_loss[row] = lam / div;
       a.tok_flags[row] = tt.flags;
       if (a.aux_logp) a.aux_logp[row] = (float)logp;
       if (a.aux_tok_loss) a.aux_tok_loss[row] = (float)lam;
@@ -494,7 +501,7 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
                                       float norm_const, float* out_loss, void* out_dlogits,
                                       int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
                                       void* workspace, size_t workspace_bytes, void* stream,
-                                      const drgrpo_aux_t* aux) {
+                                      const drgrpo_aux_t* aux, const drgrpo_variant_t* variant) {
   if (!logits || !tokens || !rewards || !logp_old || !out_loss || !out_dlogits)
     return DRGRPO_ERR_NULL;
   if (dtype != DRGRPO_F32 && dtype != DRGRPO_BF16) return DRGRPO_ERR_DTYPE;
@@ -505,6 +512,8 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
       norm_const <= 0.0f)
     return DRGRPO_ERR_PARAM;
   if (beta > 0.0f && !logp_ref) return DRGRPO_ERR_NULL;
+  int adv_mode, agg;
+  if (!read_variant(variant, &adv_mode, &agg)) return DRGRPO_ERR_PARAM;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
       workspace_bytes < ws_carve(nullptr, N, T, nullptr))
     return DRGRPO_ERR_WORKSPACE;
@@ -522,9 +531,14 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
   const drgrpo_aux_t& x = aux ? *aux : none;
 
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
-                     ws.len, ws.adv, ws.row_flags, x.len, x.mask, x.adv, (int32_t*)nullptr);
+                     adv_mode, ws.len, ws.adv, ws.row_flags, x.len, x.mask, x.adv,
+                     (int32_t*)nullptr);
   int rc = launch_status();
   if (rc != DRGRPO_OK) return rc;
+  if (agg == DRGRPO_AGG_TOKEN_MEAN) {
+    hipLaunchKernelGGL(k_total_len, dim3(1), dim3(1024), 0, st, ws.len, N, ws.total_len);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  }
 
   RowArgs a;
   a.logits = logits;
@@ -539,6 +553,8 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
   a.eps = eps;
   a.beta = beta;
   a.kappa = (double)norm_const;
+  a.agg = agg;
+  a.total_len = ws.total_len;
   a.tok_loss = ws.tok_loss;
   a.tok_flags = ws.tok_flags;
   a.aux_logp = x.logp;
@@ -549,7 +565,7 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
   if (rc != DRGRPO_OK) return rc;
 
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, ws.tok_loss, ws.tok_flags, T,
-                     ws.row_flags, N, (double)norm_const, out_loss, ws.status, x.stats);
+                     ws.row_flags, ws.len, ws.adv, beta, N, out_loss, ws.status, x.stats);
   return launch_status();
 }
 
@@ -561,7 +577,7 @@ extern "C" int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, in
                                    void* workspace, size_t workspace_bytes, void* stream) {
   return drgrpo_loss_fwd_bwd_ex(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
                                 norm_const, out_loss, out_dlogits, N, C, V, dtype, workspace,
-                                workspace_bytes, stream, nullptr);
+                                workspace_bytes, stream, nullptr, nullptr);
 }
 
 extern "C" int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t C,
@@ -571,16 +587,18 @@ extern "C" int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t 
   int64_t T;
   if (N <= 0 || C <= 0 || !mul_ok(N, C, &T) || N > INT32_MAX) return DRGRPO_ERR_SHAPE;
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, static_cast<hipStream_t>(stream),
-                     tokens, C, eos_id, (const float*)nullptr, (int64_t)1, (int32_t*)nullptr,
+                     tokens, C, eos_id, (const float*)nullptr, (int64_t)1, 0, (int32_t*)nullptr,
                      (float*)nullptr, (uint8_t*)nullptr, out_len, out_mask, (float*)nullptr,
                      (int32_t*)nullptr);
   return launch_status();
 }
 
-extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, float* out_adv,
+extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G,
+                                      int32_t adv_mode, float* out_adv,
                                       int32_t* out_nocontrast, void* stream) {
   if (!rewards || !out_adv) return DRGRPO_ERR_NULL;
   if (N <= 0 || G <= 0 || N % G != 0 || N > INT32_MAX) return DRGRPO_ERR_SHAPE;
+  if (adv_mode != DRGRPO_ADV_CENTER && adv_mode != DRGRPO_ADV_ZSCORE) return DRGRPO_ERR_PARAM;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (out_nocontrast) {
     hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(1), 0, st, out_nocontrast);
@@ -588,7 +606,8 @@ extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G
     if (rc != DRGRPO_OK) return rc;
   }
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, (const int64_t*)nullptr,
-                     (int64_t)1, (int64_t)0, rewards, G, (int32_t*)nullptr, (float*)nullptr,
+                     (int64_t)1, (int64_t)0, rewards, G, (int)adv_mode, (int32_t*)nullptr,
+                     (float*)nullptr,
                      (uint8_t*)nullptr, (int32_t*)nullptr, (uint8_t*)nullptr, out_adv,
                      out_nocontrast);
   return launch_status();

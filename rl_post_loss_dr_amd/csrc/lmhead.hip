@@ -622,9 +622,11 @@ __global__ void __launch_bounds__(256)
 k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restrict__ xy,
              const int32_t* __restrict__ counts, const int32_t* __restrict__ act_pos,
              const int32_t* __restrict__ ycol, int64_t C, const float* __restrict__ adv,
-             const float* __restrict__ logp_old, const float* __restrict__ logp_ref, float eps,
-             float beta, double kappa, float* __restrict__ lse2, float* __restrict__ coef,
-             double* __restrict__ tok_loss, uint8_t* __restrict__ tok_flags) {
+             const int32_t* __restrict__ len, const float* __restrict__ logp_old,
+             const float* __restrict__ logp_ref, float eps, float beta, double kappa, int agg,
+             const int64_t* __restrict__ total_len, float* __restrict__ lse2,
+             float* __restrict__ coef, double* __restrict__ tok_loss,
+             uint8_t* __restrict__ tok_flags) {
   const int lane = threadIdx.x & 63;
   const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (k >= counts[0]) return;
@@ -638,9 +640,10 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
     return;
   }
   const double logp = (double)xy[k] - lse;
+  const double div = row_divisor(agg, kappa, len[i], total_len);
   const TokenTerms tt = token_terms(logp, logp_old[pos], beta != 0.0f ? logp_ref[pos] : 0.0f,
-                                    adv[i], eps, beta, kappa);
-  tok_loss[pos] = tt.lam;
+                                    adv[i], eps, beta, div);
+  tok_loss[pos] = tt.lam / div;
   tok_flags[pos] = tt.flags;
   lse2[k] = (float)(lse * kL2ED);
   coef[k] = (float)tt.coef;
@@ -692,6 +695,7 @@ struct LmWs {
   int32_t* len;
   float* adv;
   uint8_t* row_flags;
+  int64_t* total_len;  // [1] counted tokens (token-mean aggregation)
   int32_t* offs;     // [N + 1]
   int32_t* counts;   // [2]: active tokens, padded to 8
   int32_t* act_pos;  // [T]
@@ -728,6 +732,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.len = reinterpret_cast<int32_t*>(take(4 * N));
   w.adv = reinterpret_cast<float*>(take(4 * N));
   w.row_flags = reinterpret_cast<uint8_t*>(take(N));
+  w.total_len = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.offs = reinterpret_cast<int32_t*>(take(4 * (N + 1)));
   w.counts = reinterpret_cast<int32_t*>(take(16));
   w.act_pos = reinterpret_cast<int32_t*>(take(4 * T));
@@ -820,14 +825,15 @@ extern "C" size_t drgrpo_lmhead_workspace_bytes(int64_t N, int64_t C, int64_t V,
   return lm_carve(nullptr, N, T, V, H, nullptr);
 }
 
-extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,
-                                          int64_t eos_id, const float* rewards,
-                                          const float* logp_old, const float* logp_ref, int64_t G,
-                                          float eps, float beta, float norm_const,
-                                          float* out_loss, void* out_dhidden, void* out_dW,
-                                          int64_t N, int64_t C, int64_t V, int64_t H,
-                                          void* workspace, size_t workspace_bytes,
-                                          void* stream) {
+extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
+                                             const int64_t* tokens, int64_t eos_id,
+                                             const float* rewards, const float* logp_old,
+                                             const float* logp_ref, int64_t G, float eps,
+                                             float beta, float norm_const, float* out_loss,
+                                             void* out_dhidden, void* out_dW, int64_t N,
+                                             int64_t C, int64_t V, int64_t H, void* workspace,
+                                             size_t workspace_bytes, void* stream,
+                                             const drgrpo_variant_t* variant) {
   if (!hidden || !W || !tokens || !rewards || !logp_old || !out_loss || !out_dhidden || !out_dW)
     return DRGRPO_ERR_NULL;
   int64_t T;
@@ -837,6 +843,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
       norm_const <= 0.0f)
     return DRGRPO_ERR_PARAM;
   if (beta > 0.0f && !logp_ref) return DRGRPO_ERR_NULL;
+  int adv_mode, agg;
+  if (!read_variant(variant, &adv_mode, &agg)) return DRGRPO_ERR_PARAM;
   const uintptr_t al = reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W) |
                        reinterpret_cast<uintptr_t>(out_dhidden) |
                        reinterpret_cast<uintptr_t>(out_dW);
@@ -855,9 +863,13 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
 
   // mask, advantage, active-token list, gathered hidden rows and transposes
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
-                     w.len, w.adv, w.row_flags, (int32_t*)nullptr, (uint8_t*)nullptr,
+                     adv_mode, w.len, w.adv, w.row_flags, (int32_t*)nullptr, (uint8_t*)nullptr,
                      (float*)nullptr, (int32_t*)nullptr);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  if (agg == DRGRPO_AGG_TOKEN_MEAN) {
+    hipLaunchKernelGGL(k_total_len, dim3(1), dim3(1024), 0, st, w.len, N, w.total_len);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  }
   hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, w.adv, N, beta, w.offs,
                      w.counts);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
@@ -888,8 +900,9 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
   g.col_base = 0;
   if ((rc = launch_gemm<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
-                     w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, logp_old, logp_ref, eps, beta,
-                     (double)norm_const, w.lse2, w.coef, w.tok_loss, w.tok_flags);
+                     w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, w.len, logp_old, logp_ref, eps,
+                     beta, (double)norm_const, agg, w.total_len, w.lse2, w.coef, w.tok_loss,
+                     w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
   // backward, one vocabulary chunk at a time
@@ -954,8 +967,21 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
                      tokens, C, V, static_cast<uint16_t*>(out_dhidden));
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, w.tok_loss, w.tok_flags, T,
-                     w.row_flags, N, (double)norm_const, out_loss, w.status, (int64_t*)nullptr);
+                     w.row_flags, w.len, w.adv, beta, N, out_loss, w.status, (int64_t*)nullptr);
   return launch_status();
+}
+
+extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,
+                                          int64_t eos_id, const float* rewards,
+                                          const float* logp_old, const float* logp_ref, int64_t G,
+                                          float eps, float beta, float norm_const,
+                                          float* out_loss, void* out_dhidden, void* out_dW,
+                                          int64_t N, int64_t C, int64_t V, int64_t H,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  return drgrpo_lmhead_loss_fwd_bwd_ex(hidden, W, tokens, eos_id, rewards, logp_old, logp_ref, G,
+                                       eps, beta, norm_const, out_loss, out_dhidden, out_dW, N, C,
+                                       V, H, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" size_t drgrpo_lmhead_logprobs_workspace_bytes(int64_t N, int64_t C, int64_t V,
@@ -985,7 +1011,7 @@ extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const i
   int rc;
   // counted tokens (first EOS inclusive), listed and gathered like the loss pass
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id,
-                     (const float*)nullptr, (int64_t)1, w.len, (float*)nullptr, (uint8_t*)nullptr,
+                     (const float*)nullptr, (int64_t)1, 0, w.len, (float*)nullptr, (uint8_t*)nullptr,
                      (int32_t*)nullptr, (uint8_t*)nullptr, (float*)nullptr, (int32_t*)nullptr);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, (const float*)nullptr, N,

@@ -93,8 +93,17 @@ def test_argument_validation(L, kw, code):
 def test_other_entry_points_validate(L):
     assert L.drgrpo_completion_mask(None, 4, 4, 0, FAKE, None, None) == dr.ERR_NULL
     assert L.drgrpo_completion_mask(FAKE, 0, 4, 0, FAKE, None, None) == dr.ERR_SHAPE
-    assert L.drgrpo_group_advantage(FAKE, 8, 3, FAKE, None, None) == dr.ERR_SHAPE
-    assert L.drgrpo_group_advantage(None, 8, 4, FAKE, None, None) == dr.ERR_NULL
+    assert L.drgrpo_group_advantage(FAKE, 8, 3, 0, FAKE, None, None) == dr.ERR_SHAPE
+    assert L.drgrpo_group_advantage(None, 8, 4, 0, FAKE, None, None) == dr.ERR_NULL
+    assert L.drgrpo_group_advantage(FAKE, 8, 4, 2, FAKE, None, None) == dr.ERR_PARAM
+    assert L.drgrpo_lmhead_logprobs(None, FAKE, FAKE, 0, 2, 4, 64, 32, FAKE, FAKE, 1 << 30,
+                                    None) == dr.ERR_NULL
+    assert L.drgrpo_lmhead_logprobs(FAKE, FAKE, FAKE, 0, 2, 4, 64, 30, FAKE, FAKE, 1 << 30,
+                                    None) == dr.ERR_SHAPE
+    assert L.drgrpo_lmhead_logprobs(FAKE, FAKE, FAKE, 0, 2, 4, 64, 32, FAKE, FAKE, 16,
+                                    None) == dr.ERR_WORKSPACE
+    assert L.drgrpo_lmhead_logprobs_workspace_bytes(2, 4, 64, 32) > 0
+    assert L.drgrpo_lmhead_logprobs_workspace_bytes(2, 4, 64, 31) == 0
     assert L.drgrpo_logprobs(FAKE, FAKE, 2, 2, 10, 9, FAKE, None) == dr.ERR_DTYPE
     assert L.drgrpo_logprobs(FAKE, FAKE, 2, 0, 10, 1, FAKE, None) == dr.ERR_SHAPE
     assert L.drgrpo_device_status(None, None) == dr.ERR_NULL
@@ -118,3 +127,18 @@ def test_graft_entry_build_compiles_and_imports():
 
     __graft_entry__.build()
     assert os.path.exists(dr.LIB)
+
+
+@pytest.mark.parametrize("adv_mode,agg,code", [(0, 0, dr.ERR_WORKSPACE), (1, 2, dr.ERR_WORKSPACE),
+                                               (2, 0, dr.ERR_PARAM), (0, 3, dr.ERR_PARAM),
+                                               (-1, 0, dr.ERR_PARAM)])
+def test_variant_validation(L, adv_mode, agg, code):
+    """Unknown normalisation modes are rejected before anything is launched
+    (valid ones get as far as the too-small workspace)."""
+    var = dr._Variant(adv_mode, agg)
+    args = (FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE * 1000000, 64, 256,
+            151936, 1, FAKE * 4096, 16, None)
+    assert L.drgrpo_loss_fwd_bwd_ex(*args, None, ctypes.byref(var)) == code
+    lm = (FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE, FAKE, 64, 256,
+          4096, 896, FAKE * 4096, 16, None)
+    assert L.drgrpo_lmhead_loss_fwd_bwd_ex(*lm, ctypes.byref(var)) == code
