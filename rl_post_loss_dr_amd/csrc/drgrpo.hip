@@ -70,9 +70,25 @@ size_t ws_carve(void* base, int64_t N, int64_t T, Ws* ws) {
 }
 
 // ----------------------------------------------------------------- element IO
-// Row data moves in 16-byte chunks (bf16 x 8 or f32 x 4) with nontemporal
-// loads and stores: every byte is touched once, so nothing is kept in cache.
+// Row data moves in 16-byte chunks (bf16 x 8 or f32 x 4).  Loads are
+// nontemporal global loads: every byte is read once.  Stores go through a
+// buffer descriptor spanning exactly the output row (the hardware drops any
+// access past it) with the nontemporal + sc1 cache policy, which measured
+// 2-5% faster than plain nontemporal stores for this write-heavy stream.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// cache-policy immediate of a buffer store on gfx950: sc1 (16) | nt (2)
+constexpr int kStorePolicy = 16 | 2;
+// third descriptor word of a raw (byte-addressed, unswizzled) buffer
+constexpr int kRawBufferWord3 = 0x00020000;
+
+struct RowOut {
+  __amdgpu_buffer_rsrc_t rsrc;  // the output row, bounded by its byte size
+};
+
+__device__ inline RowOut row_out(char* row, uint32_t bytes) {
+  return RowOut{__builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)bytes, kRawBufferWord3)};
+}
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   const __bf16 ha = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
@@ -101,19 +117,18 @@ struct Io<DRGRPO_BF16, 8> {
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
     f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
   }
-  // `sign` (0 or all ones) flips the sign bit of every stored value
-  __device__ static void store(char* row, uint32_t c, const float (&f)[8], uint32_t sign = 0) {
+  // `sign` (0 or all ones) flips the sign bit of every packed value
+  __device__ static chunk pack(const float (&f)[8], uint32_t sign) {
     const uint32_t m = sign & 0x80008000u;
-    u32x4 o;
-    o.x = pack_bf16x2(f[0], f[1]) ^ m;
-    o.y = pack_bf16x2(f[2], f[3]) ^ m;
-    o.z = pack_bf16x2(f[4], f[5]) ^ m;
-    o.w = pack_bf16x2(f[6], f[7]) ^ m;
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(row) + c);
+    return u32x4{pack_bf16x2(f[0], f[1]) ^ m, pack_bf16x2(f[2], f[3]) ^ m,
+                 pack_bf16x2(f[4], f[5]) ^ m, pack_bf16x2(f[6], f[7]) ^ m};
   }
-  __device__ static void fill(char* row, uint32_t c, float val) {
+  __device__ static void store(const RowOut& o, uint32_t c, const chunk& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, o.rsrc, (int)(c * 16u), 0, kStorePolicy);
+  }
+  __device__ static chunk splat(float val) {
     const uint32_t w = pack_bf16x2(val, val);
-    __builtin_nontemporal_store(u32x4{w, w, w, w}, reinterpret_cast<u32x4*>(row) + c);
+    return u32x4{w, w, w, w};
   }
 };
 
@@ -129,15 +144,17 @@ struct Io<DRGRPO_F32, 4> {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
-  __device__ static void store(char* row, uint32_t c, const float (&f)[4], uint32_t sign = 0) {
+  __device__ static chunk pack(const float (&f)[4], uint32_t sign) {
     const uint32_t m = sign & 0x80000000u;
-    const u32x4 o{__float_as_uint(f[0]) ^ m, __float_as_uint(f[1]) ^ m,
-                  __float_as_uint(f[2]) ^ m, __float_as_uint(f[3]) ^ m};
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(row) + c);
+    return u32x4{__float_as_uint(f[0]) ^ m, __float_as_uint(f[1]) ^ m,
+                 __float_as_uint(f[2]) ^ m, __float_as_uint(f[3]) ^ m};
   }
-  __device__ static void fill(char* row, uint32_t c, float val) {
+  __device__ static void store(const RowOut& o, uint32_t c, const chunk& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, o.rsrc, (int)(c * 16u), 0, kStorePolicy);
+  }
+  __device__ static chunk splat(float val) {
     const uint32_t w = __float_as_uint(val);
-    __builtin_nontemporal_store(u32x4{w, w, w, w}, reinterpret_cast<u32x4*>(row) + c);
+    return u32x4{w, w, w, w};
   }
 };
 
@@ -152,15 +169,16 @@ struct Io<DRGRPO_BF16, 1> {
   __device__ static void unpack(const chunk& v, float (&f)[1]) {
     f[0] = __uint_as_float((uint32_t)v << 16);
   }
-  __device__ static void store(char* row, uint32_t c, const float (&f)[1], uint32_t sign = 0) {
+  __device__ static chunk pack(const float (&f)[1], uint32_t sign) {
     const __bf16 h = (__bf16)f[0];
-    __builtin_nontemporal_store((uint16_t)(__builtin_bit_cast(uint16_t, h) ^ (sign & 0x8000u)),
-                                reinterpret_cast<uint16_t*>(row) + c);
+    return (uint16_t)(__builtin_bit_cast(uint16_t, h) ^ (sign & 0x8000u));
   }
-  __device__ static void fill(char* row, uint32_t c, float val) {
+  __device__ static void store(const RowOut& o, uint32_t c, const chunk& v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, o.rsrc, (int)(c * 2u), 0, kStorePolicy);
+  }
+  __device__ static chunk splat(float val) {
     const __bf16 h = (__bf16)val;
-    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, h),
-                                reinterpret_cast<uint16_t*>(row) + c);
+    return __builtin_bit_cast(uint16_t, h);
   }
 };
 
@@ -173,13 +191,14 @@ struct Io<DRGRPO_F32, 1> {
     return __builtin_nontemporal_load(reinterpret_cast<const float*>(row) + c);
   }
   __device__ static void unpack(const chunk& v, float (&f)[1]) { f[0] = v; }
-  __device__ static void store(char* row, uint32_t c, const float (&f)[1], uint32_t sign = 0) {
-    __builtin_nontemporal_store(__uint_as_float(__float_as_uint(f[0]) ^ (sign & 0x80000000u)),
-                                reinterpret_cast<float*>(row) + c);
+  __device__ static chunk pack(const float (&f)[1], uint32_t sign) {
+    return __uint_as_float(__float_as_uint(f[0]) ^ (sign & 0x80000000u));
   }
-  __device__ static void fill(char* row, uint32_t c, float val) {
-    __builtin_nontemporal_store(val, reinterpret_cast<float*>(row) + c);
+  __device__ static void store(const RowOut& o, uint32_t c, const chunk& v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), o.rsrc, (int)(c * 4u), 0,
+                                          kStorePolicy);
   }
+  __device__ static chunk splat(float val) { return val; }
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -235,10 +254,13 @@ __device__ inline void lse_chunk(float& m, float& s, const float (&f)[VEC]) {
 
 // Pass 2 of a row: dlogits = coef * (softmax - onehot), with |coef| folded
 // into the exponent (|coef| * exp(x - lse) = exp2(x*log2e - off2)) and the
-// sign of coef applied to the packed result bits.
+// sign of coef applied to the packed result bits.  Each register tile is
+// converted in place, then stored as one burst of 16-byte stores (the
+// stores of a tile leave back to back instead of one per converted chunk,
+// measured 2-3% faster).
 template <typename IO, int VEC>
 __device__ __attribute__((always_inline)) inline void write_dlogits(
-    typename IO::chunk (&buf)[kNch], const char* in, char* out, uint32_t nchunks,
+    typename IO::chunk (&buf)[kNch], const char* in, const RowOut& out, uint32_t nchunks,
     uint32_t ntiles, int tid, float off2, float dy, bool neg, int64_t y) {
   const uint32_t tile = (uint32_t)kNch * kThreads;
   const uint32_t last = nchunks - 1;
@@ -261,8 +283,7 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
     const int owner = here ? (int)((cy - tb) % kThreads) : -1;
 #pragma unroll
     for (int j = 0; j < kNch; ++j) {
-      const uint32_t sb = tb + (uint32_t)j * kThreads;
-      if (sb < nchunks) {
+      if (tb + (uint32_t)j * kThreads < nchunks) {
         float f[VEC];
         IO::unpack(buf[j], f);
 #pragma unroll
@@ -271,8 +292,13 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
 #pragma unroll
           for (int e = 0; e < VEC; ++e) f[e] = e == ey ? dy_pre : f[e];
         }
-        if (sb + kThreads <= nchunks || sb + tid < nchunks) IO::store(out, sb + tid, f, sign);
+        buf[j] = IO::pack(f, sign);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < kNch; ++j) {
+      const uint32_t c = tb + (uint32_t)j * kThreads + tid;
+      if (c < nchunks) IO::store(out, c, buf[j]);
     }
   }
 }
@@ -296,7 +322,9 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
   const uint32_t nchunks = (uint32_t)(V / VEC);  // < 2^31 (checked on the host)
   const uint32_t last = nchunks - 1;
   const char* in = static_cast<const char*>(a.logits) + row * V * IO::kBytes;
-  char* out = kFwdOnly ? nullptr : static_cast<char*>(a.dlogits) + row * V * IO::kBytes;
+  const RowOut out =
+      row_out(kFwdOnly ? nullptr : static_cast<char*>(a.dlogits) + row * V * IO::kBytes,
+              kFwdOnly ? 0u : (uint32_t)(V * IO::kBytes));
   const int64_t y = a.tokens[row];
 
   bool in_mask = true;
@@ -313,8 +341,8 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
       if (tid == 0) a.out_logp[row] = NAN;
       return;
     }
-    const float fillv = bad ? NAN : 0.0f;
-    for (uint32_t c = tid; c < nchunks; c += kThreads) IO::fill(out, c, fillv);
+    const typename IO::chunk fillv = IO::splat(bad ? NAN : 0.0f);
+    for (uint32_t c = tid; c < nchunks; c += kThreads) IO::store(out, c, fillv);
     if (tid == 0) {
       a.tok_loss[row] = bad ? (double)NAN : 0.0;
       a.tok_flags[row] = bad ? TF_BADTOK : 0;
@@ -421,7 +449,8 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
   // ---- pass 2: dlogits = coef * (softmax - onehot)
   const float coef = sh_coef;
   if (coef == 0.0f) {  // the clip cut the only gradient term: an exact zero row
-    for (uint32_t c = tid; c < nchunks; c += kThreads) IO::fill(out, c, 0.0f);
+    const typename IO::chunk zero = IO::splat(0.0f);
+    for (uint32_t c = tid; c < nchunks; c += kThreads) IO::store(out, c, zero);
     return;
   }
   write_dlogits<IO, VEC>(buf, in, out, nchunks, ntiles, tid, sh_off2, sh_dy, sh_neg, y);
