@@ -46,7 +46,7 @@ def _alg_bytes(cfg, adv, lens):
 
 def _src_hash():
     h = hashlib.sha256()
-    for p in ("rl_post_loss_dr_amd/csrc/drgrpo.hip",):
+    for p in ("rl_post_loss_dr_amd/csrc/drgrpo.hip", "rl_post_loss_dr_amd/csrc/common.h"):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
