@@ -244,24 +244,29 @@ __device__ inline void lse_chunk(float& m, float& s, const float (&f)[VEC]) {
   for (int e = 1; e < VEC; ++e) cm = fmaxf(cm, f[e]);
   const float nm = fmaxf(m, cm);
   const float base = nm == -INFINITY ? 0.0f : nm;  // nothing finite seen yet
-  const float b2 = base * kLog2e;
+  // exp(x - base) with the difference taken first: exact for the entries
+  // near the maximum that dominate the sum (an fma of x*log2e against
+  // base*log2e would round at the argument's magnitude, ~1e-6 absolute)
   float cs = 0.0f;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) cs += fast_exp2(fmaf(f[e], kLog2e, -b2));
+  for (int e = 0; e < VEC; ++e) cs += fast_exp2((f[e] - base) * kLog2e);
   s = s * fast_exp2((m - base) * kLog2e) + cs;
   m = nm;
 }
 
 // Pass 2 of a row: dlogits = coef * (softmax - onehot), with |coef| folded
-// into the exponent (|coef| * exp(x - lse) = exp2(x*log2e - off2)) and the
-// sign of coef applied to the packed result bits.  Each register tile is
+// into the exponent and the sign of coef applied to the packed result bits:
+// |coef| * exp(x - lse) = exp2((x - M)*log2e - off2) with M the row maximum
+// (a binary32 logit, so x - M is exact for the entries that matter) and
+// off2 = log2(S) - log2|coef| small (lse = M + ln S), which keeps the
+// exponent accurate to ~1e-6 whatever the logits' magnitude.  Each register tile is
 // converted in place, then stored as one burst of 16-byte stores (the
 // stores of a tile leave back to back instead of one per converted chunk,
 // measured 2-3% faster).
 template <typename IO, int VEC>
 __device__ __attribute__((always_inline)) inline void write_dlogits(
     typename IO::chunk (&buf)[kNch], const char* in, const RowOut& out, uint32_t nchunks,
-    uint32_t ntiles, int tid, float off2, float dy, bool neg, int64_t y) {
+    uint32_t ntiles, int tid, float mrow, float off2, float dy, bool neg, int64_t y) {
   const uint32_t tile = (uint32_t)kNch * kThreads;
   const uint32_t last = nchunks - 1;
   const uint32_t cy = (uint32_t)(y / VEC);
@@ -287,7 +292,7 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
         float f[VEC];
         IO::unpack(buf[j], f);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) f[e] = fast_exp2(fmaf(f[e], kLog2e, -off2));
+        for (int e = 0; e < VEC; ++e) f[e] = fast_exp2(fmaf(f[e] - mrow, kLog2e, -off2));
         if (j == js && tid == owner) {  // the sampled token: coef * (p_y - 1)
 #pragma unroll
           for (int e = 0; e < VEC; ++e) f[e] = e == ey ? dy_pre : f[e];
@@ -396,7 +401,7 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
   }
   __shared__ float sh_m[kWaves];
   __shared__ float sh_s[kWaves];
-  __shared__ float sh_coef, sh_off2, sh_dy;
+  __shared__ float sh_coef, sh_m_row, sh_off2, sh_dy;
   __shared__ bool sh_neg;
   if (lane == 0) {
     sh_m[wave] = m;
@@ -439,8 +444,9 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
       if (a.aux_tok_loss) a.aux_tok_loss[row] = (float)lam;
       sh_coef = (float)coef;
       sh_neg = coef < 0.0;
-      sh_off2 = (float)(lse * kLog2eD - log2(fabs(coef)));
-      sh_dy = (float)(coef * (exp(logp) - 1.0));
+      sh_m_row = M;
+      sh_off2 = (float)(log2(term) - log2(fabs(coef)));
+      sh_dy = (float)(coef * expm1(logp));
     }
   }
   if (kFwdOnly) return;
@@ -453,7 +459,8 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
     for (uint32_t c = tid; c < nchunks; c += kThreads) IO::store(out, c, zero);
     return;
   }
-  write_dlogits<IO, VEC>(buf, in, out, nchunks, ntiles, tid, sh_off2, sh_dy, sh_neg, y);
+  write_dlogits<IO, VEC>(buf, in, out, nchunks, ntiles, tid, sh_m_row, sh_off2, sh_dy, sh_neg,
+                         y);
 }
 
 

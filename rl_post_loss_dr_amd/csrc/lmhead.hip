@@ -43,12 +43,20 @@ constexpr int WM = 128, WN = 64;           // wavefront tile
 constexpr int NWM = GBM / WM, NWN = GBN / WN;  // wavefront grid: 2 (rows) x 4 (columns)
 constexpr int GT = 64 * NWM * NWN;         // 8 wavefronts, 2 per SIMD
 constexpr int FM = WM / 16, FN = WN / 16;  // 8 x 4 MFMA blocks per wavefront
-constexpr int kStages = 4;                 // LDS ring depth
+constexpr int kStages = 4;                 // LDS ring depth (3 stages of loads in flight)
 constexpr int kStageElems = (GBM + GBN) * GBK;  // bfloat16 per LDS stage (32 KB)
 constexpr int kDmaPerThread = kStageElems / 8 / GT;  // 16-byte direct loads per thread per stage
-constexpr int kRingElems = kStages * kStageElems;  // 128 KB ring
-constexpr int kTableBytes = 4096;          // per-row epilogue tables, past the ring
-constexpr size_t kGemmLds = kRingElems * sizeof(uint16_t) + kTableBytes;
+constexpr int kRingElems = kStages * kStageElems;
+constexpr int kTableBytes = 4096;          // per-row epilogue tables (after the main loop)
+// the tables sit past the ring when it leaves room, else in its last 4 KB
+// (free once the main loop is over; the epilogue staging uses its first 128 KB)
+constexpr int kLdsMax = 163840;            // gfx950: 160 KB of LDS per workgroup
+constexpr bool kTablesInRing = kRingElems * 2 + kTableBytes > kLdsMax;
+constexpr int kTableElem = kTablesInRing ? kRingElems - kTableBytes / 2 : kRingElems;
+constexpr size_t kGemmLds = kRingElems * sizeof(uint16_t) + (kTablesInRing ? 0 : kTableBytes);
+static_assert(kGemmLds <= (size_t)kLdsMax, "LDS ring too deep");
+static_assert(!kTablesInRing || kRingElems - kTableBytes / 2 >= 8 * 128 * 64,
+              "epilogue staging overlaps the tables");
 constexpr int kPad = 32;                   // token counts and vocabulary chunks are padded to this
 constexpr int kChunkV = 16384;             // vocabulary columns per backward chunk
 constexpr float kL2E = 1.4426950408889634f;
@@ -70,7 +78,7 @@ struct GemmArgs {
   const int32_t* ycol;   // [rows] sampled token id
   int64_t col_base;      // vocabulary id of column 0 (GM_LSE, GM_D)
   // GM_D
-  const float* lse2;     // [rows] lse * log2(e)
+  const float2* lsep;    // [rows] (row maximum M, log2 S) with lse = M + ln S
   const float* coef;     // [rows]
   uint16_t* D;           // [Mpad, ldd] chunk of dlogits, row-major
   int64_t ldd;
@@ -244,20 +252,24 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
-  // operations are outstanding, leave the other counters alone
-  constexpr int kWaitVm0 = 0x0F70;              // vmcnt(0)
-  constexpr int kWaitVmStage = 0x0F70 | kDmaPerThread;  // one stage still in flight
-  constexpr int kWaitVm2Stages = 0x0F70 | (2 * kDmaPerThread);
+  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, the other
+  // counters left alone): wait until at most n stages of this thread's direct
+  // loads are still in flight
+  static_assert(3 * kDmaPerThread < 16, "vmcnt immediate");
+  auto wait_stages = [](int64_t n) {
+    if (n >= 3)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * kDmaPerThread));
+    else if (n == 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerThread));
+    else if (n == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerThread);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
   if (nk > 0) {
     for (int64_t s = 0; s < kStages - 1 && s < nk; ++s) dma(s);
-    // stage 0 complete: the loads of stages 1 and 2 may still be in flight
-    if (nk >= 3)
-      __builtin_amdgcn_s_waitcnt(kWaitVm2Stages);
-    else if (nk == 2)
-      __builtin_amdgcn_s_waitcnt(kWaitVmStage);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // stage 0 complete; the later prologue stages may still be in flight
+    wait_stages(nk - 1 < kStages - 2 ? nk - 1 : kStages - 2);
     ring_barrier();
     frags(0, 0);
   }
@@ -265,10 +277,9 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // visible, refill the slot stage kt-1 used, read stage kt+1's operands into
   // the other registers while stage kt's MFMAs run
   auto step = [&](int64_t kt, int cur) {
-    if (kt + 2 < nk)
-      __builtin_amdgcn_s_waitcnt(kWaitVmStage);  // stage kt+1 done, kt+2 in flight
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // stage kt+1 complete; stages kt+2 .. kt+kStages-2 (those issued) in flight
+    const int64_t ahead = nk - 2 - kt;
+    wait_stages(ahead < kStages - 3 ? (ahead > 0 ? ahead : 0) : kStages - 3);
     ring_barrier();
     if (kt + kStages - 1 < nk) dma(kt + kStages - 1);
     // unconditional, so the LDS-read count is the same on every path (after
@@ -343,10 +354,12 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           // a quarter tile past the last vocabulary column holds no value at all
-          const float nb = mx[r] == -INFINITY ? 0.0f : -mx[r] * kL2E;
+          // difference first, then the scale: accurate for the entries near
+          // the maximum that dominate the sum
+          const float nb = mx[r] == -INFINITY ? 0.0f : mx[r];
           sm[r] = 0.0f;
 #pragma unroll
-          for (int j = 0; j < FN; ++j) sm[r] += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, nb));
+          for (int j = 0; j < FN; ++j) sm[r] += __builtin_amdgcn_exp2f((acc[i][j][r] - nb) * kL2E);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor1>(sm[r]);
@@ -384,13 +397,15 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       g.part[row * g.ntn + tn] = make_float2(mx, sm);
     }
   } else if constexpr (MODE == GM_D) {
-    float* sl = reinterpret_cast<float*>(smem + kRingElems);  // [GBM] lse * log2(e)
-    float* sc = sl + GBM;                                     // [GBM] coef
-    int32_t* yl = reinterpret_cast<int32_t*>(sc + GBM);       // [GBM] tile-local target column
+    // per-row tables: (M, log2 S) of the row's log-sum-exp, coef, target column
+    float2* sp = reinterpret_cast<float2*>(smem + kTableElem);  // [GBM]
+    float* sc = reinterpret_cast<float*>(sp + GBM);             // [GBM] coef
+    int32_t* yl = reinterpret_cast<int32_t*>(sc + GBM);         // [GBM] tile-local target column
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       const bool ok = row < M;
-      sl[r] = ok ? g.lse2[row] : INFINITY;  // rows past the active count: exact zeros
+      // rows past the active count: exp2(-inf) gives exact zeros
+      sp[r] = ok ? g.lsep[row] : make_float2(0.0f, INFINITY);
       sc[r] = ok ? g.coef[row] : 0.0f;
       yl[r] = ok ? (int32_t)(g.ycol[row] < 0 ? -1 : g.ycol[row] - (g.col_base + n0)) : -1;
     }
@@ -412,10 +427,12 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int rt0 = wm * WM + i * 16 + rq;
-        const float4 l4 = *reinterpret_cast<const float4*>(sl + rt0);
+        const float4 pa = *reinterpret_cast<const float4*>(sp + rt0);
+        const float4 pb = *reinterpret_cast<const float4*>(sp + rt0 + 2);
         const float4 c4 = *reinterpret_cast<const float4*>(sc + rt0);
         const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float mv[4] = {pa.x, pa.z, pb.x, pb.z};
+        const float lv[4] = {pa.y, pa.w, pb.y, pb.w};
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
         const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
@@ -424,7 +441,9 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
           uint16_t d[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, -lv[r]));
+            // exp(x - lse) = exp2((x - M)*log2e - log2 S): exact difference
+            // near the maximum, a small offset whatever the logits' scale
+            const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r] - mv[r], kL2E, -lv[r]));
             const float hit = lc == yv[r] ? 1.0f : 0.0f;
             d[r] = (kFull || lc < ncols) ? bf16_bits(cv[r] * (p - hit)) : (uint16_t)0;
           }
@@ -595,10 +614,15 @@ k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int6
 }
 
 // log-sum-exp of active token k from its per-column-tile (max, sum exp)
-// pairs, merged by one wavefront (binary32 per lane, binary64 across lanes);
-// every lane returns the result.
-__device__ inline double merge_lse(const float2* __restrict__ part, int64_t ntn, int64_t k,
-                                   int lane) {
+// pairs, merged by one wavefront (binary32 per lane, binary64 across lanes):
+// lse = M + ln(S); every lane returns (M, S).
+struct Lse {
+  float M;
+  double S;
+  __device__ double value() const { return (double)M + log(S); }
+};
+__device__ inline Lse merge_lse(const float2* __restrict__ part, int64_t ntn, int64_t k,
+                                int lane) {
   float m = -INFINITY, s = 0.0f;
   for (int64_t j = lane; j < ntn; j += 64) {
     const float2 p = part[k * ntn + j];
@@ -613,7 +637,7 @@ __device__ inline double merge_lse(const float2* __restrict__ part, int64_t ntn,
   double term = s != 0.0f ? (double)s * exp2(((double)m - (double)M) * kL2ED) : 0.0;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) term += __shfl_xor(term, o);
-  return (double)M + log(term);
+  return Lse{M, term};
 }
 
 // One wavefront per active token: merge the per-tile (max, sum exp), then
@@ -624,18 +648,19 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
              const int32_t* __restrict__ ycol, int64_t C, const float* __restrict__ adv,
              const int32_t* __restrict__ len, const float* __restrict__ logp_old,
              const float* __restrict__ logp_ref, float eps, float beta, double kappa, int agg,
-             const int64_t* __restrict__ total_len, float* __restrict__ lse2,
+             const int64_t* __restrict__ total_len, float2* __restrict__ lsep,
              float* __restrict__ coef, double* __restrict__ tok_loss,
              uint8_t* __restrict__ tok_flags) {
   const int lane = threadIdx.x & 63;
   const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (k >= counts[0]) return;
-  const double lse = merge_lse(part, ntn, k, lane);
+  const Lse ls = merge_lse(part, ntn, k, lane);
+  const double lse = ls.value();
   if (lane != 0) return;
   const int64_t pos = act_pos[k];
   const int64_t i = pos / C;
   if (ycol[k] < 0) {  // bad token id: excluded from the gradient, poisons the loss
-    lse2[k] = INFINITY;
+    lsep[k] = make_float2(0.0f, INFINITY);
     coef[k] = 0.0f;
     return;
   }
@@ -645,7 +670,7 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
                                     adv[i], eps, beta, div);
   tok_loss[pos] = tt.lam / div;
   tok_flags[pos] = tt.flags;
-  lse2[k] = (float)(lse * kL2ED);
+  lsep[k] = make_float2(ls.M, (float)log2(ls.S));
   coef[k] = (float)tt.coef;
 }
 
@@ -678,7 +703,7 @@ k_lm_logp(const float2* __restrict__ part, int64_t ntn, const float* __restrict_
   const int lane = threadIdx.x & 63;
   const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (k >= counts[0]) return;
-  const double lse = merge_lse(part, ntn, k, lane);
+  const double lse = merge_lse(part, ntn, k, lane).value();
   if (lane == 0) out_logp[act_pos[k]] = ycol[k] < 0 ? NAN : (float)((double)xy[k] - lse);
 }
 
@@ -704,7 +729,7 @@ struct LmWs {
   uint8_t* tok_flags;
   float2* part;      // [T, ntn]
   float* xy;         // [T]
-  float* lse2;       // [T]
+  float2* lsep;      // [T] (M, log2 S) of each active token's log-sum-exp
   float* coef;       // [T]
   uint16_t* Ha;      // [T, H]
   uint16_t* Hat;     // [H, Tcap]
@@ -741,7 +766,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.tok_flags = reinterpret_cast<uint8_t*>(take(T));
   w.part = reinterpret_cast<float2*>(take(8 * (size_t)T * ntn));
   w.xy = reinterpret_cast<float*>(take(4 * T));
-  w.lse2 = reinterpret_cast<float*>(take(4 * T));
+  w.lsep = reinterpret_cast<float2*>(take(8 * T));
   w.coef = reinterpret_cast<float*>(take(4 * T));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
   w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
@@ -901,7 +926,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   if ((rc = launch_gemm<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
                      w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, w.len, logp_old, logp_ref, eps,
-                     beta, (double)norm_const, agg, w.total_len, w.lse2, w.coef, w.tok_loss,
+                     beta, (double)norm_const, agg, w.total_len, w.lsep, w.coef, w.tok_loss,
                      w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
@@ -920,7 +945,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     d.M_dev = w.counts;
     d.ycol = w.ycol;
     d.col_base = v0;
-    d.lse2 = w.lse2;
+    d.lsep = w.lsep;
     d.coef = w.coef;
     d.D = w.Dc;
     d.ldd = vc_cap;
