@@ -203,15 +203,23 @@ int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t*
                                void* out_dW, int64_t N, int64_t C, int64_t V, int64_t H,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Optional timing hooks of the fused lm_head call; every field may be NULL. */
+typedef struct drgrpo_lmhead_aux {
+  void* fwd_event_begin;  /* hipEvent_t stamped when the dispatch of the forward
+                             (log-sum-exp over the whole vocabulary) product starts */
+  void* fwd_event_end;    /* hipEvent_t stamped when it ends */
+} drgrpo_lmhead_aux_t;
+
 /* drgrpo_lmhead_loss_fwd_bwd with a normalisation variant (NULL: Dr. GRPO),
- * as for drgrpo_loss_fwd_bwd_ex. */
+ * as for drgrpo_loss_fwd_bwd_ex, and optional timing hooks (aux may be NULL). */
 int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W, const int64_t* tokens,
                                   int64_t eos_id, const float* rewards, const float* logp_old,
                                   const float* logp_ref, int64_t G, float eps, float beta,
                                   float norm_const, float* out_loss, void* out_dhidden,
                                   void* out_dW, int64_t N, int64_t C, int64_t V, int64_t H,
                                   void* workspace, size_t workspace_bytes, void* stream,
-                                  const drgrpo_variant_t* variant);
+                                  const drgrpo_variant_t* variant,
+                                  const drgrpo_lmhead_aux_t* aux);
 
 /* Forward-only log-probs through the fused lm_head, for the no-gradient
  * old-policy and reference-policy passes of the "Dr. GRPO" pseudo-code

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
                                                  _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]
         L.drgrpo_lmhead_loss_fwd_bwd.restype = _I
         L.drgrpo_lmhead_loss_fwd_bwd_ex.argtypes = L.drgrpo_lmhead_loss_fwd_bwd.argtypes + [
-            ctypes.POINTER(_Variant)]
+            ctypes.POINTER(_Variant), ctypes.c_void_p]
         L.drgrpo_lmhead_loss_fwd_bwd_ex.restype = _I
         L.drgrpo_lmhead_logprobs_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
         L.drgrpo_lmhead_logprobs_workspace_bytes.restype = _SZ
@@ -265,11 +265,13 @@ def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Ten
                         out_dhidden: torch.Tensor | None = None,
                         out_dW: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, adv_mode: int = ADV_CENTER,
-                        agg: int = AGG_TOKEN_SUM):
+                        agg: int = AGG_TOKEN_SUM, fwd_events=None):
     """Fused lm_head variant: logits = hidden . W^T are never stored.
 
     hidden [N*C, H] (or [N, C, H]) bfloat16, W [V, H] bfloat16, tokens [N, C]
     int64.  Returns (loss [] float32, dhidden like hidden, dW like W).
+    `fwd_events`: optional pair of torch.cuda.Event (enable_timing=True) that
+    the library stamps around its forward log-sum-exp product.
     """
     if tokens.dim() != 2:
         raise ValueError("tokens must be [N, C]")
@@ -298,11 +300,15 @@ def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Ten
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     var = _Variant(int(adv_mode), int(agg))
+    lmaux = None
+    if fwd_events is not None:
+        lmaux = (ctypes.c_void_p * 2)(fwd_events[0].cuda_event, fwd_events[1].cuda_event)
     _check(lib().drgrpo_lmhead_loss_fwd_bwd_ex(
         hidden.data_ptr(), W.data_ptr(), tokens.data_ptr(), int(eos_id), rewards.data_ptr(),
         logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta), float(norm_const),
         loss.data_ptr(), out_dhidden.data_ptr(), out_dW.data_ptr(), N, C, V, H,
-        workspace.data_ptr(), workspace.numel(), _stream(dev), ctypes.byref(var)),
+        workspace.data_ptr(), workspace.numel(), _stream(dev), ctypes.byref(var),
+        None if lmaux is None else ctypes.cast(lmaux, ctypes.c_void_p)),
         "drgrpo_lmhead_loss_fwd_bwd_ex")
     return loss, out_dhidden, out_dW
 

@@ -22,6 +22,7 @@
  * chunk of W give every product its reduction dimension contiguous.  No
  * floating-point atomics: results are bitwise reproducible.
  */
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -55,8 +56,9 @@ constexpr bool kTablesInRing = kRingElems * 2 + kTableBytes > kLdsMax;
 constexpr int kTableElem = kTablesInRing ? kRingElems - kTableBytes / 2 : kRingElems;
 constexpr size_t kGemmLds = kRingElems * sizeof(uint16_t) + (kTablesInRing ? 0 : kTableBytes);
 static_assert(kGemmLds <= (size_t)kLdsMax, "LDS ring too deep");
-static_assert(!kTablesInRing || kRingElems - kTableBytes / 2 >= 8 * 128 * 64,
+static_assert(!kTablesInRing || kRingElems - kTableBytes / 2 >= (GT / 64) * WM * WN,
               "epilogue staging overlaps the tables");
+static_assert((GT / 64) * WM * WN <= kRingElems, "epilogue staging exceeds the ring");
 constexpr int kPad = 32;                   // token counts and vocabulary chunks are padded to this
 constexpr int kChunkV = 16384;             // vocabulary columns per backward chunk
 constexpr float kL2E = 1.4426950408889634f;
@@ -135,7 +137,7 @@ __device__ inline int stage_swz(int c) {
   return 2 * (((c & 3) << 1) | ((c >> 2) & 1) | (((c >> 3) & 1) << 3));
 }
 
-// Row-major 16-byte stores of a wavefront's staged 128 x 64 bfloat16 block:
+// Row-major 16-byte stores of a wavefront's staged WM x WN bfloat16 block:
 // out[t * ld + c] for rows t < rows_lim and 8-column groups c < cols_lim
 // (cols_lim a multiple of 8).  The transposing LDS read gives lane li of a
 // 16-lane group 4 consecutive columns of row tb + li when lane 4e + q4 of the
@@ -146,7 +148,7 @@ __device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t
   const int grp = lane >> 4, li = lane & 15;
   const int e = li >> 2, q4 = li & 3;
 #pragma unroll
-  for (int sidx = 0; sidx < 2 * (WM / 16); ++sidx) {
+  for (int sidx = 0; sidx < (WN / 32) * (WM / 16); ++sidx) {
     const int tb = 16 * (sidx % (WM / 16));
     const int cb = 32 * (sidx / (WM / 16)) + 8 * grp;  // 8 columns of this group
     const int qq = (tb >> 2) + q4;
@@ -252,19 +254,20 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, the other
+  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, the other
   // counters left alone): wait until at most n stages of this thread's direct
   // loads are still in flight
-  static_assert(3 * kDmaPerThread < 16, "vmcnt immediate");
-  auto wait_stages = [](int64_t n) {
+  constexpr auto vm_imm = [](int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); };
+  static_assert(3 * kDmaPerThread < 64, "vmcnt immediate");
+  auto wait_stages = [&](int64_t n) {
     if (n >= 3)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * kDmaPerThread));
+      __builtin_amdgcn_s_waitcnt(vm_imm(3 * kDmaPerThread));
     else if (n == 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerThread));
+      __builtin_amdgcn_s_waitcnt(vm_imm(2 * kDmaPerThread));
     else if (n == 1)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerThread);
+      __builtin_amdgcn_s_waitcnt(vm_imm(kDmaPerThread));
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_waitcnt(vm_imm(0));
   };
   if (nk > 0) {
     for (int64_t s = 0; s < kStages - 1 && s < nk; ++s) dma(s);
@@ -825,8 +828,10 @@ int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_
   return DRGRPO_OK;
 }
 
+// ev_begin / ev_end (optional) are stamped by the dispatch itself, to time it alone
 template <int MODE>
-int launch_gemm(const GemmArgs& g, hipStream_t st) {
+int launch_gemm(const GemmArgs& g, hipStream_t st, hipEvent_t ev_begin = nullptr,
+                hipEvent_t ev_end = nullptr) {
   const int64_t ntm = (g.M + GBM - 1) / GBM;
   const int64_t ntn = (g.N + GBN - 1) / GBN;
   const int64_t blocks = ntm * ntn;
@@ -836,7 +841,11 @@ int launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds) != hipSuccess)
     return DRGRPO_ERR_HIP;
-  hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), kGemmLds, st, g);
+  if (ev_begin || ev_end)
+    hipExtLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), kGemmLds, st, ev_begin,
+                          ev_end, 0, g);
+  else
+    hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), kGemmLds, st, g);
   return launch_status();
 }
 
@@ -858,7 +867,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
                                              void* out_dhidden, void* out_dW, int64_t N,
                                              int64_t C, int64_t V, int64_t H, void* workspace,
                                              size_t workspace_bytes, void* stream,
-                                             const drgrpo_variant_t* variant) {
+                                             const drgrpo_variant_t* variant,
+                                             const drgrpo_lmhead_aux_t* aux) {
   if (!hidden || !W || !tokens || !rewards || !logp_old || !out_loss || !out_dhidden || !out_dW)
     return DRGRPO_ERR_NULL;
   int64_t T;
@@ -923,7 +933,10 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   g.xy = w.xy;
   g.ycol = w.ycol;
   g.col_base = 0;
-  if ((rc = launch_gemm<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
+  if ((rc = launch_gemm<GM_LSE>(g, st, aux ? static_cast<hipEvent_t>(aux->fwd_event_begin) : nullptr,
+                                aux ? static_cast<hipEvent_t>(aux->fwd_event_end) : nullptr)) !=
+      DRGRPO_OK)
+    return rc;
   hipLaunchKernelGGL(k_lm_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
                      w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, w.len, logp_old, logp_ref, eps,
                      beta, (double)norm_const, agg, w.total_len, w.lsep, w.coef, w.tok_loss,
@@ -1006,7 +1019,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, con
                                           void* stream) {
   return drgrpo_lmhead_loss_fwd_bwd_ex(hidden, W, tokens, eos_id, rewards, logp_old, logp_ref, G,
                                        eps, beta, norm_const, out_loss, out_dhidden, out_dW, N, C,
-                                       V, H, workspace, workspace_bytes, stream, nullptr);
+                                       V, H, workspace, workspace_bytes, stream, nullptr,
+                                       nullptr);
 }
 
 extern "C" size_t drgrpo_lmhead_logprobs_workspace_bytes(int64_t N, int64_t C, int64_t V,

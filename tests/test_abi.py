@@ -141,4 +141,4 @@ def test_variant_validation(L, adv_mode, agg, code):
     assert L.drgrpo_loss_fwd_bwd_ex(*args, None, ctypes.byref(var)) == code
     lm = (FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE, FAKE, 64, 256,
           4096, 896, FAKE * 4096, 16, None)
-    assert L.drgrpo_lmhead_loss_fwd_bwd_ex(*lm, ctypes.byref(var)) == code
+    assert L.drgrpo_lmhead_loss_fwd_bwd_ex(*lm, ctypes.byref(var), None) == code
