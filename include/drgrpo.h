@@ -245,6 +245,35 @@ int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const int64_t* tok
                            float* out_logp, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Decode attention of the rollout step ("Making Dr GRPO go brrr", section
+ * "What is RL post-training, and why is it slow": one forward pass per
+ * generated token on a (B*G, 1, hidden) input plus a growing KV cache; this
+ * is that step's scaled dot-product attention).  For sequence s and query
+ * head h, with key/value head g = h / (Hq / Hkv) and len_s cached positions:
+ *   out[s,h] = sum_{j < len_s} softmax_j(scale * <q[s,h], K[s,g,j]>) V[s,g,j]
+ *
+ *   q        [S, Hq, D] bfloat16 (the new token's queries).
+ *   k_cache  [S, Hkv, Lmax, D] bfloat16; v_cache likewise.  Positions
+ *            j >= len_s are never read.
+ *   lens     [S] int32 on the device: cached positions per sequence; values
+ *            above Lmax count as Lmax, and len_s < 1 gives a NaN output (an
+ *            empty softmax).
+ *   scale    finite and > 0 (1/sqrt(D) for standard attention).
+ *   out      [S, Hq, D] bfloat16 (binary32 accumulation, rounded to nearest
+ *            even); out_lse [S, Hq] float log-sum-exp of the scores, may be
+ *            NULL.
+ *   D is 64 or 128, Hq a multiple of Hkv with Hq / Hkv <= 16 (else
+ *   DRGRPO_ERR_SHAPE); q, the caches and out 16-byte aligned (else
+ *   DRGRPO_ERR_ALIAS).  The workspace (drgrpo_decode_attention_workspace_bytes,
+ *   256-byte aligned, no initialisation) holds the per-split partial results. */
+size_t drgrpo_decode_attention_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax,
+                                               int64_t D);
+
+int drgrpo_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* lens, int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax,
+                            int64_t D, float scale, void* out, float* out_lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then reads the status word the last
  * drgrpo_loss_fwd_bwd call on `workspace` left: DRGRPO_OK or
  * DRGRPO_ERR_TOKEN_RANGE (DRGRPO_ERR_HIP if the read fails). */

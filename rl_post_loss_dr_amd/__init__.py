@@ -88,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.drgrpo_lmhead_logprobs.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P,
                                              _SZ, _P]
         L.drgrpo_lmhead_logprobs.restype = _I
+        L.drgrpo_decode_attention_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64]
+        L.drgrpo_decode_attention_workspace_bytes.restype = _SZ
+        L.drgrpo_decode_attention.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F,
+                                              _P, _P, _P, _SZ, _P]
+        L.drgrpo_decode_attention.restype = _I
         L.drgrpo_device_status.argtypes = [_P, _P]
         L.drgrpo_device_status.restype = _I
         L.drgrpo_status_string.argtypes = [_I]
@@ -343,6 +348,47 @@ def lmhead_logprobs(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Tensor,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)),
         "drgrpo_lmhead_logprobs")
     return out
+
+
+def decode_attention_workspace_bytes(S: int, Hq: int, Hkv: int, Lmax: int, D: int) -> int:
+    return int(lib().drgrpo_decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D))
+
+
+def decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     lens: torch.Tensor, scale: float | None = None, want_lse: bool = False,
+                     workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Decode attention of one new token per sequence against its KV cache.
+
+    q [S, Hq, D], k_cache / v_cache [S, Hkv, Lmax, D] bfloat16, lens [S] int32
+    (cached positions per sequence).  Returns out [S, Hq, D] bfloat16 (and the
+    float32 log-sum-exp [S, Hq] when want_lse).  scale defaults to 1/sqrt(D).
+    """
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [S, Hq, D] and the caches [S, Hkv, Lmax, D]")
+    S, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_cache, "k_cache", torch.bfloat16, (S, Hkv, Lmax, D))
+    _dev(v_cache, "v_cache", torch.bfloat16, (S, Hkv, Lmax, D))
+    _dev(lens, "lens", torch.int32, (S,))
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if workspace is None:
+        n = decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D)
+        if n == 0:
+            raise DrGRPOError(ERR_SHAPE, "drgrpo_decode_attention_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _dev(out, "out", torch.bfloat16, (S, Hq, D))
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    _check(lib().drgrpo_decode_attention(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(), S, Hq, Hkv, Lmax,
+        D, float(scale), out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(),
+        _stream(dev)), "drgrpo_decode_attention")
+    return (out, lse) if want_lse else out
 
 
 class DrGRPOLoss(torch.autograd.Function):

@@ -7,7 +7,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
 LIB = os.path.join(_HERE, "libdrgrpo.so")
-SOURCES = [os.path.join(_HERE, "csrc", "drgrpo.hip"), os.path.join(_HERE, "csrc", "lmhead.hip")]
+SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("drgrpo.hip", "lmhead.hip", "attention.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,90 @@
+"""GPU parity of the decode-attention step against the binary64 oracle:
+every output element and log-sum-exp on ragged caches, one-key caches, two
+head geometries and the full rollout decode shape (B*G = 64 sequences,
+14 query / 2 key-value heads of size 64, 512 and 1024 cached positions).
+
+Tolerance: the output is bfloat16 rounded from a binary32 computation, so
+|got - want| <= 2^-8 |want| + 2^-12 max|V| (one rounding of a value whose
+binary32 accumulation over at most a few thousand weighted values is good
+to well below 2^-12 of the values' scale); the log-sum-exp (binary32)
+within 2e-5 absolute."""
+import numpy as np
+import pytest
+import torch
+
+import rl_post_loss_dr_amd as dr
+from oracle import attention as att
+from synth.attention import get_decode_config, make_decode_case
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _run(case, lens=None, scale=None):
+    c = case.cfg
+    lens = case.lens if lens is None else lens
+    out, lse = dr.decode_attention(_dev_bf16(case.q), _dev_bf16(case.k), _dev_bf16(case.v),
+                                   torch.from_numpy(np.ascontiguousarray(lens, np.int32)).to(DEV),
+                                   scale=c.scale if scale is None else scale, want_lse=True)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(case, got, lse, lens=None, scale=None):
+    c = case.cfg
+    lens = case.lens if lens is None else lens
+    q, k, v = (att.bf16_to_f64(x) for x in (case.q, case.k, case.v))
+    want, want_lse = att.decode_attention(q, k, v, lens, c.scale if scale is None else scale)
+    bound = 2.0 ** -8 * np.abs(want) + 2.0 ** -12 * np.abs(v).max()
+    err = np.abs(got - want)
+    assert (err <= bound).all(), float((err - bound).max())
+    assert np.abs(lse - want_lse).max() <= 2e-5, float(np.abs(lse - want_lse).max())
+    return float(err.max())
+
+
+@pytest.mark.parametrize("name", ["decode_ragged", "decode_one_key", "decode_mha_d128",
+                                  "decode_gqa8", "decode_s64_l512", "decode_s64_l1024"])
+def test_decode_attention_parity(name):
+    print(f"case {name}", flush=True)
+    case = make_decode_case(get_decode_config(name))
+    got, lse = _run(case)
+    _check(case, got, lse)
+
+
+def test_decode_attention_deterministic_and_scale():
+    case = make_decode_case(get_decode_config("decode_gqa8"))
+    a1, l1 = _run(case)
+    a2, l2 = _run(case)
+    assert np.array_equal(a1, a2) and np.array_equal(l1, l2)
+    got, lse = _run(case, scale=0.3)
+    _check(case, got, lse, scale=0.3)
+
+
+def test_decode_attention_length_edges():
+    """len 0 gives NaN (empty softmax); lengths above the capacity count as
+    the capacity; len 1 returns the first cached value."""
+    case = make_decode_case(get_decode_config("decode_ragged"))
+    c = case.cfg
+    lens = case.lens.copy()
+    lens[1] = 0
+    lens[2] = c.Lmax + 50
+    got, lse = _run(case, lens=lens)
+    assert np.isnan(got[1]).all() and np.isnan(lse[1]).all()
+    ref_lens = lens.copy()
+    ref_lens[2] = c.Lmax
+    keep = np.ones(c.S, bool)
+    keep[1] = False
+    q, k, v = (att.bf16_to_f64(x) for x in (case.q, case.k, case.v))
+    want, _ = att.decode_attention(q[keep], k[keep], v[keep], ref_lens[keep], c.scale)
+    bound = 2.0 ** -8 * np.abs(want) + 2.0 ** -12 * np.abs(v).max()
+    assert (np.abs(got[keep] - want) <= bound).all()
+    one = lens.copy()
+    one[:] = 1
+    got1, _ = _run(case, lens=one)
+    grp = c.Hq // c.Hkv
+    for h in range(c.Hq):
+        assert np.array_equal(got1[:, h], att.bf16_to_f64(case.v)[:, h // grp, 0])
