@@ -181,6 +181,60 @@ def run_lmhead(cfg, case, args):
     }
 
 
+def run_decode(name, args):
+    """Decode attention of the rollout step: one new token per sequence against
+    its bfloat16 KV cache (S sequences, grouped-query heads)."""
+    import numpy as np
+    import torch
+
+    from synth.attention import get_decode_config, make_decode_case
+    import synth
+    from synth import attention as sa
+    import rl_post_loss_dr_amd as dr
+
+    c = get_decode_config(name)
+    dev = torch.device("cuda:0")
+    q = torch.empty((c.S, c.Hq, c.D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((c.S, c.Hkv, c.Lmax, c.D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    synth.gpu_normal_fill(q, c.seed, sa.S_QUERY, 0, c.std)
+    synth.gpu_normal_fill(k, c.seed, sa.S_KEY, 0, c.std)
+    synth.gpu_normal_fill(v, c.seed, sa.S_VALUE, 0, c.std)
+    lens_h = make_decode_case(c).lens if c.ragged else np.full(c.S, c.Lmax, np.int32)
+    lens = torch.from_numpy(lens_h).to(dev)
+    ws = torch.empty(dr.decode_attention_workspace_bytes(c.S, c.Hq, c.Hkv, c.Lmax, c.D),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((c.S, c.Hq, c.D), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        dr.decode_attention(q, k, v, lens, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dr.decode_attention(q, k, v, lens, workspace=ws, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    # algorithmic bytes: the cached keys and values read once, queries, outputs, lengths
+    kv = 2 * c.Hkv * c.D * 2 * int(lens_h.clip(0, c.Lmax).sum())
+    alg = kv + 2 * 2 * c.S * c.Hq * c.D + 4 * c.S
+    gbps = alg / (ms / 1e3) / 1e9
+    return {
+        "metric": "decode attention tokens/s and HBM GB/s (% of peak)", "value": c.S / (ms / 1e3),
+        "unit": "decoded tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded generator; no weights)",
+        "config": {"workload": c.name, "S": c.S, "Hq": c.Hq, "Hkv": c.Hkv, "D": c.D,
+                   "Lmax": c.Lmax},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "whole call (k_attn_split + k_attn_combine)",
+                     "alg_bytes_per_call": alg},
+        "device": torch.cuda.get_device_name(0),
+    }
+
+
 def synth_perturb(lp, noise):
     import synth
 
@@ -220,6 +274,9 @@ def main():
                           "calls": 3}), flush=True)
         return
 
+    if args.workload.startswith("decode_"):
+        print(json.dumps(run_decode(args.workload, args)), flush=True)
+        return
     cfg = synth.get_config(args.workload)
     case = synth.make_case(cfg)
     if cfg.H is not None:

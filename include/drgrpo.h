@@ -265,7 +265,8 @@ int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const int64_t* tok
  *   D is 64 or 128, Hq a multiple of Hkv with Hq / Hkv <= 16 (else
  *   DRGRPO_ERR_SHAPE); q, the caches and out 16-byte aligned (else
  *   DRGRPO_ERR_ALIAS).  The workspace (drgrpo_decode_attention_workspace_bytes,
- *   256-byte aligned, no initialisation) holds the per-split partial results. */
+ *   256-byte aligned, no initialisation) holds the per-split partial
+ *   results; calls that share a workspace must not overlap. */
 size_t drgrpo_decode_attention_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax,
                                                int64_t D);
 

@@ -53,6 +53,8 @@ _add(DecodeConfig("decode_ragged", S=9, Hq=14, Hkv=2, D=64, Lmax=333, ragged=Tru
 _add(DecodeConfig("decode_one_key", S=4, Hq=14, Hkv=2, D=64, Lmax=1, seed=7102))
 _add(DecodeConfig("decode_mha_d128", S=3, Hq=4, Hkv=4, D=128, Lmax=200, ragged=True, seed=7103))
 _add(DecodeConfig("decode_gqa8", S=5, Hq=16, Hkv=2, D=64, Lmax=1100, ragged=True, seed=7104))
+_add(DecodeConfig("decode_gqa16_d128", S=2, Hq=16, Hkv=1, D=128, Lmax=130, ragged=True,
+                  seed=7105))
 
 
 def get_decode_config(name: str) -> DecodeConfig:

@@ -47,7 +47,8 @@ def _check(case, got, lse, lens=None, scale=None):
 
 
 @pytest.mark.parametrize("name", ["decode_ragged", "decode_one_key", "decode_mha_d128",
-                                  "decode_gqa8", "decode_s64_l512", "decode_s64_l1024"])
+                                  "decode_gqa8", "decode_gqa16_d128", "decode_s64_l512",
+                                  "decode_s64_l1024"])
 def test_decode_attention_parity(name):
     print(f"case {name}", flush=True)
     case = make_decode_case(get_decode_config(name))
@@ -88,3 +89,25 @@ def test_decode_attention_length_edges():
     grp = c.Hq // c.Hkv
     for h in range(c.Hq):
         assert np.array_equal(got1[:, h], att.bf16_to_f64(case.v)[:, h // grp, 0])
+
+
+def test_decode_attention_reused_workspace():
+    """One workspace serves many calls (results identical call after call,
+    also across different cache lengths)."""
+    case = make_decode_case(get_decode_config("decode_gqa8"))
+    c = case.cfg
+    q, k, v = _dev_bf16(case.q), _dev_bf16(case.k), _dev_bf16(case.v)
+    ws = torch.empty(dr.decode_attention_workspace_bytes(c.S, c.Hq, c.Hkv, c.Lmax, c.D),
+                     dtype=torch.uint8, device=DEV)
+    lens = torch.from_numpy(case.lens).to(DEV)
+    first = dr.decode_attention(q, k, v, lens, workspace=ws).clone()
+    short = torch.clamp(lens, max=70)
+    for _ in range(3):
+        dr.decode_attention(q, k, v, short, workspace=ws)
+        again = dr.decode_attention(q, k, v, lens, workspace=ws)
+        assert torch.equal(again, first)
+    torch.cuda.synchronize()
+    got = first.float().cpu().numpy().astype(np.float64)
+    _, want_lse = att.decode_attention(*(att.bf16_to_f64(x) for x in (case.q, case.k, case.v)),
+                                       case.lens, c.scale)
+    assert got.shape == (c.S, c.Hq, c.D) and np.isfinite(want_lse).all()
