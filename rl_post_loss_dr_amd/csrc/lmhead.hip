@@ -67,9 +67,13 @@ constexpr double kL2ED = 1.4426950408889634074;
 enum { GM_LSE = 0, GM_D = 1, GM_ACC = 2, GM_STORE = 3 };
 
 struct GemmArgs {
-  const uint16_t* A;  // [M, K] bfloat16, row stride lda
-  const uint16_t* B;  // [N, K] bfloat16, row stride ldb
-  int64_t lda, ldb;
+  // Operands in bfloat16.  Element (r, k) of A sits at
+  // A[r * ar + (k / 32) * ak + k % 32]: a row-major [M, ld] matrix has
+  // ar = ld, ak = 32; a K-paneled one, stored as K/32 panels [rows][32],
+  // has ar = 32, ak = rows * 32.  The same holds for B ([N, K]) with br, bk.
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t ar, ak, br, bk;
   int64_t M, N, K;    // static bounds (grid); K a multiple of 8
   const int32_t* M_dev;  // if set: M = *M_dev (active-token count)
   const int32_t* K_dev;  // if set: K = *K_dev (padded active-token count)
@@ -82,10 +86,10 @@ struct GemmArgs {
   // GM_D
   const float2* lsep;    // [rows] (row maximum M, log2 S) with lse = M + ln S
   const float* coef;     // [rows]
-  uint16_t* D;           // [Mpad, ldd] chunk of dlogits, row-major
-  int64_t ldd;
-  uint16_t* Dt;          // [N, ldt] the same chunk transposed
-  int64_t ldt;
+  uint16_t* D;           // chunk of dlogits, K-paneled over its columns: (t, c) at
+  int64_t ldd;           //   D[(c / 32) * ldd + t * 32 + c % 32]
+  uint16_t* Dt;          // the chunk transposed, K-paneled over tokens: (c, t) at
+  int64_t ldt;           //   Dt[(t / 32) * ldt + c * 32 + t % 32]
   // GM_ACC / GM_STORE
   float* Cf;             // [M, ldc] binary32 accumulator
   uint16_t* Cb;          // [M, ldc] bfloat16 result
@@ -137,14 +141,17 @@ __device__ inline int stage_swz(int c) {
   return 2 * (((c & 3) << 1) | ((c >> 2) & 1) | (((c >> 3) & 1) << 3));
 }
 
-// Row-major 16-byte stores of a wavefront's staged WM x WN bfloat16 block:
-// out[t * ld + c] for rows t < rows_lim and 8-column groups c < cols_lim
-// (cols_lim a multiple of 8).  The transposing LDS read gives lane li of a
-// 16-lane group 4 consecutive columns of row tb + li when lane 4e + q4 of the
-// group points at quad tb/4 + q4 of stage row (first column + e).
+// 16-byte stores of a wavefront's staged WM x WN bfloat16 block, element
+// (t, c) to out[t * rs + (c / 32) * ps + c % 32] (row-major: rs = ld, ps = 32;
+// K-paneled over columns: rs = 32, ps = panel stride), for rows t < rows_lim
+// and 8-column groups c < cols_lim (cols_lim a multiple of 8).  One
+// instruction covers 16 rows x 32 columns: a contiguous 1 KB block when
+// paneled.  The transposing LDS read gives lane li of a 16-lane group 4
+// consecutive columns of row tb + li when lane 4e + q4 of the group points at
+// quad tb/4 + q4 of stage row (first column + e).
 template <bool kFull>
-__device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t* out, int64_t ld,
-                                         int rows_lim, int cols_lim) {
+__device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t* out, int64_t rs,
+                                         int64_t ps, int rows_lim, int cols_lim) {
   const int grp = lane >> 4, li = lane & 15;
   const int e = li >> 2, q4 = li & 3;
 #pragma unroll
@@ -160,7 +167,8 @@ __device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t
     const int t = tb + li;
     if (kFull || (t < rows_lim && cb < cols_lim)) {
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      *reinterpret_cast<u32x4*>(out + t * ld + cb) = u32x4{l2.x, l2.y, h2.x, h2.y};
+      *reinterpret_cast<u32x4*>(out + t * rs + (cb / 32) * ps + cb % 32) =
+          u32x4{l2.x, l2.y, h2.x, h2.y};
     }
   }
 }
@@ -187,7 +195,12 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // linear order, so the workgroups sharing its L2 share operand tiles.  The
   // order runs along the operand that is small: row tiles fastest when B is
   // the large operand (the vocabulary-wide products), column tiles fastest
-  // when A is (the products reducing over a dlogits chunk)
+  // when A is (the products reducing over a dlogits chunk).  The forward
+  // product walks groups of kColGroup column tiles row by row, so the 32
+  // workgroups an XCD runs at once share 4 row tiles and 8 column tiles
+  // (12 distinct operand panels per reduction step instead of 33); the
+  // dlogits product keeps whole column runs, which keeps its transposed
+  // stores local.
   // The grid covers the static row bound; only the tiles of the first M rows
   // (M read on the device) take part, spread evenly over the XCDs.
   const int64_t ntm = (M + GBM - 1) / GBM;
@@ -198,54 +211,71 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   const int64_t q8 = total / 8;
   const int64_t v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
   constexpr bool kColsFastest = MODE == GM_ACC || MODE == GM_STORE;
-  const int64_t tm = kColsFastest ? v / ntn_t : v % ntm;
-  const int64_t tn = kColsFastest ? v % ntn_t : v / ntm;
+  int64_t tm, tn;
+  if constexpr (MODE == GM_LSE) {
+    constexpr int64_t kColGroup = 8;
+    const int64_t grouped = (ntn_t / kColGroup) * kColGroup * ntm;
+    const int64_t gw = v < grouped ? kColGroup : ntn_t % kColGroup;  // width of v's group
+    const int64_t w = v < grouped ? v % (kColGroup * ntm) : v - grouped;
+    tm = w / gw;
+    tn = (v < grouped ? v / (kColGroup * ntm) * kColGroup : grouped / ntm) + w % gw;
+  } else {
+    tm = kColsFastest ? v / ntn_t : v % ntm;
+    tn = kColsFastest ? v % ntn_t : v / ntm;
+  }
   const int64_t m0 = tm * GBM;
   const int64_t n0 = tn * GBN;
 
   // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
   // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled
-  // by direct global -> LDS loads issued kStages-1 stages ahead.  Each wave
-  // instruction moves 16 rows x 64 B (lane l: row l/4, LDS chunk l%4);
-  // wavefronts 0-3 load A, 4-7 load B.  Rows past M or N re-read the last
-  // valid row (their results are never used).  K is a multiple of 32.
-  // The four 16-byte chunks of a row are stored XOR-permuted by swz(row % 16),
-  // so the fragment reads (16 rows, one chunk) spread over all LDS banks.
+  // by direct global -> LDS loads issued kStages-1 stages ahead.  Wavefronts
+  // 0-3 load A, 4-7 load B, through a buffer descriptor over the tile's rows
+  // of the current 32-wide reduction panel (buffer loads: the compiler counts
+  // them on vmcnt alone, so the LDS fragment reads keep fine-grained waits).
+  // One instruction moves 16 rows x 64 B (lane l: row l/4, chunk l%4): a
+  // single contiguous 1 KB block of a K-paneled operand.  Rows past M or N
+  // re-read the last valid row (their results are never used).  K is a
+  // multiple of 32.  The four 16-byte chunks of a row are stored XOR-permuted
+  // by swz(row % 16), so the fragment reads (16 rows, one chunk) spread over
+  // all LDS banks.
   const int64_t nk = K / GBK;
-  const int64_t mlast = M > 0 ? M - 1 : 0;
+  static_assert((GBM / 16) % kDmaPerThread == 0, "each wavefront loads rows of one operand");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool ldA = wv * kDmaPerThread < GBM / 16;
+  const int64_t r0 = ldA ? m0 : n0;
+  const int64_t rleft = (ldA ? M : g.N) - r0;  // >= 1: the tile exists
+  const int64_t nvalid = rleft < (ldA ? GBM : GBN) ? rleft : (ldA ? GBM : GBN);
+  const int64_t rs = ldA ? g.ar : g.br, ks = ldA ? g.ak : g.bk;
+  const uint16_t* obase = (ldA ? g.A : g.B) + r0 * rs;
+  const int pbytes = (int)(((nvalid - 1) * rs + GBK) * 2);  // the rows' span in one panel
+  uint32_t voff[kDmaPerThread];
+#pragma unroll
+  for (int p = 0; p < kDmaPerThread; ++p) {
+    const int64_t r = (wv * kDmaPerThread + p) * 16 + (lane >> 2) - (ldA ? 0 : GBM);
+    voff[p] = (uint32_t)(((r < nvalid ? r : nvalid - 1) * rs + 8 * ((lane & 3) ^ swz(lane >> 2))) * 2);
+  }
   auto dma = [&](int64_t kt) {
     uint16_t* slot = smem + (kt % kStages) * kStageElems;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(obase + kt * ks), 0,
+                                                        pbytes, 0x00020000);
 #pragma unroll
-    for (int p = 0; p < kDmaPerThread; ++p) {
-      const int blk = wave * kDmaPerThread + p;  // 16-row block of the stage
-      const int r = blk * 16 + (lane >> 2);
-      const int64_t k = kt * GBK + 8 * ((lane & 3) ^ swz(lane >> 2));
-      const uint16_t* src;
-      if (blk < GBM / 16) {
-        const int64_t row = m0 + r;
-        src = g.A + (row < M ? row : mlast) * g.lda + k;
-      } else {
-        const int64_t col = n0 + (r - GBM);
-        src = g.B + (col < g.N ? col : g.N - 1) * g.ldb + k;
-      }
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)src,
-          (__attribute__((address_space(3))) void*)(slot + blk * 16 * GBK), 16, 0, 0);
-    }
+    for (int p = 0; p < kDmaPerThread; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc,
+          (__attribute__((address_space(3))) void*)(slot + (wv * kDmaPerThread + p) * 16 * GBK),
+          16, voff[p], 0, 0, 0);
   };
   const int fr = lane & 15;  // row (A) / column (B) within a 16 x 16 block
   // LDS position of the lane's 8 reduction indices 8*(lane/16) .. +7
   const int fk = 8 * ((lane >> 4) ^ swz(fr));
-  bf16x8 fa[2][FM], fb[2][FN];
-  auto frags = [&](int64_t kt, int buf) {
-    const uint16_t* As = smem + (kt % kStages) * kStageElems;
-    const uint16_t* Bs = As + GBM * GBK;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[buf][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
+  // A fragments are reloaded in place, row block by row block, as soon as the
+  // MFMAs of that block have issued; B fragments are double-buffered
+  bf16x8 fa[FM], fb[2][FN];
+  auto frag_a = [&](const uint16_t* As, int i) {
+    return *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
+  };
+  auto frag_b = [&](const uint16_t* Bs, int j) {
+    return *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
   };
 
   f32x4 acc[FM][FN];
@@ -274,11 +304,17 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     // stage 0 complete; the later prologue stages may still be in flight
     wait_stages(nk - 1 < kStages - 2 ? nk - 1 : kStages - 2);
     ring_barrier();
-    frags(0, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = frag_a(smem, i);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(smem + GBM * GBK, j);
   }
-  // one step: stage kt's operands are in registers `cur`; make stage kt+1
-  // visible, refill the slot stage kt-1 used, read stage kt+1's operands into
-  // the other registers while stage kt's MFMAs run
+  // one step: stage kt's operands are in registers (fa, fb[cur]); make stage
+  // kt+1 visible, refill the slot stage kt-1 used (its last fragments were
+  // consumed in step kt-1), read stage kt+1's operands while stage kt's MFMAs
+  // run.  The scheduling groups keep that interleave: after each MFMA row
+  // block, the A fragment it freed (and in the first rows one B fragment), so
+  // at most 12 LDS reads are in flight and each has most of a step to land.
   auto step = [&](int64_t kt, int cur) {
     // stage kt+1 complete; stages kt+2 .. kt+kStages-2 (those issued) in flight
     const int64_t ahead = nk - 2 - kt;
@@ -287,13 +323,32 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     if (kt + kStages - 1 < nk) dma(kt + kStages - 1);
     // unconditional, so the LDS-read count is the same on every path (after
     // the last stage it reads a stale slot, in bounds, never used)
-    frags(kt + 1, cur ^ 1);
+    const uint16_t* As = smem + ((kt + 1) % kStages) * kStageElems;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0,
-                                                            0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
+      if (i < FN) fb[cur ^ 1][i] = frag_b(As + GBM * GBK, i);
+      fa[i] = frag_a(As, i);
+    }
+    static_assert(FM == 8 && FN == 4, "scheduling groups below assume 8 x 4 MFMA blocks");
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   };
   int64_t kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -454,17 +509,24 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
         }
       }
       __syncthreads();
-      const int grp = lane >> 4, li = lane & 15;
       const int rw0 = wm * WM, cw0 = wn * WN;  // wavefront block within the tile
-      store_staged_rows<kFull>(stg, lane, g.D + (m0 + rw0) * g.ldd + n0 + cw0, g.ldd,
-                               nrows_w - rw0, ncols_w - cw0);
-      // transposed rows: 16 bytes (8 rows of one column) per lane
+      // (both are multiples of 32, so the block starts at a panel boundary)
+      store_staged_rows<kFull>(stg, lane, g.D + (n0 + cw0) / 32 * g.ldd + (m0 + rw0) * 32, 32,
+                               g.ldd, nrows_w - rw0, ncols_w - cw0);
+      // transposed: lane l takes column c = 16*cg + l%16 and its 8 rows
+      // 32*tp + 8*(l/16) .. +7, so one instruction writes the 64-byte records
+      // of 16 consecutive columns in one 32-row panel (a contiguous 1 KB
+      // block) and the 16 columns' distinct stage permutations keep the LDS
+      // reads free of bank conflicts
+      const int cl = lane & 15, q = lane >> 4;
 #pragma unroll
-      for (int sidx = 0; sidx < WN / 4; ++sidx) {
-        const int c = 4 * sidx + grp;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + c * WM + 4 * ((2 * li) ^ stage_swz(c)));
-        if (kFull || (cw0 + c < ncols_w && rw0 + 8 * li < nrows_w))
-          *reinterpret_cast<u32x4*>(g.Dt + (n0 + cw0 + c) * g.ldt + m0 + rw0 + 8 * li) = v;
+      for (int sidx = 0; sidx < (WM / 32) * (WN / 16); ++sidx) {
+        const int tp = sidx % (WM / 32), c = 16 * (sidx / (WM / 32)) + cl;
+        const int t8 = 4 * tp + q;  // 8-row group within the block
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + c * WM + 4 * ((2 * t8) ^ stage_swz(c)));
+        if (kFull || (cw0 + c < ncols_w && rw0 + 8 * t8 < nrows_w))
+          *reinterpret_cast<u32x4*>(g.Dt + ((m0 + rw0) / 32 + tp) * g.ldt + (n0 + cw0 + c) * 32 +
+                                    8 * q) = v;
       }
     };
     if (ncols == GBN && nrows_w == GBM)
@@ -510,7 +572,7 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       if constexpr (MODE == GM_STORE) {
         __syncthreads();
         store_staged_rows<kFull>(stg, lane, g.Cb + (m0 + wm * WM) * g.ldc + n0 + wn * WN, g.ldc,
-                                 nrows - wm * WM, ncols - wn * WN);
+                                 32, nrows - wm * WM, ncols - wn * WN);
       }
     };
     if (ncols == GBN && nrows == GBM)
@@ -557,13 +619,14 @@ k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int
 
 // One workgroup per completion: list its active tokens, gather their hidden
 // rows, and zero the loss terms of its other tokens (tok_loss == NULL: no
-// loss terms, the forward-only pass).
+// loss terms, the forward-only pass).  The gathered rows are K-paneled:
+// element (k, h) of active token k at Ha[(h / 32) * ha_ps + k * 32 + h % 32].
 __global__ void __launch_bounds__(256)
 k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __restrict__ tokens,
             int64_t C, int64_t V, const int32_t* __restrict__ len,
             const int32_t* __restrict__ offs, int32_t* __restrict__ act_pos,
-            int32_t* __restrict__ ycol, uint16_t* __restrict__ Ha, double* __restrict__ tok_loss,
-            uint8_t* __restrict__ tok_flags) {
+            int32_t* __restrict__ ycol, uint16_t* __restrict__ Ha, int64_t ha_ps,
+            double* __restrict__ tok_loss, uint8_t* __restrict__ tok_flags) {
   const int64_t i = blockIdx.x;
   const int32_t n_act = offs[i + 1] - offs[i];
   const int32_t k0 = offs[i];
@@ -581,22 +644,27 @@ k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __res
       tok_flags[pos] = bad ? TF_BADTOK : 0;
     }
   }
-  // hidden rows of the active tokens: 16-byte copies
-  const int64_t per_row = H / 8;
-  for (int64_t q = threadIdx.x; q < (int64_t)n_act * per_row; q += blockDim.x) {
-    const int64_t t = q / per_row, c = q - t * per_row;
-    *reinterpret_cast<u32x4*>(Ha + (k0 + t) * H + 8 * c) =
-        *reinterpret_cast<const u32x4*>(hidden + (i * C + t) * H + 8 * c);
+  // hidden rows of the active tokens: 16-byte copies, four lanes per 64-byte
+  // panel record, so a wavefront writes whole records of 16 tokens
+  const int64_t npan = H / 32;
+  for (int64_t q = threadIdx.x; q < (int64_t)n_act * npan * 4; q += blockDim.x) {
+    const int64_t c4 = q & 3, rest = q >> 2;
+    const int64_t t = rest % n_act, pn = rest / n_act;
+    *reinterpret_cast<u32x4*>(Ha + pn * ha_ps + (k0 + t) * 32 + 8 * c4) =
+        *reinterpret_cast<const u32x4*>(hidden + (i * C + t) * H + 32 * pn + 8 * c4);
   }
 }
 
-// dst[c, r] = src[r, c] for r < rows (or the device count rows_dev) and zeros
-// for r up to rows_pad (or rows_dev rounded up to kPad); 64 x 64 tiles through
-// LDS.  The grid covers ceil(rows_pad / 64) x ceil(cols / 64) tiles.
+// Transpose into a K-paneled operand: element (c, r) of dst, at
+// dst[(r / 32) * d_ps + c * 32 + r % 32], is element (r, c) of src, at
+// src[r * s_rs + (c / 32) * s_ps + c % 32] (row-major: s_rs = ld, s_ps = 32),
+// for r < rows (or the device count rows_dev) and zero for r up to rows_pad
+// (or rows_dev rounded up to kPad); 64 x 64 tiles through LDS.  The grid
+// covers ceil(rows_pad / 64) x ceil(cols / 64) tiles.
 __global__ void __launch_bounds__(256)
-k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int64_t rows_pad,
-            int64_t cols, const int32_t* __restrict__ rows_dev, uint16_t* __restrict__ dst,
-            int64_t ld_dst) {
+k_transpose(const uint16_t* __restrict__ src, int64_t s_rs, int64_t s_ps, int64_t rows,
+            int64_t rows_pad, int64_t cols, const int32_t* __restrict__ rows_dev,
+            uint16_t* __restrict__ dst, int64_t d_ps) {
   __shared__ uint16_t tile[64][65];
   const int64_t R = rows_dev ? (int64_t)*rows_dev : rows;
   const int64_t Rpad = rows_dev ? (R + kPad - 1) / kPad * kPad : rows_pad;
@@ -607,12 +675,12 @@ k_transpose(const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows, int6
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int k = ty; k < 64; k += 4) {
     const int64_t r = r0 + k, c = c0 + tx;
-    tile[k][tx] = (r < R && c < cols) ? src[r * ld_src + c] : (uint16_t)0;
+    tile[k][tx] = (r < R && c < cols) ? src[r * s_rs + (c / 32) * s_ps + c % 32] : (uint16_t)0;
   }
   __syncthreads();
   for (int k = ty; k < 64; k += 4) {
     const int64_t c = c0 + k, r = r0 + tx;
-    if (c < cols && r < Rpad) dst[c * ld_dst + r] = tile[tx][k];
+    if (c < cols && r < Rpad) dst[(r / 32) * d_ps + c * 32 + r % 32] = tile[tx][k];
   }
 }
 
@@ -725,7 +793,7 @@ struct LmWs {
   uint8_t* row_flags;
   int64_t* total_len;  // [1] counted tokens (token-mean aggregation)
   int32_t* offs;     // [N + 1]
-  int32_t* counts;   // [2]: active tokens, padded to 8
+  int32_t* counts;   // [2]: active tokens, that count padded to kPad
   int32_t* act_pos;  // [T]
   int32_t* ycol;     // [T]
   double* tok_loss;  // [T]
@@ -734,11 +802,11 @@ struct LmWs {
   float* xy;         // [T]
   float2* lsep;      // [T] (M, log2 S) of each active token's log-sum-exp
   float* coef;       // [T]
-  uint16_t* Ha;      // [T, H]
-  uint16_t* Hat;     // [H, Tcap]
-  uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W, transposed
-  uint16_t* Dc;      // [Tcap, kChunkV]
-  uint16_t* Dtc;     // [kChunkV, Tcap]
+  uint16_t* Ha;      // [T, H] K-paneled over H (H/32 panels [T][32])
+  uint16_t* Hat;     // [H, Tcap] K-paneled over tokens (Tcap/32 panels [H][32])
+  uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W transposed, K-paneled over it
+  uint16_t* Dc;      // [Tcap, kChunkV] dlogits chunk, K-paneled over its columns
+  uint16_t* Dtc;     // [kChunkV, Tcap] the chunk transposed, K-paneled over tokens
   float* dH;         // [Tcap, H]
 };
 
@@ -791,7 +859,7 @@ struct LpWs {
   int32_t* ycol;     // [T]
   float2* part;      // [T, ntn]
   float* xy;         // [T]
-  uint16_t* Ha;      // [T, H]
+  uint16_t* Ha;      // [T, H] K-paneled over H (H/32 panels [T][32])
 };
 
 size_t lp_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LpWs* ws) {
@@ -908,22 +976,28 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, w.adv, N, beta, w.offs,
                      w.counts);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  // operand layouts: the gathered hidden rows Ha, K-paneled over H (panel
+  // stride T * 32); their transpose Hat [H, Tcap], K-paneled over tokens;
+  // each dlogits chunk D, K-paneled over its vocabulary columns, and its
+  // transpose Dt over tokens; the W chunk transposed, Wtc, over vocabulary
   hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st, hid, H, tokens, C, V, w.len,
-                     w.offs, w.act_pos, w.ycol, w.Ha, w.tok_loss, w.tok_flags);
+                     w.offs, w.act_pos, w.ycol, w.Ha, T * 32, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   {
     const int64_t blocks2 = ((Tcap + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, H, T, Tcap, H,
-                       w.counts, w.Hat, Tcap);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, (int64_t)32,
+                       T * 32, T, Tcap, H, w.counts, w.Hat, H * 32);
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
   }
 
   // forward: per-token log-sum-exp over the vocabulary, logits never stored
   GemmArgs g = {};
   g.A = w.Ha;
-  g.lda = H;
+  g.ar = 32;
+  g.ak = T * 32;
   g.B = Wb;
-  g.ldb = H;
+  g.br = H;
+  g.bk = 32;
   g.M = T;
   g.N = V;
   g.K = H;
@@ -949,9 +1023,11 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
     GemmArgs d = {};
     d.A = w.Ha;
-    d.lda = H;
+    d.ar = 32;
+    d.ak = T * 32;
     d.B = Wb + v0 * H;
-    d.ldb = H;
+    d.br = H;
+    d.bk = 32;
     d.M = T;
     d.N = wv;
     d.K = H;
@@ -961,23 +1037,25 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     d.lsep = w.lsep;
     d.coef = w.coef;
     d.D = w.Dc;
-    d.ldd = vc_cap;
+    d.ldd = Tcap * 32;
     d.Dt = w.Dtc;
-    d.ldt = Tcap;
+    d.ldt = vc_cap * 32;
     if ((rc = launch_gemm<GM_D>(d, st)) != DRGRPO_OK) return rc;
 
     // the chunk of W transposed, [H, vc_cap] with zero columns past wv
     const int64_t wv_pad = round_up(wv, kPad);
     const int64_t tblocks = ((wv_pad + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb + v0 * H, H, wv,
-                       wv_pad, H, (const int32_t*)nullptr, w.Wtc, vc_cap);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb + v0 * H, H,
+                       (int64_t)32, wv, wv_pad, H, (const int32_t*)nullptr, w.Wtc, H * 32);
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
     GemmArgs a = {};  // dhidden += D_chunk . W_chunk
     a.A = w.Dc;
-    a.lda = vc_cap;
+    a.ar = 32;
+    a.ak = Tcap * 32;
     a.B = w.Wtc;
-    a.ldb = vc_cap;
+    a.br = 32;
+    a.bk = H * 32;
     a.M = T;
     a.N = H;
     a.K = round_up(wv, kPad);
@@ -989,9 +1067,11 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
 
     GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a
     s.A = w.Dtc;
-    s.lda = Tcap;
+    s.ar = 32;
+    s.ak = vc_cap * 32;
     s.B = w.Hat;
-    s.ldb = Tcap;
+    s.br = 32;
+    s.bk = H * 32;
     s.M = wv;
     s.N = H;
     s.K = Tcap;
@@ -1058,15 +1138,17 @@ extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const i
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st,
                      static_cast<const uint16_t*>(hidden), H, tokens, C, V, w.len, w.offs,
-                     w.act_pos, w.ycol, w.Ha, (double*)nullptr, (uint8_t*)nullptr);
+                     w.act_pos, w.ycol, w.Ha, T * 32, (double*)nullptr, (uint8_t*)nullptr);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_logp_tail, dim3((unsigned)N), dim3(256), 0, st, w.len, C, out_logp);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   GemmArgs g = {};
   g.A = w.Ha;
-  g.lda = H;
+  g.ar = 32;
+  g.ak = T * 32;
   g.B = static_cast<const uint16_t*>(W);
-  g.ldb = H;
+  g.br = H;
+  g.bk = 32;
   g.M = T;
   g.N = V;
   g.K = H;
