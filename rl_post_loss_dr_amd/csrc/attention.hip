@@ -10,24 +10,20 @@
  *
  *   x_j = scale * <q[s,h], K[s,g,j]>  (j < len_s),   o = sum_j softmax(x)_j V[s,g,j]
  *
- * The step is bound by reading the cache once (bfloat16 K and V), so the
- * work is split along the cached positions:
- *   k_attn_split    a 256-thread workgroup per (sequence, key/value head,
- *                   split of the cached positions).  Each K/V tile of 64
- *                   positions is read from HBM once with 16-byte loads (the
- *                   queries and the first tile requested together, the next
- *                   tile in flight while one is computed) into LDS and serves
- *                   every query head of the group.  A wavefront owns a fixed
- *                   set of query heads: as 64 keys (one per lane) it forms
- *                   binary32 scores and the online softmax state; as 64
- *                   head-dimension columns it accumulates the weighted values
- *                   (V is stored transposed in LDS, so a column's 64 keys are
- *                   eight 16-byte reads), so the rescale factors stay in its
- *                   registers and only the weights pass through LDS.  Writes
- *                   a partial (unnormalised output, max, sum of exp).
+ * The step is bound by reading the cache once (bfloat16 K and V) and, at
+ * the sizes of a rollout, by the latency of that read, so a workgroup issues
+ * all of its loads at once:
+ *   k_attn_fused    a 1024-thread workgroup per (sequence, key/value head,
+ *                   split of the cached positions); each of its 16
+ *                   wavefronts takes 32 positions, forms the scores of every
+ *                   query head of the group and the weighted values on MFMAs
+ *                   (details at the kernel) and keeps an online softmax; the
+ *                   16 partials are merged in LDS.  With one split (the usual
+ *                   decode batch) it writes the bfloat16 output and the
+ *                   log-sum-exp itself; otherwise a partial (unnormalised
+ *                   output, max, sum of exp) per split.
  *   k_attn_combine  merges the splits of each (sequence, query head) in
- *                   split order and writes the bfloat16 output and the
- *                   log-sum-exp.
+ *                   split order and writes the output and the log-sum-exp.
  */
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -38,13 +34,17 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kAttnThreads = 256;  // 4 wavefronts
-constexpr int kTileKeys = 64;      // cached positions per LDS tile (one per lane)
-constexpr int kMaxGroup = 16;      // query heads per key/value head
-constexpr int kKeyPad = 8;         // bfloat16 of padding per K row in LDS (spreads banks)
-constexpr int kTargetBlocks = 512;  // split workgroups aimed for (2 per CU; measured best)
-constexpr int kMaxSplit = 32;      // splits of the cached positions at most
+constexpr int kAttnWaves = 16;                   // wavefronts per workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kWaveKeys = 32;                    // cached positions per wavefront and round
+constexpr int kMaxGroup = 16;                    // query heads per key/value head (one MFMA block)
+constexpr int kTargetBlocks = 128;               // split workgroups aimed for
+constexpr int kMaxSplit = 32;                    // splits of the cached positions at most
 constexpr float kLog2eA = 1.4426950408889634f;
 
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -90,7 +90,7 @@ struct AttnArgs {
   int64_t S, Hq, Hkv, Lmax;
   float scale;
   int nsplit;           // splits of the cached positions
-  int chunk;            // positions per split (a multiple of kTileKeys)
+  int chunk;            // positions per split (a multiple of kWaveKeys)
   float* part;          // [S, Hq, nsplit, D + 2]: unnormalised output, max, sum of exp
   uint16_t* out;        // [S, Hq, D]
   float* out_lse;       // [S, Hq] or NULL
@@ -103,21 +103,52 @@ __device__ inline int seq_len(const AttnArgs& a, int64_t s) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(kAttnThreads) k_attn_split(AttnArgs a) {
+__device__ inline int vswz(int key) {
+  // 16-byte chunk permutation of a cached value row in LDS: the transposing
+  // reads (4 keys x 2 chunks per 16-lane group, 32 lanes per LDS pass) then
+  // touch every bank once
+  return D == 128 ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
+}
+
+template <int D>
+constexpr int attn_rounds() { return D == 64 ? 2 : 1; }  // value slots per wavefront in LDS
+
+// One workgroup of 16 wavefronts per (sequence, key/value head, split of the
+// cached positions); wavefront w takes positions j0 + w*32 + 512*n .. +31 for
+// rounds n = 0, 1, ...  The loads of attn_rounds<D>() rounds (1024 positions
+// at D = 64, 512 at D = 128) are issued together, so one split of that size
+// costs one round trip to memory.  Per round of 32 positions a wavefront
+//   - loads its keys straight into MFMA operands and forms the transposed
+//     scores S^T = K Q^T for all query heads of the group (v_mfma_f32_16x16x32_bf16:
+//     16 positions x 16 heads per block, binary32 accumulation of exact
+//     bf16 products; the scale is applied to the binary32 scores),
+//   - updates an online softmax per head: in S^T's accumulator layout a lane
+//     holds 8 positions of one head, so a head's max and sum take two
+//     cross-lane exchanges,
+//   - forms O^T += V^T P^T: the weights' registers are the B operand as they
+//     stand, because the 32 reduction slots may enumerate the positions in any
+//     order as long as both operands agree; the values reach LDS through
+//     direct loads and come back as the A operand through transposing LDS
+//     reads in that same order.  P is split into bfloat16 high and low parts
+//     (two MFMAs), so the weights keep about 17 bits.
+// The 16 partial softmaxes are merged through LDS at the end.
+template <int D>
+__global__ void __launch_bounds__(kAttnThreads) k_attn_fused(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head size");
-  constexpr int KROW = D + kKeyPad;           // LDS row of one cached key
-  constexpr int kWavesPerSet = D / 64;        // wavefronts sharing a head set (one per 64 columns)
-  constexpr int kHeadStride = 4 / kWavesPerSet;
-  constexpr int kSlots = kMaxGroup / kHeadStride;  // heads per wavefront at most
-  __shared__ __attribute__((aligned(16))) float sq[kMaxGroup][D];  // scaled queries
-  constexpr int VROW = kTileKeys + kKeyPad;   // LDS row of one value column (transposed tile)
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kTileKeys][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[D][VROW];
-  __shared__ __attribute__((aligned(16))) float sp[kMaxGroup][kTileKeys];  // softmax weights
+  constexpr int NCH = D / 8;                     // 16-byte chunks per cached row
+  constexpr int NST = D / 32;                    // MFMA steps of one score block
+  constexpr int NCB = D / 16;                    // 16-column blocks of the output
+  constexpr int VW = kWaveKeys * D;              // bfloat16 of values per wavefront and round
+  constexpr int kDma = VW / 8 / 64;              // 16-byte direct loads per lane and round
+  constexpr int NR = attn_rounds<D>();           // rounds whose loads are issued together
+  static_assert(NR * kAttnWaves * VW * 2 >= kAttnWaves * 16 * D * 4, "merge area fits the value area");
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NR * kAttnWaves * VW];
+  __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, li = lane & 15;
   const int grp = (int)(a.Hq / a.Hkv);
   const int64_t b = blockIdx.x;
   const int split = (int)(b % a.nsplit);
@@ -128,167 +159,171 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_split(AttnArgs a) {
   const int j0 = split * a.chunk;
   const int j1 = min(L, j0 + a.chunk);
 
-  // this wavefront's heads: h0, h0 + kHeadStride, ...; its value columns d
-  const int h0 = wave / kWavesPerSet;
-  const int d = (wave % kWavesPerSet) * 64 + lane;
-  const bool writer = (wave % kWavesPerSet) == 0;  // one copy of the weights per head
-
-  float m_run[kSlots], l_run[kSlots], acc[kSlots];
+  // queries, the B operand of S^T: lane (head li, dims 32*st + 8*g16 .. +7)
+  bf16x8 qf[NST];
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.0f;
-    acc[i] = 0.0f;
+  for (int st = 0; st < NST; ++st) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (li < grp) w = *reinterpret_cast<const u32x4*>(a.q + (s * a.Hq + g * grp + li) * D + 32 * st + 8 * g16);
+    qf[st] = __builtin_bit_cast(bf16x8, w);
   }
 
-  const uint16_t* kbase = a.k + (s * a.Hkv + g) * a.Lmax * D;
-  const uint16_t* vbase = a.v + (s * a.Hkv + g) * a.Lmax * D;
-  constexpr int kVec = 8;  // bfloat16 per 16-byte load
-  constexpr int kPer = kTileKeys * D / kVec / kAttnThreads;  // 16-byte loads per thread per tile
-  // registers of one tile: thread slot e = tid + kAttnThreads * p covers key
-  // r = e / (D / kVec), columns c .. c+7 with c = (e % (D / kVec)) * kVec;
-  // positions past the tile's end are zero (their weights are 0 and must not
-  // meet NaN bits)
-  u32x4 kreg[kPer], vreg[kPer];
-  auto load_tile = [&](int t0, int nk) {
+  const int64_t cache_off = (s * a.Hkv + g) * a.Lmax * D;
+  const uint16_t* kb = a.k + cache_off;
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v + cache_off), 0,
+                                                       (int)(a.Lmax * D * 2), 0x00020000);
+  float m_run = -INFINITY, l_run = 0.0f;  // head li
+  f32x4 o[NCB];                            // O^T[16*cb + 4*g16 + r][head li]
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int e = tid + kAttnThreads * p;
-      const int r = e / (D / kVec), c = (e - r * (D / kVec)) * kVec;
-      kreg[p] = u32x4{0u, 0u, 0u, 0u};
-      vreg[p] = u32x4{0u, 0u, 0u, 0u};
-      if (r < nk) {
-        const int64_t off = (int64_t)(t0 + r) * D + c;
-        kreg[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
-        vreg[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  constexpr int kRoundKeys = kAttnWaves * kWaveKeys;
+  for (int base = j0 + wv * kWaveKeys; base < j1; base += NR * kRoundKeys) {
+    // issue every load of these rounds: values into this wavefront's LDS slot
+    // of the round (lane slot e of direct load p holds chunk (e % NCH) ^
+    // vswz(key) of position key = e / NCH of the round), keys straight into
+    // the A operands of S^T (lane: position 16*bk + li, dims 32*st + 8*g16 ..)
+    bf16x8 kf[NR][2][NST];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      const int r0 = base + n * kRoundKeys;
+      if (r0 >= j1) break;  // uniform across the wavefront
+      const int klast = min(kWaveKeys, j1 - r0) - 1 + r0;  // later positions re-read it (weight 0)
+      uint16_t* slot = sv + (n * kAttnWaves + wv) * VW;
+#pragma unroll
+      for (int p = 0; p < kDma; ++p) {
+        const int e = 64 * p + lane;
+        const int key = e / NCH;
+        const int c = (e % NCH) ^ vswz<D>(key);
+        const int kk = min(r0 + key, klast);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vrsrc, (__attribute__((address_space(3))) void*)(slot + 64 * 8 * p), 16,
+            (uint32_t)((kk * D + 8 * c) * 2), 0, 0, 0);
+      }
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        const int kk = min(r0 + 16 * bk + li, klast);
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          kf[n][bk][st] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kb + (int64_t)kk * D + 32 * st + 8 * g16));
       }
     }
-  };
-  // the queries and the first tile are requested together
-  constexpr int kQPer = (kMaxGroup * D + kAttnThreads - 1) / kAttnThreads;
-  float qreg[kQPer];
+    // every value of these rounds has landed in this wavefront's LDS slots
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
 #pragma unroll
-  for (int p = 0; p < kQPer; ++p) {
-    const int e = tid + kAttnThreads * p;
-    qreg[p] = e < grp * D ? bf16f(a.q[(s * a.Hq + g * grp) * D + e]) * a.scale : 0.0f;
-  }
-  if (j0 < j1) load_tile(j0, min(kTileKeys, j1 - j0));
+    for (int n = 0; n < NR; ++n) {
+      const int r0 = base + n * kRoundKeys;
+      if (r0 >= j1) break;
+      const int nk = min(kWaveKeys, j1 - r0);  // >= 1
+      const uint16_t* slot = sv + (n * kAttnWaves + wv) * VW;
+      f32x4 sc[2];
 #pragma unroll
-  for (int p = 0; p < kQPer; ++p) {
-    const int e = tid + kAttnThreads * p;
-    if (e < grp * D) sq[e / D][e % D] = qreg[p];
-  }
-
-  for (int t0 = j0; t0 < j1; t0 += kTileKeys) {
-    const int nk = min(kTileKeys, j1 - t0);
-    __syncthreads();  // the previous tile's K, V and weights are consumed (and sq is written)
-    // K rows as they are; V transposed (column-major), so that the value
-    // role reads a column's 64 keys as 16-byte vectors
+      for (int bk = 0; bk < 2; ++bk) {
+        sc[bk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int e = tid + kAttnThreads * p;
-      const int r = e / (D / kVec), c = (e - r * (D / kVec)) * kVec;
-      *reinterpret_cast<u32x4*>(&sk[r][c]) = kreg[p];
-      const uint32_t w[4] = {vreg[p].x, vreg[p].y, vreg[p].z, vreg[p].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        svt[c + 2 * u][r] = (uint16_t)(w[u] & 0xFFFFu);
-        svt[c + 2 * u + 1][r] = (uint16_t)(w[u] >> 16);
+        for (int st = 0; st < NST; ++st)
+          sc[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n][bk][st], qf[st], sc[bk], 0, 0, 0);
       }
-    }
-    __syncthreads();
-    // the next tile's loads fly while this one is computed
-    if (t0 + kTileKeys < j1) load_tile(t0 + kTileKeys, min(kTileKeys, j1 - t0 - kTileKeys));
-    // scores of key `lane` for this wavefront's heads, online softmax
-    float corr[kSlots];
+      // lane holds positions 16*bk + 4*g16 + r of head li
+      float x[8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-      const int h = h0 + kHeadStride * i;
-      corr[i] = 1.0f;
-      if (h < grp) {  // uniform across the wavefront
-        float x = -INFINITY;
-        if (lane < nk) {
-          float dot = 0.0f;
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-          for (int c = 0; c < D; c += kVec) {
-            const u32x4 kk = *reinterpret_cast<const u32x4*>(&sk[lane][c]);
-            const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              dot = fmaf(sq[h][c + 2 * u], __uint_as_float(w[u] << 16), dot);
-              dot = fmaf(sq[h][c + 2 * u + 1], __uint_as_float(w[u] & 0xFFFF0000u), dot);
-            }
-          }
-          x = dot;
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * bk + 4 * g16 + r;
+          x[4 * bk + r] = key < nk ? sc[bk][r] * a.scale : -INFINITY;
+          mx = fmaxf(mx, x[4 * bk + r]);
         }
-        const float tm = wave_max(x);
-        const float mn = fmaxf(m_run[i], tm);  // finite: the tile holds at least one key
-        const float p = lane < nk ? exp2f((x - mn) * kLog2eA) : 0.0f;
-        const float ps = wave_sum(p);
-        corr[i] = m_run[i] == -INFINITY ? 0.0f : exp2f((m_run[i] - mn) * kLog2eA);
-        l_run[i] = l_run[i] * corr[i] + ps;
-        m_run[i] = mn;
-        if (writer) sp[h][lane] = p;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m_run, mx);  // finite: position r0 is valid
+      const float corr = m_run == -INFINITY ? 0.0f : exp2f((m_run - mn) * kLog2eA);
+      float ps = 0.0f;
+      bf16x8 phi, plo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pv = exp2f((x[i] - mn) * kLog2eA);  // exactly 0 past the round's end
+        ps += pv;
+        const __bf16 h = (__bf16)pv;
+        phi[i] = h;
+        plo[i] = (__bf16)(pv - (float)h);
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = fmaf(l_run, corr, ps);
+      m_run = mn;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        // lane (4e + q) of a 16-lane group points at position k0 + e, columns
+        // 16*cb + 4q .. +3; it receives positions k0 .. k0+3 of column 16*cb + li
+        const int d = 16 * cb + 4 * (li & 3);
+        const int k0a = 4 * g16 + (li >> 2), k0b = 16 + 4 * g16 + (li >> 2);
+        const s16x4 ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(slot + (k0a * NCH + ((d >> 3) ^ vswz<D>(k0a))) * 8 + (d & 7)));
+        const s16x4 tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(slot + (k0b * NCH + ((d >> 3) ^ vswz<D>(k0b))) * 8 + (d & 7)));
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, s16x8{ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]});
+        o[cb] *= corr;
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, o[cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, o[cb], 0, 0, 0);
       }
     }
-    __syncthreads();  // weights visible
-    // weighted values of column d for the same heads: the column's 64 keys
-    // in eight 16-byte reads, the weights as broadcast 16-byte reads
-    u32x4 vcol[kTileKeys / kVec];
-#pragma unroll
-    for (int c = 0; c < kTileKeys / kVec; ++c)
-      vcol[c] = *reinterpret_cast<const u32x4*>(&svt[d][c * kVec]);
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-      const int h = h0 + kHeadStride * i;
-      if (h < grp) {
-        float o = acc[i] * corr[i];
-#pragma unroll
-        for (int c = 0; c < kTileKeys / kVec; ++c) {
-          const float4 pa = *reinterpret_cast<const float4*>(&sp[h][c * kVec]);
-          const float4 pb = *reinterpret_cast<const float4*>(&sp[h][c * kVec + 4]);
-          const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-          const uint32_t w[4] = {vcol[c].x, vcol[c].y, vcol[c].z, vcol[c].w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            o = fmaf(pw[2 * u], __uint_as_float(w[u] << 16), o);
-            o = fmaf(pw[2 * u + 1], __uint_as_float(w[u] & 0xFFFF0000u), o);
-          }
-        }
-        acc[i] = o;
-      }
-    }
+    // the next group's direct loads overwrite the slots only after these
+    // reads (their results feed the MFMAs above)
   }
 
+  // merge the wavefronts' partial softmaxes; the value area is reused
+  __syncthreads();
+  float* so = reinterpret_cast<float*>(sv);  // [wave][head][D]
+  if (g16 == 0) {
+    sm[wv][li] = m_run;
+    sl[wv][li] = l_run;
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) so[(wv * 16 + li) * D + 16 * cb + 4 * g16 + r] = o[cb][r];
+  __syncthreads();
+  constexpr int kCols = D / 64;  // columns per thread
+  const int h = tid >> 6;        // 16 heads x 64 threads
+  if (h >= grp) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
+  float l = 0.0f, ov[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) ov[c] = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      if (sm[w][h] == -INFINITY) continue;  // a wavefront without positions
+      const float f = exp2f((sm[w][h] - M) * kLog2eA);
+      l = fmaf(sl[w][h], f, l);
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) ov[c] = fmaf(so[(w * 16 + h) * D + lane + 64 * c], f, ov[c]);
+    }
+  }
+  const int64_t sh = s * a.Hq + g * grp + h;
   if (a.nsplit == 1) {  // the whole cache in one split: normalise and write the output here
+    const bool empty = M == -INFINITY;  // no cached key: an empty softmax
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-      const int h = h0 + kHeadStride * i;
-      if (h < grp) {
-        const int64_t sh = s * a.Hq + g * grp + h;
-        const bool empty = m_run[i] == -INFINITY;  // no cached key: an empty softmax
-        a.out[sh * D + d] = to_bf16(empty ? NAN : acc[i] / l_run[i]);
-        if (a.out_lse && writer && lane == 0)
-          a.out_lse[sh] = empty ? NAN : m_run[i] + logf(l_run[i]);
-      }
-    }
+    for (int c = 0; c < kCols; ++c) a.out[sh * D + lane + 64 * c] = to_bf16(empty ? NAN : ov[c] / l);
+    if (a.out_lse && lane == 0) a.out_lse[sh] = empty ? NAN : M + logf(l);
     return;
   }
-  // partial of every head of the group (an empty split: max -inf, sum 0)
-  float* gpart = a.part + (s * a.Hq + g * grp) * (int64_t)a.nsplit * (D + 2);
+  // partial of this split (an empty split: max -inf, sum 0)
+  float* pp = a.part + (sh * a.nsplit + split) * (int64_t)(D + 2);
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const int h = h0 + kHeadStride * i;
-    if (h < grp) {
-      float* pp = gpart + ((int64_t)h * a.nsplit + split) * (D + 2);
-      pp[d] = acc[i];
-      if (writer && lane == 0) {
-        pp[D] = m_run[i];
-        pp[D + 1] = l_run[i];
-      }
-    }
+  for (int c = 0; c < kCols; ++c) pp[lane + 64 * c] = ov[c];
+  if (lane == 0) {
+    pp[D] = M;
+    pp[D + 1] = l;
   }
-
 }
 
 // One workgroup per (sequence, key/value head, block of up to 1024 / D query
@@ -353,23 +388,31 @@ void launch_combine(const AttnArgs& a, hipStream_t st) {
                      st, a);
 }
 
-// splits: about kTargetBlocks workgroups, whole tiles per split
-void attn_splits(int64_t S, int64_t Hkv, int64_t Lmax, int* nsplit, int* chunk) {
-  const int64_t tiles = (Lmax + kTileKeys - 1) / kTileKeys;
-  int64_t ns = (kTargetBlocks + S * Hkv - 1) / (S * Hkv);
-  if (ns > tiles) ns = tiles;
+// splits: at most the positions whose loads a workgroup issues together
+// (1024 at D = 64, 512 at D = 128) per split unless that needs more than
+// kMaxSplit splits; more splits, down to 128 positions each, while there are
+// fewer than kTargetBlocks workgroups.  A second launch (the combine) costs
+// more than a second round trip inside one workgroup, so splits are few.
+void attn_splits(int64_t S, int64_t Hkv, int64_t Lmax, int64_t D, int* nsplit, int* chunk) {
+  const int64_t kRound = kAttnWaves * kWaveKeys * (D == 64 ? attn_rounds<64>() : attn_rounds<128>());
+  int64_t ns = (Lmax + kRound - 1) / kRound;
+  const int64_t ns_par = (kTargetBlocks + S * Hkv - 1) / (S * Hkv);
+  const int64_t ns_fine = (Lmax + 4 * kWaveKeys - 1) / (4 * kWaveKeys);
+  const int64_t ns_more = ns_par < ns_fine ? ns_par : ns_fine;
+  if (ns < ns_more) ns = ns_more;
   if (ns > kMaxSplit) ns = kMaxSplit;
   if (ns < 1) ns = 1;
-  const int64_t tiles_per = (tiles + ns - 1) / ns;
-  *chunk = (int)(tiles_per * kTileKeys);
-  *nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
+  const int64_t per = ((Lmax + ns - 1) / ns + kWaveKeys - 1) / kWaveKeys * kWaveKeys;
+  *chunk = (int)per;
+  *nsplit = (int)((Lmax + per - 1) / per);
 }
 
 int attn_check(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D) {
   if (S <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv != 0 || Hq / Hkv > kMaxGroup)
     return DRGRPO_ERR_SHAPE;
   if (D != 64 && D != 128) return DRGRPO_ERR_SHAPE;
-  if (Lmax > (int64_t(1) << 30) || S * Hkv > (int64_t(1) << 25) || S * Hq > INT32_MAX)
+  // one (sequence, head) cache region is addressed with 32-bit byte offsets
+  if (Lmax * D * 2 > INT32_MAX || S * Hkv > (int64_t(1) << 25) || S * Hq > INT32_MAX)
     return DRGRPO_ERR_SHAPE;
   return DRGRPO_OK;
 }
@@ -381,7 +424,7 @@ extern "C" size_t drgrpo_decode_attention_workspace_bytes(int64_t S, int64_t Hq,
                                                           int64_t Lmax, int64_t D) {
   if (attn_check(S, Hq, Hkv, Lmax, D) != DRGRPO_OK) return 0;
   int nsplit, chunk;
-  attn_splits(S, Hkv, Lmax, &nsplit, &chunk);
+  attn_splits(S, Hkv, Lmax, D, &nsplit, &chunk);
   return (size_t)(S * Hq) * nsplit * (D + 2) * sizeof(float);
 }
 
@@ -410,18 +453,18 @@ extern "C" int drgrpo_decode_attention(const void* q, const void* k_cache, const
   a.Hkv = Hkv;
   a.Lmax = Lmax;
   a.scale = scale;
-  attn_splits(S, Hkv, Lmax, &a.nsplit, &a.chunk);
+  attn_splits(S, Hkv, Lmax, D, &a.nsplit, &a.chunk);
   a.part = static_cast<float*>(workspace);
   a.out = static_cast<uint16_t*>(out);
   a.out_lse = out_lse;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned blocks = (unsigned)(S * Hkv * a.nsplit);
   if (D == 64) {
-    hipLaunchKernelGGL(k_attn_split<64>, dim3(blocks), dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_fused<64>, dim3(blocks), dim3(kAttnThreads), 0, st, a);
     if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
     if (a.nsplit > 1) launch_combine<64>(a, st);
   } else {
-    hipLaunchKernelGGL(k_attn_split<128>, dim3(blocks), dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_fused<128>, dim3(blocks), dim3(kAttnThreads), 0, st, a);
     if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
     if (a.nsplit > 1) launch_combine<128>(a, st);
   }
