@@ -262,11 +262,14 @@ int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const int64_t* tok
  *   out      [S, Hq, D] bfloat16 (binary32 accumulation, rounded to nearest
  *            even); out_lse [S, Hq] float log-sum-exp of the scores, may be
  *            NULL.
- *   D is 64 or 128, Hq a multiple of Hkv with Hq / Hkv <= 16 (else
- *   DRGRPO_ERR_SHAPE); q, the caches and out 16-byte aligned (else
+ *   D is 64 or 128, Hq a multiple of Hkv with Hq / Hkv <= 16, and one
+ *   (sequence, key/value head) cache region Lmax * D * 2 bytes below 2^31
+ *   (else DRGRPO_ERR_SHAPE); q, the caches and out 16-byte aligned (else
  *   DRGRPO_ERR_ALIAS).  The workspace (drgrpo_decode_attention_workspace_bytes,
  *   256-byte aligned, no initialisation) holds the per-split partial
- *   results; calls that share a workspace must not overlap. */
+ *   results; calls that share a workspace must not overlap.  The call only
+ *   enqueues kernels (no memset, no host synchronisation), so it can be
+ *   captured into a graph. */
 size_t drgrpo_decode_attention_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax,
                                                int64_t D);
 

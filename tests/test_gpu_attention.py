@@ -111,3 +111,37 @@ def test_decode_attention_reused_workspace():
     _, want_lse = att.decode_attention(*(att.bf16_to_f64(x) for x in (case.q, case.k, case.v)),
                                        case.lens, c.scale)
     assert got.shape == (c.S, c.Hq, c.D) and np.isfinite(want_lse).all()
+
+
+@pytest.mark.parametrize("name", ["decode_s64_l512", "decode_gqa8"])
+def test_decode_attention_graph_replay(name):
+    """The decode step replayed from a captured graph (as a decode loop, and
+    the benchmark, issue it): every replay equals the eager result, with eager
+    work and synchronisations between replays.  decode_gqa8 takes the split
+    path (fused kernel + combine), decode_s64_l512 the single kernel."""
+    print(f"case {name}", flush=True)
+    case = make_decode_case(get_decode_config(name))
+    c = case.cfg
+    q, k, v = _dev_bf16(case.q), _dev_bf16(case.k), _dev_bf16(case.v)
+    lens = torch.from_numpy(np.ascontiguousarray(case.lens, np.int32)).to(DEV)
+    ws = torch.empty(dr.decode_attention_workspace_bytes(c.S, c.Hq, c.Hkv, c.Lmax, c.D),
+                     dtype=torch.uint8, device=DEV)
+    eager = dr.decode_attention(q, k, v, lens, workspace=ws).clone()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dr.decode_attention(q, k, v, lens, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dr.decode_attention(q, k, v, lens, workspace=ws, out=out)
+    short = torch.clamp(lens, max=40)
+    for _ in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        other = dr.decode_attention(q, k, v, short, workspace=ws)  # eager work in between
+        torch.cuda.synchronize()
+        assert other.shape == eager.shape
