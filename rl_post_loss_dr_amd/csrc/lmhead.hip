@@ -36,7 +36,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int GBM = 256;                   // workgroup tile rows (A rows)
 constexpr int GBN = 256;                   // workgroup tile columns (B rows)
@@ -72,8 +71,6 @@ struct GemmArgs {
   // A[r * ar + (k / 32) * ak + k % 32]: a row-major [M, ld] matrix has
   // ar = ld, ak = 32; a K-paneled one, stored as K/32 panels [rows][32],
   // has ar = 32, ak = rows * 32.  The same holds for B ([N, K]) with br, bk.
-  // GM_STORE reads A paneled over its rows instead (the dlogits chunk as
-  // written, rows = vocabulary columns): (r, k) at A[(r / 32) * ar + k * 32 + r % 32].
   const uint16_t* A;
   const uint16_t* B;
   int64_t ar, ak, br, bk;
@@ -91,6 +88,8 @@ struct GemmArgs {
   const float* coef;     // [rows]
   uint16_t* D;           // chunk of dlogits, K-paneled over its columns: (t, c) at
   int64_t ldd;           //   D[(c / 32) * ldd + t * 32 + c % 32]
+  uint16_t* Dt;          // the chunk transposed, K-paneled over tokens: (c, t) at
+  int64_t ldt;           //   Dt[(t / 32) * ldt + c * 32 + t % 32]
   // GM_ACC / GM_STORE
   float* Cf;             // [M, ldc] binary32 accumulator
   uint16_t* Cb;          // [M, ldc] bfloat16 result
@@ -134,13 +133,6 @@ constexpr int kDppMirror = 0x140;
 // chunk permutation of LDS row r (see the main loop): rows of one parity
 // among 8 consecutive, and rows equal mod 4 among 16, get distinct values
 __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// chunk permutation of reduction record k in a stage of GM_STORE's A (a 32 x 32
-// block per row panel, 64-byte records of 32 rows): records k and k + 8 use
-// opposite chunk pairs, so the transposing fragment reads (4 records x 2
-// chunks per 16 lanes, records k..k+3 and k+8..k+11 in one LDS pass) touch
-// every bank once
-__device__ inline int tsw(int k) { return 2 * ((k >> 3) & 1); }
 
 // quad permutation of row c of an epilogue stage: an even value, so 16-byte
 // pairs of quads stay in order; 16 consecutive rows get distinct values, and
@@ -246,45 +238,21 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // multiple of 32.  The four 16-byte chunks of a row are stored XOR-permuted
   // by swz(row % 16), so the fragment reads (16 rows, one chunk) spread over
   // all LDS banks.
-  // GM_STORE's A (paneled over rows) lands as one [32 k][32 rows] block per
-  // row panel (2 KB; instruction p of a wavefront fills half a block, 16
-  // contiguous 64-byte records); its fragments come back through transposing
-  // LDS reads.  Panels past M re-read the last valid one.
-  constexpr bool kAT = MODE == GM_STORE;
   const int64_t nk = K / GBK;
   static_assert((GBM / 16) % kDmaPerThread == 0, "each wavefront loads rows of one operand");
-  static_assert(GBM % 32 == 0 && kDmaPerThread % 2 == 0, "row panels of GM_STORE's A");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const bool ldA = wv * kDmaPerThread < GBM / 16;
   const int64_t r0 = ldA ? m0 : n0;
   const int64_t rleft = (ldA ? M : g.N) - r0;  // >= 1: the tile exists
   const int64_t nvalid = rleft < (ldA ? GBM : GBN) ? rleft : (ldA ? GBM : GBN);
-  const uint16_t* obase;
-  int64_t ks;
-  int pbytes;  // the span one stage's loads address
+  const int64_t rs = ldA ? g.ar : g.br, ks = ldA ? g.ak : g.bk;
+  const uint16_t* obase = (ldA ? g.A : g.B) + r0 * rs;
+  const int pbytes = (int)(((nvalid - 1) * rs + GBK) * 2);  // the rows' span in one panel
   uint32_t voff[kDmaPerThread];
-  if (kAT && ldA) {
-    const int64_t plast = (nvalid - 1) >> 5;
-    obase = g.A + (r0 >> 5) * g.ar;
-    ks = GBK * 32;
-    pbytes = (int)((plast * g.ar + GBK * 32) * 2);
 #pragma unroll
-    for (int p = 0; p < kDmaPerThread; ++p) {
-      const int b = wv * kDmaPerThread + p;  // half block: row panel b/2, records 16*(b%2) ..
-      const int k = 16 * (b & 1) + (lane >> 2);
-      const int64_t pb = (b >> 1) < plast ? (b >> 1) : plast;
-      voff[p] = (uint32_t)((pb * g.ar + k * 32 + 8 * ((lane & 3) ^ tsw(k))) * 2);
-    }
-  } else {
-    const int64_t rs = ldA ? g.ar : g.br;
-    ks = ldA ? g.ak : g.bk;
-    obase = (ldA ? g.A : g.B) + r0 * rs;
-    pbytes = (int)(((nvalid - 1) * rs + GBK) * 2);
-#pragma unroll
-    for (int p = 0; p < kDmaPerThread; ++p) {
-      const int64_t r = (wv * kDmaPerThread + p) * 16 + (lane >> 2) - (ldA ? 0 : GBM);
-      voff[p] = (uint32_t)(((r < nvalid ? r : nvalid - 1) * rs + 8 * ((lane & 3) ^ swz(lane >> 2))) * 2);
-    }
+  for (int p = 0; p < kDmaPerThread; ++p) {
+    const int64_t r = (wv * kDmaPerThread + p) * 16 + (lane >> 2) - (ldA ? 0 : GBM);
+    voff[p] = (uint32_t)(((r < nvalid ? r : nvalid - 1) * rs + 8 * ((lane & 3) ^ swz(lane >> 2))) * 2);
   }
   auto dma = [&](int64_t kt) {
     uint16_t* slot = smem + (kt % kStages) * kStageElems;
@@ -303,42 +271,11 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // A fragments are reloaded in place, row block by row block, as soon as the
   // MFMAs of that block have issued; B fragments are double-buffered
   bf16x8 fa[FM], fb[2][FN];
-  auto frag_a = [&](const uint16_t* As, int i) -> bf16x8 {
-    if constexpr (kAT) {
-      // rows wm*WM + i*16 + fr: panel pb, rows rb.. of it; lane (4e + q) of a
-      // 16-lane group points at record k = 8*(lane/16) + 4*hh + e, rows
-      // rb + 4q .. +3, and receives records k0 .. k0+3 of row rb + fr
-      // The reads are inline assembly: the compiler models the transposing
-      // builtin as possibly aliasing the direct loads in flight and would
-      // drain them all (vmcnt(0)) before it, every step.  In this mode every
-      // fragment read is inline assembly (frag_b too) and the waits are
-      // explicit, before each MFMA row block of the step.
-      const int pb = (wm * WM + i * 16) >> 5, rb = (i * 16) & 31;
-      const int e = fr >> 2, q = fr & 3;
-      s16x4 t[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int k = 8 * (lane >> 4) + 4 * hh + e;
-        const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)(
-            As + pb * 1024 + k * 32 + 8 * (((rb >> 3) + (q >> 1)) ^ tsw(k)) + 4 * (q & 1));
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(t[hh]) : "v"(addr) : "memory");
-      }
-      return __builtin_bit_cast(
-          bf16x8, s16x8{t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]});
-    } else {
-      return *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
-    }
+  auto frag_a = [&](const uint16_t* As, int i) {
+    return *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
   };
-  auto frag_b = [&](const uint16_t* Bs, int j) -> bf16x8 {
-    const uint16_t* p = Bs + (wn * WN + j * 16 + fr) * GBK + fk;
-    if constexpr (kAT) {
-      bf16x8 v;
-      const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
-      asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-      return v;
-    } else {
-      return *reinterpret_cast<const bf16x8*>(p);
-    }
+  auto frag_b = [&](const uint16_t* Bs, int j) {
+    return *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
   };
 
   f32x4 acc[FM][FN];
@@ -371,7 +308,6 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     for (int i = 0; i < FM; ++i) fa[i] = frag_a(smem, i);
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(smem + GBM * GBK, j);
-    if constexpr (kAT) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   // one step: stage kt's operands are in registers (fa, fb[cur]); make stage
   // kt+1 visible, refill the slot stage kt-1 used (its last fragments were
@@ -390,23 +326,6 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     const uint16_t* As = smem + ((kt + 1) % kStages) * kStageElems;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      // GM_STORE (all fragment reads inline assembly, issued in program
-      // order: per row block the MFMAs, one B read in the first four blocks,
-      // the two A reads).  A wavefront's LDS reads complete in order, so "at
-      // most n outstanding" lands every read with more than n issued after
-      // it.  Row block 0 needs the step-old B fragments, the last of which
-      // has 10 reads after it; A fragment i has at least 17 after it.  The
-      // wait names the fragments as operands, so the MFMAs cannot move above it.
-      if constexpr (kAT) {
-        if (i == 0)
-          asm volatile("s_waitcnt lgkmcnt(10)"
-                       : "+v"(fa[0]), "+v"(fb[cur][0]), "+v"(fb[cur][1]), "+v"(fb[cur][2]),
-                         "+v"(fb[cur][3])
-                       :
-                       : "memory");
-        else
-          asm volatile("s_waitcnt lgkmcnt(14)" : "+v"(fa[i]) : : "memory");
-      }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
@@ -414,24 +333,22 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       fa[i] = frag_a(As, i);
     }
     static_assert(FM == 8 && FN == 4, "scheduling groups below assume 8 x 4 MFMA blocks");
-    if constexpr (!kAT) {  // (GM_STORE's order is fixed by its inline assembly)
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   };
   int64_t kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -439,7 +356,6 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     step(kt + 1, 1);
   }
   if (kt < nk) step(kt, 0);
-  if constexpr (kAT) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // no read in flight
   __syncthreads();  // every wavefront is done with the ring before the epilogue reuses it
 
   // accumulator layout: acc[i][j][r] = C[m0 + wm*WM + i*16 + 4*(lane/16) + r]
@@ -561,9 +477,7 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     // Each wavefront stages its 128 x 64 block of dlogits in its own 16 KB of
     // the (now idle) ring, column-major: row c of the stage holds column c of
     // the block, 128 bfloat16 in 32 eight-byte quads, quad q stored at
-    // q ^ stage_swz(c).  The block then leaves with contiguous 1 KB stores.
-    // (The dW product reads this same layout through transposing LDS reads,
-    // so no transposed copy is written.)
+    // q ^ stage_swz(c).  Both stores then leave with 16-byte accesses.
     uint16_t* stg = smem + wave * (WM * WN);
     __syncthreads();
     auto body = [&](auto full_tag) {
@@ -599,6 +513,21 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       // (both are multiples of 32, so the block starts at a panel boundary)
       store_staged_rows<kFull>(stg, lane, g.D + (n0 + cw0) / 32 * g.ldd + (m0 + rw0) * 32, 32,
                                g.ldd, nrows_w - rw0, ncols_w - cw0);
+      // transposed: lane l takes column c = 16*cg + l%16 and its 8 rows
+      // 32*tp + 8*(l/16) .. +7, so one instruction writes the 64-byte records
+      // of 16 consecutive columns in one 32-row panel (a contiguous 1 KB
+      // block) and the 16 columns' distinct stage permutations keep the LDS
+      // reads free of bank conflicts
+      const int cl = lane & 15, q = lane >> 4;
+#pragma unroll
+      for (int sidx = 0; sidx < (WM / 32) * (WN / 16); ++sidx) {
+        const int tp = sidx % (WM / 32), c = 16 * (sidx / (WM / 32)) + cl;
+        const int t8 = 4 * tp + q;  // 8-row group within the block
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + c * WM + 4 * ((2 * t8) ^ stage_swz(c)));
+        if (kFull || (cw0 + c < ncols_w && rw0 + 8 * t8 < nrows_w))
+          *reinterpret_cast<u32x4*>(g.Dt + ((m0 + rw0) / 32 + tp) * g.ldt + (n0 + cw0 + c) * 32 +
+                                    8 * q) = v;
+      }
     };
     if (ncols == GBN && nrows_w == GBM)
       body(BoolC<true>{});
@@ -877,6 +806,7 @@ struct LmWs {
   uint16_t* Hat;     // [H, Tcap] K-paneled over tokens (Tcap/32 panels [H][32])
   uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W transposed, K-paneled over it
   uint16_t* Dc;      // [Tcap, kChunkV] dlogits chunk, K-paneled over its columns
+  uint16_t* Dtc;     // [kChunkV, Tcap] the chunk transposed, K-paneled over tokens
   float* dH;         // [Tcap, H]
 };
 
@@ -913,6 +843,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
   w.Wtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * vc));
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
+  w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
   if (ws) *ws = w;
   return off;
@@ -956,9 +887,8 @@ size_t lp_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LpWs* ws
 int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_t* T) {
   if (N <= 0 || C <= 0 || V <= 0 || H <= 0 || G <= 0 || N % G != 0) return DRGRPO_ERR_SHAPE;
   if (V % 8 != 0 || H % kPad != 0 || V > (int64_t(1) << 30) || H > 65536) return DRGRPO_ERR_SHAPE;
-  // token rows up to 2^22 keep every in-tile offset (the epilogues, and the dW
-  // product's loads across 8 dlogits panels of Tcap * 64 bytes) in 32 bits
-  if (!mul_ok(N, C, T) || *T > (int64_t(1) << 22)) return DRGRPO_ERR_SHAPE;
+  // token rows up to 2^24 keep every in-tile offset of the epilogues in 32 bits
+  if (!mul_ok(N, C, T) || *T > (int64_t(1) << 24)) return DRGRPO_ERR_SHAPE;
   int64_t tmp;
   if (!mul_ok(*T, (V + GBN - 1) / GBN * 8, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
       !mul_ok(V, H * 2, &tmp))
@@ -1048,9 +978,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   // operand layouts: the gathered hidden rows Ha, K-paneled over H (panel
   // stride T * 32); their transpose Hat [H, Tcap], K-paneled over tokens;
-  // each dlogits chunk D, K-paneled over its vocabulary columns (the dW
-  // product reads it as paneled over its rows); the W chunk transposed, Wtc,
-  // over vocabulary
+  // each dlogits chunk D, K-paneled over its vocabulary columns, and its
+  // transpose Dt over tokens; the W chunk transposed, Wtc, over vocabulary
   hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st, hid, H, tokens, C, V, w.len,
                      w.offs, w.act_pos, w.ycol, w.Ha, T * 32, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
@@ -1109,6 +1038,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     d.coef = w.coef;
     d.D = w.Dc;
     d.ldd = Tcap * 32;
+    d.Dt = w.Dtc;
+    d.ldt = vc_cap * 32;
     if ((rc = launch_gemm<GM_D>(d, st)) != DRGRPO_OK) return rc;
 
     // the chunk of W transposed, [H, vc_cap] with zero columns past wv
@@ -1134,10 +1065,10 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     a.accumulate = v0 > 0;
     if ((rc = launch_gemm<GM_ACC>(a, st)) != DRGRPO_OK) return rc;
 
-    GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a, A = D paneled over its rows (vocabulary)
-    s.A = w.Dc;
-    s.ar = Tcap * 32;
-    s.ak = 0;
+    GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a
+    s.A = w.Dtc;
+    s.ar = 32;
+    s.ak = vc_cap * 32;
     s.B = w.Hat;
     s.br = 32;
     s.bk = H * 32;
