@@ -55,6 +55,12 @@ _add(DecodeConfig("decode_mha_d128", S=3, Hq=4, Hkv=4, D=128, Lmax=200, ragged=T
 _add(DecodeConfig("decode_gqa8", S=5, Hq=16, Hkv=2, D=64, Lmax=1100, ragged=True, seed=7104))
 _add(DecodeConfig("decode_gqa16_d128", S=2, Hq=16, Hkv=1, D=128, Lmax=130, ragged=True,
                   seed=7105))
+# long caches: more positions per split than one workgroup's loads cover
+# (32 splits at most), so a split runs several load groups with the online
+# softmax carried across them; ragged lengths leave some splits empty
+_add(DecodeConfig("decode_long_d64", S=2, Hq=4, Hkv=1, D=64, Lmax=40000, ragged=True, seed=7106))
+_add(DecodeConfig("decode_long_d128", S=2, Hq=4, Hkv=2, D=128, Lmax=20000, ragged=True,
+                  seed=7107))
 
 
 def get_decode_config(name: str) -> DecodeConfig:
