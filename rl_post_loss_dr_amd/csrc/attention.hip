@@ -39,8 +39,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kAttnWaves = 16;                   // wavefronts per workgroup
-constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kManyPairs = 512;                  // (sequence, KV head) pairs that fill the chip
+constexpr int kGroupsPerSplit = 4;               // load groups per split when pairs are many
 constexpr int kWaveKeys = 32;                    // cached positions per wavefront and round
 constexpr int kMaxGroup = 16;                    // query heads per key/value head (one MFMA block)
 constexpr int kTargetBlocks = 128;               // split workgroups aimed for
@@ -113,11 +113,12 @@ __device__ inline int vswz(int key) {
 template <int D>
 constexpr int attn_rounds() { return D == 64 ? 2 : 1; }  // value slots per wavefront in LDS
 
-// One workgroup of 16 wavefronts per (sequence, key/value head, split of the
-// cached positions); wavefront w takes positions j0 + w*32 + 512*n .. +31 for
-// rounds n = 0, 1, ...  The loads of attn_rounds<D>() rounds (1024 positions
-// at D = 64, 512 at D = 128) are issued together, so one split of that size
-// costs one round trip to memory.  Per round of 32 positions a wavefront
+// One workgroup of NW wavefronts (8 or 16) per (sequence, key/value head,
+// split of the cached positions); wavefront w takes positions
+// j0 + w*32 + 32*NW*n .. +31 for rounds n = 0, 1, ...  The loads of
+// attn_rounds<D>() rounds (64 positions per wavefront at D = 64, 32 at
+// D = 128) are issued together, so a load group costs one round trip to
+// memory.  Per round of 32 positions a wavefront
 //   - loads its keys straight into MFMA operands and forms the transposed
 //     scores S^T = K Q^T for all query heads of the group (v_mfma_f32_16x16x32_bf16:
 //     16 positions x 16 heads per block, binary32 accumulation of exact
@@ -131,9 +132,11 @@ constexpr int attn_rounds() { return D == 64 ? 2 : 1; }  // value slots per wave
 //     direct loads and come back as the A operand through transposing LDS
 //     reads in that same order.  P is split into bfloat16 high and low parts
 //     (two MFMAs), so the weights keep about 17 bits.
-// The 16 partial softmaxes are merged through LDS at the end.
-template <int D>
-__global__ void __launch_bounds__(kAttnThreads) k_attn_fused(AttnArgs a) {
+// The NW partial softmaxes are merged through LDS at the end.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) k_attn_fused(AttnArgs a) {
+  constexpr int kAttnWaves = NW;
+  constexpr int kAttnThreads = 64 * NW;
   static_assert(D == 64 || D == 128, "head size");
   constexpr int NCH = D / 8;                     // 16-byte chunks per cached row
   constexpr int NST = D / 32;                    // MFMA steps of one score block
@@ -289,40 +292,38 @@ __global__ void __launch_bounds__(kAttnThreads) k_attn_fused(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) so[(wv * 16 + li) * D + 16 * cb + 4 * g16 + r] = o[cb][r];
   __syncthreads();
-  constexpr int kCols = D / 64;  // columns per thread
-  const int h = tid >> 6;        // 16 heads x 64 threads
-  if (h >= grp) return;
-  float M = -INFINITY;
+  // thread t merges (head, column) pairs t, t + kAttnThreads, ... of the
+  // 16 x D partial outputs
+  const int64_t sh0 = s * a.Hq + g * grp;
+  for (int idx = tid; idx < 16 * D; idx += kAttnThreads) {
+    const int h = idx / D, c = idx % D;
+    if (h >= grp) break;  // pairs are head-major: the rest belong to absent heads
+    float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
-  float l = 0.0f, ov[kCols];
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
+    float l = 0.0f, ov = 0.0f;
+    if (M != -INFINITY) {
 #pragma unroll
-  for (int c = 0; c < kCols; ++c) ov[c] = 0.0f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      if (sm[w][h] == -INFINITY) continue;  // a wavefront without positions
-      const float f = exp2f((sm[w][h] - M) * kLog2eA);
-      l = fmaf(sl[w][h], f, l);
-#pragma unroll
-      for (int c = 0; c < kCols; ++c) ov[c] = fmaf(so[(w * 16 + h) * D + lane + 64 * c], f, ov[c]);
+      for (int w = 0; w < kAttnWaves; ++w) {
+        if (sm[w][h] == -INFINITY) continue;  // a wavefront without positions
+        const float f = exp2f((sm[w][h] - M) * kLog2eA);
+        l = fmaf(sl[w][h], f, l);
+        ov = fmaf(so[(w * 16 + h) * D + c], f, ov);
+      }
     }
-  }
-  const int64_t sh = s * a.Hq + g * grp + h;
-  if (a.nsplit == 1) {  // the whole cache in one split: normalise and write the output here
-    const bool empty = M == -INFINITY;  // no cached key: an empty softmax
-#pragma unroll
-    for (int c = 0; c < kCols; ++c) a.out[sh * D + lane + 64 * c] = to_bf16(empty ? NAN : ov[c] / l);
-    if (a.out_lse && lane == 0) a.out_lse[sh] = empty ? NAN : M + logf(l);
-    return;
-  }
-  // partial of this split (an empty split: max -inf, sum 0)
-  float* pp = a.part + (sh * a.nsplit + split) * (int64_t)(D + 2);
-#pragma unroll
-  for (int c = 0; c < kCols; ++c) pp[lane + 64 * c] = ov[c];
-  if (lane == 0) {
-    pp[D] = M;
-    pp[D + 1] = l;
+    const int64_t sh = sh0 + h;
+    if (a.nsplit == 1) {  // the whole cache in one split: normalise and write the output here
+      const bool empty = M == -INFINITY;  // no cached key: an empty softmax
+      a.out[sh * D + c] = to_bf16(empty ? NAN : ov / l);
+      if (a.out_lse && c == 0) a.out_lse[sh] = empty ? NAN : M + logf(l);
+    } else {  // partial of this split (an empty split: max -inf, sum 0)
+      float* pp = a.part + (sh * a.nsplit + split) * (int64_t)(D + 2);
+      pp[c] = ov;
+      if (c == 0) {
+        pp[D] = M;
+        pp[D + 1] = l;
+      }
+    }
   }
 }
 
@@ -388,23 +389,36 @@ void launch_combine(const AttnArgs& a, hipStream_t st) {
                      st, a);
 }
 
-// splits: at most the positions whose loads a workgroup issues together
-// (1024 at D = 64, 512 at D = 128) per split unless that needs more than
-// kMaxSplit splits; more splits, down to 128 positions each, while there are
-// fewer than kTargetBlocks workgroups.  A second launch (the combine) costs
-// more than a second round trip inside one workgroup, so splits are few.
-void attn_splits(int64_t S, int64_t Hkv, int64_t Lmax, int64_t D, int* nsplit, int* chunk) {
-  const int64_t kRound = kAttnWaves * kWaveKeys * (D == 64 ? attn_rounds<64>() : attn_rounds<128>());
-  int64_t ns = (Lmax + kRound - 1) / kRound;
-  const int64_t ns_par = (kTargetBlocks + S * Hkv - 1) / (S * Hkv);
+// Launch plan: 8-wavefront workgroups (two fit a CU, so one's loads overlap
+// the other's products and merge), or 16 when that covers a cache of up to
+// 1024 positions (D = 64) in one load group and there are few (sequence, KV
+// head) pairs: a second launch (the combine) costs more than a bigger
+// workgroup.  Positions per split: one load group, or kGroupsPerSplit of them
+// when there are kManyPairs pairs anyway; at most kMaxSplit splits; more
+// splits, down to 128 positions, while there are fewer than kTargetBlocks
+// workgroups.
+struct AttnPlan {
+  int nw, nsplit, chunk;
+};
+
+AttnPlan attn_plan(int64_t S, int64_t Hkv, int64_t Lmax, int64_t D) {
+  const int64_t pairs = S * Hkv;
+  const int64_t per_wave = kWaveKeys * (D == 64 ? attn_rounds<64>() : attn_rounds<128>());
+  AttnPlan p;
+  p.nw = 8;
+  if (D == 64 && pairs <= kTargetBlocks && Lmax > 8 * per_wave && Lmax <= 16 * per_wave) p.nw = 16;
+  const int64_t group = p.nw * per_wave * (pairs >= kManyPairs ? kGroupsPerSplit : 1);
+  int64_t ns = (Lmax + group - 1) / group;
+  const int64_t ns_par = (kTargetBlocks + pairs - 1) / pairs;
   const int64_t ns_fine = (Lmax + 4 * kWaveKeys - 1) / (4 * kWaveKeys);
   const int64_t ns_more = ns_par < ns_fine ? ns_par : ns_fine;
   if (ns < ns_more) ns = ns_more;
   if (ns > kMaxSplit) ns = kMaxSplit;
   if (ns < 1) ns = 1;
   const int64_t per = ((Lmax + ns - 1) / ns + kWaveKeys - 1) / kWaveKeys * kWaveKeys;
-  *chunk = (int)per;
-  *nsplit = (int)((Lmax + per - 1) / per);
+  p.chunk = (int)per;
+  p.nsplit = (int)((Lmax + per - 1) / per);
+  return p;
 }
 
 int attn_check(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D) {
@@ -423,9 +437,7 @@ int attn_check(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D) {
 extern "C" size_t drgrpo_decode_attention_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv,
                                                           int64_t Lmax, int64_t D) {
   if (attn_check(S, Hq, Hkv, Lmax, D) != DRGRPO_OK) return 0;
-  int nsplit, chunk;
-  attn_splits(S, Hkv, Lmax, D, &nsplit, &chunk);
-  return (size_t)(S * Hq) * nsplit * (D + 2) * sizeof(float);
+  return (size_t)(S * Hq) * attn_plan(S, Hkv, Lmax, D).nsplit * (D + 2) * sizeof(float);
 }
 
 extern "C" int drgrpo_decode_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -453,20 +465,26 @@ extern "C" int drgrpo_decode_attention(const void* q, const void* k_cache, const
   a.Hkv = Hkv;
   a.Lmax = Lmax;
   a.scale = scale;
-  attn_splits(S, Hkv, Lmax, D, &a.nsplit, &a.chunk);
+  const AttnPlan plan = attn_plan(S, Hkv, Lmax, D);
+  a.nsplit = plan.nsplit;
+  a.chunk = plan.chunk;
   a.part = static_cast<float*>(workspace);
   a.out = static_cast<uint16_t*>(out);
   a.out_lse = out_lse;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned blocks = (unsigned)(S * Hkv * a.nsplit);
-  if (D == 64) {
-    hipLaunchKernelGGL(k_attn_fused<64>, dim3(blocks), dim3(kAttnThreads), 0, st, a);
-    if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
-    if (a.nsplit > 1) launch_combine<64>(a, st);
-  } else {
-    hipLaunchKernelGGL(k_attn_fused<128>, dim3(blocks), dim3(kAttnThreads), 0, st, a);
-    if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
-    if (a.nsplit > 1) launch_combine<128>(a, st);
+  if (D == 64 && plan.nw == 16)
+    hipLaunchKernelGGL((k_attn_fused<64, 16>), dim3(blocks), dim3(64 * 16), 0, st, a);
+  else if (D == 64)
+    hipLaunchKernelGGL((k_attn_fused<64, 8>), dim3(blocks), dim3(64 * 8), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn_fused<128, 8>), dim3(blocks), dim3(64 * 8), 0, st, a);
+  if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
+  if (a.nsplit > 1) {
+    if (D == 64)
+      launch_combine<64>(a, st);
+    else
+      launch_combine<128>(a, st);
   }
   return attn_launch_status();
 }

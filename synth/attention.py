@@ -47,6 +47,10 @@ def _add(c: DecodeConfig) -> DecodeConfig:
 # completion, the bench workload), and a 1024-token cache.
 _add(DecodeConfig("decode_s64_l512", S=64, Hq=14, Hkv=2, D=64, Lmax=512))
 _add(DecodeConfig("decode_s64_l1024", S=64, Hq=14, Hkv=2, D=64, Lmax=1024))
+# a larger rollout batch (B=32 x G=8 sequences), where the cache read is
+# bandwidth- rather than latency-bound, and a 512-sequence, 2048-position one
+_add(DecodeConfig("decode_s256_l1024", S=256, Hq=14, Hkv=2, D=64, Lmax=1024))
+_add(DecodeConfig("decode_s512_l2048", S=512, Hq=14, Hkv=2, D=64, Lmax=2048))
 # parity cases: ragged lengths, a tail that is not a multiple of any tile,
 # one-key caches, another head geometry
 _add(DecodeConfig("decode_ragged", S=9, Hq=14, Hkv=2, D=64, Lmax=333, ragged=True, seed=7101))

@@ -48,7 +48,8 @@ def _check(case, got, lse, lens=None, scale=None):
 
 @pytest.mark.parametrize("name", ["decode_ragged", "decode_one_key", "decode_mha_d128",
                                   "decode_gqa8", "decode_gqa16_d128", "decode_s64_l512",
-                                  "decode_s64_l1024", "decode_long_d64", "decode_long_d128"])
+                                  "decode_s64_l1024", "decode_s256_l1024", "decode_long_d64",
+                                  "decode_long_d128"])
 def test_decode_attention_parity(name):
     print(f"case {name}", flush=True)
     case = make_decode_case(get_decode_config(name))
