@@ -13,15 +13,17 @@
  * The step is bound by reading the cache once (bfloat16 K and V) and, at
  * the sizes of a rollout, by the latency of that read, so a workgroup issues
  * all of its loads at once:
- *   k_attn_fused    a 1024-thread workgroup per (sequence, key/value head,
- *                   split of the cached positions); each of its 16
- *                   wavefronts takes 32 positions, forms the scores of every
- *                   query head of the group and the weighted values on MFMAs
- *                   (details at the kernel) and keeps an online softmax; the
- *                   16 partials are merged in LDS.  With one split (the usual
- *                   decode batch) it writes the bfloat16 output and the
- *                   log-sum-exp itself; otherwise a partial (unnormalised
- *                   output, max, sum of exp) per split.
+ *   k_attn_fused    a workgroup of 8 (or 16) wavefronts per (sequence,
+ *                   key/value head, split of the cached positions); each
+ *                   wavefront takes 32 positions per round, forms the scores
+ *                   of every query head of the group and the weighted values
+ *                   on MFMAs (details at the kernel) and keeps an online
+ *                   softmax; the partials are merged in LDS.  With one split
+ *                   (the usual decode batch) it writes the bfloat16 output
+ *                   and the log-sum-exp itself; otherwise a partial
+ *                   (unnormalised output, max, sum of exp) per split.  The
+ *                   launch plan (attn_plan) picks the wavefront count and
+ *                   the splits.
  *   k_attn_combine  merges the splits of each (sequence, query head) in
  *                   split order and writes the output and the log-sum-exp.
  */
