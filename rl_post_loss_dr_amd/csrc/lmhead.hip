@@ -617,21 +617,27 @@ k_lm_offsets(const int32_t* __restrict__ len, const float* __restrict__ adv, int
   }
 }
 
-// One workgroup per completion: list its active tokens, gather their hidden
-// rows, and zero the loss terms of its other tokens (tok_loss == NULL: no
-// loss terms, the forward-only pass).  The gathered rows are K-paneled:
-// element (k, h) of active token k at Ha[(h / 32) * ha_ps + k * 32 + h % 32].
+// One workgroup per (completion, block of kGatherTok tokens): list the
+// block's active tokens, gather their hidden rows, and zero the loss terms of
+// its other tokens (tok_loss == NULL: no loss terms, the forward-only pass).
+// The gathered rows are K-paneled: element (k, h) of active token k at
+// Ha[(h / 32) * ha_ps + k * 32 + h % 32].  A completion's active tokens are
+// its first n_act (all counted tokens, or none).
+constexpr int kGatherTok = 32;
 __global__ void __launch_bounds__(256)
 k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __restrict__ tokens,
             int64_t C, int64_t V, const int32_t* __restrict__ len,
             const int32_t* __restrict__ offs, int32_t* __restrict__ act_pos,
             int32_t* __restrict__ ycol, uint16_t* __restrict__ Ha, int64_t ha_ps,
             double* __restrict__ tok_loss, uint8_t* __restrict__ tok_flags) {
-  const int64_t i = blockIdx.x;
+  const int64_t nb = (C + kGatherTok - 1) / kGatherTok;
+  const int64_t i = blockIdx.x / nb;
+  const int64_t t0 = (blockIdx.x - i * nb) * kGatherTok;
+  const int64_t t1 = C - t0 < kGatherTok ? C : t0 + kGatherTok;
   const int32_t n_act = offs[i + 1] - offs[i];
   const int32_t k0 = offs[i];
   const int32_t L = len[i];
-  for (int64_t t = threadIdx.x; t < C; t += blockDim.x) {
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
     const int64_t pos = i * C + t;
     const int64_t y = tokens[pos];
     const bool bad = t < L && (y < 0 || y >= V);
@@ -644,12 +650,13 @@ k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __res
       tok_flags[pos] = bad ? TF_BADTOK : 0;
     }
   }
-  // hidden rows of the active tokens: 16-byte copies, four lanes per 64-byte
-  // panel record, so a wavefront writes whole records of 16 tokens
+  // hidden rows of the block's active tokens: 16-byte copies, four lanes per
+  // 64-byte panel record, so a wavefront writes whole records of 16 tokens
+  const int64_t nt = (t1 < n_act ? t1 : (int64_t)n_act) - t0;
   const int64_t npan = H / 32;
-  for (int64_t q = threadIdx.x; q < (int64_t)n_act * npan * 4; q += blockDim.x) {
+  for (int64_t q = threadIdx.x; q < nt * npan * 4; q += blockDim.x) {
     const int64_t c4 = q & 3, rest = q >> 2;
-    const int64_t t = rest % n_act, pn = rest / n_act;
+    const int64_t t = t0 + rest % nt, pn = rest / nt;
     *reinterpret_cast<u32x4*>(Ha + pn * ha_ps + (k0 + t) * 32 + 8 * c4) =
         *reinterpret_cast<const u32x4*>(hidden + (i * C + t) * H + 32 * pn + 8 * c4);
   }
@@ -659,28 +666,42 @@ k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __res
 // dst[(r / 32) * d_ps + c * 32 + r % 32], is element (r, c) of src, at
 // src[r * s_rs + (c / 32) * s_ps + c % 32] (row-major: s_rs = ld, s_ps = 32),
 // for r < rows (or the device count rows_dev) and zero for r up to rows_pad
-// (or rows_dev rounded up to kPad); 64 x 64 tiles through LDS.  The grid
-// covers ceil(rows_pad / 64) x ceil(cols / 64) tiles.
+// (or rows_dev rounded up to kPad); 64 x 64 tiles through LDS with 16-byte
+// accesses on both sides (8 columns of a row in, 8 rows of a column out: a
+// quarter of a 64-byte panel record), so cols and the row counts are
+// multiples of 8 and every offset a multiple of 8 elements.  The grid covers
+// ceil(rows_pad / 64) x ceil(cols / 64) tiles.
 __global__ void __launch_bounds__(256)
 k_transpose(const uint16_t* __restrict__ src, int64_t s_rs, int64_t s_ps, int64_t rows,
             int64_t rows_pad, int64_t cols, const int32_t* __restrict__ rows_dev,
             uint16_t* __restrict__ dst, int64_t d_ps) {
-  __shared__ uint16_t tile[64][65];
+  constexpr int TS = 64, TP = TS + 8;  // tile, padded LDS row (16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TS][TP];
   const int64_t R = rows_dev ? (int64_t)*rows_dev : rows;
   const int64_t Rpad = rows_dev ? (R + kPad - 1) / kPad * kPad : rows_pad;
-  const int64_t ntr = (rows_pad + 63) / 64;
-  const int64_t r0 = (blockIdx.x % ntr) * 64;
-  const int64_t c0 = (blockIdx.x / ntr) * 64;
+  const int64_t ntr = (rows_pad + TS - 1) / TS;
+  const int64_t r0 = (blockIdx.x % ntr) * TS;
+  const int64_t c0 = (blockIdx.x / ntr) * TS;
   if (r0 >= Rpad) return;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k, c = c0 + tx;
-    tile[k][tx] = (r < R && c < cols) ? src[r * s_rs + (c / 32) * s_ps + c % 32] : (uint16_t)0;
+  for (int e = threadIdx.x; e < TS * (TS / 8); e += blockDim.x) {
+    const int k = e >> 3, cc = (e & 7) * 8;  // tile row, first of its 8 columns
+    const int64_t r = r0 + k, c = c0 + cc;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (r < R && c < cols)
+      v = *reinterpret_cast<const u32x4*>(src + r * s_rs + (c / 32) * s_ps + c % 32);
+    *reinterpret_cast<u32x4*>(&tile[k][cc]) = v;
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t c = c0 + k, r = r0 + tx;
-    if (c < cols && r < Rpad) dst[(r / 32) * d_ps + c * 32 + r % 32] = tile[tx][k];
+  for (int e = threadIdx.x; e < TS * (TS / 8); e += blockDim.x) {
+    const int k = e >> 3, rr = (e & 7) * 8;  // tile column, first of its 8 rows
+    const int64_t c = c0 + k, r = r0 + rr;
+    if (c >= cols || r >= Rpad) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = (uint32_t)tile[rr + 2 * u][k] | ((uint32_t)tile[rr + 2 * u + 1][k] << 16);
+    *reinterpret_cast<u32x4*>(dst + (r / 32) * d_ps + c * 32 + r % 32) =
+        u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -980,7 +1001,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   // stride T * 32); their transpose Hat [H, Tcap], K-paneled over tokens;
   // each dlogits chunk D, K-paneled over its vocabulary columns, and its
   // transpose Dt over tokens; the W chunk transposed, Wtc, over vocabulary
-  hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st, hid, H, tokens, C, V, w.len,
+  hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)(N * ((C + kGatherTok - 1) / kGatherTok))),
+                     dim3(256), 0, st, hid, H, tokens, C, V, w.len,
                      w.offs, w.act_pos, w.ycol, w.Ha, T * 32, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   {
@@ -1136,8 +1158,9 @@ extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const i
   hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, (const float*)nullptr, N,
                      0.0f, w.offs, w.counts);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
-  hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)N), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(hidden), H, tokens, C, V, w.len, w.offs,
+  hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)(N * ((C + kGatherTok - 1) / kGatherTok))),
+                     dim3(256), 0, st, static_cast<const uint16_t*>(hidden), H, tokens, C, V,
+                     w.len, w.offs,
                      w.act_pos, w.ycol, w.Ha, T * 32, (double*)nullptr, (uint8_t*)nullptr);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_logp_tail, dim3((unsigned)N), dim3(256), 0, st, w.len, C, out_logp);
