@@ -46,7 +46,11 @@ constexpr int GT = 64 * NWM * NWN;         // 8 wavefronts, 2 per SIMD
 constexpr int FM = WM / 16, FN = WN / 16;  // 8 x 4 MFMA blocks per wavefront
 constexpr int kStages = 4;                 // LDS ring depth (3 stages of loads in flight)
 constexpr int kStageElems = (GBM + GBN) * GBK;  // bfloat16 per LDS stage (32 KB)
-constexpr int kDmaPerThread = kStageElems / 8 / GT;  // 16-byte direct loads per thread per stage
+constexpr int kDmaA = GBM / 16 / (GT / 64);  // 16-row direct loads of A per wavefront per stage
+constexpr int kDmaB = GBN / 16 / (GT / 64);  // and of B
+constexpr int kDmaPerThread = kDmaA + kDmaB;
+static_assert(kDmaA * (GT / 64) * 16 == GBM && kDmaB * (GT / 64) * 16 == GBN,
+              "the wavefronts split both operands' row groups evenly");
 constexpr int kRingElems = kStages * kStageElems;
 constexpr int kTableBytes = 4096;          // per-row epilogue tables (after the main loop)
 // the tables sit past the ring when it leaves room, else in its last 4 KB
@@ -119,12 +123,26 @@ __device__ inline uint16_t bf16_bits(float x) {
 // Cross-lane moves within a DPP row of 16 lanes (lanes sharing l / 16).  A
 // max or sum over the row takes four steps: swaps within quads (xor 1, xor 2),
 // then across quad pairs (half-row mirror) and row halves (row mirror); every
-// lane of the row ends with the result.
+// lane of the row ends with the result.  Every source lane of these patterns
+// lies in the row, so bound_ctrl never applies; the compiler folds the move
+// into the integer max and the float add that consume it.
+template <int CTRL>
+__device__ inline int dpp_i32(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
 template <int CTRL>
 __device__ inline float dpp_f32(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
 }
+// An order-preserving map of non-NaN binary32 values to int32 (its own
+// inverse): the magnitude bits of negative values are flipped, so the integer
+// max is the float max (a float max would be canonicalised first and could
+// not absorb the lane move).
+__device__ inline int f32_ord(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ inline float ord_f32(int b) { return __builtin_bit_cast(float, b ^ ((b >> 31) & 0x7FFFFFFF)); }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
@@ -182,8 +200,10 @@ __device__ inline void stage_quad(uint16_t* stg, int lane, int i, int j, const u
       make_uint2((uint32_t)d[0] | ((uint32_t)d[1] << 16), (uint32_t)d[2] | ((uint32_t)d[3] << 16));
 }
 
+// two wavefronts per SIMD: the register budget of 8 wavefronts per CU, whatever the
+// workgroup size (with 4-wavefront workgroups, two workgroups share a CU)
 template <int MODE>
-__global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
+__global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,10 +248,11 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
 
   // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
   // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled
-  // by direct global -> LDS loads issued kStages-1 stages ahead.  Wavefronts
-  // 0-3 load A, 4-7 load B, through a buffer descriptor over the tile's rows
-  // of the current 32-wide reduction panel (buffer loads: the compiler counts
-  // them on vmcnt alone, so the LDS fragment reads keep fine-grained waits).
+  // by direct global -> LDS loads issued kStages-1 stages ahead.  Each
+  // wavefront loads kDmaA 16-row groups of A and kDmaB of B, through buffer
+  // descriptors over the tile's rows of the current 32-wide reduction panel
+  // (buffer loads: the compiler counts them on vmcnt alone, so the LDS
+  // fragment reads keep fine-grained waits).
   // One instruction moves 16 rows x 64 B (lane l: row l/4, chunk l%4): a
   // single contiguous 1 KB block of a K-paneled operand.  Rows past M or N
   // re-read the last valid row (their results are never used).  K is a
@@ -239,31 +260,41 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   // by swz(row % 16), so the fragment reads (16 rows, one chunk) spread over
   // all LDS banks.
   const int64_t nk = K / GBK;
-  static_assert((GBM / 16) % kDmaPerThread == 0, "each wavefront loads rows of one operand");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const bool ldA = wv * kDmaPerThread < GBM / 16;
-  const int64_t r0 = ldA ? m0 : n0;
-  const int64_t rleft = (ldA ? M : g.N) - r0;  // >= 1: the tile exists
-  const int64_t nvalid = rleft < (ldA ? GBM : GBN) ? rleft : (ldA ? GBM : GBN);
-  const int64_t rs = ldA ? g.ar : g.br, ks = ldA ? g.ak : g.bk;
-  const uint16_t* obase = (ldA ? g.A : g.B) + r0 * rs;
-  const int pbytes = (int)(((nvalid - 1) * rs + GBK) * 2);  // the rows' span in one panel
-  uint32_t voff[kDmaPerThread];
+  const int64_t nvA = M - m0 < GBM ? M - m0 : GBM;    // >= 1: the tile exists
+  const int64_t nvB = g.N - n0 < GBN ? g.N - n0 : GBN;
+  const uint16_t* baseA = g.A + m0 * g.ar;
+  const uint16_t* baseB = g.B + n0 * g.br;
+  const int pbA = (int)(((nvA - 1) * g.ar + GBK) * 2);  // the rows' span in one panel
+  const int pbB = (int)(((nvB - 1) * g.br + GBK) * 2);
+  const int dchunk = 8 * ((lane & 3) ^ swz(lane >> 2));
+  uint32_t voffA[kDmaA], voffB[kDmaB];
 #pragma unroll
-  for (int p = 0; p < kDmaPerThread; ++p) {
-    const int64_t r = (wv * kDmaPerThread + p) * 16 + (lane >> 2) - (ldA ? 0 : GBM);
-    voff[p] = (uint32_t)(((r < nvalid ? r : nvalid - 1) * rs + 8 * ((lane & 3) ^ swz(lane >> 2))) * 2);
+  for (int p = 0; p < kDmaA; ++p) {
+    const int64_t r = (wv * kDmaA + p) * 16 + (lane >> 2);
+    voffA[p] = (uint32_t)(((r < nvA ? r : nvA - 1) * g.ar + dchunk) * 2);
+  }
+#pragma unroll
+  for (int p = 0; p < kDmaB; ++p) {
+    const int64_t r = (wv * kDmaB + p) * 16 + (lane >> 2);
+    voffB[p] = (uint32_t)(((r < nvB ? r : nvB - 1) * g.br + dchunk) * 2);
   }
   auto dma = [&](int64_t kt) {
     uint16_t* slot = smem + (kt % kStages) * kStageElems;
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(obase + kt * ks), 0,
-                                                        pbytes, 0x00020000);
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(baseA + kt * g.ak), 0,
+                                                      pbA, 0x00020000);
+    const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(baseB + kt * g.bk), 0,
+                                                      pbB, 0x00020000);
 #pragma unroll
-    for (int p = 0; p < kDmaPerThread; ++p)
+    for (int p = 0; p < kDmaA; ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc,
-          (__attribute__((address_space(3))) void*)(slot + (wv * kDmaPerThread + p) * 16 * GBK),
-          16, voff[p], 0, 0, 0);
+          ra, (__attribute__((address_space(3))) void*)(slot + (wv * kDmaA + p) * 16 * GBK), 16,
+          voffA[p], 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < kDmaB; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(slot + (GBM + (wv * kDmaB + p) * 16) * GBK),
+          16, voffB[p], 0, 0, 0);
   };
   const int fr = lane & 15;  // row (A) / column (B) within a 16 x 16 block
   // LDS position of the lane's 8 reduction indices 8*(lane/16) .. +7
@@ -299,8 +330,40 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     else
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
   };
-  if (nk > 0) {
+  // Per-row epilogue tables in the area past the ring.  Their entries are
+  // loaded into registers here, before the first stages' loads, and written
+  // to LDS after the main loop, whose last wait has seen them land: the
+  // loads cost no wait of their own.
+  //   GM_LSE: tile-local column of the row's sampled token (-1: none, or a
+  //           column of another tile, which never equals a local column)
+  //   GM_D:   (M, log2 S) of the row's log-sum-exp, coef, sampled column
+  float2* const t_sp = reinterpret_cast<float2*>(smem + kTableElem);  // GM_D [GBM]
+  float* const t_sc = reinterpret_cast<float*>(t_sp + GBM);          // GM_D [GBM]
+  int32_t* const t_yl =
+      MODE == GM_LSE ? reinterpret_cast<int32_t*>(smem + kTableElem)  // [GBM]
+                     : reinterpret_cast<int32_t*>(t_sc + GBM);
+  constexpr bool kTables = MODE == GM_LSE || MODE == GM_D;
+  static_assert(!kTables || !kTablesInRing, "the epilogue tables are written while waves may still read the ring");
+  constexpr int kYPer = (GBM + GT - 1) / GT;
+  int32_t ypre[kYPer];
+  float2 lpre[kYPer];
+  float cpre[kYPer];
+  if constexpr (kTables) {
+#pragma unroll
+    for (int k = 0; k < kYPer; ++k) {
+      const int r = tid + k * GT;
+      const bool ok = r < GBM && m0 + r < M;
+      ypre[k] = ok ? g.ycol[m0 + r] : -1;
+      if constexpr (MODE == GM_D) {
+        // rows past the active count: exp2(-inf) gives exact zeros
+        lpre[k] = ok ? g.lsep[m0 + r] : make_float2(0.0f, INFINITY);
+        cpre[k] = ok ? g.coef[m0 + r] : 0.0f;
+      }
+    }
+  }
+  if (nk > 0)
     for (int64_t s = 0; s < kStages - 1 && s < nk; ++s) dma(s);
+  if (nk > 0) {
     // stage 0 complete; the later prologue stages may still be in flight
     wait_stages(nk - 1 < kStages - 2 ? nk - 1 : kStages - 2);
     ring_barrier();
@@ -356,7 +419,22 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     step(kt + 1, 1);
   }
   if (kt < nk) step(kt, 0);
-  __syncthreads();  // every wavefront is done with the ring before the epilogue reuses it
+  if constexpr (kTables) {
+#pragma unroll
+    for (int k = 0; k < kYPer; ++k) {
+      const int r = tid + k * GT;
+      if (r < GBM) {
+        t_yl[r] = ypre[k] < 0 ? -1 : (int32_t)(ypre[k] - (g.col_base + n0));
+        if constexpr (MODE == GM_D) {
+          t_sp[r] = lpre[k];
+          t_sc[r] = cpre[k];
+        }
+      }
+    }
+  }
+  // every wavefront is done with the ring before the epilogue reuses it, and
+  // the tables are visible
+  __syncthreads();
 
   // accumulator layout: acc[i][j][r] = C[m0 + wm*WM + i*16 + 4*(lane/16) + r]
   //                                    [n0 + wn*WN + j*16 + lane%16]
@@ -367,14 +445,8 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
   const int ncols = (int)(g.N - n0 < GBN ? g.N - n0 : GBN);
   const int lc0 = wn * WN + fr;  // tile-local column of acc[.][0]
   if constexpr (MODE == GM_LSE) {
-    float2* red = reinterpret_cast<float2*>(smem);              // [NWN][GBM]
-    int32_t* yl = reinterpret_cast<int32_t*>(red + NWN * GBM);  // [GBM] tile-local target column
-    for (int r = tid; r < GBM; r += GT) {
-      const int64_t row = m0 + r;
-      // -1 (no target) or a column of another tile never equals a local column
-      yl[r] = row < M ? (int32_t)(g.ycol[row] < 0 ? -1 : g.ycol[row] - (g.col_base + n0)) : -1;
-    }
-    __syncthreads();
+    float2* red = reinterpret_cast<float2*>(smem);  // [NWN][GBM]
+    const int32_t* yl = t_yl;
     // full tiles (the common case) compile without the column checks
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
@@ -384,40 +456,58 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       for (int i = 0; i < FM; ++i) {
         const int rt0 = wm * WM + i * 16 + rq;
         const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
-        const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+        // the sampled token's column is held by the lane whose columns
+        // lc0 + 16j include it: a rare, divergent store
+        const int dy[4] = {y4.x - lc0, y4.y - lc0, y4.z - lc0, y4.w - lc0};
+        bool hit[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hit[r] = (unsigned)dy[r] < (unsigned)WN && (dy[r] & 15) == 0;
+        if (hit[0] || hit[1] || hit[2] || hit[3]) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // a bitwise select (a variable index would send acc to scratch);
+            // each element is copied out first, since a bit cast of a vector
+            // element expression reads the vector's first element
+            uint32_t xb = 0;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const float a = acc[i][j][r];
+              xb |= __builtin_bit_cast(uint32_t, a) & (dy[r] == 16 * j ? ~0u : 0u);
+            }
+            if (hit[r]) g.xy[m0 + rt0 + r] = __builtin_bit_cast(float, xb);
+          }
+        }
+        int mo[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if (!kFull && lc0 + j * 16 >= ncols) acc[i][j][r] = -INFINITY;
+            m = fmaxf(m, acc[i][j][r]);
+          }
+          mo[r] = f32_ord(m);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppXor1>(mo[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppXor2>(mo[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppHalfMirror>(mo[r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppMirror>(mo[r]));
         float mx[4], sm[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float xv = 0.0f;
-          bool hit = false;
-          mx[r] = -INFINITY;
+          mx[r] = ord_f32(mo[r]);
+          // (a quarter tile past the last vocabulary column holds no value at
+          // all, only in a partial tile); exp(x - M) as exp2(x*log2e - M*log2e), one fused step per
+          // entry (the rounding of M*log2e scales the whole partial sum by one
+          // factor 2^d, |d| <= 2^-24 |M| log2e)
+          const float nb = kFull || mx[r] != -INFINITY ? -mx[r] * kL2E : 0.0f;
+          sm[r] = __builtin_amdgcn_exp2f(fmaf(acc[i][0][r], kL2E, nb));
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int lc = lc0 + j * 16;
-            if (!kFull && lc >= ncols) acc[i][j][r] = -INFINITY;
-            mx[r] = fmaxf(mx[r], acc[i][j][r]);
-            xv = lc == yv[r] ? acc[i][j][r] : xv;
-            hit = hit || lc == yv[r];
-          }
-          if (hit) g.xy[m0 + rt0 + r] = xv;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppXor1>(mx[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppXor2>(mx[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppHalfMirror>(mx[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], dpp_f32<kDppMirror>(mx[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // a quarter tile past the last vocabulary column holds no value at all
-          // difference first, then the scale: accurate for the entries near
-          // the maximum that dominate the sum
-          const float nb = mx[r] == -INFINITY ? 0.0f : mx[r];
-          sm[r] = 0.0f;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) sm[r] += __builtin_amdgcn_exp2f((acc[i][j][r] - nb) * kL2E);
+          for (int j = 1; j < FN; ++j) sm[r] += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, nb));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor1>(sm[r]);
@@ -455,18 +545,10 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
       g.part[row * g.ntn + tn] = make_float2(mx, sm);
     }
   } else if constexpr (MODE == GM_D) {
-    // per-row tables: (M, log2 S) of the row's log-sum-exp, coef, target column
-    float2* sp = reinterpret_cast<float2*>(smem + kTableElem);  // [GBM]
-    float* sc = reinterpret_cast<float*>(sp + GBM);             // [GBM] coef
-    int32_t* yl = reinterpret_cast<int32_t*>(sc + GBM);         // [GBM] tile-local target column
-    for (int r = tid; r < GBM; r += GT) {
-      const int64_t row = m0 + r;
-      const bool ok = row < M;
-      // rows past the active count: exp2(-inf) gives exact zeros
-      sp[r] = ok ? g.lsep[row] : make_float2(0.0f, INFINITY);
-      sc[r] = ok ? g.coef[row] : 0.0f;
-      yl[r] = ok ? (int32_t)(g.ycol[row] < 0 ? -1 : g.ycol[row] - (g.col_base + n0)) : -1;
-    }
+    // per-row tables
+    const float2* sp = t_sp;
+    const float* sc = t_sc;
+    const int32_t* yl = t_yl;
     // rows up to the active count rounded up to kPad, columns up to the
     // chunk width rounded up to kPad are written (zeros past the data), so
     // the products over the chunk may read whole kPad blocks
@@ -479,7 +561,6 @@ __global__ void __launch_bounds__(GT) k_gemm(GemmArgs g) {
     // the block, 128 bfloat16 in 32 eight-byte quads, quad q stored at
     // q ^ stage_swz(c).  Both stores then leave with 16-byte accesses.
     uint16_t* stg = smem + wave * (WM * WN);
-    __syncthreads();
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
