@@ -119,6 +119,13 @@ __device__ inline uint16_t bf16_bits(float x) {
   const __bf16 h = (__bf16)x;  // round to nearest even
   return __builtin_bit_cast(uint16_t, h);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two values rounded to bfloat16 (nearest even) in one packed conversion, a
+// in the low half
+__device__ inline uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 
 // Cross-lane moves within a DPP row of 16 lanes (lanes sharing l / 16).  A
 // max or sum over the row takes four steps: swaps within quads (xor 1, xor 2),
@@ -192,12 +199,12 @@ __device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t
 }
 
 // Stage column c = j*16 + (lane % 16) of the wavefront block, rows
-// i*16 + 4*(lane/16) .. +3 (one MFMA accumulator quad, as bfloat16 bits).
-__device__ inline void stage_quad(uint16_t* stg, int lane, int i, int j, const uint16_t d[4]) {
+// i*16 + 4*(lane/16) .. +3 (one MFMA accumulator quad, as bfloat16 bits:
+// rows 0-1 in lo, 2-3 in hi, the lower row in the low half).
+__device__ inline void stage_pair(uint16_t* stg, int lane, int i, int j, uint32_t lo, uint32_t hi) {
   const int q = i * 4 + (lane >> 4);
   const int c = j * 16 + (lane & 15);
-  *reinterpret_cast<uint2*>(stg + c * WM + 4 * (q ^ stage_swz(c))) =
-      make_uint2((uint32_t)d[0] | ((uint32_t)d[1] << 16), (uint32_t)d[2] | ((uint32_t)d[3] << 16));
+  *reinterpret_cast<uint2*>(stg + c * WM + 4 * (q ^ stage_swz(c))) = make_uint2(lo, hi);
 }
 
 // two wavefronts per SIMD: the register budget of 8 wavefronts per CU, whatever the
@@ -573,20 +580,58 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
         const float mv[4] = {pa.x, pa.z, pb.x, pb.z};
         const float lv[4] = {pa.y, pa.w, pb.y, pb.w};
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-        const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+        const int dy[4] = {y4.x - lc0, y4.y - lc0, y4.z - lc0, y4.w - lc0};
+        // Every entry but the sampled token's is coef * exp(x - lse) =
+        // sign(coef) * exp2(x*log2e + c) with c = log2|coef| - M*log2e - log2 S
+        // per row: one fused step and one exp per entry.  The rounding of c
+        // scales a row's entries by one factor 2^d, |d| <= 2^-24 |c|, far
+        // below the bfloat16 result's resolution; coef = 0 gives c = -inf and
+        // exact zeros.  The sign goes onto the packed bfloat16 bits.
+        float cr[4];
+        uint32_t sg[2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          cr[r] = fmaf(-mv[r], kL2E, __builtin_amdgcn_logf(fabsf(cv[r])) - lv[r]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          sg[h] = ((__builtin_bit_cast(uint32_t, cv[2 * h]) >> 16) & 0x8000u) |
+                  (__builtin_bit_cast(uint32_t, cv[2 * h + 1]) & 0x80000000u);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int lc = lc0 + j * 16;
-          uint16_t d[4];
+          const bool live = kFull || lc0 + j * 16 < ncols;
+          float e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            e[r] = live ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, cr[r])) : 0.0f;
+          stage_pair(stg, lane, i, j, bf16x2_bits(e[0], e[1]) | sg[0],
+                     bf16x2_bits(e[2], e[3]) | sg[1]);
+        }
+        // the sampled token's entry, coef * (p - 1), is rewritten in the
+        // stage by the one lane holding it (a rare, divergent store after the
+        // lane's own quad write)
+        bool hit[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hit[r] = (unsigned)dy[r] < (unsigned)WN && (dy[r] & 15) == 0;
+        if (hit[0] || hit[1] || hit[2] || hit[3]) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            // exp(x - lse) = exp2((x - M)*log2e - log2 S): exact difference
-            // near the maximum, a small offset whatever the logits' scale
-            const float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r] - mv[r], kL2E, -lv[r]));
-            const float hit = lc == yv[r] ? 1.0f : 0.0f;
-            d[r] = (kFull || lc < ncols) ? bf16_bits(cv[r] * (p - hit)) : (uint16_t)0;
+            if (hit[r]) {
+              // a bitwise select (a variable index would send acc to scratch);
+              // each element is copied out first, since a bit cast of a vector
+              // element expression reads the vector's first element
+              uint32_t xb = 0;
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const float a = acc[i][j][r];
+                xb |= __builtin_bit_cast(uint32_t, a) & (dy[r] == 16 * j ? ~0u : 0u);
+              }
+              const float p =
+                  __builtin_amdgcn_exp2f(fmaf(__builtin_bit_cast(float, xb) - mv[r], kL2E, -lv[r]));
+              const int c = dy[r] + fr;  // column within the wavefront block
+              const int q = i * 4 + (lane >> 4);
+              stg[c * WM + 4 * (q ^ stage_swz(c)) + r] = bf16_bits(cv[r] * (p - 1.0f));
+            }
           }
-          stage_quad(stg, lane, i, j, d);
         }
       }
       __syncthreads();
@@ -643,11 +688,9 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
               if (ok(j, r)) c[r * ldc + j * 16] = old[j][r] + acc[i][j][r];
         } else {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const uint16_t d[4] = {bf16_bits(acc[i][j][0]), bf16_bits(acc[i][j][1]),
-                                   bf16_bits(acc[i][j][2]), bf16_bits(acc[i][j][3])};
-            stage_quad(stg, lane, i, j, d);
-          }
+          for (int j = 0; j < FN; ++j)
+            stage_pair(stg, lane, i, j, bf16x2_bits(acc[i][j][0], acc[i][j][1]),
+                       bf16x2_bits(acc[i][j][2], acc[i][j][3]));
         }
       }
       if constexpr (MODE == GM_STORE) {
