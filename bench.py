@@ -328,6 +328,7 @@ def main():
     torch.cuda.synchronize()
     lens = aux["len"].cpu().numpy()
     adv = aux["adv"].cpu().numpy()
+    stats = aux["stats"].cpu().numpy()
     n_act, n_inact, alg_bytes, per_act, per_inact = _alg_bytes(cfg, adv, lens)
 
     for _ in range(args.warmup):
@@ -341,21 +342,39 @@ def main():
         e0.record()
         e1.record()
     torch.cuda.synchronize()
+    # whole-call events between the calls (median / min per call)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
     for k in range(args.steps):
+        cev[k].record()
         dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, rows_events=evs[k], **kw)
+    cev[args.steps].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+    call_ms = [cev[k].elapsed_time(cev[k + 1]) for k in range(args.steps)]
     rows_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     rows_ms_avg = float(np.mean(rows_ms))
     if dr.device_status(ws) != dr.OK:
         raise SystemExit("device status not OK")
+    # a plain device copy of the logits into the dlogits buffer on the same
+    # box (read + write of N*C*V elements), after the timed region
+    copy_bytes = 2 * logits.numel() * logits.element_size()
+    for _ in range(2):
+        dlogits.copy_(logits)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dlogits.copy_(logits)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = copy_bytes / (c0.elapsed_time(c1) / 5 / 1e3) / 1e9
 
     tok_s = cfg.T / (ms_step / 1e3)
     achieved = alg_bytes / (rows_ms_avg / 1e3) / 1e9
@@ -382,6 +401,22 @@ def main():
                      "alg_bytes_per_launch": alg_bytes, "bytes_per_active_row": per_act,
                      "bytes_per_inactive_row": per_inact},
         "step_gbps_alg": alg_bytes / (ms_step / 1e3) / 1e9,
+        "call_ms_median": float(np.median(call_ms)),
+        "call_ms_min": float(np.min(call_ms)),
+        "k_rows_ms_median": float(np.median(rows_ms)),
+        "k_rows_ms_min": float(np.min(rows_ms)),
+        "valid_tokens_per_s": float(stats[4]) / (ms_step / 1e3),
+        "copy_ref": {"gbps": copy_gbps, "bytes_per_call": copy_bytes,
+                     "how": "torch copy_ of the logits tensor into the dlogits tensor",
+                     "k_rows_frac_of_copy": achieved / copy_gbps},
+        "rollout_stats": {
+            "groups": cfg.B, "groups_without_contrast": int(stats[0]),
+            "contrast_frac": 1.0 - float(stats[0]) / cfg.B,
+            "useful_groups_per_s": (cfg.B - float(stats[0])) / (ms_step / 1e3),
+            "rows_without_eos": int(stats[1]), "truncation_rate": float(stats[1]) / cfg.N,
+            "mean_completion_len": float(stats[4]) / cfg.N, "counted_tokens": int(stats[4]),
+            "active_tokens": int(stats[5]), "ratio_outside_clip": int(stats[2]),
+            "clip_cut_tokens": int(stats[3])},
         "wall_s_timed": wall,
         "device": torch.cuda.get_device_name(0),
     }

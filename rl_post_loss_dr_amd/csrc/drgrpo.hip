@@ -90,11 +90,12 @@ __device__ inline RowOut row_out(char* row, uint32_t bytes) {
   return RowOut{__builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)bytes, kRawBufferWord3)};
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// a and b rounded to bfloat16 (nearest even), a in the low half: one
+// v_cvt_pk_bf16_f32 (a vector conversion; scalar ones take one each)
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 ha = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
-  const __bf16 hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -130,6 +131,12 @@ struct Io<DRGRPO_BF16, 8> {
     const uint32_t w = pack_bf16x2(val, val);
     return u32x4{w, w, w, w};
   }
+  // element idx of the row set to val (rounded to nearest even)
+  __device__ static void store_one(const RowOut& o, int64_t idx, float val) {
+    const __bf16 h = (__bf16)val;
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), o.rsrc, (int)(idx * 2),
+                                          0, kStorePolicy);
+  }
 };
 
 // binary32, 4 per 16-byte chunk
@@ -156,6 +163,10 @@ struct Io<DRGRPO_F32, 4> {
     const uint32_t w = __float_as_uint(val);
     return u32x4{w, w, w, w};
   }
+  __device__ static void store_one(const RowOut& o, int64_t idx, float val) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), o.rsrc, (int)(idx * 4), 0,
+                                          kStorePolicy);
+  }
 };
 
 // bfloat16, one element per access (rows not 16-byte aligned)
@@ -180,6 +191,9 @@ struct Io<DRGRPO_BF16, 1> {
     const __bf16 h = (__bf16)val;
     return __builtin_bit_cast(uint16_t, h);
   }
+  __device__ static void store_one(const RowOut& o, int64_t idx, float val) {
+    store(o, (uint32_t)idx, splat(val));
+  }
 };
 
 // binary32, one element per access (rows not 16-byte aligned)
@@ -199,6 +213,9 @@ struct Io<DRGRPO_F32, 1> {
                                           kStorePolicy);
   }
   __device__ static chunk splat(float val) { return val; }
+  __device__ static void store_one(const RowOut& o, int64_t idx, float val) {
+    store(o, (uint32_t)idx, val);
+  }
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -245,11 +262,12 @@ __device__ inline void lse_chunk(float& m, float& s, const float (&f)[VEC]) {
   const float nm = fmaxf(m, cm);
   const float base = nm == -INFINITY ? 0.0f : nm;  // nothing finite seen yet
   // exp(x - base) with the difference taken first: exact for the entries
-  // near the maximum that dominate the sum (an fma of x*log2e against
-  // base*log2e would round at the argument's magnitude, ~1e-6 absolute)
-  float cs = 0.0f;
+  // near the maximum that dominate the sum, and exactly 1 at the maximum (so
+  // a one-entry vocabulary gives log-prob 0 exactly; a fused x*log2e -
+  // base*log2e would leave that product's rounding)
+  float cs = fast_exp2((f[0] - base) * kLog2e);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) cs += fast_exp2((f[e] - base) * kLog2e);
+  for (int e = 1; e < VEC; ++e) cs += fast_exp2((f[e] - base) * kLog2e);
   s = s * fast_exp2((m - base) * kLog2e) + cs;
   m = nm;
 }
@@ -257,21 +275,23 @@ __device__ inline void lse_chunk(float& m, float& s, const float (&f)[VEC]) {
 // Pass 2 of a row: dlogits = coef * (softmax - onehot), with |coef| folded
 // into the exponent and the sign of coef applied to the packed result bits:
 // |coef| * exp(x - lse) = exp2((x - M)*log2e - off2) with M the row maximum
-// (a binary32 logit, so x - M is exact for the entries that matter) and
-// off2 = log2(S) - log2|coef| small (lse = M + ln S), which keeps the
-// exponent accurate to ~1e-6 whatever the logits' magnitude.  Each register tile is
+// (lse = M + ln S) and off2 = log2 S - log2|coef|.  Binary32 results take the
+// difference first (x - M is exact for the entries that matter, accurate to
+// ~1e-6 relative whatever the logits' magnitude); bfloat16 results take one
+// fused step, exp2(x*log2e + c2) with c2 = -M*log2e - off2 formed in binary64
+// and rounded once, which scales the row by one factor 2^d, |d| <= 2^-24 |c2|
+// (below 1e-4 relative for |M| up to 10^4, under the bfloat16 rounding).
+// Each register tile is
 // converted in place, then stored as one burst of 16-byte stores (the
 // stores of a tile leave back to back instead of one per converted chunk,
 // measured 2-3% faster).
 template <typename IO, int VEC>
 __device__ __attribute__((always_inline)) inline void write_dlogits(
     typename IO::chunk (&buf)[kNch], const char* in, const RowOut& out, uint32_t nchunks,
-    uint32_t ntiles, int tid, float mrow, float off2, float dy, bool neg, int64_t y) {
+    uint32_t ntiles, int tid, float mrow, float off2, float c2, float dy, bool neg, int64_t y) {
   const uint32_t tile = (uint32_t)kNch * kThreads;
   const uint32_t last = nchunks - 1;
   const uint32_t cy = (uint32_t)(y / VEC);
-  const int ey = (int)(y - (int64_t)cy * VEC);
-  const float dy_pre = neg ? -dy : dy;  // the sign flip below restores it
   const uint32_t sign = neg ? 0xFFFFFFFFu : 0u;
   for (uint32_t k = 0; k < ntiles; ++k) {
     const uint32_t tb = k * tile;
@@ -284,18 +304,18 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
     }
     // slot and lane holding the sampled token's chunk in this tile
     const bool here = cy >= tb && cy - tb < tile;
-    const int js = here ? (int)((cy - tb) / kThreads) : -1;
     const int owner = here ? (int)((cy - tb) % kThreads) : -1;
 #pragma unroll
     for (int j = 0; j < kNch; ++j) {
       if (tb + (uint32_t)j * kThreads < nchunks) {
         float f[VEC];
         IO::unpack(buf[j], f);
+        if constexpr (IO::kBytes == 2) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) f[e] = fast_exp2(fmaf(f[e] - mrow, kLog2e, -off2));
-        if (j == js && tid == owner) {  // the sampled token: coef * (p_y - 1)
+          for (int e = 0; e < VEC; ++e) f[e] = fast_exp2(fmaf(f[e], kLog2e, c2));
+        } else {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) f[e] = e == ey ? dy_pre : f[e];
+          for (int e = 0; e < VEC; ++e) f[e] = fast_exp2(fmaf(f[e] - mrow, kLog2e, -off2));
         }
         buf[j] = IO::pack(f, sign);
       }
@@ -305,6 +325,10 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
       const uint32_t c = tb + (uint32_t)j * kThreads + tid;
       if (c < nchunks) IO::store(out, c, buf[j]);
     }
+    // the sampled token's entry, coef * (p_y - 1), rewritten by the lane that
+    // stored its chunk (its later store to the same address lands last), so
+    // no lane pays a select per entry
+    if (tid == owner) IO::store_one(out, y, dy);
   }
 }
 
@@ -401,7 +425,7 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
   }
   __shared__ float sh_m[kWaves];
   __shared__ float sh_s[kWaves];
-  __shared__ float sh_coef, sh_m_row, sh_off2, sh_dy;
+  __shared__ float sh_coef, sh_m_row, sh_off2, sh_c2, sh_dy;
   __shared__ bool sh_neg;
   if (lane == 0) {
     sh_m[wave] = m;
@@ -446,6 +470,7 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
       sh_neg = coef < 0.0;
       sh_m_row = M;
       sh_off2 = (float)(log2(term) - log2(fabs(coef)));
+      sh_c2 = (float)(log2(fabs(coef)) - log2(term) - (double)M * (double)kLog2e);
       sh_dy = (float)(coef * expm1(logp));
     }
   }
@@ -459,8 +484,8 @@ __global__ void __launch_bounds__(kThreads) k_rows(RowArgs a) {
     for (uint32_t c = tid; c < nchunks; c += kThreads) IO::store(out, c, zero);
     return;
   }
-  write_dlogits<IO, VEC>(buf, in, out, nchunks, ntiles, tid, sh_m_row, sh_off2, sh_dy, sh_neg,
-                         y);
+  write_dlogits<IO, VEC>(buf, in, out, nchunks, ntiles, tid, sh_m_row, sh_off2, sh_c2, sh_dy,
+                         sh_neg, y);
 }
 
 

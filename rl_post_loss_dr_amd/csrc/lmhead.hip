@@ -230,28 +230,29 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // stores local.
   // The grid covers the static row bound; only the tiles of the first M rows
   // (M read on the device) take part, spread evenly over the XCDs.
-  const int64_t ntm = (M + GBM - 1) / GBM;
-  const int64_t ntn_t = (g.N + GBN - 1) / GBN;
-  const int64_t total = ntm * ntn_t;
-  const int64_t b = blockIdx.x;
+  // (32-bit index arithmetic: the host keeps the grid below 2^31 workgroups)
+  const int ntm = (int)((M + GBM - 1) / GBM);
+  const int ntn_t = (int)((g.N + GBN - 1) / GBN);
+  const int total = ntm * ntn_t;
+  const int b = blockIdx.x;
   if (b >= total) return;
-  const int64_t q8 = total / 8;
-  const int64_t v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
+  const int q8 = total / 8;
+  const int v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
   constexpr bool kColsFastest = MODE == GM_ACC || MODE == GM_STORE;
-  int64_t tm, tn;
+  int tm, tn;
   if constexpr (MODE == GM_LSE) {
-    constexpr int64_t kColGroup = 8;
-    const int64_t grouped = (ntn_t / kColGroup) * kColGroup * ntm;
-    const int64_t gw = v < grouped ? kColGroup : ntn_t % kColGroup;  // width of v's group
-    const int64_t w = v < grouped ? v % (kColGroup * ntm) : v - grouped;
+    constexpr int kColGroup = 8;
+    const int grouped = (ntn_t / kColGroup) * kColGroup * ntm;
+    const int gw = v < grouped ? kColGroup : ntn_t % kColGroup;  // width of v's group
+    const int w = v < grouped ? v % (kColGroup * ntm) : v - grouped;
     tm = w / gw;
     tn = (v < grouped ? v / (kColGroup * ntm) * kColGroup : grouped / ntm) + w % gw;
   } else {
     tm = kColsFastest ? v / ntn_t : v % ntm;
     tn = kColsFastest ? v % ntn_t : v / ntm;
   }
-  const int64_t m0 = tm * GBM;
-  const int64_t n0 = tn * GBN;
+  const int64_t m0 = (int64_t)tm * GBM;
+  const int64_t n0 = (int64_t)tn * GBN;
 
   // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
   // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled

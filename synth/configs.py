@@ -110,6 +110,12 @@ LMHEAD = _add(Config(
     eos_rows=_round_half_even(0.7 * 64), p=0.2, old_noise=0.02, seed=20261202 + 5))
 
 NAMED = ["tiny_fp32", "qwen_b8g8c256", "qwen_b8g16c512", "qwen_kl_b16g8c1024", "lmhead_b8g8c512"]
+# Dense mode of the B=8, G=8, C=256 batch: no EOS and Bernoulli(0.5) rewards
+# (this seed leaves no group without contrast), so every token row is active
+# and carries the full 4V bytes: the raw streaming rate of the row kernel.
+QWEN_DENSE = _add(Config(
+    name="qwen_dense_b8g8c256", B=8, G=8, C=256, V=QWEN_V, eos_rows=0, p=0.5, old_noise=0.02,
+    seed=20261202 + 6))
 
 # Parity-only cases the oracle finishes in seconds: several vocab tiles and a
 # ragged tail, every edge the method has.

@@ -16,7 +16,7 @@ from _cases import compare_dlogits, compare_loss, f32, oracle_logp_all, tol
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-FULL = ["qwen_b8g8c256", "qwen_b8g16c512", "qwen_kl_b16g8c1024"]
+FULL = ["qwen_b8g8c256", "qwen_b8g16c512", "qwen_kl_b16g8c1024", "qwen_dense_b8g8c256"]
 
 
 def _sample_rows(cfg, res, k=48):

@@ -124,6 +124,15 @@ def test_bernoulli_no_contrast_frequency(p, G):
         assert round(n / M, 2) == 0.66  # the pages' "about two-thirds"
 
 
+def test_dense_workload_has_every_row_active():
+    """The dense-mode batch (no EOS, Bernoulli(0.5) rewards) leaves no token
+    row inactive: every completion runs to C and every group has contrast."""
+    cfg = synth.get_config("qwen_dense_b8g8c256")
+    case = synth.make_case(cfg)
+    assert (oracle.completion_len(case.tokens, cfg.eos_id) == cfg.C).all()
+    assert (oracle.group_advantage(case.rewards, cfg.G) != 0).all()
+
+
 # ---------------------------------------------------------------- log-probs
 def test_logprob_normalises_and_is_nonpositive():
     rng = np.random.default_rng(1)
