@@ -35,7 +35,10 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it; no call synchronises except
  *     drgrpo_device_status.  Results are valid once the stream has reached
- *     the end of the call.
+ *     the end of the call.  Every call except drgrpo_device_status only
+ *     enqueues kernels (no memset, no host synchronisation, no host read of
+ *     device data), so it can be captured into a HIP graph and replayed; the
+ *     workspace is re-initialised by the captured kernels themselves.
  *   - Host-side argument errors are returned before anything is enqueued.
  *   - Layouts are dense row-major: logits/dlogits [N, C, V]; tokens, logp_old,
  *     logp_ref [N, C]; rewards [N].

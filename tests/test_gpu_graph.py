@@ -1,0 +1,108 @@
+"""The loss entry points captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed, as a training or rollout loop would issue them: every replay equals
+the eager call bit for bit, with eager work and synchronisations between
+replays and the outputs overwritten before each replay.  The library only
+launches kernels (no memset, no host synchronisation; the workspace state is
+cleared by its own kernels), which is what makes the capture valid."""
+import numpy as np
+import pytest
+import torch
+
+import rl_post_loss_dr_amd as dr
+from _cases import lm_case, small_case, to_device_logits
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph; returns the
+    graph and what the captured call returned."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        res = fn()
+    return graph, res
+
+
+def _bits_to_dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mini_kl_bf16", "ragged_bf16"])
+def test_loss_graph_replay(name):
+    print(f"case {name}", flush=True)
+    cfg, case, x, old, ref, _ = small_case(name)
+    logits = to_device_logits(x, cfg, DEV)
+    tokens = torch.from_numpy(case.tokens).to(DEV)
+    rewards = torch.from_numpy(case.rewards).to(DEV)
+    lo = torch.from_numpy(old).to(DEV)
+    lr = None if ref is None else torch.from_numpy(ref).to(DEV)
+    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const)
+    ws = dr.make_workspace(cfg.N, cfg.C, cfg.V, cfg.G, DEV)
+    loss_e, d_e = dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, lo, lr, workspace=ws, **kw)
+    loss_e, d_e = loss_e.clone(), d_e.clone()
+    d_g = torch.empty_like(d_e)
+    ws_g = dr.make_workspace(cfg.N, cfg.C, cfg.V, cfg.G, DEV)
+    graph, (loss_g, _) = _capture(lambda: dr.loss_fwd_bwd(
+        logits, tokens, cfg.eos_id, rewards, lo, lr, out_dlogits=d_g, workspace=ws_g, **kw))
+    flipped = rewards.flip(0).contiguous()
+    for _ in range(4):
+        d_g.fill_(1.0)
+        loss_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss_g, loss_e)
+        assert torch.equal(d_g, d_e)
+        # eager work between replays, on the other workspace
+        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, flipped, lo, lr, workspace=ws, **kw)
+        torch.cuda.synchronize()
+    assert dr.device_status(ws_g) == dr.OK
+
+
+def test_lmhead_graph_replay():
+    """Fused lm_head loss (compaction, chunked products, device-side active
+    count) and its forward-only log-probs, each replayed from a graph."""
+    cfg, case, hb, Wb, old, ref, _ = lm_case("lmhead_multi")
+    hidden, W = _bits_to_dev(hb), _bits_to_dev(Wb)
+    tokens = torch.from_numpy(case.tokens).to(DEV)
+    rewards = torch.from_numpy(case.rewards).to(DEV)
+    lo = torch.from_numpy(old).to(DEV)
+    lr = None if ref is None else torch.from_numpy(ref).to(DEV)
+    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const)
+    ws_bytes = dr.lmhead_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H, cfg.G)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    loss_e, dh_e, dW_e = dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, lo, lr,
+                                                 workspace=ws, **kw)
+    loss_e, dh_e, dW_e = loss_e.clone(), dh_e.clone(), dW_e.clone()
+    lp_e = dr.lmhead_logprobs(hidden, W, tokens, cfg.eos_id).clone()
+
+    dh_g, dW_g = torch.empty_like(dh_e), torch.empty_like(dW_e)
+    ws_g = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    graph, (loss_g, _, _) = _capture(lambda: dr.lmhead_loss_fwd_bwd(
+        hidden, W, tokens, cfg.eos_id, rewards, lo, lr, out_dhidden=dh_g, out_dW=dW_g,
+        workspace=ws_g, **kw))
+    ws_lp = torch.empty(dr.lmhead_logprobs_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H),
+                        dtype=torch.uint8, device=DEV)
+    graph_lp, lp_g = _capture(lambda: dr.lmhead_logprobs(hidden, W, tokens, cfg.eos_id,
+                                                         workspace=ws_lp))
+    for _ in range(3):
+        dh_g.fill_(1.0)
+        dW_g.fill_(1.0)
+        loss_g.fill_(float("nan"))
+        lp_g.fill_(1.0)
+        graph.replay()
+        graph_lp.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss_g, loss_e)
+        assert torch.equal(dh_g, dh_e) and torch.equal(dW_g, dW_e)
+        assert torch.equal(lp_g, lp_e)
+        # eager work between replays, on the other workspace
+        dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards.flip(0).contiguous(), lo,
+                               lr, workspace=ws, **kw)
+        torch.cuda.synchronize()
