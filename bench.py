@@ -262,6 +262,112 @@ def run_decode(name, args):
     }
 
 
+def run_rollout(name, args):
+    """The rollout step with the decode attention integrated: one decode step
+    of a Qwen2.5-0.5B-shaped policy (24 layers, random weights) for S
+    sequences at L cached positions, eager and replayed from a captured graph,
+    beside the attention call alone on a layer's cache of the same shape."""
+    import torch
+
+    import rl_post_loss_dr_amd as dr
+    from rl_post_loss_dr_amd.rollout import QWEN25_05B, DecodePolicy
+
+    sizes = {"rollout_s64_l512": (64, 512)}
+    if name not in sizes:
+        raise SystemExit(f"unknown rollout workload {name}: {sorted(sizes)}")
+    S, L = sizes[name]
+    sh = QWEN25_05B
+    dev = torch.device("cuda:0")
+    pol = DecodePolicy(sh, S, L + 64, seed=7401, device=dev)
+    pol.fill_cache(7402)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7403)
+    tok = torch.randint(0, sh.vocab, (S,), device=dev, generator=g)
+    # every step writes position L-1 and attends over L positions (the same
+    # work each time; a rollout advances the position, which the graph test
+    # covers)
+    pos = torch.full((S,), L - 1, dtype=torch.int32, device=dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        pol.step(tok, pos)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        pol.step(tok, pos)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pol.step(tok, pos)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pol.step(tok, pos)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # the attention call alone on layer 0's cache (graph of 20 calls replayed)
+    q = torch.randn((S, sh.heads, sh.head_dim), generator=g, device=dev).to(torch.bfloat16)
+    lens = pos + 1
+    ws = torch.empty(dr.decode_attention_workspace_bytes(S, sh.heads, sh.kv_heads, L + 64,
+                                                         sh.head_dim),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    args_a = (q, pol.k_cache[0], pol.v_cache[0], lens)
+    dr.decode_attention(*args_a, workspace=ws, out=out)
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        for _ in range(20):
+            dr.decode_attention(*args_a, workspace=ws, out=out)
+    ga.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(5):
+        ga.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    attn_ms = ev0.elapsed_time(ev1) / 100
+    # algorithmic bytes per step: every weight once (the output projection is
+    # the tied embedding), the cached keys and values once, the new keys and
+    # values and the logits written
+    n_w = pol.embed.numel() + sum(t.numel() for L_ in pol.layers for t in L_.values()) + \
+        pol.ln_f.numel()
+    kv_read = sh.layers * 2 * S * sh.kv_heads * L * sh.head_dim * 2
+    alg = 2 * n_w + kv_read + sh.layers * 2 * S * sh.kv_heads * sh.head_dim * 2 + S * sh.vocab * 2
+    gbps = alg / (ms / 1e3) / 1e9
+    return {
+        "metric": "rollout decode step tokens/s (decode attention integrated)",
+        "value": S / (ms / 1e3), "unit": "decoded tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights of the Qwen2.5-0.5B shape; random cache)",
+        "config": {"workload": name, "S": S, "cached_positions": L, "layers": sh.layers,
+                   "hidden": sh.hidden, "heads": sh.heads, "kv_heads": sh.kv_heads,
+                   "head_dim": sh.head_dim, "vocab": sh.vocab},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "whole decode step (all layers), replayed from a captured graph",
+                     "alg_bytes_per_step": alg, "weight_bytes": 2 * n_w,
+                     "kv_cache_bytes_read": kv_read},
+        "ms_per_step_eager": ms_eager,
+        "attention_standalone_ms_per_layer": attn_ms,
+        "attention_standalone_share": sh.layers * attn_ms / ms,
+        "note": "ms_per_step: the step replayed from a captured graph; ms_per_step_eager: "
+                "launched op by op from Python; attention_standalone: the same call on one "
+                "layer's cache replayed alone (the in-loop kernel time is in the rocprofv3 "
+                "summary)",
+        "device": torch.cuda.get_device_name(0),
+    }
+
+
 def synth_perturb(lp, noise):
     import synth
 
@@ -303,6 +409,9 @@ def main():
 
     if args.workload.startswith("decode_"):
         print(json.dumps(run_decode(args.workload, args)), flush=True)
+        return
+    if args.workload.startswith("rollout_"):
+        print(json.dumps(run_rollout(args.workload, args)), flush=True)
         return
     cfg = synth.get_config(args.workload)
     case = synth.make_case(cfg)

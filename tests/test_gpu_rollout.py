@@ -1,0 +1,82 @@
+"""The decode attention integrated into a rollout step (a Qwen2.5-0.5B-shaped
+policy with random weights, fewer layers and a small vocabulary here): the
+step with the library's attention against the same step with a binary32
+reference attention, over several tokens at ragged positions; and the step
+captured into a HIP graph (next token and positions advanced inside the
+graph) against eager steps, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from rl_post_loss_dr_amd.rollout import DecodePolicy, PolicyShape
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+SMALL = PolicyShape(layers=2, vocab=4096)
+
+
+def _pair(S, Lmax, seed):
+    a = DecodePolicy(SMALL, S, Lmax, seed, DEV, std=0.05)
+    b = DecodePolicy(SMALL, S, Lmax, seed, DEV, std=0.05)
+    a.fill_cache(seed + 1)
+    b.fill_cache(seed + 1)
+    return a, b
+
+
+def test_rollout_step_library_vs_reference_attention():
+    S, Lmax = 6, 48
+    lib, ref = _pair(S, Lmax, 7301)
+    rng = np.random.default_rng(7301)
+    pos = torch.from_numpy(np.array([0, 1, 5, 17, 30, 40], dtype=np.int32)).to(DEV)
+    for t in range(6):
+        tok = torch.from_numpy(rng.integers(0, SMALL.vocab, S)).to(DEV)
+        la, _ = lib.step(tok, pos, attention="library")
+        lb, _ = ref.step(tok, pos, attention="reference")
+        torch.cuda.synchronize()
+        a, b = la.float().cpu().numpy(), lb.float().cpu().numpy()
+        assert np.isfinite(a).all()
+        # the two differ only by the attention's rounding (one bfloat16 ulp
+        # at most per output), carried through two layers into bfloat16
+        # logits, where such a difference flips many entries by one ulp
+        # (0.4-0.8% of the value); a wrong position, length or cache layout
+        # would change them by their own size
+        assert np.abs(a - b).max() <= 3e-2 * np.abs(b).max(), (t, np.abs(a - b).max())
+        assert np.abs(a - b).mean() <= 1e-2 * np.abs(b).mean(), (t, np.abs(a - b).mean())
+        pos = pos + 1
+    # the caches hold the same keys and values either way
+    assert torch.equal(lib.k_cache, ref.k_cache) or (
+        (lib.k_cache.float() - ref.k_cache.float()).abs().max() <= 3e-2 *
+        ref.k_cache.float().abs().max())
+
+
+def test_rollout_step_graph_replay():
+    S, Lmax = 8, 64
+    eager, graphed = _pair(S, Lmax, 7302)
+    tok0 = torch.from_numpy(np.random.default_rng(7302).integers(0, SMALL.vocab, S)).to(DEV)
+    pos0 = torch.arange(10, 10 + 3 * S, 3, dtype=torch.int32, device=DEV)
+    want = []
+    tok, pos = tok0.clone(), pos0.clone()
+    for _ in range(5):
+        logits, nxt = eager.step(tok, pos)
+        want.append(logits.clone())
+        tok, pos = nxt, pos + 1
+    torch.cuda.synchronize()
+
+    tok_s, pos_s = tok0.clone(), pos0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graphed.step(tok_s, pos_s)  # warm-up: rewrites the first step's cache entry
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        logits_g, nxt_g = graphed.step(tok_s, pos_s)
+        tok_s.copy_(nxt_g)
+        pos_s.add_(1)
+    for i in range(5):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits_g, want[i]), i
+        torch.empty(1 << 20, device=DEV).normal_()  # eager work between replays
+    assert torch.equal(pos_s, pos0 + 5)
