@@ -51,3 +51,77 @@ def decode_attention(q, k, v, lens, scale):
             out[s, h] = (p @ v[s, g, :L]) / z
             lse[s, h] = m + np.log(z)
     return out, lse
+
+
+# ------------------------------------------------------------------- rotary
+# The rollout step's attention block (same page and section): before the
+# scores, the new token's query and key head vectors are rotated by its
+# position (rotary position embedding, the rotate-half form of the
+# Qwen2.5-0.5B policy), the rotated key and the value are appended to the
+# cache at that position, and attention runs over position + 1 cached
+# positions.  For a head vector x of size D, pair i < D/2 is
+# (x_i, x_{i+D/2}) and is turned by the angle pos * theta_i:
+#     x'_i       = x_i cos - x_{i+D/2} sin
+#     x'_{i+D/2} = x_{i+D/2} cos + x_i sin
+# The library's definition computes this in binary32 with each product and
+# the sum rounded separately, then rounds to bfloat16 (the cache format);
+# rope_bf16 follows those steps, rope_f64 is the exact rotation.
+
+def rope_f64(x, cos, sin):
+    """x [..., D], cos / sin [..., D/2] broadcastable (binary64) -> rotated x."""
+    h = x.shape[-1] // 2
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round binary32 values to bfloat16 bits (nearest, ties to even; finite
+    inputs)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def rope_bf16(x_bits, cos32, sin32):
+    """x_bits [..., D] bfloat16 bits, cos32 / sin32 [..., D/2] binary32 ->
+    bfloat16 bits of the rotation, each product and the sum rounded to
+    binary32 (numpy's float32 arithmetic: IEEE single, no fused steps)."""
+    x = (np.ascontiguousarray(x_bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32)
+    h = x.shape[-1] // 2
+    a, b = x[..., :h], x[..., h:]
+    c, s = np.asarray(cos32, np.float32), np.asarray(sin32, np.float32)
+    lo = (a * c).astype(np.float32) - (b * s).astype(np.float32)
+    hi = (b * c).astype(np.float32) + (a * s).astype(np.float32)
+    return f32_to_bf16_bits(np.concatenate([lo, hi], axis=-1).astype(np.float32))
+
+
+def decode_attention_rope(qkv_bits, cos32, sin32, pos, k_bits, v_bits, Hq, Hkv, scale):
+    """The attention block of one decode step.  qkv_bits [S, (Hq + 2 Hkv) D]
+    bfloat16 bits (query heads, then key heads, then value heads), cos32 /
+    sin32 [Lmax, D/2] binary32 tables, pos [S], k_bits / v_bits
+    [S, Hkv, Lmax, D] bfloat16 bits of the cache before the step.  Returns
+    (out [S, Hq, D], lse [S, Hq], k_new, v_new): the binary64 attention of the
+    rotated (bfloat16) queries over pos + 1 positions, and the caches after
+    the append (bits).  A position outside [0, Lmax) appends nothing and its
+    sequence's output is NaN (no cached key)."""
+    S = qkv_bits.shape[0]
+    Lmax, D = k_bits.shape[2], k_bits.shape[3]
+    x = np.ascontiguousarray(qkv_bits, np.uint16).reshape(S, Hq + 2 * Hkv, D)
+    k_new = np.array(k_bits, dtype=np.uint16, copy=True)
+    v_new = np.array(v_bits, dtype=np.uint16, copy=True)
+    q_rot = np.empty((S, Hq, D), np.uint16)
+    lens = np.zeros(S, np.int64)
+    for s in range(S):
+        p = int(pos[s])
+        ok = 0 <= p < Lmax
+        cs = cos32[p] if ok else np.ones(D // 2, np.float32)
+        sn = sin32[p] if ok else np.zeros(D // 2, np.float32)
+        q_rot[s] = rope_bf16(x[s, :Hq], cs, sn)
+        if ok:
+            k_new[s, :, p] = rope_bf16(x[s, Hq:Hq + Hkv], cs, sn)
+            v_new[s, :, p] = x[s, Hq + Hkv:]
+            lens[s] = p + 1
+    out, lse = decode_attention(bf16_to_f64(q_rot), bf16_to_f64(k_new), bf16_to_f64(v_new), lens,
+                                scale)
+    return out, lse, k_new, v_new
