@@ -314,6 +314,22 @@ def run_rollout(name, args):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # the same step with the rotary embedding and the cache append in PyTorch
+    # around the plain attention call (graph-replayed as well)
+    with torch.cuda.stream(side):
+        pol.step(tok, pos, attention="library_unfused")
+    torch.cuda.current_stream().wait_stream(side)
+    graph_u = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_u):
+        pol.step(tok, pos, attention="library_unfused")
+    graph_u.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        graph_u.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_unfused = ev0.elapsed_time(ev1) / args.steps
     # the attention call alone on layer 0's cache (graph of 20 calls replayed)
     q = torch.randn((S, sh.heads, sh.head_dim), generator=g, device=dev).to(torch.bfloat16)
     lens = pos + 1
@@ -358,12 +374,16 @@ def run_rollout(name, args):
                      "alg_bytes_per_step": alg, "weight_bytes": 2 * n_w,
                      "kv_cache_bytes_read": kv_read},
         "ms_per_step_eager": ms_eager,
+        "ms_per_step_unfused_rope_append": ms_unfused,
         "attention_standalone_ms_per_layer": attn_ms,
         "attention_standalone_share": sh.layers * attn_ms / ms,
-        "note": "ms_per_step: the step replayed from a captured graph; ms_per_step_eager: "
-                "launched op by op from Python; attention_standalone: the same call on one "
-                "layer's cache replayed alone (the in-loop kernel time is in the rocprofv3 "
-                "summary)",
+        "note": "ms_per_step: the step replayed from a captured graph, its attention block "
+                "(rotary embedding, cache append, attention) one library call; "
+                "ms_per_step_eager: launched op by op from Python; "
+                "ms_per_step_unfused_rope_append: graph-replayed with the rotary embedding and "
+                "the append in PyTorch around the attention call; attention_standalone: the "
+                "attention call on one layer's cache replayed alone (the in-loop kernel times "
+                "are in the rocprofv3 summary)",
         "device": torch.cuda.get_device_name(0),
     }
 

@@ -281,6 +281,40 @@ int drgrpo_decode_attention(const void* q, const void* k_cache, const void* v_ca
                             int64_t D, float scale, void* out, float* out_lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* The attention block of the same decode step with the rotary position
+ * embedding and the cache append folded in (the step between the q/k/v
+ * projection and the output projection: the new token's keys and values are
+ * appended to the cache before it is read).  For sequence s with position
+ * p = pos[s] in [0, Lmax):
+ *   qkv      [S, (Hq + 2 Hkv) * D] bfloat16: the projection output, per
+ *            sequence Hq query heads, then Hkv key heads, then Hkv value
+ *            heads, each D contiguous (2-byte aligned).
+ *   rope_cos, rope_sin  [Lmax, D/2] float: cosine and sine of the angle of
+ *            pair i at each position (the caller's frequencies; Qwen2.5
+ *            uses p * base^(-2i/D), base 10^6).
+ *   pos      [S] int32 on the device.
+ *   Each head vector x is rotated in the rotate-half form: for i < D/2,
+ *     x'_i = x_i c - x_{i+D/2} s,  x'_{i+D/2} = x_{i+D/2} c + x_i s
+ *   with (c, s) = (rope_cos[p, i], rope_sin[p, i]), in binary32 with each
+ *   product and the sum rounded separately, then rounded to bfloat16 (nearest
+ *   even).  The rotated key heads and the value heads are written to
+ *   k_cache / v_cache at [s, g, p] (nothing else in the caches changes), and
+ *   out[s] is drgrpo_decode_attention of the rotated queries over p + 1
+ *   cached positions (same layouts, scale, out_lse and accuracy).  A
+ *   position outside [0, Lmax) writes nothing and gives a NaN output row.
+ * Errors as drgrpo_decode_attention (caches and out 16-byte aligned); the
+ * workspace (drgrpo_decode_attention_rope_workspace_bytes, 256-byte aligned)
+ * also holds the rotated queries and the lengths.  Only enqueues kernels;
+ * calls that share a workspace or a cache must not overlap. */
+size_t drgrpo_decode_attention_rope_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv,
+                                                    int64_t Lmax, int64_t D);
+
+int drgrpo_decode_attention_rope(const void* qkv, const float* rope_cos, const float* rope_sin,
+                                 const int32_t* pos, int64_t S, int64_t Hq, int64_t Hkv,
+                                 int64_t Lmax, int64_t D, float scale, void* k_cache,
+                                 void* v_cache, void* out, float* out_lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then reads the status word the last
  * drgrpo_loss_fwd_bwd call on `workspace` left: DRGRPO_OK or
  * DRGRPO_ERR_TOKEN_RANGE (DRGRPO_ERR_HIP if the read fails). */

@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
         L.drgrpo_decode_attention.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F,
                                               _P, _P, _P, _SZ, _P]
         L.drgrpo_decode_attention.restype = _I
+        L.drgrpo_decode_attention_rope_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64]
+        L.drgrpo_decode_attention_rope_workspace_bytes.restype = _SZ
+        L.drgrpo_decode_attention_rope.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                                   _F, _P, _P, _P, _P, _P, _SZ, _P]
+        L.drgrpo_decode_attention_rope.restype = _I
         L.drgrpo_device_status.argtypes = [_P, _P]
         L.drgrpo_device_status.restype = _I
         L.drgrpo_status_string.argtypes = [_I]
@@ -388,6 +393,49 @@ def decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(), S, Hq, Hkv, Lmax,
         D, float(scale), out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(),
         _stream(dev)), "drgrpo_decode_attention")
+    return (out, lse) if want_lse else out
+
+
+def decode_attention_rope_workspace_bytes(S: int, Hq: int, Hkv: int, Lmax: int, D: int) -> int:
+    return int(lib().drgrpo_decode_attention_rope_workspace_bytes(S, Hq, Hkv, Lmax, D))
+
+
+def decode_attention_rope(qkv: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                          pos: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, Hq: int,
+                          scale: float | None = None, want_lse: bool = False,
+                          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """The decode step's attention block: rotary embedding of the new token's
+    query and key heads (rotate-half form), append of its key and value to
+    the caches at pos, then decode attention over pos + 1 positions.
+
+    qkv [S, (Hq + 2 Hkv) * D] bfloat16 (query, key, value heads), rope_cos /
+    rope_sin [Lmax, D/2] float32, pos [S] int32, caches [S, Hkv, Lmax, D]
+    bfloat16 (updated in place).  Returns out [S, Hq, D] bfloat16 (and the
+    float32 log-sum-exp when want_lse)."""
+    S, Hkv, Lmax, D = k_cache.shape
+    dev = k_cache.device
+    _dev(k_cache, "k_cache", torch.bfloat16)
+    _dev(v_cache, "v_cache", torch.bfloat16, (S, Hkv, Lmax, D))
+    _dev(qkv, "qkv", torch.bfloat16, (S, (Hq + 2 * Hkv) * D))
+    _dev(rope_cos, "rope_cos", torch.float32, (Lmax, D // 2))
+    _dev(rope_sin, "rope_sin", torch.float32, (Lmax, D // 2))
+    _dev(pos, "pos", torch.int32, (S,))
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if workspace is None:
+        n = decode_attention_rope_workspace_bytes(S, Hq, Hkv, Lmax, D)
+        if n == 0:
+            raise DrGRPOError(ERR_SHAPE, "drgrpo_decode_attention_rope_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _dev(out, "out", torch.bfloat16, (S, Hq, D))
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    _check(lib().drgrpo_decode_attention_rope(
+        qkv.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(), pos.data_ptr(), S, Hq, Hkv,
+        Lmax, D, float(scale), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), _ptr(lse),
+        workspace.data_ptr(), workspace.numel(), _stream(dev)), "drgrpo_decode_attention_rope")
     return (out, lse) if want_lse else out
 
 

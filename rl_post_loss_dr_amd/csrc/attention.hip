@@ -381,6 +381,8 @@ __global__ void __launch_bounds__(1024) k_attn_combine(AttnArgs a) {
 
 int attn_launch_status() { return hipGetLastError() == hipSuccess ? DRGRPO_OK : DRGRPO_ERR_HIP; }
 
+inline size_t attn_align(size_t x) { return (x + 255) & ~size_t(255); }  // 256-byte carve-up
+
 template <int D>
 void launch_combine(const AttnArgs& a, hipStream_t st) {
   constexpr int kHeadsPerBlock = 1024 / D;
@@ -433,6 +435,94 @@ int attn_check(int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D) {
   return DRGRPO_OK;
 }
 
+// ------------------------------------------------- rotary embedding + append
+// The attention block of the rollout step ("Making Dr GRPO go brrr", section
+// "What is RL post-training, and why is it slow": one forward pass per
+// generated token with a growing KV cache).  One workgroup per sequence: each
+// query head vector of the projection output is rotated by the token's
+// position into q_rot; each key head is rotated and written to the key cache
+// at [s, g, pos_s]; each value head is copied to the value cache there;
+// lens[s] = pos_s + 1.  Rotate-half form: pair i < D/2 is (x_i, x_{i+D/2})
+// turned by the angle whose cosine and sine the tables hold, in binary32 with
+// each product and the sum rounded separately (no fused steps), then rounded
+// to bfloat16.  A position outside [0, Lmax) writes nothing, rotates the
+// queries by angle 0 and gives lens = 0 (the attention output is then NaN).
+template <int D>
+__global__ void __launch_bounds__(256)
+k_rope_append(const uint16_t* __restrict__ qkv, const float* __restrict__ rcos,
+              const float* __restrict__ rsin, const int32_t* __restrict__ pos, int Hq, int Hkv,
+              int64_t Lmax, uint16_t* __restrict__ q_rot, uint16_t* __restrict__ kc,
+              uint16_t* __restrict__ vc, int32_t* __restrict__ lens) {
+#pragma clang fp contract(off)
+  constexpr int kHalf = D / 2;
+  const int64_t s = blockIdx.x;
+  const int32_t p = pos[s];
+  const bool ok = p >= 0 && p < Lmax;
+  const uint16_t* x = qkv + s * (Hq + 2 * Hkv) * D;
+  if (threadIdx.x == 0) lens[s] = ok ? p + 1 : 0;
+  for (int w = threadIdx.x; w < (Hq + Hkv) * kHalf; w += blockDim.x) {
+    const int h = w / kHalf, i = w % kHalf;
+    const float a = __uint_as_float((uint32_t)x[h * D + i] << 16);
+    const float b = __uint_as_float((uint32_t)x[h * D + i + kHalf] << 16);
+    const float c = ok ? rcos[p * kHalf + i] : 1.0f;
+    const float sn = ok ? rsin[p * kHalf + i] : 0.0f;
+    const float ac = a * c, bs = b * sn, bc = b * c, as = a * sn;
+    const uint16_t lo = to_bf16(ac - bs), hi = to_bf16(bc + as);
+    if (h < Hq) {
+      uint16_t* dst = q_rot + (s * Hq + h) * D;
+      dst[i] = lo;
+      dst[i + kHalf] = hi;
+    } else if (ok) {
+      uint16_t* dst = kc + ((s * Hkv + (h - Hq)) * Lmax + p) * D;
+      dst[i] = lo;
+      dst[i + kHalf] = hi;
+    }
+  }
+  if (ok) {
+    for (int w = threadIdx.x; w < Hkv * D; w += blockDim.x) {
+      const int g = w / D, e = w % D;
+      vc[((s * Hkv + g) * Lmax + p) * D + e] = x[(Hq + Hkv + g) * D + e];
+    }
+  }
+}
+
+// The attention launches for checked arguments (plan, fused kernel, combine).
+int attn_run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* lens,
+             int64_t S, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, float* part,
+             uint16_t* out, float* out_lse, hipStream_t st) {
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lens = lens;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Lmax = Lmax;
+  a.scale = scale;
+  const AttnPlan plan = attn_plan(S, Hkv, Lmax, D);
+  a.nsplit = plan.nsplit;
+  a.chunk = plan.chunk;
+  a.part = part;
+  a.out = out;
+  a.out_lse = out_lse;
+  const unsigned blocks = (unsigned)(S * Hkv * a.nsplit);
+  if (D == 64 && plan.nw == 16)
+    hipLaunchKernelGGL((k_attn_fused<64, 16>), dim3(blocks), dim3(64 * 16), 0, st, a);
+  else if (D == 64)
+    hipLaunchKernelGGL((k_attn_fused<64, 8>), dim3(blocks), dim3(64 * 8), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn_fused<128, 8>), dim3(blocks), dim3(64 * 8), 0, st, a);
+  if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
+  if (a.nsplit > 1) {
+    if (D == 64)
+      launch_combine<64>(a, st);
+    else
+      launch_combine<128>(a, st);
+  }
+  return attn_launch_status();
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -457,36 +547,49 @@ extern "C" int drgrpo_decode_attention(const void* q, const void* k_cache, const
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
       workspace_bytes < drgrpo_decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D))
     return DRGRPO_ERR_WORKSPACE;
-  AttnArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_cache);
-  a.v = static_cast<const uint16_t*>(v_cache);
-  a.lens = lens;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.Lmax = Lmax;
-  a.scale = scale;
-  const AttnPlan plan = attn_plan(S, Hkv, Lmax, D);
-  a.nsplit = plan.nsplit;
-  a.chunk = plan.chunk;
-  a.part = static_cast<float*>(workspace);
-  a.out = static_cast<uint16_t*>(out);
-  a.out_lse = out_lse;
+  return attn_run(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                  static_cast<const uint16_t*>(v_cache), lens, S, Hq, Hkv, Lmax, D, scale,
+                  static_cast<float*>(workspace), static_cast<uint16_t*>(out), out_lse,
+                  static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t drgrpo_decode_attention_rope_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv,
+                                                               int64_t Lmax, int64_t D) {
+  const size_t a = drgrpo_decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D);
+  if (a == 0) return 0;
+  return attn_align(a) + attn_align((size_t)(S * Hq * D) * 2) + attn_align((size_t)S * 4);
+}
+
+extern "C" int drgrpo_decode_attention_rope(const void* qkv, const float* rope_cos,
+                                            const float* rope_sin, const int32_t* pos, int64_t S,
+                                            int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D,
+                                            float scale, void* k_cache, void* v_cache, void* out,
+                                            float* out_lse, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (!qkv || !rope_cos || !rope_sin || !pos || !k_cache || !v_cache || !out)
+    return DRGRPO_ERR_NULL;
+  const int sh = attn_check(S, Hq, Hkv, Lmax, D);
+  if (sh != DRGRPO_OK) return sh;
+  if (!(scale > 0.0f) || scale - scale != 0.0f) return DRGRPO_ERR_PARAM;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out);
+  if (al % 16 != 0 || reinterpret_cast<uintptr_t>(qkv) % 2 != 0) return DRGRPO_ERR_ALIAS;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < drgrpo_decode_attention_rope_workspace_bytes(S, Hq, Hkv, Lmax, D))
+    return DRGRPO_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(w);
+  w += attn_align(drgrpo_decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D));
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(w);
+  w += attn_align((size_t)(S * Hq * D) * 2);
+  int32_t* lens = reinterpret_cast<int32_t*>(w);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const unsigned blocks = (unsigned)(S * Hkv * a.nsplit);
-  if (D == 64 && plan.nw == 16)
-    hipLaunchKernelGGL((k_attn_fused<64, 16>), dim3(blocks), dim3(64 * 16), 0, st, a);
-  else if (D == 64)
-    hipLaunchKernelGGL((k_attn_fused<64, 8>), dim3(blocks), dim3(64 * 8), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_attn_fused<128, 8>), dim3(blocks), dim3(64 * 8), 0, st, a);
+  auto rope = D == 64 ? k_rope_append<64> : k_rope_append<128>;
+  hipLaunchKernelGGL(rope, dim3((unsigned)S), dim3(256), 0, st, static_cast<const uint16_t*>(qkv),
+                     rope_cos, rope_sin, pos, (int)Hq, (int)Hkv, Lmax, q_rot,
+                     static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), lens);
   if (attn_launch_status() != DRGRPO_OK) return DRGRPO_ERR_HIP;
-  if (a.nsplit > 1) {
-    if (D == 64)
-      launch_combine<64>(a, st);
-    else
-      launch_combine<128>(a, st);
-  }
-  return attn_launch_status();
+  return attn_run(q_rot, static_cast<const uint16_t*>(k_cache),
+                  static_cast<const uint16_t*>(v_cache), lens, S, Hq, Hkv, Lmax, D, scale, part,
+                  static_cast<uint16_t*>(out), out_lse, st);
 }

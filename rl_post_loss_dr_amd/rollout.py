@@ -5,9 +5,10 @@ it slow": rollout is one forward pass per generated token, and a decode
 kernel's standalone win has to survive integration into that loop).
 
 The weights are random (no checkpoint is used or needed: the step's cost does
-not depend on their values).  Every op but attention is plain PyTorch (the
-projections are hipBLASLt GEMMs); attention is the library's
-drgrpo_decode_attention on the layer's cache.  The whole step reads the
+not depend on their values).  Every op but the attention block is plain PyTorch
+(the projections are hipBLASLt GEMMs); the attention block (rotary
+embedding of the new query and key, their append to the layer's cache, and
+attention over it) is one library call.  The whole step reads the
 positions from the device and writes the new keys and values with indexed
 stores, so it can be captured once into a HIP graph and replayed per token, as
 a rollout loop would run it.
@@ -50,9 +51,12 @@ class DecodePolicy:
     each sequence's newest token, pos [S] int32 its position (the number of
     positions already cached); the step writes that token's keys and values
     at pos, attends over pos + 1 positions, and returns the logits [S, V]
-    (bfloat16) and the greedy next tokens [S] int64.  attention="library" uses
-    drgrpo_decode_attention; "reference" a binary32 softmax attention written
-    out in PyTorch (for checks, not for timing)."""
+    (bfloat16) and the greedy next tokens [S] int64.  attention="library" runs
+    the rotary embedding, cache append and attention as one library call
+    (drgrpo_decode_attention_rope); "library_unfused" the rotary embedding and
+    append in PyTorch around drgrpo_decode_attention; "reference" those
+    PyTorch steps around a binary32 softmax attention written out in PyTorch
+    (for checks, not for timing)."""
 
     def __init__(self, shape: PolicyShape, S: int, Lmax: int, seed: int, device,
                  std: float = 0.02):
@@ -82,15 +86,17 @@ class DecodePolicy:
         half = sh.head_dim // 2
         inv = 1.0 / (sh.rope_base ** (torch.arange(0, half, dtype=torch.float64) / half))
         ang = torch.arange(Lmax, dtype=torch.float64)[:, None] * inv[None, :]
-        self.cos = torch.cat([ang.cos(), ang.cos()], 1).float().to(device)  # [Lmax, D]
-        self.sin = torch.cat([ang.sin(), ang.sin()], 1).float().to(device)
+        self.cos_h = ang.cos().float().to(device).contiguous()  # [Lmax, D/2]
+        self.sin_h = ang.sin().float().to(device).contiguous()
+        self.cos = torch.cat([self.cos_h, self.cos_h], 1)  # [Lmax, D]
+        self.sin = torch.cat([self.sin_h, self.sin_h], 1)
         self.rows = torch.arange(S, device=device)
         self.scale = 1.0 / math.sqrt(sh.head_dim)
         self._attn_out = torch.empty((S, sh.heads, sh.head_dim), dtype=torch.bfloat16,
                                      device=device)
-        from . import decode_attention_workspace_bytes
-        self._ws = torch.empty(decode_attention_workspace_bytes(S, sh.heads, sh.kv_heads, Lmax,
-                                                                sh.head_dim),
+        from . import decode_attention_rope_workspace_bytes
+        self._ws = torch.empty(decode_attention_rope_workspace_bytes(S, sh.heads, sh.kv_heads,
+                                                                     Lmax, sh.head_dim),
                                dtype=torch.uint8, device=device)
 
     def fill_cache(self, seed: int, std: float = 1.0):
@@ -124,27 +130,35 @@ class DecodePolicy:
         return o.reshape(self.S, sh.heads, sh.head_dim).to(torch.bfloat16)
 
     def step(self, tok: torch.Tensor, pos: torch.Tensor, attention: str = "library"):
-        from . import decode_attention
+        from . import decode_attention, decode_attention_rope
+        if attention not in ("library", "library_unfused", "reference"):
+            raise ValueError(f"unknown attention {attention!r}")
         sh = self.shape
         nq, nkv = sh.heads * sh.head_dim, sh.kv_heads * sh.head_dim
         S = self.S
-        cos, sin = self.cos[pos.long()], self.sin[pos.long()]  # [S, D]
-        lens = pos + 1
+        if attention != "library":  # the fused call gathers the angles itself
+            cos, sin = self.cos[pos.long()], self.sin[pos.long()]  # [S, D]
+            lens = pos + 1
         x = self.embed[tok]  # [S, hidden]
         for li, L in enumerate(self.layers):
             h = self._rms(x, L["ln1"])
             qkv = F.linear(h, L["wqkv"], L["bqkv"])
-            q = self._rope(qkv[:, :nq].reshape(S, sh.heads, sh.head_dim), cos, sin)
-            k = self._rope(qkv[:, nq:nq + nkv].reshape(S, sh.kv_heads, sh.head_dim), cos, sin)
-            v = qkv[:, nq + nkv:].reshape(S, sh.kv_heads, sh.head_dim)
             kc, vc = self.k_cache[li], self.v_cache[li]
-            kc[self.rows, :, pos.long(), :] = k
-            vc[self.rows, :, pos.long(), :] = v
             if attention == "library":
-                a = decode_attention(q.contiguous(), kc, vc, lens, self.scale,
-                                     workspace=self._ws, out=self._attn_out)
+                # rotary embedding, cache append and attention in one library call
+                a = decode_attention_rope(qkv, self.cos_h, self.sin_h, pos, kc, vc, sh.heads,
+                                          self.scale, workspace=self._ws, out=self._attn_out)
             else:
-                a = self._attention_reference(q, kc, vc, lens)
+                q = self._rope(qkv[:, :nq].reshape(S, sh.heads, sh.head_dim), cos, sin)
+                k = self._rope(qkv[:, nq:nq + nkv].reshape(S, sh.kv_heads, sh.head_dim), cos, sin)
+                v = qkv[:, nq + nkv:].reshape(S, sh.kv_heads, sh.head_dim)
+                kc[self.rows, :, pos.long(), :] = k
+                vc[self.rows, :, pos.long(), :] = v
+                if attention == "library_unfused":
+                    a = decode_attention(q.contiguous(), kc, vc, lens, self.scale,
+                                         workspace=self._ws, out=self._attn_out)
+                else:
+                    a = self._attention_reference(q, kc, vc, lens)
             x = x + F.linear(a.reshape(S, nq), L["wo"])
             h = self._rms(x, L["ln2"])
             gu = F.linear(h, L["wgu"])

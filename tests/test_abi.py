@@ -112,6 +112,17 @@ def test_other_entry_points_validate(L):
     assert L.drgrpo_decode_attention(*att[:5], 15, *att[6:]) == dr.ERR_SHAPE
     assert L.drgrpo_decode_attention(*att[:9], -1.0, *att[10:]) == dr.ERR_PARAM
     assert L.drgrpo_decode_attention(*att[:13], 16, None) == dr.ERR_WORKSPACE
+    na = L.drgrpo_decode_attention_workspace_bytes(64, 14, 2, 512, 64)
+    nr = L.drgrpo_decode_attention_rope_workspace_bytes(64, 14, 2, 512, 64)
+    assert nr >= na + 64 * 14 * 64 * 2 + 64 * 4
+    assert L.drgrpo_decode_attention_rope_workspace_bytes(64, 14, 3, 512, 64) == 0
+    rope = (FAKE, FAKE, FAKE, FAKE, 64, 14, 2, 512, 64, 0.125, FAKE, FAKE, FAKE, None,
+            FAKE * 4096, 1 << 30, None)
+    assert L.drgrpo_decode_attention_rope(None, *rope[1:]) == dr.ERR_NULL
+    assert L.drgrpo_decode_attention_rope(*rope[:3], None, *rope[4:]) == dr.ERR_NULL
+    assert L.drgrpo_decode_attention_rope(*rope[:8], 96, *rope[9:]) == dr.ERR_SHAPE
+    assert L.drgrpo_decode_attention_rope(*rope[:9], 0.0, *rope[10:]) == dr.ERR_PARAM
+    assert L.drgrpo_decode_attention_rope(*rope[:15], nr - 1, None) == dr.ERR_WORKSPACE
     assert L.drgrpo_lmhead_logprobs_workspace_bytes(2, 4, 64, 31) == 0
     assert L.drgrpo_logprobs(FAKE, FAKE, 2, 2, 10, 9, FAKE, None) == dr.ERR_DTYPE
     assert L.drgrpo_logprobs(FAKE, FAKE, 2, 0, 10, 1, FAKE, None) == dr.ERR_SHAPE

@@ -146,3 +146,51 @@ def test_decode_attention_graph_replay(name):
         other = dr.decode_attention(q, k, v, short, workspace=ws)  # eager work in between
         torch.cuda.synchronize()
         assert other.shape == eager.shape
+
+
+def _rope_tables(Lmax, D, base=1.0e6):
+    inv = 1.0 / base ** (np.arange(0, D // 2, dtype=np.float64) / (D // 2))
+    ang = np.arange(Lmax, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _bf16_bits(rng_seed, shape, std=1.0):
+    g = torch.Generator().manual_seed(rng_seed)
+    t = (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D,Lmax", [(64, 14, 2, 64, 512), (8, 16, 2, 128, 300),
+                                            (5, 4, 4, 64, 40)])
+def test_decode_attention_rope_parity(S, Hq, Hkv, D, Lmax):
+    """Rotary embedding + cache append + attention against the oracle: the
+    appended cache entries bit for bit (every other entry unchanged), the
+    output and log-sum-exp within the attention tolerance; positions 0,
+    Lmax - 1 and (small case) outside the cache."""
+    print(f"case S={S} Hq={Hq} Hkv={Hkv} D={D} Lmax={Lmax}", flush=True)
+    rng = np.random.default_rng(S * 1000 + D + Lmax)
+    pos = rng.integers(0, Lmax, S).astype(np.int32)
+    pos[0], pos[-1] = 0, Lmax - 1
+    if S >= 5 and Lmax == 40:
+        pos[1], pos[2] = Lmax, -1  # outside the cache: no append, NaN output
+    qkv = _bf16_bits(S + D, (S, (Hq + 2 * Hkv) * D))
+    k0 = _bf16_bits(S + D + 1, (S, Hkv, Lmax, D))
+    v0 = _bf16_bits(S + D + 2, (S, Hkv, Lmax, D))
+    cos, sin = _rope_tables(Lmax, D)
+    scale = 1.0 / np.sqrt(D)
+    kc, vc = _dev_bf16(k0), _dev_bf16(v0)
+    out, lse = dr.decode_attention_rope(
+        _dev_bf16(qkv), torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV),
+        torch.from_numpy(pos).to(DEV), kc, vc, Hq, scale=scale, want_lse=True)
+    torch.cuda.synchronize()
+    want, want_lse, k1, v1 = att.decode_attention_rope(qkv, cos, sin, pos, k0, v0, Hq, Hkv, scale)
+    assert np.array_equal(kc.view(torch.int16).cpu().numpy().view(np.uint16), k1)
+    assert np.array_equal(vc.view(torch.int16).cpu().numpy().view(np.uint16), v1)
+    got = out.float().cpu().numpy().astype(np.float64)
+    bad = (pos < 0) | (pos >= Lmax)
+    assert np.isnan(got[bad]).all()
+    ok = ~bad
+    bound = 2.0 ** -8 * np.abs(want[ok]) + 2.0 ** -12 * np.abs(att.bf16_to_f64(v1)).max()
+    assert (np.abs(got[ok] - want[ok]) <= bound).all()
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(lg[ok] - want_lse[ok]).max() <= 2e-5

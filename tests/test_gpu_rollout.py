@@ -80,3 +80,23 @@ def test_rollout_step_graph_replay():
         assert torch.equal(logits_g, want[i]), i
         torch.empty(1 << 20, device=DEV).normal_()  # eager work between replays
     assert torch.equal(pos_s, pos0 + 5)
+
+
+def test_rollout_fused_block_equals_unfused():
+    """The one-call attention block (rotary embedding + append + attention)
+    and the same steps in PyTorch around the plain attention call give the
+    same logits and caches bit for bit: both round each binary32 product and
+    sum of the rotation to bfloat16 the same way."""
+    S, Lmax = 6, 40
+    fused, unfused = _pair(S, Lmax, 7303)
+    rng = np.random.default_rng(7303)
+    pos = torch.from_numpy(np.array([0, 2, 9, 20, 33, 38], dtype=np.int32)).to(DEV)
+    for _ in range(2):
+        tok = torch.from_numpy(rng.integers(0, SMALL.vocab, S)).to(DEV)
+        la, _ = fused.step(tok, pos, attention="library")
+        lb, _ = unfused.step(tok, pos, attention="library_unfused")
+        torch.cuda.synchronize()
+        assert torch.equal(la, lb)
+        pos = pos + 1
+    assert torch.equal(fused.k_cache, unfused.k_cache)
+    assert torch.equal(fused.v_cache, unfused.v_cache)
