@@ -195,20 +195,18 @@ k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_fl
   double s = 0.0;
   int n_out = 0, n_cut = 0, n_bad = 0, n_trunc = 0, n_noc = 0;
   long long n_len = 0, n_act = 0;
-  // each thread sums a contiguous block of tokens in index order (the loads
-  // of 8 entries go out before their adds, so they overlap), then the
-  // wavefront butterflies and the 16 wavefront partials in order: a fixed
-  // summation order, bitwise reproducible
-  const int64_t per = (T + 1023) / 1024;
-  const int64_t k0 = tid * per;
-  const int64_t k1 = k0 + per < T ? k0 + per : T;
-  for (int64_t k = k0; k < k1; k += 8) {
+  // each thread sums tokens tid, tid + 1024, ... in that order (coalesced
+  // across the wavefront; the loads of 8 of them go out before their adds),
+  // then the wavefront butterflies and the 16 wavefront partials in order: a
+  // fixed summation order, bitwise reproducible
+  for (int64_t k = tid; k < T; k += 8 * 1024) {
     double v[8];
     uint8_t f[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      v[u] = k + u < k1 ? tok_loss[k + u] : 0.0;
-      f[u] = k + u < k1 ? tok_flags[k + u] : (uint8_t)0;
+      const int64_t kk = k + (int64_t)u * 1024;
+      v[u] = kk < T ? tok_loss[kk] : 0.0;
+      f[u] = kk < T ? tok_flags[kk] : (uint8_t)0;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
