@@ -153,6 +153,11 @@ _add(Config(name="lmhead_mini", B=2, G=4, C=32, V=4096, H=QWEN_H, eos_id=3, tok_
 _add(Config(name="lmhead_multi", B=2, G=2, C=7, V=20488, H=96, eos_id=3, tok_lo=0,
             tok_hi=20488, eos_rows=2, reward="tiny", p=0.5, old_noise=0.05, ref_noise=0.1,
             beta=0.04, w_std=0.1, seed=7012))
+# three backward vocabulary chunks (the last ragged), small enough for the
+# oracle's full gradients
+_add(Config(name="lmhead_chunks3", B=2, G=2, C=4, V=70000, H=64, eos_id=3, tok_lo=0,
+            tok_hi=70000, eos_rows=1, reward="tiny", p=0.5, old_noise=0.05, w_std=0.1,
+            seed=7014))
 # tiny fp64-checkable shape for finite differences of the lm_head oracle
 _add(Config(name="lmhead_fd", B=2, G=2, C=3, V=48, H=32, eos_id=3, tok_lo=0, tok_hi=48,
             eos_rows=1, reward="tiny", p=0.5, old_noise=0.3, ref_noise=0.2, beta=0.04,

@@ -43,7 +43,7 @@ def _close(got, want, frac=1e-2):
     return err, scale
 
 
-@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi"])
+@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3"])
 def test_lmhead_small(name):
     print(f"case {name}", flush=True)
     cfg, case, hb, Wb, old, ref, t = lm_case(name)
@@ -127,7 +127,7 @@ def _logp_bound(h64, W64, rows):
     return 2 * gamma * a.max(axis=1) + 1e-5
 
 
-@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi"])
+@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3"])
 def test_lmhead_logprobs_small(name):
     """Forward-only fused log-probs: every counted token against the oracle,
     zeros after the first EOS, and every token when no EOS id is given."""
