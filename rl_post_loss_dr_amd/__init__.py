@@ -454,5 +454,11 @@ class DrGRPOLoss(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         (dlogits,) = ctx.saved_tensors
-        g = dlogits * grad_out.to(dlogits.dtype)
-        return g, None, None, None, None, None, None, None, None, None
+        none = (None,) * 9
+        # loss.backward() on this loss alone seeds grad_out = 1: dlogits is then
+        # the gradient as it stands, and a multiply would stream all of it
+        # through HBM again.  Reading the seed syncs the stream, so it is
+        # skipped while a graph is being captured.
+        if not torch.cuda.is_current_stream_capturing() and float(grad_out) == 1.0:
+            return (dlogits,) + none
+        return (dlogits * grad_out.to(dlogits.dtype),) + none

@@ -198,6 +198,15 @@ def test_autograd_wrapper():
     (3.0 * loss).backward()
     g = logits.grad.detach().cpu().numpy().astype(np.float64).reshape(cfg.T, cfg.V)
     assert np.abs(g - 3.0 * res.dlogits).max() <= 3e-5
+    # seed 1 (loss.backward()): the gradient is dlogits itself, bit for bit
+    logits.grad = None
+    args = (torch.from_numpy(case.tokens).to(DEV), cfg.eos_id,
+            torch.from_numpy(case.rewards).to(DEV), torch.from_numpy(old).to(DEV), None, cfg.G,
+            cfg.eps, 0.0, cfg.norm_const)
+    dr.DrGRPOLoss.apply(logits, *args).backward()
+    _, d = dr.loss_fwd_bwd(logits.detach(), *args[:4], G=cfg.G, eps=cfg.eps, beta=0.0,
+                           norm_const=cfg.norm_const)
+    assert torch.equal(logits.grad, d)
 
 
 def test_generator_bits_match_cpu():
