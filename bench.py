@@ -107,9 +107,45 @@ def cpu_baseline(cfg, case, target_s: float = 15.0):
             break
     tok_s = reps * len(rows) / el
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # the same oracle on one thread (OpenMP's thread count set through its
+    # runtime) on the first 16 rows of the sample
+    single = None
+    try:
+        import ctypes
+
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        try:
+            x1, tok1 = x[:16], tok[:16]
+            n1 = 0
+            t1 = time.perf_counter()
+            while time.perf_counter() - t1 < 3.0:
+                l1, lp1, _ = oracle.row_logprob(x1, tok1)
+                lam1, coef1, _ = oracle.token_terms(lp1[:, None], old[:16, None], None if ref is None
+                                                    else ref[:16, None], adv_s[:16], lens_s[:16],
+                                                    eps, beta, kappa)
+                oracle.dlogits_rows(x1, tok1, l1, coef1.reshape(-1))
+                n1 += 1
+            single = {"value": n1 * 16 / (time.perf_counter() - t1), "cores": 1,
+                      "sample": f"16 token rows x V={cfg.V}, {n1} passes"}
+        finally:
+            gomp.omp_set_num_threads(threads)
+    except OSError:
+        pass
+    host = {"nproc": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            host["cpu_model"] = next(l.split(":", 1)[1].strip() for l in f
+                                     if l.startswith("model name"))
+        with open("/proc/meminfo") as f:
+            host["ram_gb"] = round(int(next(l for l in f if l.startswith("MemTotal")).split()[1])
+                                   / 2 ** 20, 1)
+    except (OSError, StopIteration):
+        pass
     return {"value": tok_s, "unit": "completion tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} token rows (every {step}th of {T}) x V={cfg.V}, "
-                      f"{reps} passes in {el:.1f} s; mask and advantage over the whole batch"}
+                      f"{reps} passes in {el:.1f} s; mask and advantage over the whole batch",
+            "single_thread": single, "host": host}
 
 
 def run_lmhead(cfg, case, args):
