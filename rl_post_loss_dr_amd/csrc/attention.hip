@@ -26,6 +26,11 @@
  *                   the splits.
  *   k_attn_combine  merges the splits of each (sequence, query head) in
  *                   split order and writes the output and the log-sum-exp.
+ *   k_rope_append   (drgrpo_decode_attention_rope) the step's attention
+ *                   block before those: rotary embedding of the new token's
+ *                   query and key heads from the q/k/v projection output and
+ *                   the append of its key and value to the cache, one
+ *                   workgroup per sequence.
  */
 #include <hip/hip_runtime.h>
 #include <math.h>
