@@ -162,3 +162,17 @@ def test_variant_validation(L, adv_mode, agg, code):
     lm = (FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE, FAKE, 64, 256,
           4096, 896, FAKE * 4096, 16, None)
     assert L.drgrpo_lmhead_loss_fwd_bwd_ex(*lm, ctypes.byref(var), None) == code
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without its HIP library the package raises; it never computes on the CPU."""
+    import torch
+
+    monkeypatch.setattr(dr, "LIB", os.path.join(ROOT, "_no_such_dir", "libdrgrpo.so"))
+    monkeypatch.setattr(dr, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        dr.lib()
+    # host tensors are refused too (no host path to fall back on)
+    tokens = torch.zeros((2, 3), dtype=torch.int64)
+    with pytest.raises(TypeError, match="device tensor"):
+        dr.completion_mask(tokens, 1)
