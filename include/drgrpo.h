@@ -66,7 +66,8 @@ enum {
   DRGRPO_ERR_WORKSPACE = -5,   /* workspace NULL, too small or not 256-byte aligned */
   DRGRPO_ERR_ALIAS = -6,       /* out_dlogits partially overlaps logits */
   DRGRPO_ERR_HIP = -7,         /* a HIP launch failed */
-  DRGRPO_ERR_TOKEN_RANGE = -8  /* device-side: a token at a mask=1 position is outside [0, V) */
+  DRGRPO_ERR_TOKEN_RANGE = -8, /* device-side: a token at a mask=1 position is outside [0, V) */
+  DRGRPO_ERR_ALIGN = -9        /* a pointer lacks the alignment the call requires */
 };
 
 /* Bytes of device workspace drgrpo_loss_fwd_bwd needs for these sizes (0 if
@@ -190,7 +191,7 @@ int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_
  *   out_dW      [V, H] bfloat16 = dL/dW = dlogits^T . hidden.
  *   H must be a multiple of 32 and at most 65536, V a multiple of 8 and
  *   N*C at most 2^24 (else DRGRPO_ERR_SHAPE); hidden, W and the outputs
- *   16-byte aligned (else DRGRPO_ERR_ALIAS).  Other arguments as for
+ *   16-byte aligned (else DRGRPO_ERR_ALIGN).  Other arguments as for
  *   drgrpo_loss_fwd_bwd.  Logits accumulate in binary32 on the matrix cores;
  *   dlogits enter the two gradient products rounded to bfloat16, one
  *   vocabulary chunk at a time.
@@ -230,7 +231,7 @@ int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W, const int64
  * sampled token), without storing the [N*C, V] logits.
  *
  *   hidden   [N*C, H] bfloat16 (row i*C + t scores tokens[i, t]); W [V, H]
- *            bfloat16; both 16-byte aligned (else DRGRPO_ERR_ALIAS).
+ *            bfloat16; both 16-byte aligned (else DRGRPO_ERR_ALIGN).
  *   tokens   [N, C] int64; eos_id as for drgrpo_loss_fwd_bwd: log-probs are
  *            computed for the counted tokens (up to and including the first
  *            EOS; every token when eos_id is outside [0, V)).
@@ -268,7 +269,7 @@ int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const int64_t* tok
  *   D is 64 or 128, Hq a multiple of Hkv with Hq / Hkv <= 16, and one
  *   (sequence, key/value head) cache region Lmax * D * 2 bytes below 2^31
  *   (else DRGRPO_ERR_SHAPE); q, the caches and out 16-byte aligned (else
- *   DRGRPO_ERR_ALIAS).  The workspace (drgrpo_decode_attention_workspace_bytes,
+ *   DRGRPO_ERR_ALIGN).  The workspace (drgrpo_decode_attention_workspace_bytes,
  *   256-byte aligned, no initialisation) holds the per-split partial
  *   results; calls that share a workspace must not overlap.  The call only
  *   enqueues kernels (no memset, no host synchronisation), so it can be

@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE = -1, -2, -3, -4
-ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOKEN_RANGE = -5, -6, -7, -8
+ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOKEN_RANGE, ERR_ALIGN = -5, -6, -7, -8, -9
 
 
 class DrGRPOError(RuntimeError):

@@ -548,7 +548,7 @@ extern "C" int drgrpo_decode_attention(const void* q, const void* k_cache, const
   if (!(scale > 0.0f) || scale - scale != 0.0f) return DRGRPO_ERR_PARAM;
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
                        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out);
-  if (al % 16 != 0) return DRGRPO_ERR_ALIAS;
+  if (al % 16 != 0) return DRGRPO_ERR_ALIGN;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
       workspace_bytes < drgrpo_decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D))
     return DRGRPO_ERR_WORKSPACE;
@@ -578,7 +578,7 @@ extern "C" int drgrpo_decode_attention_rope(const void* qkv, const float* rope_c
   if (!(scale > 0.0f) || scale - scale != 0.0f) return DRGRPO_ERR_PARAM;
   const uintptr_t al = reinterpret_cast<uintptr_t>(k_cache) |
                        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out);
-  if (al % 16 != 0 || reinterpret_cast<uintptr_t>(qkv) % 2 != 0) return DRGRPO_ERR_ALIAS;
+  if (al % 16 != 0 || reinterpret_cast<uintptr_t>(qkv) % 2 != 0) return DRGRPO_ERR_ALIGN;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
       workspace_bytes < drgrpo_decode_attention_rope_workspace_bytes(S, Hq, Hkv, Lmax, D))
     return DRGRPO_ERR_WORKSPACE;

@@ -716,6 +716,7 @@ extern "C" const char* drgrpo_status_string(int status) {
     case DRGRPO_ERR_ALIAS: return "out_dlogits partially overlaps logits";
     case DRGRPO_ERR_HIP: return "HIP launch or runtime error";
     case DRGRPO_ERR_TOKEN_RANGE: return "a token at a mask=1 position is outside [0, V)";
+    case DRGRPO_ERR_ALIGN: return "a pointer lacks the alignment the call requires";
     default: return "unknown status";
   }
 }

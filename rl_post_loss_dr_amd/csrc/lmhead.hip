@@ -1104,7 +1104,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   const uintptr_t al = reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W) |
                        reinterpret_cast<uintptr_t>(out_dhidden) |
                        reinterpret_cast<uintptr_t>(out_dW);
-  if (al % 16 != 0) return DRGRPO_ERR_ALIAS;
+  if (al % 16 != 0) return DRGRPO_ERR_ALIGN;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
       workspace_bytes < lm_carve(nullptr, N, T, V, H, nullptr))
     return DRGRPO_ERR_WORKSPACE;
@@ -1273,7 +1273,7 @@ extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const i
   const int sh = lm_check_shape(N, C, V, H, 1, &T);
   if (sh != DRGRPO_OK) return sh;
   if ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W)) % 16 != 0)
-    return DRGRPO_ERR_ALIAS;
+    return DRGRPO_ERR_ALIGN;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
       workspace_bytes < lp_carve(nullptr, N, T, V, H, nullptr))
     return DRGRPO_ERR_WORKSPACE;

@@ -40,7 +40,7 @@ def test_workspace_bytes(L):
 
 
 def test_status_strings(L):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert dr.status_string(code)
     assert "unknown" in dr.status_string(-99)
 
@@ -102,6 +102,8 @@ def test_other_entry_points_validate(L):
                                     None) == dr.ERR_SHAPE
     assert L.drgrpo_lmhead_logprobs(FAKE, FAKE, FAKE, 0, 2, 4, 64, 32, FAKE, FAKE, 16,
                                     None) == dr.ERR_WORKSPACE
+    assert L.drgrpo_lmhead_logprobs(FAKE + 8, FAKE, FAKE, 0, 2, 4, 64, 32, FAKE, FAKE,
+                                    1 << 30, None) == dr.ERR_ALIGN
     assert L.drgrpo_lmhead_logprobs_workspace_bytes(2, 4, 64, 32) > 0
     assert L.drgrpo_decode_attention_workspace_bytes(64, 14, 2, 512, 64) > 0
     assert L.drgrpo_decode_attention_workspace_bytes(64, 14, 3, 512, 64) == 0
@@ -112,6 +114,8 @@ def test_other_entry_points_validate(L):
     assert L.drgrpo_decode_attention(*att[:5], 15, *att[6:]) == dr.ERR_SHAPE
     assert L.drgrpo_decode_attention(*att[:9], -1.0, *att[10:]) == dr.ERR_PARAM
     assert L.drgrpo_decode_attention(*att[:13], 16, None) == dr.ERR_WORKSPACE
+    assert L.drgrpo_decode_attention(FAKE + 8, *att[1:]) == dr.ERR_ALIGN
+    assert L.drgrpo_decode_attention(*att[:10], FAKE + 2, *att[11:]) == dr.ERR_ALIGN
     na = L.drgrpo_decode_attention_workspace_bytes(64, 14, 2, 512, 64)
     nr = L.drgrpo_decode_attention_rope_workspace_bytes(64, 14, 2, 512, 64)
     assert nr >= na + 64 * 14 * 64 * 2 + 64 * 4
@@ -122,6 +126,8 @@ def test_other_entry_points_validate(L):
     assert L.drgrpo_decode_attention_rope(*rope[:3], None, *rope[4:]) == dr.ERR_NULL
     assert L.drgrpo_decode_attention_rope(*rope[:8], 96, *rope[9:]) == dr.ERR_SHAPE
     assert L.drgrpo_decode_attention_rope(*rope[:9], 0.0, *rope[10:]) == dr.ERR_PARAM
+    assert L.drgrpo_decode_attention_rope(FAKE + 1, *rope[1:]) == dr.ERR_ALIGN
+    assert L.drgrpo_decode_attention_rope(*rope[:10], FAKE + 8, *rope[11:]) == dr.ERR_ALIGN
     assert L.drgrpo_decode_attention_rope(*rope[:15], nr - 1, None) == dr.ERR_WORKSPACE
     assert L.drgrpo_lmhead_logprobs_workspace_bytes(2, 4, 64, 31) == 0
     assert L.drgrpo_logprobs(FAKE, FAKE, 2, 2, 10, 9, FAKE, None) == dr.ERR_DTYPE
@@ -176,3 +182,16 @@ def test_missing_library_fails_loudly(monkeypatch):
     tokens = torch.zeros((2, 3), dtype=torch.int64)
     with pytest.raises(TypeError, match="device tensor"):
         dr.completion_mask(tokens, 1)
+
+
+def test_alignment_is_its_own_error(L):
+    """A misaligned operand is DRGRPO_ERR_ALIGN, distinct from the overlap
+    error, and is reported before anything is launched."""
+    lm = [FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE, FAKE, 64, 256,
+          4096, 896, FAKE * 4096, 1 << 40, None]
+    for idx in (0, 1, 12, 13):  # hidden, W, out_dhidden, out_dW
+        bad = list(lm)
+        bad[idx] = FAKE + 8
+        assert L.drgrpo_lmhead_loss_fwd_bwd(*bad) == dr.ERR_ALIGN, idx
+    assert "alignment" in dr.status_string(dr.ERR_ALIGN)
+    assert "overlaps" in dr.status_string(dr.ERR_ALIAS)
