@@ -14,7 +14,9 @@
  *             shuffles and one LDS exchange, evaluates the per-token surrogate
  *             and KL in binary64, then writes dlogits = coef*(softmax - onehot)
  *             from the same registers.  Rows longer than one register tile
- *             are swept tile by tile and re-read for the write pass.  Tokens
+ *             are swept tile by tile, last tile first; the write pass starts
+ *             from the first tile, still in the registers, and re-reads only
+ *             the rest.  Tokens
  *             whose loss term is identically zero only write zeros.
  *   k_finish  one workgroup: fixed-order binary64 sum of the per-token terms
  *             (each already divided by its completion's aggregation divisor:
@@ -295,7 +297,7 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
   const uint32_t sign = neg ? 0xFFFFFFFFu : 0u;
   for (uint32_t k = 0; k < ntiles; ++k) {
     const uint32_t tb = k * tile;
-    if (ntiles > 1) {
+    if (k > 0) {  // tile 0 is still in the registers from pass 1
 #pragma unroll
       for (int j = 0; j < kNch; ++j) {
         const uint32_t c = tb + (uint32_t)j * NT + tid;
@@ -401,8 +403,10 @@ __global__ void __launch_bounds__(NT) k_rows(RowArgs a) {
   const uint32_t ntiles = (nchunks + tile - 1) / tile;
   float m = -INFINITY;
   float s = 0.0f;
-  for (uint32_t k = 0; k < ntiles; ++k) {
-    const uint32_t tb = k * tile;
+  // tiles in reverse order, so the first (full) tile is the one left in the
+  // registers for pass 2, which re-reads only the others
+  for (uint32_t kk = ntiles; kk-- > 0;) {
+    const uint32_t tb = kk * tile;
 #pragma unroll
     for (int j = 0; j < kNch; ++j) {
       const uint32_t c = tb + (uint32_t)j * NT + tid;
