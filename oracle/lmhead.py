@@ -54,18 +54,36 @@ def loss_and_terms(hidden64, W64, tokens, eos_id, rewards, logp_old, logp_ref, G
                 coef=coef.reshape(-1), active_rows=rows, len=lens, adv=adv, stats=stats)
 
 
+def dlogits_token_rows(hidden64, W64, tokens_flat, terms, rows):
+    """dlogits [len(rows), V] of the given token rows (zero rows where the
+    token has no gradient): the raw-logits oracle's gradient rows of
+    hidden[rows] . W^T."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, W64.shape[0]))
+    live = np.flatnonzero(terms["coef"][rows] != 0.0)
+    if live.size:
+        r = rows[live]
+        logits = hidden64[r] @ W64.T
+        out[live] = dlogits_rows(logits, tokens_flat[r], terms["lse"][r], terms["coef"][r])
+    return out
+
+
+def dlogits_vocab_cols(hidden64, W64, tokens_flat, terms, vocab_rows):
+    """dlogits [active tokens, len(vocab_rows)]: column v of the active tokens'
+    gradient rows, dlogits[t, v] = coef_t (exp(logits[t, v] - lse_t) - [y_t = v])."""
+    act = terms["active_rows"]
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    Ha = hidden64[act]
+    lse = terms["lse"][act]
+    coef = terms["coef"][act]
+    y = tokens_flat[act]
+    cols = Ha @ W64[vocab_rows].T                  # logits[t, v] for the active tokens
+    return coef[:, None] * (np.exp(cols - lse[:, None]) - (y[:, None] == vocab_rows[None, :]))
+
+
 def dhidden_rows(hidden64, W64, tokens_flat, terms, rows):
     """dL/dhidden for the given token rows: (dlogits row) . W."""
-    rows = np.asarray(rows, dtype=np.int64)
-    out = np.zeros((rows.size, W64.shape[1]))
-    for k, r in enumerate(rows):
-        if terms["coef"][r] == 0.0:
-            continue
-        logits = hidden64[r:r + 1] @ W64.T
-        D = dlogits_rows(logits, tokens_flat[r:r + 1], terms["lse"][r:r + 1],
-                         terms["coef"][r:r + 1])
-        out[k] = D[0] @ W64
-    return out
+    return dlogits_token_rows(hidden64, W64, tokens_flat, terms, rows) @ W64
 
 
 def dW_rows(hidden64, W64, tokens_flat, terms, vocab_rows):
@@ -74,15 +92,7 @@ def dW_rows(hidden64, W64, tokens_flat, terms, vocab_rows):
     out = np.zeros((len(vocab_rows), hidden64.shape[1]))
     if act.size == 0:
         return out
-    Ha = hidden64[act]
-    lse = terms["lse"][act]
-    coef = terms["coef"][act]
-    y = tokens_flat[act]
-    for k, v in enumerate(vocab_rows):
-        col = Ha @ W64[v]                              # logits[t, v] for the active tokens
-        D = coef * (np.exp(col - lse) - (y == v))      # dlogits[t, v]
-        out[k] = D @ Ha
-    return out
+    return dlogits_vocab_cols(hidden64, W64, tokens_flat, terms, vocab_rows).T @ hidden64[act]
 
 
 def full(hidden_bits, W_bits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa,

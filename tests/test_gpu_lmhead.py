@@ -2,8 +2,13 @@
 
 Small cases: loss, every dhidden and dW entry.  Full size (B=8, G=8, C=512,
 H=896, V=151936): loss over every token, sampled dhidden rows and dW rows.
-Tolerances: loss rel <= 2e-3; dhidden, dW max|diff| <= 1e-2 * max|ref| (bf16
-outputs from binary32 accumulation, dlogits entering the products in bf16)."""
+Tolerances: loss rel <= 2e-3; dhidden and dW through ``_lmcheck``: every
+element against a worst-case rounding model of the precision path (bfloat16
+dlogits entering binary32 products, bfloat16 results), every row and part
+against its RMS model, and the regression slope of each part, with the
+vocabulary rows of dW that no active token sampled and the softmax part of
+dhidden checked as parts of their own (test_lmcheck.py shows the checks fail
+when one of those parts is wrong)."""
 import numpy as np
 import pytest
 import torch
@@ -13,6 +18,7 @@ import synth
 import rl_post_loss_dr_amd as dr
 from oracle import lmhead
 from _cases import f32, lm_case
+from _lmcheck import check_dW, check_dhidden
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -36,11 +42,16 @@ def _run(cfg, case, hb, Wb, old, ref):
     return float(loss.item()), dh, dW
 
 
-def _close(got, want, frac=1e-2):
-    scale = float(np.abs(want).max())
-    err = float(np.abs(got - want).max())
-    assert err <= frac * scale, (err, scale)
-    return err, scale
+def check_small_grads(cfg, case, hb, Wb, t, dh, dW):
+    """Every dhidden row and every dW row of a small case through the checker."""
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    tok = case.tokens.reshape(-1)
+    D = t["dlogits"]
+    act = t["active_rows"]
+    r1 = check_dhidden(_dev_to_f64(dh), D, W64, t["coef"], tok)
+    r2 = check_dW(_dev_to_f64(dW), D[act], h64[act], np.isin(np.arange(cfg.V), tok[act]))
+    print(f"[{cfg.name}] {r1} {r2}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3"])
@@ -49,8 +60,7 @@ def test_lmhead_small(name):
     cfg, case, hb, Wb, old, ref, t = lm_case(name)
     loss, dh, dW = _run(cfg, case, hb, Wb, old, ref)
     assert abs(loss - t["loss"]) <= 2e-3 * abs(t["loss"]), (loss, t["loss"])
-    _close(_dev_to_f64(dh), t["dhidden"])
-    _close(_dev_to_f64(dW), t["dW"])
+    check_small_grads(cfg, case, hb, Wb, t, dh, dW)
     # tokens without gradient have exactly zero dhidden rows
     zero = t["coef"] == 0
     assert (_dev_to_f64(dh)[zero] == 0).all()
@@ -100,16 +110,24 @@ def test_lmhead_full_size_sampled():
     print(f"[{cfg.name}] loss gpu {loss!r} oracle {t['loss']!r}", flush=True)
     assert abs(loss - t["loss"]) <= 2e-3 * abs(t["loss"])
     rng = np.random.default_rng(cfg.seed)
-    rows = np.unique(np.concatenate([rng.choice(active, 12, replace=False), active[:2],
+    tok = case.tokens.reshape(-1)
+    rows = np.unique(np.concatenate([rng.choice(active, 28, replace=False), active[:2],
                                      active[-2:], [0]]))
-    want_h = lmhead.dhidden_rows(h64, W64, case.tokens.reshape(-1), t, rows)
-    got_h = _dev_to_f64(dh[torch.from_numpy(rows).to(DEV)])
-    _close(got_h, want_h)
-    vs = np.unique(np.concatenate([rng.choice(cfg.V, 10, replace=False),
-                                   case.tokens.reshape(-1)[active[:4]], [0, cfg.V - 1]]))
-    want_w = lmhead.dW_rows(h64, W64, case.tokens.reshape(-1), t, vs)
-    got_w = _dev_to_f64(dW[torch.from_numpy(vs).to(DEV)])
-    _close(got_w, want_w)
+    print(f"[{cfg.name}] oracle dlogits of {rows.size} token rows", flush=True)
+    D = lmhead.dlogits_token_rows(h64, W64, tok, t, rows)
+    r1 = check_dhidden(_dev_to_f64(dh[torch.from_numpy(rows).to(DEV)]), D, W64, t["coef"][rows],
+                       tok[rows])
+    # vocabulary rows: some that active tokens sampled, more that none did
+    # (their gradient is the softmax part alone), and both ends
+    samp_ids = np.unique(tok[active])
+    others = np.setdiff1d(np.arange(cfg.V), samp_ids)
+    vs = np.unique(np.concatenate([rng.choice(samp_ids, 8, replace=False),
+                                   rng.choice(others, 48, replace=False), [0, cfg.V - 1]]))
+    print(f"[{cfg.name}] oracle dlogits columns of {vs.size} vocabulary rows", flush=True)
+    Dc = lmhead.dlogits_vocab_cols(h64, W64, tok, t, vs)
+    r2 = check_dW(_dev_to_f64(dW[torch.from_numpy(vs).to(DEV)]), Dc, h64[active],
+                  np.isin(vs, samp_ids))
+    print(f"[{cfg.name}] {r1} {r2}", flush=True)
     # every inactive token's dhidden row is exactly zero
     inactive = np.setdiff1d(np.arange(cfg.T), active)
     assert float(dh[torch.from_numpy(inactive).to(DEV)].float().abs().max()) == 0.0
