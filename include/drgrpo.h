@@ -31,7 +31,8 @@
  *
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller unless stated.  The
- *     library keeps no global state and allocates no device memory.
+ *     library allocates no device memory and keeps no global state, except
+ *     the static scratch array of drgrpo_loss_fwd_bwd_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it; no call synchronises except
  *     drgrpo_device_status.  Results are valid once the stream has reached
@@ -67,7 +68,9 @@ enum {
   DRGRPO_ERR_ALIAS = -6,       /* out_dlogits partially overlaps logits */
   DRGRPO_ERR_HIP = -7,         /* a HIP launch failed */
   DRGRPO_ERR_TOKEN_RANGE = -8, /* device-side: a token at a mask=1 position is outside [0, V) */
-  DRGRPO_ERR_ALIGN = -9        /* a pointer lacks the alignment the call requires */
+  DRGRPO_ERR_ALIGN = -9,       /* a pointer lacks the alignment the call requires */
+  DRGRPO_ERR_SCRATCH_LIMIT = -10 /* sizes exceed the static scratch of
+                                    drgrpo_loss_fwd_bwd_noalloc */
 };
 
 /* Bytes of device workspace drgrpo_loss_fwd_bwd needs for these sizes (0 if
@@ -109,6 +112,33 @@ int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_i
                         void* out_dlogits, int64_t N, int64_t C, int64_t V,
                         drgrpo_dtype_t dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* drgrpo_loss_fwd_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without the workspace, which comes from a
+ * static device array of DRGRPO_NOALLOC_SCRATCH_BYTES per GPU instead.
+ *
+ *   - The call allocates nothing (no hipMalloc, hipFree or allocating library
+ *     routine).  The first call on a device looks up that device's array
+ *     (hipGetSymbolAddress); the array stays allocated until the process
+ *     ends.  The current device (hipGetDevice) is used; `stream` must belong
+ *     to it.
+ *   - Sizes whose workspace (drgrpo_workspace_bytes) exceeds the array are
+ *     rejected with DRGRPO_ERR_SCRATCH_LIMIT before anything is enqueued;
+ *     every batch of at most 655,360 token rows (N*C) fits.
+ *   - Every call on one GPU shares that GPU's array: calls that can run
+ *     concurrently on one GPU (other streams, other threads) race and must
+ *     not overlap.  No field needs clearing between calls.
+ *   - A device-side error (a token outside [0, V) at a mask=1 position)
+ *     makes the loss NaN; the status word lives in the static array, so
+ *     drgrpo_device_status does not apply to this call. */
+#define DRGRPO_NOALLOC_SCRATCH_BYTES (12u << 20)
+
+int drgrpo_loss_fwd_bwd_noalloc(const void* logits, const int64_t* tokens, int64_t eos_id,
+                                const float* rewards, const float* logp_old,
+                                const float* logp_ref, int64_t G, float eps, float beta,
+                                float norm_const, float* out_loss, void* out_dlogits, int64_t N,
+                                int64_t C, int64_t V, drgrpo_dtype_t dtype, void* stream);
 
 /* Normalisation variants ("Making Dr GRPO go brrr", sections "GRPO" and
  * "Dr. GRPO": Dr. GRPO deletes GRPO's division by the group standard

@@ -23,6 +23,8 @@ F32, BF16 = 0, 1
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOKEN_RANGE, ERR_ALIGN = -5, -6, -7, -8, -9
+ERR_SCRATCH_LIMIT = -10
+NOALLOC_SCRATCH_BYTES = 12 << 20  # DRGRPO_NOALLOC_SCRATCH_BYTES
 
 
 class DrGRPOError(RuntimeError):
@@ -69,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.drgrpo_loss_fwd_bwd_ex.argtypes = common + [ctypes.POINTER(_Aux),
                                                       ctypes.POINTER(_Variant)]
         L.drgrpo_loss_fwd_bwd_ex.restype = _I
+        L.drgrpo_loss_fwd_bwd_noalloc.argtypes = common[:16] + [_P]
+        L.drgrpo_loss_fwd_bwd_noalloc.restype = _I
         L.drgrpo_completion_mask.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
         L.drgrpo_completion_mask.restype = _I
         L.drgrpo_group_advantage.argtypes = [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P]
@@ -218,6 +222,43 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
     _check(lib().drgrpo_loss_fwd_bwd_ex(*args, ctypes.byref(s), ctypes.byref(var)),
            "drgrpo_loss_fwd_bwd_ex")
     return loss, out_dlogits
+
+
+def loss_fwd_bwd_noalloc(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int,
+                         rewards: torch.Tensor, logp_old: torch.Tensor,
+                         logp_ref: torch.Tensor | None, *, G: int, eps: float = 0.2,
+                         beta: float = 0.0, norm_const: float | None = None,
+                         out_loss: torch.Tensor, out_dlogits: torch.Tensor):
+    """loss_fwd_bwd through drgrpo_loss_fwd_bwd_noalloc: no workspace, and no
+    device memory allocated by this call or the library (the caller passes the
+    outputs: out_loss a float32 scalar, out_dlogits like logits).  Returns
+    (out_loss, out_dlogits)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [N, C, V]")
+    N, C, V = logits.shape
+    dt = _dtype_code(logits)
+    _dev(logits, "logits", logits.dtype)
+    dev = logits.device
+    _dev(tokens, "tokens", torch.int64, (N, C))
+    _dev(rewards, "rewards", torch.float32, (N,))
+    _dev(logp_old, "logp_old", torch.float32, (N, C))
+    if logp_ref is not None:
+        _dev(logp_ref, "logp_ref", torch.float32, (N, C))
+    _dev(out_loss, "out_loss", torch.float32)
+    if out_loss.numel() != 1:
+        raise ValueError("out_loss must hold one element")
+    _dev(out_dlogits, "out_dlogits", logits.dtype, (N, C, V))
+    for t in (tokens, rewards, logp_old, logp_ref, out_loss, out_dlogits):
+        if t is not None and t.device != dev:
+            raise ValueError("every tensor must be on the logits' device")
+    if norm_const is None:
+        norm_const = float(G * C)
+    _check(lib().drgrpo_loss_fwd_bwd_noalloc(
+        logits.data_ptr(), tokens.data_ptr(), int(eos_id), rewards.data_ptr(),
+        logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta), float(norm_const),
+        out_loss.data_ptr(), out_dlogits.data_ptr(), N, C, V, dt, _stream(dev)),
+        "drgrpo_loss_fwd_bwd_noalloc")
+    return out_loss, out_dlogits
 
 
 def logprobs(logits: torch.Tensor, tokens: torch.Tensor) -> torch.Tensor:

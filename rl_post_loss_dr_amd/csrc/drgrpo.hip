@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "drgrpo.h"
 #include "common.h"
 
@@ -581,18 +583,20 @@ extern "C" size_t drgrpo_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_
   return ws_carve(nullptr, N, T, nullptr);
 }
 
-extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
-                                      const float* rewards, const float* logp_old,
-                                      const float* logp_ref, int64_t G, float eps, float beta,
-                                      float norm_const, float* out_loss, void* out_dlogits,
-                                      int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
-                                      void* workspace, size_t workspace_bytes, void* stream,
-                                      const drgrpo_aux_t* aux, const drgrpo_variant_t* variant) {
+namespace {
+
+// Host-side argument checks of the loss calls (everything but the workspace
+// and the overlap of dlogits with logits, which come after it), before
+// anything is enqueued.  On success *T and *elems hold N*C and N*C*V.
+int check_loss_args(const void* logits, const int64_t* tokens, const float* rewards,
+                    const float* logp_old, const float* logp_ref, int64_t G, float eps,
+                    float beta, float norm_const, const float* out_loss, const void* out_dlogits,
+                    int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
+                    const drgrpo_variant_t* variant, int64_t* T, int64_t* elems) {
   if (!logits || !tokens || !rewards || !logp_old || !out_loss || !out_dlogits)
     return DRGRPO_ERR_NULL;
   if (dtype != DRGRPO_F32 && dtype != DRGRPO_BF16) return DRGRPO_ERR_DTYPE;
-  int64_t T, elems;
-  const int sh = check_shape(N, C, V, G, &T, &elems);
+  const int sh = check_shape(N, C, V, G, T, elems);
   if (sh != DRGRPO_OK) return sh;
   if (!finite_f(eps) || eps < 0.0f || !finite_f(beta) || beta < 0.0f || !finite_f(norm_const) ||
       norm_const <= 0.0f)
@@ -600,18 +604,31 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
   if (beta > 0.0f && !logp_ref) return DRGRPO_ERR_NULL;
   int adv_mode, agg;
   if (!read_variant(variant, &adv_mode, &agg)) return DRGRPO_ERR_PARAM;
-  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
-      workspace_bytes < ws_carve(nullptr, N, T, nullptr))
-    return DRGRPO_ERR_WORKSPACE;
+  return DRGRPO_OK;
+}
+
+// out_dlogits is exactly logits (in place) or disjoint from it.
+int check_alias(const void* logits, const void* out_dlogits, int64_t elems,
+                drgrpo_dtype_t dtype) {
   const size_t esz = dtype == DRGRPO_BF16 ? 2 : 4;
   const uintptr_t lo = reinterpret_cast<uintptr_t>(logits);
   const uintptr_t dl = reinterpret_cast<uintptr_t>(out_dlogits);
   const uintptr_t nbytes = (uintptr_t)elems * esz;
   if (lo != dl && lo < dl + nbytes && dl < lo + nbytes) return DRGRPO_ERR_ALIAS;
+  return DRGRPO_OK;
+}
 
+// The three launches of one loss call over a carved workspace (arguments
+// already checked).
+int enqueue_loss(const void* logits, const int64_t* tokens, int64_t eos_id, const float* rewards,
+                 const float* logp_old, const float* logp_ref, int64_t G, float eps, float beta,
+                 float norm_const, float* out_loss, void* out_dlogits, int64_t N, int64_t C,
+                 int64_t V, int64_t T, drgrpo_dtype_t dtype, void* workspace, hipStream_t st,
+                 const drgrpo_aux_t* aux, const drgrpo_variant_t* variant) {
+  int adv_mode, agg;
+  read_variant(variant, &adv_mode, &agg);
   Ws ws;
   ws_carve(workspace, N, T, &ws);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const drgrpo_aux_t none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                              nullptr};
   const drgrpo_aux_t& x = aux ? *aux : none;
@@ -655,6 +672,29 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
   return launch_status();
 }
 
+}  // namespace
+
+extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
+                                      const float* rewards, const float* logp_old,
+                                      const float* logp_ref, int64_t G, float eps, float beta,
+                                      float norm_const, float* out_loss, void* out_dlogits,
+                                      int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      const drgrpo_aux_t* aux, const drgrpo_variant_t* variant) {
+  int64_t T, elems;
+  const int rc = check_loss_args(logits, tokens, rewards, logp_old, logp_ref, G, eps, beta,
+                                 norm_const, out_loss, out_dlogits, N, C, V, dtype, variant, &T,
+                                 &elems);
+  if (rc != DRGRPO_OK) return rc;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < ws_carve(nullptr, N, T, nullptr))
+    return DRGRPO_ERR_WORKSPACE;
+  if (check_alias(logits, out_dlogits, elems, dtype) != DRGRPO_OK) return DRGRPO_ERR_ALIAS;
+  return enqueue_loss(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
+                      norm_const, out_loss, out_dlogits, N, C, V, T, dtype, workspace,
+                      static_cast<hipStream_t>(stream), aux, variant);
+}
+
 extern "C" int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_id,
                                    const float* rewards, const float* logp_old,
                                    const float* logp_ref, int64_t G, float eps, float beta,
@@ -664,6 +704,60 @@ extern "C" int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, in
   return drgrpo_loss_fwd_bwd_ex(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
                                 norm_const, out_loss, out_dlogits, N, C, V, dtype, workspace,
                                 workspace_bytes, stream, nullptr, nullptr);
+}
+
+// ------------------------------------------------ no-allocation entry point
+// The scratch of drgrpo_loss_fwd_bwd_noalloc: the same carve-up as a caller's
+// workspace, in a static device array.  Every GPU the library runs on holds
+// its own copy (at its own address) until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol: kernels and copies get the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[DRGRPO_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DRGRPO_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DRGRPO_ERR_HIP;
+    if (reinterpret_cast<uintptr_t>(p) % 256 != 0) return DRGRPO_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DRGRPO_OK;
+}
+
+}  // namespace
+
+extern "C" int drgrpo_loss_fwd_bwd_noalloc(const void* logits, const int64_t* tokens,
+                                           int64_t eos_id, const float* rewards,
+                                           const float* logp_old, const float* logp_ref,
+                                           int64_t G, float eps, float beta, float norm_const,
+                                           float* out_loss, void* out_dlogits, int64_t N,
+                                           int64_t C, int64_t V, drgrpo_dtype_t dtype,
+                                           void* stream) {
+  int64_t T, elems;
+  int rc = check_loss_args(logits, tokens, rewards, logp_old, logp_ref, G, eps, beta, norm_const,
+                           out_loss, out_dlogits, N, C, V, dtype, nullptr, &T, &elems);
+  if (rc != DRGRPO_OK) return rc;
+  if (ws_carve(nullptr, N, T, nullptr) > (size_t)DRGRPO_NOALLOC_SCRATCH_BYTES)
+    return DRGRPO_ERR_SCRATCH_LIMIT;
+  if (check_alias(logits, out_dlogits, elems, dtype) != DRGRPO_OK) return DRGRPO_ERR_ALIAS;
+  void* ws = nullptr;
+  if ((rc = current_scratch(&ws)) != DRGRPO_OK) return rc;
+  // every scratch field is written before it is read within the call, so the
+  // previous call's contents need no clearing
+  return enqueue_loss(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
+                      norm_const, out_loss, out_dlogits, N, C, V, T, dtype, ws,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr);
 }
 
 extern "C" int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t C,
@@ -738,6 +832,8 @@ extern "C" const char* drgrpo_status_string(int status) {
     case DRGRPO_ERR_HIP: return "HIP launch or runtime error";
     case DRGRPO_ERR_TOKEN_RANGE: return "a token at a mask=1 position is outside [0, V)";
     case DRGRPO_ERR_ALIGN: return "a pointer lacks the alignment the call requires";
+    case DRGRPO_ERR_SCRATCH_LIMIT:
+      return "sizes exceed the static scratch of drgrpo_loss_fwd_bwd_noalloc";
     default: return "unknown status";
   }
 }

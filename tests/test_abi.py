@@ -40,7 +40,7 @@ def test_workspace_bytes(L):
 
 
 def test_status_strings(L):
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         assert dr.status_string(code)
     assert "unknown" in dr.status_string(-99)
 
@@ -195,3 +195,32 @@ def test_alignment_is_its_own_error(L):
         assert L.drgrpo_lmhead_loss_fwd_bwd(*bad) == dr.ERR_ALIGN, idx
     assert "alignment" in dr.status_string(dr.ERR_ALIGN)
     assert "overlaps" in dr.status_string(dr.ERR_ALIAS)
+
+
+def test_noalloc_validates_before_touching_the_scratch(L):
+    """The no-allocation entry point returns its host errors (the loss call's,
+    then DRGRPO_ERR_SCRATCH_LIMIT for a batch whose workspace exceeds the
+    static array) before it looks up the device array or enqueues anything:
+    these calls never reach the GPU."""
+    base = [FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE * 1000000, 64, 256,
+            151936, 1, None]
+
+    def call(changes):
+        a = list(base)
+        for k, v in changes.items():
+            a[k] = v
+        return L.drgrpo_loss_fwd_bwd_noalloc(*a)
+
+    assert call({0: None}) == dr.ERR_NULL
+    assert call({6: 7}) == dr.ERR_SHAPE
+    assert call({7: -1.0}) == dr.ERR_PARAM
+    assert call({15: 4}) == dr.ERR_DTYPE
+    assert call({8: 0.04}) == dr.ERR_NULL  # beta > 0 without logp_ref
+    # 2048 x 1024 token rows: a 19 MB workspace, beyond the 12 MiB array
+    assert dr.workspace_bytes(2048, 1024, 8, 8) > dr.NOALLOC_SCRATCH_BYTES
+    assert call({12: 2048, 13: 1024, 14: 8}) == dr.ERR_SCRATCH_LIMIT
+    # the largest batch the header promises fits
+    assert dr.workspace_bytes(655360, 1, 151936, 1) <= dr.NOALLOC_SCRATCH_BYTES
+    assert dr.workspace_bytes(655360, 1, 8, 1) <= dr.NOALLOC_SCRATCH_BYTES
+    # partial overlap of dlogits with logits
+    assert call({11: FAKE + 64}) == dr.ERR_ALIAS
