@@ -7,10 +7,16 @@ over one synthetic rollout batch resident in HBM.  Prints ONE JSON line.
 Default workload: B=8 prompts x G=8 completions x C=256 tokens over the
 151,936-entry vocabulary in bfloat16 (the Qwen2.5-0.5B-Instruct-shaped
 batch), synthetic seeded inputs.  logp_old is the library's own forward
-log-prob plus N(0, 0.02^2) noise, as an update step would receive it.
+log-prob plus N(0, 0.02^2) noise, as an update step would receive it.  The
+same line carries, under "workloads", the larger loss batches (B=8 G=16
+C=512; B=16 G=8 C=1024 with the KL term; the all-active dense batch) and the
+fused lm_head (B=8 G=8 C=512, H=896), each timed over several calls in this
+process (median and spread), and "ceilings": the row kernel's own access
+pattern with no arithmetic (copy, fill, read, and the batch's active / zero
+row mix) on the same buffers.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--headline-only]
 """
 from __future__ import annotations
 
@@ -53,8 +59,9 @@ def _src_hash():
 
 
 def _traffic(workload):
-    """HBM bytes per launch measured by rocprofv3 counters (profiles/), if the
-    committed measurement was taken on the current kernel source."""
+    """HBM bytes per launch of the row kernel measured by rocprofv3 counters
+    (profiles/), if the committed measurement was taken on the current kernel
+    source."""
     p = os.path.join(ROOT, "profiles", f"k_rows_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
@@ -63,6 +70,108 @@ def _traffic(workload):
     if rec.get("src_hash") != _src_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def _row_stride(T: int) -> int:
+    """The row kernel's workgroup-to-row stride (coprime with T, near T/phi^2)."""
+    import math
+
+    s = int(T * 0.3819660112501051) | 1
+    while math.gcd(s, T) != 1:
+        s += 1
+    return s
+
+
+_ceil = None
+
+
+def _ceil_lib():
+    """libceiling.so: the measurement kernels and device properties."""
+    global _ceil
+    if _ceil is None:
+        import ctypes
+
+        from rl_post_loss_dr_amd.build import CEIL_LIB
+
+        L = ctypes.CDLL(CEIL_LIB)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        L.ceiling_rows.argtypes = [P, P, I64, I64, I64, ctypes.c_int32, P, P, P, P, P]
+        L.ceiling_rows.restype = ctypes.c_int
+        L.ceiling_device_info.restype = ctypes.c_int
+        _ceil = L
+    return _ceil
+
+
+def provenance(seed):
+    """Versions and configuration this measurement ran with."""
+    import ctypes
+    import platform
+    import subprocess
+
+    import torch
+
+    class Info(ctypes.Structure):
+        _fields_ = [("name", ctypes.c_char * 256), ("arch", ctypes.c_char * 256),
+                    ("compute_units", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
+                    ("memory_clock_khz", ctypes.c_int32), ("memory_bus_bits", ctypes.c_int32),
+                    ("total_mem_bytes", ctypes.c_int64), ("l2_bytes", ctypes.c_int32),
+                    ("runtime_version", ctypes.c_int32), ("driver_version", ctypes.c_int32)]
+
+    out = {"seed": seed, "torch": torch.__version__, "torch_hip": torch.version.hip,
+           "python": platform.python_version()}
+    info = Info()
+    if _ceil_lib().ceiling_device_info(0, ctypes.byref(info)) == 0:
+        out["device"] = {"name": info.name.decode(), "arch": info.arch.decode(),
+                         "compute_units": info.compute_units,
+                         "max_clock_mhz": info.clock_khz / 1000.0,
+                         "memory_clock_mhz": info.memory_clock_khz / 1000.0,
+                         "memory_bus_bits": info.memory_bus_bits,
+                         "hbm_gib": round(info.total_mem_bytes / 2 ** 30, 1),
+                         "l2_bytes": info.l2_bytes, "hip_runtime_version": info.runtime_version,
+                         "driver_version": info.driver_version}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            out["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=30)
+        out["hipcc"] = " | ".join(l.strip() for l in r.stdout.splitlines()[:2])
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
+                           capture_output=True, text=True, timeout=30)
+        if r.returncode == 0:
+            out["git_head"] = r.stdout.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    out["build_flags"] = " ".join(__import__("rl_post_loss_dr_amd.build",
+                                             fromlist=["HIPCC_FLAGS"]).HIPCC_FLAGS)
+    return out
+
+
+def host_info():
+    host = {"nproc": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            lines = f.read().splitlines()
+        kv = {}
+        for l in lines:
+            if ":" in l:
+                k, v = l.split(":", 1)
+                kv.setdefault(k.strip(), v.strip())
+        host["cpu_model"] = kv.get("model name")
+        host["cpu_family_model_stepping"] = "/".join(
+            kv.get(k, "?") for k in ("cpu family", "model", "stepping"))
+        host["cpu_vendor"] = kv.get("vendor_id")
+        host["cpu_mhz"] = kv.get("cpu MHz")
+        with open("/proc/meminfo") as f:
+            host["ram_gb"] = round(int(next(l for l in f if l.startswith("MemTotal")).split()[1])
+                                   / 2 ** 20, 1)
+    except (OSError, StopIteration, ValueError):
+        pass
+    return host
 
 
 def cpu_baseline(cfg, case, target_s: float = 15.0):
@@ -132,24 +241,25 @@ def cpu_baseline(cfg, case, target_s: float = 15.0):
             gomp.omp_set_num_threads(threads)
     except OSError:
         pass
-    host = {"nproc": os.cpu_count()}
-    try:
-        with open("/proc/cpuinfo") as f:
-            host["cpu_model"] = next(l.split(":", 1)[1].strip() for l in f
-                                     if l.startswith("model name"))
-        with open("/proc/meminfo") as f:
-            host["ram_gb"] = round(int(next(l for l in f if l.startswith("MemTotal")).split()[1])
-                                   / 2 ** 20, 1)
-    except (OSError, StopIteration):
-        pass
+    host = host_info()
     return {"value": tok_s, "unit": "completion tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} token rows (every {step}th of {T}) x V={cfg.V}, "
                       f"{reps} passes in {el:.1f} s; mask and advantage over the whole batch",
             "single_thread": single, "host": host}
 
 
-def run_lmhead(cfg, case, args):
-    """Fused lm_head workload: hidden [T, H] and W [V, H] in, loss, dhidden, dW out."""
+def _spread(xs):
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def measure_lmhead(cfg, case, steps, warmup):
+    """Fused lm_head workload: hidden [T, H] and W [V, H] in, loss, dhidden,
+    dW out.  Per call: whole-call time (events between calls) and the
+    forward product's time (events stamped by its dispatch)."""
     import numpy as np
     import torch
 
@@ -176,45 +286,183 @@ def run_lmhead(cfg, case, args):
     _, mask_rows = dr.completion_mask(tokens, cfg.eos_id)
     adv, _ = dr.group_advantage(rewards, cfg.G)
     n_act = int(((mask_rows != 0) & (adv[:, None] != 0)).sum().item())
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None, **kw)
     torch.cuda.synchronize()
     # forward-product events on the stream the library launches on
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        e1.record()
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        cev[k].record()
+        dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None,
+                               fwd_events=evs[k], **kw)
+    cev[steps].record()
+    torch.cuda.synchronize()
+    ms_total = cev[0].elapsed_time(cev[steps])
+    call_ms = [cev[k].elapsed_time(cev[k + 1]) for k in range(steps)]
+    fwd_ms = [a.elapsed_time(b) for a, b in evs]
+    per_gemm = 2.0 * n_act * cfg.V * cfg.H  # one product over the active tokens
+    med = float(np.median(call_ms))
+    fwd_med = float(np.median(fwd_ms))
+    req = 3 * per_gemm / (med / 1e3) / 1e12
+    del kw, hidden, W, dh, dW, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": cfg.name, "B": cfg.B, "G": cfg.G, "C": cfg.C, "V": cfg.V, "H": cfg.H,
+        "token_rows": cfg.T, "active_tokens": n_act, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_total / steps, "call_ms": _spread(call_ms),
+        "tokens_per_s": cfg.T / (ms_total / steps / 1e3),
+        "forward_product": {"kernel": "k_gemm<GM_LSE>", "ms": _spread(fwd_ms),
+                            "tflops": per_gemm / (fwd_med / 1e3) / 1e12,
+                            "frac": per_gemm / (fwd_med / 1e3) / 1e12 / 2500.0},
+        "required_tflop_per_call": 3 * per_gemm / 1e12,
+        "call_tflops_required": req, "call_frac_required": req / 2500.0,
+        "call_tflops_executed": 4 * per_gemm / (med / 1e3) / 1e12,
+        "note": "required = logits, dhidden and dW products over the active tokens (the "
+                "recompute of the logits in the backward chunks is executed, not required); "
+                "frac against 2.5 PFLOP/s dense bf16",
+    }
+
+
+def _timed_ceiling(mode, src, dst, rows, row_bytes, stride, row_read, sink, reps=5):
+    """Median device time (HIP events stamped by the dispatch) of one
+    measurement-kernel launch on the current stream."""
+    import numpy as np
+    import torch
+
+    L = _ceil_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps + 1)]
     for e0, e1 in evs:
         e0.record()
         e1.record()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for k in range(args.steps):
-        dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None,
-                               fwd_events=evs[k], **kw)
-    t1.record()
+    for e0, e1 in evs:  # the first launch is a warm-up
+        rc = L.ceiling_rows(ptr(src), ptr(dst), rows, row_bytes, stride, mode, ptr(row_read),
+                            ptr(sink), st, e0.cuda_event, e1.cuda_event)
+        if rc != 0:
+            raise RuntimeError(f"ceiling_rows({mode}) returned {rc}")
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    per_gemm = 2.0 * n_act * cfg.V * cfg.H  # one product over the active tokens
-    achieved = per_gemm / (fwd_ms / 1e3) / 1e12
-    return {
-        "metric": METRIC, "value": cfg.T / (ms / 1e3), "unit": "completion tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded generator; no dataset or weights)",
-        "config": {"workload": cfg.name, "B": cfg.B, "G": cfg.G, "C": cfg.C, "V": cfg.V,
-                   "H": cfg.H, "token_rows": cfg.T, "active_tokens": n_act},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": achieved / 2500.0, "traffic": None,
-                     "kernel": "k_gemm<GM_LSE> (forward log-sum-exp product)",
-                     "kernel_ms": fwd_ms, "alg_flops_per_launch": per_gemm},
-        "call_tflops_required": 3 * per_gemm / (ms / 1e3) / 1e12,
-        "call_tflops_executed": 4 * per_gemm / (ms / 1e3) / 1e12,
-        "note": "required = logits, dhidden, dW products over the active tokens; executed "
-                "adds the logits recompute of the backward chunks",
-        "device": torch.cuda.get_device_name(0),
+    return float(np.median([a.elapsed_time(b) for a, b in evs[1:]]))
+
+
+def measure_loss(cfg, case, steps, warmup, ceilings=False):
+    """One loss workload: K timed calls after W warm-up calls; per call the
+    whole call (events between calls) and the row kernel (events stamped by
+    its dispatch).  With ceilings, the measurement kernels run afterwards on
+    the same buffers."""
+    import numpy as np
+    import torch
+
+    import synth
+    import rl_post_loss_dr_amd as dr
+
+    dev = torch.device("cuda:0")
+    torch_dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    logits = torch.empty((cfg.N, cfg.C, cfg.V), dtype=torch_dt, device=dev)
+    synth.gpu_normal_fill(logits, cfg.seed, synth.S_LOGITS, 0, cfg.logit_std)
+    tokens = torch.from_numpy(case.tokens).to(dev)
+    rewards = torch.from_numpy(case.rewards).to(dev)
+    lp = dr.logprobs(logits, tokens).double().cpu().numpy()
+    old = torch.from_numpy(synth.perturb(lp, case.old_noise)).to(dev)
+    ref = None if case.ref_noise is None else torch.from_numpy(
+        synth.perturb(lp, case.ref_noise)).to(dev)
+    dlogits = torch.empty_like(logits)
+    ws = dr.make_workspace(cfg.N, cfg.C, cfg.V, cfg.G, dev)
+    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const,
+              out_dlogits=dlogits, workspace=ws)
+    aux = {}
+    counts = torch.empty(2, dtype=torch.int64, device=dev)
+    dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, aux=aux, out_counts=counts,
+                    **kw)
+    torch.cuda.synchronize()
+    lens = aux["len"].cpu().numpy()
+    adv = aux["adv"].cpu().numpy()
+    stats = aux["stats"].cpu().numpy()
+    cnt = counts.cpu().numpy()
+    n_act, n_inact, alg_bytes, per_act, per_inact = _alg_bytes(cfg, adv, lens)
+    for _ in range(warmup):
+        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, **kw)
+    torch.cuda.synchronize()
+    # per-row-kernel events on the stream the library launches on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:  # create the underlying HIP events
+        e0.record()
+        e1.record()
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(steps):
+        cev[k].record()
+        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, rows_events=evs[k], **kw)
+    cev[steps].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = cev[0].elapsed_time(cev[steps])
+    call_ms = [cev[k].elapsed_time(cev[k + 1]) for k in range(steps)]
+    rows_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    rows_avg = float(np.mean(rows_ms))
+    if dr.device_status(ws) != dr.OK:
+        raise SystemExit("device status not OK")
+    achieved = alg_bytes / (rows_avg / 1e3) / 1e9
+    out = {
+        "workload": cfg.name, "B": cfg.B, "G": cfg.G, "C": cfg.C, "V": cfg.V, "dtype": cfg.dtype,
+        "token_rows": cfg.T, "beta": cfg.beta, "eps": cfg.eps, "norm_const": cfg.norm_const,
+        "active_rows": n_act, "inactive_rows": n_inact, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_total / steps, "tokens_per_s": cfg.T / (ms_total / steps / 1e3),
+        "valid_tokens_per_s": float(cnt[0]) / (ms_total / steps / 1e3),
+        "call_ms": _spread(call_ms), "k_rows_ms": _spread(rows_ms), "k_rows_ms_mean": rows_avg,
+        "alg_bytes_per_launch": alg_bytes, "bytes_per_active_row": per_act,
+        "bytes_per_inactive_row": per_inact, "achieved_gbps": achieved,
+        "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic(cfg.name),
+        "wall_s_timed": wall,
+        "rollout_stats": {
+            "groups": cfg.B, "groups_without_contrast": int(stats[0]),
+            "contrast_frac": 1.0 - float(stats[0]) / cfg.B,
+            "useful_groups_per_s": (cfg.B - float(stats[0])) / (ms_total / steps / 1e3),
+            "rows_without_eos": int(stats[1]), "truncation_rate": float(stats[1]) / cfg.N,
+            "mean_completion_len": float(cnt[0]) / cfg.N, "counted_tokens": int(cnt[0]),
+            "active_tokens": int(cnt[1]), "ratio_outside_clip": int(stats[2]),
+            "clip_cut_tokens": int(stats[3])},
     }
+    if ceilings and cfg.dtype == "bf16":
+        rb = cfg.V * 2
+        mask = np.arange(cfg.C)[None, :] < lens[:, None]
+        active = (mask & ((adv[:, None] != 0) | (cfg.beta != 0))).reshape(-1).astype(np.uint8)
+        act_t = torch.from_numpy(active).to(dev)
+        sink = torch.zeros(cfg.T, dtype=torch.int32, device=dev)
+        stride = _row_stride(cfg.T)
+        full = 2 * cfg.T * rb
+        t_copy = _timed_ceiling(0, logits, dlogits, cfg.T, rb, 1, None, sink)
+        t_fill = _timed_ceiling(1, None, dlogits, cfg.T, rb, 1, None, sink)
+        t_read = _timed_ceiling(2, logits, dlogits, cfg.T, rb, 1, None, sink)
+        t_skel = _timed_ceiling(0, logits, dlogits, cfg.T, rb, stride, act_t, sink)
+        skel_bytes = n_act * 2 * rb + n_inact * rb
+        out["ceilings"] = {
+            "how": "libceiling.so: one 1024-thread workgroup per row, every 16-byte load of a "
+                   "row in flight, nontemporal loads, sc1|nt buffer stores (the row kernel's "
+                   "access pattern, no arithmetic), on the same logits / dlogits buffers; "
+                   "median of 5 launches timed by dispatch events",
+            "copy_gbps": full / (t_copy / 1e3) / 1e9,
+            "fill_gbps": cfg.T * rb / (t_fill / 1e3) / 1e9,
+            "read_gbps": cfg.T * rb / (t_read / 1e3) / 1e9,
+            "skeleton": {"what": "this batch's active rows copied and zero rows filled, in the "
+                                 "row kernel's order: its data movement alone",
+                         "ms": t_skel, "gbps": skel_bytes / (t_skel / 1e3) / 1e9,
+                         "k_rows_frac_of_skeleton": t_skel / rows_avg},
+            "k_rows_frac_of_copy": achieved / (full / (t_copy / 1e3) / 1e9),
+        }
+    del kw, aux, logits, dlogits, ws, old, ref
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_decode(name, args):
@@ -446,6 +694,10 @@ def synth_perturb(lp, noise):
     return synth.perturb(lp, noise)
 
 
+EXTRA_LOSS = ["qwen_b8g16c512", "qwen_kl_b16g8c1024", "qwen_dense_b8g8c256"]
+EXTRA_STEPS = {"qwen_b8g16c512": 10, "qwen_kl_b16g8c1024": 10, "qwen_dense_b8g8c256": 20}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -453,6 +705,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen_b8g8c256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other workloads and the ceilings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 4 GiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -461,11 +715,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
-    import rl_post_loss_dr_amd as dr
 
     if args.calibrate_copy:
         # a plain copy kernel of known size: 4 GiB read + 4 GiB written per call
@@ -488,86 +740,33 @@ def main():
     cfg = synth.get_config(args.workload)
     case = synth.make_case(cfg)
     if cfg.H is not None:
-        print(json.dumps(run_lmhead(cfg, case, args)), flush=True)
+        r = measure_lmhead(cfg, case, args.steps, args.warmup)
+        rec = {
+            "metric": METRIC, "value": r["tokens_per_s"], "unit": "completion tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded generator; no dataset or weights)",
+            "config": {k: r[k] for k in ("workload", "B", "G", "C", "V", "H", "token_rows",
+                                         "active_tokens")},
+            "roofline": {"bound": "mfma", "achieved": r["forward_product"]["tflops"],
+                         "peak": 2500.0, "unit": "TFLOP/s", "frac": r["forward_product"]["frac"],
+                         "traffic": None, "kernel": "k_gemm<GM_LSE> (forward log-sum-exp product)",
+                         "kernel_ms": r["forward_product"]["ms"]["median"]},
+            "lmhead": r, "provenance": provenance(cfg.seed),
+        }
+        print(json.dumps(rec), flush=True)
         return
-    dev = torch.device("cuda:0")
-    torch_dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    logits = torch.empty((cfg.N, cfg.C, cfg.V), dtype=torch_dt, device=dev)
-    synth.gpu_normal_fill(logits, cfg.seed, synth.S_LOGITS, 0, cfg.logit_std)
-    tokens = torch.from_numpy(case.tokens).to(dev)
-    rewards = torch.from_numpy(case.rewards).to(dev)
-    lp = dr.logprobs(logits, tokens).double().cpu().numpy()
-    old = torch.from_numpy(synth.perturb(lp, case.old_noise)).to(dev)
-    ref = None if case.ref_noise is None else torch.from_numpy(
-        synth.perturb(lp, case.ref_noise)).to(dev)
-    dlogits = torch.empty_like(logits)
-    ws = dr.make_workspace(cfg.N, cfg.C, cfg.V, cfg.G, dev)
-    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const,
-              out_dlogits=dlogits, workspace=ws)
-    aux = {}
-    dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, aux=aux, **kw)
-    torch.cuda.synchronize()
-    lens = aux["len"].cpu().numpy()
-    adv = aux["adv"].cpu().numpy()
-    stats = aux["stats"].cpu().numpy()
-    n_act, n_inact, alg_bytes, per_act, per_inact = _alg_bytes(cfg, adv, lens)
 
-    for _ in range(args.warmup):
-        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, **kw)
-    torch.cuda.synchronize()
-
-    # per-row-kernel events on the stream the library launches on
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e0, e1 in evs:  # create the underlying HIP events
-        e0.record()
-        e1.record()
-    torch.cuda.synchronize()
-    # whole-call events between the calls (median / min per call)
-    cev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for k in range(args.steps):
-        cev[k].record()
-        dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, rows_events=evs[k], **kw)
-    cev[args.steps].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    call_ms = [cev[k].elapsed_time(cev[k + 1]) for k in range(args.steps)]
-    rows_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    rows_ms_avg = float(np.mean(rows_ms))
-    if dr.device_status(ws) != dr.OK:
-        raise SystemExit("device status not OK")
-    # a plain device copy of the logits into the dlogits buffer on the same
-    # box (read + write of N*C*V elements), after the timed region
-    copy_bytes = 2 * logits.numel() * logits.element_size()
-    for _ in range(2):
-        dlogits.copy_(logits)
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(5):
-        dlogits.copy_(logits)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbps = copy_bytes / (c0.elapsed_time(c1) / 5 / 1e3) / 1e9
-
-    tok_s = cfg.T / (ms_step / 1e3)
-    achieved = alg_bytes / (rows_ms_avg / 1e3) / 1e9
-    traffic = _traffic(args.workload)
+    head = measure_loss(cfg, case, args.steps, args.warmup, ceilings=not args.headline_only)
     rec = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": head["tokens_per_s"],
         "unit": "completion tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -575,32 +774,37 @@ def main():
         "data": "synthetic (seeded generator; no dataset or weights)",
         "config": {"workload": cfg.name, "B": cfg.B, "G": cfg.G, "C": cfg.C, "V": cfg.V,
                    "token_rows": cfg.T, "beta": cfg.beta, "eps": cfg.eps,
-                   "norm_const": cfg.norm_const, "active_rows": n_act, "inactive_rows": n_inact},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "k_rows", "kernel_ms": rows_ms_avg,
-                     "alg_bytes_per_launch": alg_bytes, "bytes_per_active_row": per_act,
-                     "bytes_per_inactive_row": per_inact},
-        "step_gbps_alg": alg_bytes / (ms_step / 1e3) / 1e9,
-        "call_ms_median": float(np.median(call_ms)),
-        "call_ms_min": float(np.min(call_ms)),
-        "k_rows_ms_median": float(np.median(rows_ms)),
-        "k_rows_ms_min": float(np.min(rows_ms)),
-        "valid_tokens_per_s": float(stats[4]) / (ms_step / 1e3),
-        "copy_ref": {"gbps": copy_gbps, "bytes_per_call": copy_bytes,
-                     "how": "torch copy_ of the logits tensor into the dlogits tensor",
-                     "k_rows_frac_of_copy": achieved / copy_gbps},
-        "rollout_stats": {
-            "groups": cfg.B, "groups_without_contrast": int(stats[0]),
-            "contrast_frac": 1.0 - float(stats[0]) / cfg.B,
-            "useful_groups_per_s": (cfg.B - float(stats[0])) / (ms_step / 1e3),
-            "rows_without_eos": int(stats[1]), "truncation_rate": float(stats[1]) / cfg.N,
-            "mean_completion_len": float(stats[4]) / cfg.N, "counted_tokens": int(stats[4]),
-            "active_tokens": int(stats[5]), "ratio_outside_clip": int(stats[2]),
-            "clip_cut_tokens": int(stats[3])},
-        "wall_s_timed": wall,
-        "device": torch.cuda.get_device_name(0),
+                   "norm_const": cfg.norm_const, "active_rows": head["active_rows"],
+                   "inactive_rows": head["inactive_rows"]},
+        "roofline": {"bound": "hbm", "achieved": head["achieved_gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": head["frac"], "traffic": head["traffic"],
+                     "kernel": "k_rows", "kernel_ms": head["k_rows_ms_mean"],
+                     "alg_bytes_per_launch": head["alg_bytes_per_launch"],
+                     "bytes_per_active_row": head["bytes_per_active_row"],
+                     "bytes_per_inactive_row": head["bytes_per_inactive_row"]},
+        "step_gbps_alg": head["alg_bytes_per_launch"] / (head["ms_per_step"] / 1e3) / 1e9,
+        "call_ms": head["call_ms"],
+        "k_rows_ms": head["k_rows_ms"],
+        "valid_tokens_per_s": head["valid_tokens_per_s"],
+        "rollout_stats": head["rollout_stats"],
+        "wall_s_timed": head["wall_s_timed"],
     }
+    if "ceilings" in head:
+        rec["ceilings"] = head["ceilings"]
+    rec["provenance"] = provenance(cfg.seed)
+    if not args.headline_only and cfg.name == "qwen_b8g8c256":
+        work = {}
+        for name in EXTRA_LOSS:
+            c = synth.get_config(name)
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            r = measure_loss(c, synth.make_case(c), EXTRA_STEPS[name], 3,
+                             ceilings=name == "qwen_dense_b8g8c256")
+            r.pop("rollout_stats", None)
+            work[name] = r
+        c = synth.get_config("lmhead_b8g8c512")
+        print(f"[bench] {c.name}", file=sys.stderr, flush=True)
+        work[c.name] = measure_lmhead(c, synth.make_case(c), 5, 2)
+        rec["workloads"] = work
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, case)
     print(json.dumps(rec), flush=True)

@@ -65,10 +65,10 @@ enum {
   DRGRPO_ERR_PARAM = -3,       /* eps, beta or norm_const invalid (see each call) */
   DRGRPO_ERR_DTYPE = -4,       /* unknown drgrpo_dtype_t */
   DRGRPO_ERR_WORKSPACE = -5,   /* workspace NULL, too small or not 256-byte aligned */
-  DRGRPO_ERR_ALIAS = -6,       /* out_dlogits partially overlaps logits */
+  DRGRPO_ERR_ALIGN = -6,       /* a pointer lacks the alignment the call requires */
   DRGRPO_ERR_HIP = -7,         /* a HIP launch failed */
   DRGRPO_ERR_TOKEN_RANGE = -8, /* device-side: a token at a mask=1 position is outside [0, V) */
-  DRGRPO_ERR_ALIGN = -9,       /* a pointer lacks the alignment the call requires */
+  DRGRPO_ERR_ALIAS = -9,       /* out_dlogits partially overlaps logits */
   DRGRPO_ERR_SCRATCH_LIMIT = -10 /* sizes exceed the static scratch of
                                     drgrpo_loss_fwd_bwd_noalloc */
 };
@@ -102,8 +102,10 @@ size_t drgrpo_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t G);
  *               bfloat16 results are rounded to nearest even from binary32.
  *   workspace   device buffer of drgrpo_workspace_bytes(N, C, V, G) bytes.
  *
- * The logits may have any V; rows whose byte size is a multiple of 16 with
- * 16-byte aligned bases take the vector path, others the element path.
+ * The logits may have any V up to 2^28; rows whose byte size is a multiple of
+ * 16 with 16-byte aligned bases take the vector path, others the element
+ * path.  One workgroup runs per token row, so N*C is limited to 2^24 - 1
+ * rows for V <= 4864 and to 2^22 - 1 rows above (DRGRPO_ERR_SHAPE).
  * Device-side errors (a token outside [0, V) at a mask=1 position) make the
  * loss and that token's dlogits row NaN and set the status word. */
 int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_id,
@@ -167,41 +169,64 @@ typedef struct drgrpo_aux {
   float* adv;       /* [N] advantages */
   float* logp;      /* [N, C] log-probs of active tokens, 0 elsewhere */
   float* tok_loss;  /* [N, C] per-token lambda, 0 for inactive tokens */
-  int64_t* stats;   /* [6] groups without reward contrast, rows without EOS,
+  int32_t* stats;   /* [4] groups without reward contrast, rows without EOS,
                        active tokens with r outside [1-eps, 1+eps], active
-                       tokens whose surrogate gradient the clip cuts, counted
-                       tokens (sum of len), active tokens (counted tokens of
-                       rows with A != 0, or all counted tokens if beta > 0) */
-  void* rows_event_begin; /* hipEvent_t stamped when the per-row kernel's
-                             dispatch starts (NULL: none), to time it alone */
-  void* rows_event_end;   /* hipEvent_t stamped when it ends (NULL: none) */
+                       tokens whose surrogate gradient the clip cuts */
 } drgrpo_aux_t;
 
-/* drgrpo_loss_fwd_bwd plus the diagnostics `aux` asks for (aux may be NULL)
- * and a normalisation variant (variant may be NULL: Dr. GRPO; an unknown
- * mode is DRGRPO_ERR_PARAM).  With a variant, coef = -g / div_i where div_i
- * is row i's divisor above (norm_const, norm_const*len_i or
- * norm_const*sum len). */
+/* drgrpo_loss_fwd_bwd plus the diagnostics `aux` asks for (aux may be NULL). */
 int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
                            const float* rewards, const float* logp_old, const float* logp_ref,
                            int64_t G, float eps, float beta, float norm_const, float* out_loss,
                            void* out_dlogits, int64_t N, int64_t C, int64_t V,
                            drgrpo_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                           void* stream, const drgrpo_aux_t* aux,
-                           const drgrpo_variant_t* variant);
+                           void* stream, const drgrpo_aux_t* aux);
+
+/* Further options of the loss call; every field may be NULL / 0. */
+typedef struct drgrpo_loss_opts {
+  const drgrpo_variant_t* variant; /* normalisation variant (NULL: Dr. GRPO; an unknown
+                                      mode is DRGRPO_ERR_PARAM).  With a variant,
+                                      coef = -g / div_i where div_i is row i's divisor
+                                      above (norm_const, norm_const*len_i or
+                                      norm_const*sum len) */
+  int64_t* token_counts;  /* [2] on the device: counted tokens (sum of len), active
+                             tokens (counted tokens of rows with A != 0, or all counted
+                             tokens if beta > 0) */
+  void* rows_event_begin; /* hipEvent_t stamped when the per-row kernel's dispatch
+                             starts, to time it alone */
+  void* rows_event_end;   /* hipEvent_t stamped when it ends */
+  int32_t require_vector_path; /* nonzero: operands that would take the element path
+                                  (row bytes not a multiple of 16, or logits / dlogits
+                                  not 16-byte aligned) return DRGRPO_ERR_ALIGN
+                                  before anything is enqueued */
+} drgrpo_loss_opts_t;
+
+/* drgrpo_loss_fwd_bwd_ex plus the options `opts` holds (opts may be NULL). */
+int drgrpo_loss_fwd_bwd_opts(const void* logits, const int64_t* tokens, int64_t eos_id,
+                             const float* rewards, const float* logp_old,
+                             const float* logp_ref, int64_t G, float eps, float beta,
+                             float norm_const, float* out_loss, void* out_dlogits, int64_t N,
+                             int64_t C, int64_t V, drgrpo_dtype_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream, const drgrpo_aux_t* aux,
+                             const drgrpo_loss_opts_t* opts);
 
 /* Completion mask alone ("The completion mask"): out_len [N] int32 (required),
  * out_mask [N, C] uint8 (may be NULL). */
 int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t C, int64_t eos_id,
                            int32_t* out_len, uint8_t* out_mask, void* stream);
 
-/* Group advantages alone ("Dr. GRPO", or "GRPO" with adv_mode =
- * DRGRPO_ADV_ZSCORE; another value is DRGRPO_ERR_PARAM): out_adv [N] float
- * (required); out_nocontrast [1] int32 (may be NULL) receives the number of
- * groups whose rewards are all equal ("The sparse-reward bottleneck" of "The
- * Quiet Library"). */
-int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, int32_t adv_mode,
-                           float* out_adv, int32_t* out_nocontrast, void* stream);
+/* Group advantages alone ("Dr. GRPO": A_i = R_i - group mean): out_adv [N]
+ * float (required); out_nocontrast [1] int32 (may be NULL) receives the
+ * number of groups whose rewards are all equal ("The sparse-reward
+ * bottleneck" of "The Quiet Library"). */
+int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G, float* out_adv,
+                           int32_t* out_nocontrast, void* stream);
+
+/* drgrpo_group_advantage with an advantage mode: DRGRPO_ADV_CENTER (the
+ * same result) or DRGRPO_ADV_ZSCORE ("GRPO": divided by the group's sample
+ * standard deviation); another value is DRGRPO_ERR_PARAM. */
+int drgrpo_group_advantage_ex(const float* rewards, int64_t N, int64_t G, int32_t adv_mode,
+                              float* out_adv, int32_t* out_nocontrast, void* stream);
 
 /* Forward-only log-probs of every token ("compute_logprobs"), the no-gradient
  * pass that produces logp_old / logp_ref: out_logp [N, C] float.  A token
@@ -245,7 +270,7 @@ typedef struct drgrpo_lmhead_aux {
 } drgrpo_lmhead_aux_t;
 
 /* drgrpo_lmhead_loss_fwd_bwd with a normalisation variant (NULL: Dr. GRPO),
- * as for drgrpo_loss_fwd_bwd_ex, and optional timing hooks (aux may be NULL). */
+ * as in drgrpo_loss_opts_t, and optional timing hooks (aux may be NULL). */
 int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W, const int64_t* tokens,
                                   int64_t eos_id, const float* rewards, const float* logp_old,
                                   const float* logp_ref, int64_t G, float eps, float beta,

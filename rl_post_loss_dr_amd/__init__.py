@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE = -1, -2, -3, -4
-ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOKEN_RANGE, ERR_ALIGN = -5, -6, -7, -8, -9
+ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_TOKEN_RANGE, ERR_ALIAS = -5, -6, -7, -8, -9
 ERR_SCRATCH_LIMIT = -10
 NOALLOC_SCRATCH_BYTES = 12 << 20  # DRGRPO_NOALLOC_SCRATCH_BYTES
 
@@ -44,8 +44,13 @@ class _Variant(ctypes.Structure):
 class _Aux(ctypes.Structure):
     _fields_ = [("len", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("adv", ctypes.c_void_p),
                 ("logp", ctypes.c_void_p), ("tok_loss", ctypes.c_void_p),
-                ("stats", ctypes.c_void_p), ("rows_event_begin", ctypes.c_void_p),
-                ("rows_event_end", ctypes.c_void_p)]
+                ("stats", ctypes.c_void_p)]
+
+
+class _LossOpts(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_void_p), ("token_counts", ctypes.c_void_p),
+                ("rows_event_begin", ctypes.c_void_p), ("rows_event_end", ctypes.c_void_p),
+                ("require_vector_path", ctypes.c_int32)]
 
 
 _lib = None
@@ -68,15 +73,19 @@ def lib() -> ctypes.CDLL:
                   _SZ, _P]
         L.drgrpo_loss_fwd_bwd.argtypes = common
         L.drgrpo_loss_fwd_bwd.restype = _I
-        L.drgrpo_loss_fwd_bwd_ex.argtypes = common + [ctypes.POINTER(_Aux),
-                                                      ctypes.POINTER(_Variant)]
+        L.drgrpo_loss_fwd_bwd_ex.argtypes = common + [ctypes.POINTER(_Aux)]
         L.drgrpo_loss_fwd_bwd_ex.restype = _I
+        L.drgrpo_loss_fwd_bwd_opts.argtypes = common + [ctypes.POINTER(_Aux),
+                                                        ctypes.POINTER(_LossOpts)]
+        L.drgrpo_loss_fwd_bwd_opts.restype = _I
         L.drgrpo_loss_fwd_bwd_noalloc.argtypes = common[:16] + [_P]
         L.drgrpo_loss_fwd_bwd_noalloc.restype = _I
         L.drgrpo_completion_mask.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
         L.drgrpo_completion_mask.restype = _I
-        L.drgrpo_group_advantage.argtypes = [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P]
+        L.drgrpo_group_advantage.argtypes = [_P, _I64, _I64, _P, _P, _P]
         L.drgrpo_group_advantage.restype = _I
+        L.drgrpo_group_advantage_ex.argtypes = [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P]
+        L.drgrpo_group_advantage_ex.restype = _I
         L.drgrpo_logprobs.argtypes = [_P, _P, _I64, _I64, _I64, _I, _P, _P]
         L.drgrpo_logprobs.restype = _I
         L.drgrpo_lmhead_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64]
@@ -139,6 +148,21 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> torch.Te
     return t
 
 
+def _ws(workspace: torch.Tensor, dev: torch.device) -> torch.Tensor:
+    """A caller-supplied workspace: a contiguous uint8 tensor on the inputs'
+    device (a host buffer would be written by the kernels)."""
+    _dev(workspace, "workspace", torch.uint8)
+    if workspace.device != dev:
+        raise ValueError(f"workspace must be on {dev}, got {workspace.device}")
+    return workspace
+
+
+def _same_device(dev: torch.device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be on {dev}, got {t.device}")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -163,7 +187,8 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
                  eps: float = 0.2, beta: float = 0.0, norm_const: float | None = None,
                  out_dlogits: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  aux: dict | None = None, rows_events=None, adv_mode: int = ADV_CENTER,
-                 agg: int = AGG_TOKEN_SUM):
+                 agg: int = AGG_TOKEN_SUM, out_counts: torch.Tensor | None = None,
+                 require_vector_path: bool = False):
     """Loss and dlogits of the Dr. GRPO update for one rollout batch.
 
     logits [N, C, V] float32/bfloat16 (the completion slice: row t scores
@@ -171,11 +196,15 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
     logp_ref [N, C] float32.  norm_const defaults to G*C.  Returns
     (loss [] float32 device tensor, dlogits like logits).  `out_dlogits` may
     be `logits` itself (in place).  `aux` (a dict) receives device tensors
-    len, mask, adv, logp, tok_loss, stats when given.  `rows_events` is an
+    len, mask, adv, logp, tok_loss and stats (int32 [4]) when given;
+    `out_counts` (int64 [2] device tensor) receives the counted and active
+    tokens.  `rows_events` is an
     optional pair of recorded torch.cuda.Event (enable_timing=True) that the
     library records around its per-row kernel on the current stream.
     adv_mode / agg select GRPO's normalisations (ADV_ZSCORE, AGG_SEQ_MEAN) or
     the token mean (AGG_TOKEN_MEAN) instead of Dr. GRPO's.
+    require_vector_path turns an operand that would take the element path
+    (row bytes not a multiple of 16, unaligned bases) into ERR_ALIGN.
     """
     if logits.dim() != 3:
         raise ValueError("logits must be [N, C, V]")
@@ -194,15 +223,24 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
         out_dlogits = torch.empty_like(logits)
     else:
         _dev(out_dlogits, "out_dlogits", logits.dtype, (N, C, V))
+    _same_device(dev, tokens=tokens, rewards=rewards, logp_old=logp_old, logp_ref=logp_ref,
+                 out_dlogits=out_dlogits)
     if workspace is None:
         workspace = make_workspace(N, C, V, G, dev)
+    else:
+        _ws(workspace, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     args = (logits.data_ptr(), tokens.data_ptr(), int(eos_id), rewards.data_ptr(),
             logp_old.data_ptr(), _ptr(logp_ref), int(G), float(eps), float(beta),
             float(norm_const), loss.data_ptr(), out_dlogits.data_ptr(), N, C, V, dt,
             workspace.data_ptr(), workspace.numel(), _stream(dev))
+    if out_counts is not None:
+        _dev(out_counts, "out_counts", torch.int64, (2,))
+        _same_device(dev, out_counts=out_counts)
     variant = (adv_mode, agg) != (ADV_CENTER, AGG_TOKEN_SUM)
-    if aux is None and rows_events is None and not variant:
+    opts_needed = (variant or rows_events is not None or require_vector_path or
+                   out_counts is not None)
+    if aux is None and not opts_needed:
         _check(lib().drgrpo_loss_fwd_bwd(*args), "drgrpo_loss_fwd_bwd")
         return loss, out_dlogits
     s = _Aux()
@@ -212,15 +250,24 @@ def loss_fwd_bwd(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int, reward
         aux["adv"] = torch.empty(N, dtype=torch.float32, device=dev)
         aux["logp"] = torch.empty((N, C), dtype=torch.float32, device=dev)
         aux["tok_loss"] = torch.empty((N, C), dtype=torch.float32, device=dev)
-        aux["stats"] = torch.empty(6, dtype=torch.int64, device=dev)
+        aux["stats"] = torch.empty(4, dtype=torch.int32, device=dev)
         for k in ("len", "mask", "adv", "logp", "tok_loss", "stats"):
             setattr(s, k, aux[k].data_ptr())
-    if rows_events is not None:
-        s.rows_event_begin = rows_events[0].cuda_event
-        s.rows_event_end = rows_events[1].cuda_event
+    if not opts_needed:
+        _check(lib().drgrpo_loss_fwd_bwd_ex(*args, ctypes.byref(s)), "drgrpo_loss_fwd_bwd_ex")
+        return loss, out_dlogits
     var = _Variant(int(adv_mode), int(agg))
-    _check(lib().drgrpo_loss_fwd_bwd_ex(*args, ctypes.byref(s), ctypes.byref(var)),
-           "drgrpo_loss_fwd_bwd_ex")
+    o = _LossOpts()
+    if variant:
+        o.variant = ctypes.addressof(var)
+    if out_counts is not None:
+        o.token_counts = out_counts.data_ptr()
+    if rows_events is not None:
+        o.rows_event_begin = rows_events[0].cuda_event
+        o.rows_event_end = rows_events[1].cuda_event
+    o.require_vector_path = 1 if require_vector_path else 0
+    _check(lib().drgrpo_loss_fwd_bwd_opts(*args, ctypes.byref(s), ctypes.byref(o)),
+           "drgrpo_loss_fwd_bwd_opts")
     return loss, out_dlogits
 
 
@@ -248,9 +295,8 @@ def loss_fwd_bwd_noalloc(logits: torch.Tensor, tokens: torch.Tensor, eos_id: int
     if out_loss.numel() != 1:
         raise ValueError("out_loss must hold one element")
     _dev(out_dlogits, "out_dlogits", logits.dtype, (N, C, V))
-    for t in (tokens, rewards, logp_old, logp_ref, out_loss, out_dlogits):
-        if t is not None and t.device != dev:
-            raise ValueError("every tensor must be on the logits' device")
+    _same_device(dev, tokens=tokens, rewards=rewards, logp_old=logp_old, logp_ref=logp_ref,
+                 out_loss=out_loss, out_dlogits=out_dlogits)
     if norm_const is None:
         norm_const = float(G * C)
     _check(lib().drgrpo_loss_fwd_bwd_noalloc(
@@ -293,15 +339,22 @@ def group_advantage(rewards: torch.Tensor, G: int, mode: int = ADV_CENTER):
     N = rewards.numel()
     adv = torch.empty(N, dtype=torch.float32, device=rewards.device)
     cnt = torch.empty(1, dtype=torch.int32, device=rewards.device)
-    _check(lib().drgrpo_group_advantage(rewards.data_ptr(), N, int(G), int(mode), adv.data_ptr(),
-                                        cnt.data_ptr(), _stream(rewards.device)),
-           "drgrpo_group_advantage")
+    if mode == ADV_CENTER:
+        _check(lib().drgrpo_group_advantage(rewards.data_ptr(), N, int(G), adv.data_ptr(),
+                                            cnt.data_ptr(), _stream(rewards.device)),
+               "drgrpo_group_advantage")
+    else:
+        _check(lib().drgrpo_group_advantage_ex(rewards.data_ptr(), N, int(G), int(mode),
+                                               adv.data_ptr(), cnt.data_ptr(),
+                                               _stream(rewards.device)),
+               "drgrpo_group_advantage_ex")
     return adv, cnt
 
 
 def device_status(workspace: torch.Tensor) -> int:
     """Synchronises the current stream and returns the status word of the last
     loss call that used `workspace` (OK or ERR_TOKEN_RANGE)."""
+    _dev(workspace, "workspace", torch.uint8)
     return int(lib().drgrpo_device_status(workspace.data_ptr(), _stream(workspace.device)))
 
 
@@ -342,13 +395,21 @@ def lmhead_loss_fwd_bwd(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Ten
         norm_const = float(G * C)
     if out_dhidden is None:
         out_dhidden = torch.empty_like(hidden)
+    else:
+        _dev(out_dhidden, "out_dhidden", torch.bfloat16, hidden.shape)
     if out_dW is None:
         out_dW = torch.empty_like(W)
+    else:
+        _dev(out_dW, "out_dW", torch.bfloat16, (V, H))
+    _same_device(dev, W=W, tokens=tokens, rewards=rewards, logp_old=logp_old, logp_ref=logp_ref,
+                 out_dhidden=out_dhidden, out_dW=out_dW)
     if workspace is None:
         n = lmhead_workspace_bytes(N, C, V, H, G)
         if n == 0:
             raise DrGRPOError(ERR_SHAPE, "drgrpo_lmhead_workspace_bytes")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    else:
+        _ws(workspace, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     var = _Variant(int(adv_mode), int(agg))
     lmaux = None
@@ -383,11 +444,14 @@ def lmhead_logprobs(hidden: torch.Tensor, W: torch.Tensor, tokens: torch.Tensor,
         raise ValueError(f"hidden must hold N*C rows of H={H}")
     _dev(tokens, "tokens", torch.int64)
     dev = hidden.device
+    _same_device(dev, W=W, tokens=tokens)
     if workspace is None:
         n = lmhead_logprobs_workspace_bytes(N, C, V, H)
         if n == 0:
             raise DrGRPOError(ERR_SHAPE, "drgrpo_lmhead_logprobs_workspace_bytes")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    else:
+        _ws(workspace, dev)
     out = torch.empty((N, C), dtype=torch.float32, device=dev)
     _check(lib().drgrpo_lmhead_logprobs(
         hidden.data_ptr(), W.data_ptr(), tokens.data_ptr(), int(eos_id), N, C, V, H,
@@ -420,11 +484,14 @@ def decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     dev = q.device
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
+    _same_device(dev, k_cache=k_cache, v_cache=v_cache, lens=lens)
     if workspace is None:
         n = decode_attention_workspace_bytes(S, Hq, Hkv, Lmax, D)
         if n == 0:
             raise DrGRPOError(ERR_SHAPE, "drgrpo_decode_attention_workspace_bytes")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    else:
+        _ws(workspace, dev)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
     else:
@@ -463,11 +530,14 @@ def decode_attention_rope(qkv: torch.Tensor, rope_cos: torch.Tensor, rope_sin: t
     _dev(pos, "pos", torch.int32, (S,))
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
+    _same_device(dev, qkv=qkv, v_cache=v_cache, rope_cos=rope_cos, rope_sin=rope_sin, pos=pos)
     if workspace is None:
         n = decode_attention_rope_workspace_bytes(S, Hq, Hkv, Lmax, D)
         if n == 0:
             raise DrGRPOError(ERR_SHAPE, "drgrpo_decode_attention_rope_workspace_bytes")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    else:
+        _ws(workspace, dev)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
     else:

@@ -1,0 +1,112 @@
+/*
+ * ceiling.hip - measurement kernels for gfx950, outside the loss: the HBM
+ * rate of the per-row kernel's access pattern with no arithmetic, and the
+ * device's properties, so that a benchmark can put the row kernel next to
+ * what its data movement alone reaches on the same GPU in the same process.
+ *
+ * One workgroup of 1024 threads per row of up to 311,296 bytes, as the loss
+ * kernel runs a vocabulary row: every lane issues all of its (up to 19)
+ * 16-byte nontemporal loads before using any, then stores 16-byte chunks
+ * through a buffer descriptor bounded by the row with the same cache policy
+ * (sc1 | nt).  Rows are visited in the order workgroup b -> row
+ * (b * row_stride) mod rows.
+ */
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "ceiling.h"
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kNch = 19;
+constexpr int kStorePolicy = 16 | 2;          // sc1 | nt
+constexpr int kRawBufferWord3 = 0x00020000;   // raw, byte-addressed buffer
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// mode: CEILING_COPY (read the row, write it to dst), CEILING_FILL (write
+// zeros), CEILING_READ (read the row; one word per row written so the loads
+// stay live).  With row_read set, rows whose flag is 0 are written as zeros
+// without a read and the others copied (the loss's active / zero-row mix).
+__global__ void __launch_bounds__(kThreads)
+k_ceiling(const char* __restrict__ src, char* __restrict__ dst, uint32_t row_bytes, uint32_t rows,
+          uint32_t row_stride, int mode, const uint8_t* __restrict__ row_read,
+          uint32_t* __restrict__ sink) {
+  const uint32_t row = (uint32_t)(((uint64_t)blockIdx.x * row_stride) % rows);
+  const int tid = threadIdx.x;
+  const uint32_t nchunks = row_bytes / 16;
+  const uint32_t last = nchunks - 1;
+  const u32x4* in = reinterpret_cast<const u32x4*>(src + (size_t)row * row_bytes);
+  const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+      dst + (size_t)row * row_bytes, (short)0, (int)row_bytes, kRawBufferWord3);
+  bool read = mode != CEILING_FILL;
+  if (row_read && mode == CEILING_COPY) read = row_read[row] != 0;
+  if (!read) {
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    for (uint32_t c = tid; c < nchunks; c += kThreads)
+      __builtin_amdgcn_raw_buffer_store_b128(z, out, (int)(c * 16u), 0, kStorePolicy);
+    return;
+  }
+  u32x4 buf[kNch];
+#pragma unroll
+  for (int j = 0; j < kNch; ++j) {
+    const uint32_t c = (uint32_t)j * kThreads + tid;
+    buf[j] = __builtin_nontemporal_load(in + (c < nchunks ? c : last));
+  }
+  if (mode == CEILING_READ) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < kNch; ++j) x ^= buf[j].x ^ buf[j].y ^ buf[j].z ^ buf[j].w;
+    if (x == 0x9E3779B9u) sink[row] = x;  // practically never: keeps the loads live
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < kNch; ++j) {
+    const uint32_t c = (uint32_t)j * kThreads + tid;
+    if (c < nchunks) __builtin_amdgcn_raw_buffer_store_b128(buf[j], out, (int)(c * 16u), 0, kStorePolicy);
+  }
+}
+
+}  // namespace
+
+extern "C" int ceiling_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                            int64_t row_stride, int32_t mode, const uint8_t* row_read,
+                            uint32_t* sink, void* stream, void* ev_begin, void* ev_end) {
+  // one 1024-thread workgroup per row: fewer than 2^32 work-items per dispatch
+  if (rows <= 0 || rows > (int64_t)(UINT32_MAX / kThreads) || row_bytes <= 0 || row_bytes % 16 != 0 ||
+      row_bytes > (int64_t)kNch * kThreads * 16 || row_stride <= 0 || row_stride > UINT32_MAX)
+    return -2;
+  if (mode != CEILING_COPY && mode != CEILING_FILL && mode != CEILING_READ) return -3;
+  if (!dst || ((mode != CEILING_FILL) && !src) || (mode == CEILING_READ && !sink)) return -1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0) return -6;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipExtLaunchKernelGGL(k_ceiling, dim3((unsigned)rows), dim3(kThreads), 0, st,
+                        static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end), 0,
+                        static_cast<const char*>(src), static_cast<char*>(dst),
+                        (uint32_t)row_bytes, (uint32_t)rows, (uint32_t)row_stride, (int)mode,
+                        row_read, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+extern "C" int ceiling_device_info(int device, ceiling_device_info_t* out) {
+  if (!out) return -1;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, device) != hipSuccess) return -7;
+  memset(out, 0, sizeof *out);
+  strncpy(out->name, p.name, sizeof out->name - 1);
+  strncpy(out->arch, p.gcnArchName, sizeof out->arch - 1);
+  out->compute_units = p.multiProcessorCount;
+  out->clock_khz = p.clockRate;
+  out->memory_clock_khz = p.memoryClockRate;
+  out->memory_bus_bits = p.memoryBusWidth;
+  out->total_mem_bytes = (int64_t)p.totalGlobalMem;
+  out->l2_bytes = p.l2CacheSize;
+  int rt = 0, drv = 0;
+  hipRuntimeGetVersion(&rt);
+  hipDriverGetVersion(&drv);
+  out->runtime_version = rt;
+  out->driver_version = drv;
+  return 0;
+}

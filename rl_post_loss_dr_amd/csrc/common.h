@@ -185,12 +185,14 @@ __device__ inline int wave_sum_i(int v) {
 }
 
 // tok_loss holds each token's term already divided by its row divisor, so
-// the loss is their plain sum (fixed order).  Counters: see drgrpo_aux_t.
+// the loss is their plain sum (fixed order).  Counters: drgrpo_aux_t.stats
+// and drgrpo_loss_opts_t.token_counts.
 __global__ void __launch_bounds__(1024)
 k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_flags, int64_t T,
          const uint8_t* __restrict__ row_flags, const int32_t* __restrict__ len,
          const float* __restrict__ adv, float beta, int64_t N, float* __restrict__ out_loss,
-         int32_t* __restrict__ status, int64_t* __restrict__ aux_stats) {
+         int32_t* __restrict__ status, int32_t* __restrict__ aux_stats,
+         int64_t* __restrict__ aux_counts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   double s = 0.0;
   int n_out = 0, n_cut = 0, n_bad = 0, n_trunc = 0, n_noc = 0;
@@ -262,13 +264,15 @@ k_finish(const double* __restrict__ tok_loss, const uint8_t* __restrict__ tok_fl
     status[0] = c[2] ? kStatusTokenRange : 0;
     status[1] = (int32_t)c[3];
     status[2] = (int32_t)c[4];
-    if (aux_stats) {
-      aux_stats[0] = c[4];
-      aux_stats[1] = c[3];
-      aux_stats[2] = c[0];
-      aux_stats[3] = c[1];
-      aux_stats[4] = nl;
-      aux_stats[5] = na;
+    if (aux_stats) {  // each count is at most the token rows, below 2^31
+      aux_stats[0] = (int32_t)c[4];
+      aux_stats[1] = (int32_t)c[3];
+      aux_stats[2] = (int32_t)c[0];
+      aux_stats[3] = (int32_t)c[1];
+    }
+    if (aux_counts) {
+      aux_counts[0] = nl;
+      aux_counts[1] = na;
     }
   }
 }

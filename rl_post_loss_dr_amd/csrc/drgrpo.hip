@@ -522,15 +522,20 @@ uint32_t row_stride_for(int64_t T) {
   return (uint32_t)s;
 }
 
+// Rows move in 16-byte chunks when their byte size is a multiple of 16 and
+// both bases are 16-byte aligned (dlogits NULL: the forward-only pass).
+bool vector_path(const void* logits, const void* dlogits, int64_t V, drgrpo_dtype_t dtype) {
+  const size_t esz = dtype == DRGRPO_BF16 ? 2 : 4;
+  return ((size_t)V * esz) % 16 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(dlogits) % 16 == 0;
+}
+
 template <bool kFwdOnly>
 int launch_rows(RowArgs a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
                 hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
   a.T = (uint32_t)T;
   a.row_stride = row_stride_for(T);
-  const size_t esz = dtype == DRGRPO_BF16 ? 2 : 4;
-  const bool vec = ((size_t)a.V * esz) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 &&
-                   (kFwdOnly || reinterpret_cast<uintptr_t>(a.dlogits) % 16 == 0);
+  const bool vec = vector_path(a.logits, kFwdOnly ? nullptr : a.dlogits, a.V, dtype);
   const dim3 grid((unsigned)T);
   auto go = [&](auto kernel, int nt) {
     const dim3 block((unsigned)nt);
@@ -568,6 +573,11 @@ int check_shape(int64_t N, int64_t C, int64_t V, int64_t G, int64_t* T, int64_t*
   if (V > (int64_t(1) << 28)) return DRGRPO_ERR_SHAPE;  // per-row offsets are 32-bit
   if (!mul_ok(N, C, T)) return DRGRPO_ERR_SHAPE;
   if (*T > INT32_MAX) return DRGRPO_ERR_SHAPE;  // one workgroup per token row
+  // and a dispatch holds fewer than 2^32 work-items: T x 256 threads when a
+  // 256-thread register tile holds every row whatever the path (V up to
+  // kNch * 256 elements), else T x 1024
+  const int64_t nt_max = V <= (int64_t)kNch * 256 ? 256 : kThreads;
+  if (*T > (int64_t)UINT32_MAX / nt_max) return DRGRPO_ERR_SHAPE;
   if (!mul_ok(*T, V, elems)) return DRGRPO_ERR_SHAPE;
   int64_t bytes;
   if (!mul_ok(*elems, 4, &bytes)) return DRGRPO_ERR_SHAPE;
@@ -624,13 +634,14 @@ int enqueue_loss(const void* logits, const int64_t* tokens, int64_t eos_id, cons
                  const float* logp_old, const float* logp_ref, int64_t G, float eps, float beta,
                  float norm_const, float* out_loss, void* out_dlogits, int64_t N, int64_t C,
                  int64_t V, int64_t T, drgrpo_dtype_t dtype, void* workspace, hipStream_t st,
-                 const drgrpo_aux_t* aux, const drgrpo_variant_t* variant) {
+                 const drgrpo_aux_t* aux, const drgrpo_loss_opts_t* opts) {
+  const drgrpo_loss_opts_t no_opts = {};
+  const drgrpo_loss_opts_t& o = opts ? *opts : no_opts;
   int adv_mode, agg;
-  read_variant(variant, &adv_mode, &agg);
+  read_variant(o.variant, &adv_mode, &agg);
   Ws ws;
   ws_carve(workspace, N, T, &ws);
-  const drgrpo_aux_t none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                             nullptr};
+  const drgrpo_aux_t none = {};
   const drgrpo_aux_t& x = aux ? *aux : none;
 
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
@@ -663,16 +674,41 @@ int enqueue_loss(const void* logits, const int64_t* tokens, int64_t eos_id, cons
   a.aux_logp = x.logp;
   a.aux_tok_loss = x.tok_loss;
   a.out_logp = nullptr;
-  rc = launch_rows<false>(a, T, dtype, st, static_cast<hipEvent_t>(x.rows_event_begin),
-                         static_cast<hipEvent_t>(x.rows_event_end));
+  rc = launch_rows<false>(a, T, dtype, st, static_cast<hipEvent_t>(o.rows_event_begin),
+                         static_cast<hipEvent_t>(o.rows_event_end));
   if (rc != DRGRPO_OK) return rc;
 
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, ws.tok_loss, ws.tok_flags, T,
-                     ws.row_flags, ws.len, ws.adv, beta, N, out_loss, ws.status, x.stats);
+                     ws.row_flags, ws.len, ws.adv, beta, N, out_loss, ws.status, x.stats,
+                     o.token_counts);
   return launch_status();
 }
 
 }  // namespace
+
+extern "C" int drgrpo_loss_fwd_bwd_opts(const void* logits, const int64_t* tokens,
+                                        int64_t eos_id, const float* rewards,
+                                        const float* logp_old, const float* logp_ref, int64_t G,
+                                        float eps, float beta, float norm_const, float* out_loss,
+                                        void* out_dlogits, int64_t N, int64_t C, int64_t V,
+                                        drgrpo_dtype_t dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream,
+                                        const drgrpo_aux_t* aux, const drgrpo_loss_opts_t* opts) {
+  int64_t T, elems;
+  const int rc = check_loss_args(logits, tokens, rewards, logp_old, logp_ref, G, eps, beta,
+                                 norm_const, out_loss, out_dlogits, N, C, V, dtype,
+                                 opts ? opts->variant : nullptr, &T, &elems);
+  if (rc != DRGRPO_OK) return rc;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < ws_carve(nullptr, N, T, nullptr))
+    return DRGRPO_ERR_WORKSPACE;
+  if (check_alias(logits, out_dlogits, elems, dtype) != DRGRPO_OK) return DRGRPO_ERR_ALIAS;
+  if (opts && opts->require_vector_path && !vector_path(logits, out_dlogits, V, dtype))
+    return DRGRPO_ERR_ALIGN;
+  return enqueue_loss(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
+                      norm_const, out_loss, out_dlogits, N, C, V, T, dtype, workspace,
+                      static_cast<hipStream_t>(stream), aux, opts);
+}
 
 extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens, int64_t eos_id,
                                       const float* rewards, const float* logp_old,
@@ -680,19 +716,10 @@ extern "C" int drgrpo_loss_fwd_bwd_ex(const void* logits, const int64_t* tokens,
                                       float norm_const, float* out_loss, void* out_dlogits,
                                       int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
                                       void* workspace, size_t workspace_bytes, void* stream,
-                                      const drgrpo_aux_t* aux, const drgrpo_variant_t* variant) {
-  int64_t T, elems;
-  const int rc = check_loss_args(logits, tokens, rewards, logp_old, logp_ref, G, eps, beta,
-                                 norm_const, out_loss, out_dlogits, N, C, V, dtype, variant, &T,
-                                 &elems);
-  if (rc != DRGRPO_OK) return rc;
-  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
-      workspace_bytes < ws_carve(nullptr, N, T, nullptr))
-    return DRGRPO_ERR_WORKSPACE;
-  if (check_alias(logits, out_dlogits, elems, dtype) != DRGRPO_OK) return DRGRPO_ERR_ALIAS;
-  return enqueue_loss(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
-                      norm_const, out_loss, out_dlogits, N, C, V, T, dtype, workspace,
-                      static_cast<hipStream_t>(stream), aux, variant);
+                                      const drgrpo_aux_t* aux) {
+  return drgrpo_loss_fwd_bwd_opts(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps,
+                                  beta, norm_const, out_loss, out_dlogits, N, C, V, dtype,
+                                  workspace, workspace_bytes, stream, aux, nullptr);
 }
 
 extern "C" int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_id,
@@ -701,9 +728,9 @@ extern "C" int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, in
                                    float norm_const, float* out_loss, void* out_dlogits,
                                    int64_t N, int64_t C, int64_t V, drgrpo_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  return drgrpo_loss_fwd_bwd_ex(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta,
-                                norm_const, out_loss, out_dlogits, N, C, V, dtype, workspace,
-                                workspace_bytes, stream, nullptr, nullptr);
+  return drgrpo_loss_fwd_bwd_opts(logits, tokens, eos_id, rewards, logp_old, logp_ref, G, eps,
+                                  beta, norm_const, out_loss, out_dlogits, N, C, V, dtype,
+                                  workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 // ------------------------------------------------ no-allocation entry point
@@ -773,9 +800,9 @@ extern "C" int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t 
   return launch_status();
 }
 
-extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G,
-                                      int32_t adv_mode, float* out_adv,
-                                      int32_t* out_nocontrast, void* stream) {
+extern "C" int drgrpo_group_advantage_ex(const float* rewards, int64_t N, int64_t G,
+                                         int32_t adv_mode, float* out_adv,
+                                         int32_t* out_nocontrast, void* stream) {
   if (!rewards || !out_adv) return DRGRPO_ERR_NULL;
   if (N <= 0 || G <= 0 || N % G != 0 || N > INT32_MAX) return DRGRPO_ERR_SHAPE;
   if (adv_mode != DRGRPO_ADV_CENTER && adv_mode != DRGRPO_ADV_ZSCORE) return DRGRPO_ERR_PARAM;
@@ -791,6 +818,12 @@ extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G
                      (uint8_t*)nullptr, (int32_t*)nullptr, (uint8_t*)nullptr, out_adv,
                      out_nocontrast);
   return launch_status();
+}
+
+extern "C" int drgrpo_group_advantage(const float* rewards, int64_t N, int64_t G,
+                                      float* out_adv, int32_t* out_nocontrast, void* stream) {
+  return drgrpo_group_advantage_ex(rewards, N, G, DRGRPO_ADV_CENTER, out_adv, out_nocontrast,
+                                   stream);
 }
 
 extern "C" int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_t C,

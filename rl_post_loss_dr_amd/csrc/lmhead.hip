@@ -1239,7 +1239,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
                      tokens, C, V, static_cast<uint16_t*>(out_dhidden));
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, st, w.tok_loss, w.tok_flags, T,
-                     w.row_flags, w.len, w.adv, beta, N, out_loss, w.status, (int64_t*)nullptr);
+                     w.row_flags, w.len, w.adv, beta, N, out_loss, w.status, (int32_t*)nullptr,
+                     (int64_t*)nullptr);
   return launch_status();
 }
 

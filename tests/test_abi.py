@@ -34,6 +34,9 @@ def test_exports_every_declared_symbol(L):
 
 def test_workspace_bytes(L):
     assert L.drgrpo_workspace_bytes(64, 256, 151936, 8) > 64 * 256 * 8
+    # the dispatch limit: T x 1024 threads below 2^32 (V > 4864)
+    assert L.drgrpo_workspace_bytes(1 << 14, 1 << 8, 151936, 8) == 0
+    assert L.drgrpo_workspace_bytes((1 << 14) - 8, 1 << 8, 151936, 8) > 0
     assert L.drgrpo_workspace_bytes(0, 256, 151936, 8) == 0
     assert L.drgrpo_workspace_bytes(64, 256, 151936, 7) == 0
     assert L.drgrpo_workspace_bytes(64, 0, 10, 8) == 0
@@ -73,6 +76,12 @@ def _call(L, **kw):
     (dict(G=0), dr.ERR_SHAPE),
     (dict(G=7), dr.ERR_SHAPE),
     (dict(N=1 << 40, C=1 << 30), dr.ERR_SHAPE),
+    # one 1024-thread workgroup per token row: at most 2^22 - 1 rows
+    (dict(N=1 << 14, C=1 << 8), dr.ERR_SHAPE),
+    (dict(N=(1 << 14) - 8, C=1 << 8, ws=None), dr.ERR_WORKSPACE),
+    # 256-thread workgroups (V <= 4864): at most 2^24 - 1 rows
+    (dict(N=1 << 16, C=1 << 8, V=4864), dr.ERR_SHAPE),
+    (dict(N=(1 << 16) - 8, C=1 << 8, V=4864, ws=None), dr.ERR_WORKSPACE),
     (dict(eps=-0.1), dr.ERR_PARAM),
     (dict(eps=float("nan")), dr.ERR_PARAM),
     (dict(beta=-1.0, ref=FAKE), dr.ERR_PARAM),
@@ -93,9 +102,11 @@ def test_argument_validation(L, kw, code):
 def test_other_entry_points_validate(L):
     assert L.drgrpo_completion_mask(None, 4, 4, 0, FAKE, None, None) == dr.ERR_NULL
     assert L.drgrpo_completion_mask(FAKE, 0, 4, 0, FAKE, None, None) == dr.ERR_SHAPE
-    assert L.drgrpo_group_advantage(FAKE, 8, 3, 0, FAKE, None, None) == dr.ERR_SHAPE
-    assert L.drgrpo_group_advantage(None, 8, 4, 0, FAKE, None, None) == dr.ERR_NULL
-    assert L.drgrpo_group_advantage(FAKE, 8, 4, 2, FAKE, None, None) == dr.ERR_PARAM
+    assert L.drgrpo_group_advantage(FAKE, 8, 3, FAKE, None, None) == dr.ERR_SHAPE
+    assert L.drgrpo_group_advantage(None, 8, 4, FAKE, None, None) == dr.ERR_NULL
+    assert L.drgrpo_group_advantage_ex(FAKE, 8, 3, 0, FAKE, None, None) == dr.ERR_SHAPE
+    assert L.drgrpo_group_advantage_ex(None, 8, 4, 0, FAKE, None, None) == dr.ERR_NULL
+    assert L.drgrpo_group_advantage_ex(FAKE, 8, 4, 2, FAKE, None, None) == dr.ERR_PARAM
     assert L.drgrpo_lmhead_logprobs(None, FAKE, FAKE, 0, 2, 4, 64, 32, FAKE, FAKE, 1 << 30,
                                     None) == dr.ERR_NULL
     assert L.drgrpo_lmhead_logprobs(FAKE, FAKE, FAKE, 0, 2, 4, 64, 30, FAKE, FAKE, 1 << 30,
@@ -164,7 +175,9 @@ def test_variant_validation(L, adv_mode, agg, code):
     var = dr._Variant(adv_mode, agg)
     args = (FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE * 1000000, 64, 256,
             151936, 1, FAKE * 4096, 16, None)
-    assert L.drgrpo_loss_fwd_bwd_ex(*args, None, ctypes.byref(var)) == code
+    opts = dr._LossOpts()
+    opts.variant = ctypes.addressof(var)
+    assert L.drgrpo_loss_fwd_bwd_opts(*args, None, ctypes.byref(opts)) == code
     lm = (FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE, FAKE, 64, 256,
           4096, 896, FAKE * 4096, 16, None)
     assert L.drgrpo_lmhead_loss_fwd_bwd_ex(*lm, ctypes.byref(var), None) == code
@@ -224,3 +237,79 @@ def test_noalloc_validates_before_touching_the_scratch(L):
     assert dr.workspace_bytes(655360, 1, 8, 1) <= dr.NOALLOC_SCRATCH_BYTES
     # partial overlap of dlogits with logits
     assert call({11: FAKE + 64}) == dr.ERR_ALIAS
+
+
+# The boundary as built, call by call: the status codes and, for the calls
+# the loss's scope names, the parameter types in order (`void* stream` is a
+# hipStream_t, so the header needs no HIP include).  Extra calls and options
+# (variants, counters, timing hooks, the fused lm_head's variant entry point,
+# the decode attention, the no-allocation call) are additions after these.
+STATUS = {"DRGRPO_OK": 0, "DRGRPO_ERR_NULL": -1, "DRGRPO_ERR_SHAPE": -2,
+          "DRGRPO_ERR_PARAM": -3, "DRGRPO_ERR_DTYPE": -4, "DRGRPO_ERR_WORKSPACE": -5,
+          "DRGRPO_ERR_ALIGN": -6, "DRGRPO_ERR_HIP": -7, "DRGRPO_ERR_TOKEN_RANGE": -8,
+          "DRGRPO_ERR_ALIAS": -9, "DRGRPO_ERR_SCRATCH_LIMIT": -10}
+_LOSS = ("const void*,const int64_t*,int64_t,const float*,const float*,const float*,int64_t,"
+         "float,float,float,float*,void*,int64_t,int64_t,int64_t,drgrpo_dtype_t,void*,size_t,"
+         "void*")
+SIGNATURES = {
+    "drgrpo_workspace_bytes": "int64_t,int64_t,int64_t,int64_t",
+    "drgrpo_loss_fwd_bwd": _LOSS,
+    "drgrpo_loss_fwd_bwd_ex": _LOSS + ",const drgrpo_aux_t*",
+    "drgrpo_completion_mask": "const int64_t*,int64_t,int64_t,int64_t,int32_t*,uint8_t*,void*",
+    "drgrpo_group_advantage": "const float*,int64_t,int64_t,float*,int32_t*,void*",
+    "drgrpo_logprobs": "const void*,const int64_t*,int64_t,int64_t,int64_t,drgrpo_dtype_t,"
+                       "float*,void*",
+    "drgrpo_lmhead_loss_fwd_bwd": "const void*,const void*,const int64_t*,int64_t,const float*,"
+                                  "const float*,const float*,int64_t,float,float,float,float*,"
+                                  "void*,void*,int64_t,int64_t,int64_t,int64_t,void*,size_t,void*",
+    "drgrpo_device_status": "const void*,void*",
+    "drgrpo_status_string": "int",
+}
+AUX_FIELDS = ["int32_t* len", "uint8_t* mask", "float* adv", "float* logp", "float* tok_loss",
+              "int32_t* stats"]
+
+
+def _header():
+    src = open(os.path.join(ROOT, "include", "drgrpo.h")).read()
+    return re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+
+
+def _norm_type(t):
+    t = re.sub(r"\s+", " ", t.strip())
+    return re.sub(r"\s*\*", "*", t)
+
+
+def test_boundary_matches_its_record():
+    src = _header()
+    enum = dict((k, int(v)) for k, v in re.findall(r"\b(DRGRPO_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", src))
+    assert enum == STATUS
+    decls = {}
+    for name, params in re.findall(r"\b(drgrpo_\w+)\s*\(([^;{]*?)\)\s*;", src, flags=re.S):
+        types = [_norm_type(re.sub(r"\b\w+\s*$", "", p)) for p in params.split(",")]
+        decls[name] = ",".join(types)
+    for name, sig in SIGNATURES.items():
+        assert decls.get(name) == sig, (name, decls.get(name))
+    body = re.search(r"typedef struct drgrpo_aux \{(.*?)\} drgrpo_aux_t;", src, flags=re.S).group(1)
+    fields = [_norm_type(f.strip()).replace("*", "* ").replace("  ", " ").strip()
+              for f in body.split(";") if f.strip()]
+    assert fields == AUX_FIELDS
+    # the status codes the binding mirrors
+    for k, v in STATUS.items():
+        assert getattr(dr, k.replace("DRGRPO_", "")) == v, k
+
+
+def test_require_vector_path_turns_the_element_path_into_an_align_error(L):
+    """Opt-in strict mode: a bfloat16 row whose byte size is not a multiple of
+    16 (V % 8 != 0) or an unaligned base is DRGRPO_ERR_ALIGN before any
+    launch; without it such rows take the element path."""
+    args = [FAKE, FAKE, 0, FAKE, FAKE, None, 8, 0.2, 0.0, 2048.0, FAKE, FAKE * 10 ** 7, 64, 256,
+            151937, 1, FAKE * 4096, 1 << 40, None]
+    opts = dr._LossOpts()
+    opts.require_vector_path = 1
+    assert L.drgrpo_loss_fwd_bwd_opts(*args, None, ctypes.byref(opts)) == dr.ERR_ALIGN
+    args[14] = 151936
+    args[0] = FAKE + 2
+    assert L.drgrpo_loss_fwd_bwd_opts(*args, None, ctypes.byref(opts)) == dr.ERR_ALIGN
+    # float32 rows of any V are a multiple of 4 bytes: V % 4 != 0 is the element path
+    args[0], args[14], args[15] = FAKE, 151937, 0
+    assert L.drgrpo_loss_fwd_bwd_opts(*args, None, ctypes.byref(opts)) == dr.ERR_ALIGN

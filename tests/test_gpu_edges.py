@@ -46,11 +46,12 @@ def _run_case(x, tokens, eos_id, rewards, G, dtype, beta=0.0, kappa=None, ref_no
     kappa = float(G * C) if kappa is None else kappa
     res = oracle.loss_fwd_bwd(host, tokens, eos_id, rewards, old, ref, G, f32(0.2), f32(beta),
                               f32(kappa))
-    aux = {}
+    aux = {"counts": torch.empty(2, dtype=torch.int64, device=DEV)}
     loss, d = dr.loss_fwd_bwd(dev, torch.from_numpy(tokens).to(DEV), eos_id,
                               torch.from_numpy(rewards).to(DEV), torch.from_numpy(old).to(DEV),
                               None if ref is None else torch.from_numpy(ref).to(DEV), G=G,
-                              eps=0.2, beta=beta, norm_const=kappa, aux=aux)
+                              eps=0.2, beta=beta, norm_const=kappa, aux=aux,
+                              out_counts=aux["counts"])
     torch.cuda.synchronize()
     got = d.float().cpu().numpy().astype(np.float64).reshape(N * C, V)
     cfg = _Cfg(dtype, kappa, beta=beta)
@@ -131,7 +132,7 @@ def test_no_reward_contrast_anywhere():
     loss, got, res, aux, cfg = _run_case(x, tokens, 0, rewards, 4, "bf16")
     assert loss == 0.0 and (got == 0).all()
     st = aux["stats"].cpu().numpy()
-    assert st[0] == 4 and st[5] == 0
+    assert st[0] == 4 and int(aux["counts"][1]) == 0
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

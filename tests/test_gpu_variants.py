@@ -41,11 +41,12 @@ def test_variant_parity_small(name, adv_mode, agg, kappa_one):
     print(f"case {name} adv_mode={adv_mode} agg={agg} kappa_one={kappa_one}", flush=True)
     cfg, case, x, old, ref, res, k = _case(name, adv_mode, agg, 1.0 if kappa_one else None)
     aux = {}
+    counts = torch.empty(2, dtype=torch.int64, device=DEV)
     loss, d = dr.loss_fwd_bwd(
         to_device_logits(x, cfg, DEV), torch.from_numpy(case.tokens).to(DEV), cfg.eos_id,
         torch.from_numpy(case.rewards).to(DEV), torch.from_numpy(old).to(DEV),
         None if ref is None else torch.from_numpy(ref).to(DEV), G=cfg.G, eps=cfg.eps,
-        beta=cfg.beta, norm_const=k, aux=aux, adv_mode=adv_mode, agg=agg)
+        beta=cfg.beta, norm_const=k, aux=aux, adv_mode=adv_mode, agg=agg, out_counts=counts)
     torch.cuda.synchronize()
     # advantages: bit-exact binary32 (sample std, correctly rounded sqrt and division)
     assert np.array_equal(aux["adv"].cpu().numpy().view(np.uint32), res.adv.view(np.uint32))
@@ -53,7 +54,8 @@ def test_variant_parity_small(name, adv_mode, agg, kappa_one):
     st = aux["stats"].cpu().numpy()
     mask = np.arange(cfg.C)[None, :] < res.len[:, None]
     act = mask & ((res.adv[:, None] != 0) | (cfg.beta != 0))
-    assert st[4] == res.len.sum() and st[5] == act.sum()
+    ct = counts.cpu().numpy()
+    assert ct[0] == res.len.sum() and ct[1] == act.sum()
     assert st[2] == res.stats[0] and st[3] == res.stats[1]
     # loss: relative to the same aggregation of |lambda| when it cancels
     div = oracle.row_divisor(res.len, k, agg)
