@@ -8,19 +8,21 @@
  * have a non-zero gradient; they are compacted first and every GEMM runs over
  * them alone.  All products are C = A . B^T with both operands stored with
  * the reduction dimension contiguous ("NT"), computed by one MFMA kernel
- * (v_mfma_f32_16x16x32_bf16, binary32 accumulation) with four epilogues:
+ * (v_mfma_f32_16x16x32_bf16, binary32 accumulation) with three epilogues:
  *
  *   GM_LSE    logits tile of H_a . W^T -> per-token (max, sum exp) over the
- *             tile's vocabulary columns, plus the sampled token's logit
- *   GM_D      logits tile recomputed for one vocabulary chunk ->
- *             dlogits = coef*(softmax - onehot) in bfloat16, stored for the
- *             chunk only, row-major and transposed
+ *             tile's vocabulary columns, the sampled token's logit, and
+ *             E = exp(x - m) of every logit in binary16 (m the maximum of
+ *             its row in a 64-column block)
  *   GM_ACC    dhidden += dlogits_chunk . W_chunk   (binary32 accumulator)
  *   GM_STORE  dW_chunk = dlogits_chunk^T . H_a     (bfloat16 result)
  *
- * Transposed copies of the compacted hidden states and of each vocabulary
- * chunk of W give every product its reduction dimension contiguous.  No
- * floating-point atomics: results are bitwise reproducible.
+ * Between them, one vocabulary chunk at a time, k_lm_dchunk streams E into
+ * dlogits = coef*(softmax - onehot) in bfloat16, row-major and transposed
+ * (no product is computed twice).  Transposed copies of the compacted hidden
+ * states and of each vocabulary chunk of W give every product its reduction
+ * dimension contiguous.  No floating-point atomics: results are bitwise
+ * reproducible.
  */
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -60,6 +62,12 @@ constexpr bool kTablesInRing = kRingElems * 2 + kTableBytes > kLdsMax;
 constexpr int kTableElem = kTablesInRing ? kRingElems - kTableBytes / 2 : kRingElems;
 constexpr size_t kGemmLds = kRingElems * sizeof(uint16_t) + (kTablesInRing ? 0 : kTableBytes);
 static_assert(kGemmLds <= (size_t)kLdsMax, "LDS ring too deep");
+// The forward product's per-wavefront (max, sum exp) table sits past the row
+// tables: its epilogue stages the exponentials in the ring.
+constexpr int kRedElem = (int)(kGemmLds / sizeof(uint16_t));
+constexpr size_t kRedBytes = sizeof(float2) * NWN * GBM;
+constexpr size_t kGemmLdsLse = kGemmLds + kRedBytes;
+static_assert(kGemmLdsLse <= (size_t)kLdsMax, "forward product's LDS");
 static_assert(!kTablesInRing || kRingElems - kTableBytes / 2 >= (GT / 64) * WM * WN,
               "epilogue staging overlaps the tables");
 static_assert((GT / 64) * WM * WN <= kRingElems, "epilogue staging exceeds the ring");
@@ -71,7 +79,8 @@ constexpr int kChunkV = 32768;
 constexpr float kL2E = 1.4426950408889634f;
 constexpr double kL2ED = 1.4426950408889634074;
 
-enum { GM_LSE = 0, GM_D = 1, GM_ACC = 2, GM_STORE = 3 };
+enum { GM_LSE = 0, GM_ACC = 2, GM_STORE = 3 };
+
 
 struct GemmArgs {
   // Operands in bfloat16.  Element (r, k) of A sits at
@@ -89,14 +98,15 @@ struct GemmArgs {
   int64_t ntn;
   float* xy;             // [rows] sampled token's logit
   const int32_t* ycol;   // [rows] sampled token id
-  int64_t col_base;      // vocabulary id of column 0 (GM_LSE, GM_D)
-  // GM_D
-  const float2* lsep;    // [rows] (row maximum M, log2 S) with lse = M + ln S
-  const float* coef;     // [rows]
-  uint16_t* D;           // chunk of dlogits, K-paneled over its columns: (t, c) at
-  int64_t ldd;           //   D[(c / 32) * ldd + t * 32 + c % 32]
-  uint16_t* Dt;          // the chunk transposed, K-paneled over tokens: (c, t) at
-  int64_t ldt;           //   Dt[(t / 32) * ldt + c * 32 + t % 32]
+  int64_t col_base;      // vocabulary id of column 0
+  // GM_LSE, optional (NULL: not stored): E = exp(x - m) of every logit in
+  // binary16, with m the maximum of its row over the 64 columns of one
+  // wavefront block, K-paneled over the vocabulary: (t, v) at
+  // E[(v / 32) * lde + t * 32 + v % 32]; the maxima at wmax[t * ldw + v / 64]
+  uint16_t* E;
+  int64_t lde;
+  float* wmax;
+  int64_t ldw;
   // GM_ACC / GM_STORE
   float* Cf;             // [M, ldc] binary32 accumulator
   uint16_t* Cb;          // [M, ldc] bfloat16 result
@@ -128,6 +138,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // in the low half
 __device__ inline uint32_t bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// the same in binary16 (one v_cvt_pk_f16_f32, nearest even)
+__device__ inline uint32_t f16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 
 // Cross-lane moves within a DPP row of 16 lanes (lanes sharing l / 16).  A
@@ -226,14 +241,11 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   const int64_t K = g.K_dev ? (int64_t)*g.K_dev : g.K;
   // tile order: each XCD (workgroup id mod 8) takes a contiguous run of one
   // linear order, so the workgroups sharing its L2 share operand tiles.  The
-  // order runs along the operand that is small: row tiles fastest when B is
-  // the large operand (the vocabulary-wide products), column tiles fastest
-  // when A is (the products reducing over a dlogits chunk).  The forward
-  // product walks groups of kColGroup column tiles row by row, so the 32
-  // workgroups an XCD runs at once share 4 row tiles and 8 column tiles
-  // (12 distinct operand panels per reduction step instead of 33); the
-  // dlogits product keeps whole column runs, which keeps its transposed
-  // stores local.
+  // order runs along the operand that is small: column tiles fastest for
+  // the products reducing over a dlogits chunk (A is the large operand).
+  // The forward product walks groups of kColGroup column tiles row by row,
+  // so the 32 workgroups an XCD runs at once share 4 row tiles and 8 column
+  // tiles (12 distinct operand panels per reduction step instead of 33).
   // The grid covers the static row bound; only the tiles of the first M rows
   // (M read on the device) take part, spread evenly over the XCDs.
   // (32-bit index arithmetic: the host keeps the grid below 2^31 workgroups)
@@ -244,7 +256,6 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   if (b >= total) return;
   const int q8 = total / 8;
   const int v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
-  constexpr bool kColsFastest = MODE == GM_ACC || MODE == GM_STORE;
   int tm, tn;
   if constexpr (MODE == GM_LSE) {
     constexpr int kColGroup = 8;
@@ -254,8 +265,8 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     tm = w / gw;
     tn = (v < grouped ? v / (kColGroup * ntm) * kColGroup : grouped / ntm) + w % gw;
   } else {
-    tm = kColsFastest ? v / ntn_t : v % ntm;
-    tn = kColsFastest ? v % ntn_t : v / ntm;
+    tm = v / ntn_t;
+    tn = v % ntn_t;
   }
   const int64_t m0 = (int64_t)tm * GBM;
   const int64_t n0 = (int64_t)tn * GBN;
@@ -350,29 +361,17 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // loads cost no wait of their own.
   //   GM_LSE: tile-local column of the row's sampled token (-1: none, or a
   //           column of another tile, which never equals a local column)
-  //   GM_D:   (M, log2 S) of the row's log-sum-exp, coef, sampled column
-  float2* const t_sp = reinterpret_cast<float2*>(smem + kTableElem);  // GM_D [GBM]
-  float* const t_sc = reinterpret_cast<float*>(t_sp + GBM);          // GM_D [GBM]
-  int32_t* const t_yl =
-      MODE == GM_LSE ? reinterpret_cast<int32_t*>(smem + kTableElem)  // [GBM]
-                     : reinterpret_cast<int32_t*>(t_sc + GBM);
-  constexpr bool kTables = MODE == GM_LSE || MODE == GM_D;
+  int32_t* const t_yl = reinterpret_cast<int32_t*>(smem + kTableElem);  // [GBM]
+  constexpr bool kTables = MODE == GM_LSE;
   static_assert(!kTables || !kTablesInRing, "the epilogue tables are written while waves may still read the ring");
   constexpr int kYPer = (GBM + GT - 1) / GT;
   int32_t ypre[kYPer];
-  float2 lpre[kYPer];
-  float cpre[kYPer];
   if constexpr (kTables) {
 #pragma unroll
     for (int k = 0; k < kYPer; ++k) {
       const int r = tid + k * GT;
       const bool ok = r < GBM && m0 + r < M;
       ypre[k] = ok ? g.ycol[m0 + r] : -1;
-      if constexpr (MODE == GM_D) {
-        // rows past the active count: exp2(-inf) gives exact zeros
-        lpre[k] = ok ? g.lsep[m0 + r] : make_float2(0.0f, INFINITY);
-        cpre[k] = ok ? g.coef[m0 + r] : 0.0f;
-      }
     }
   }
   if (nk > 0)
@@ -439,10 +438,6 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
       const int r = tid + k * GT;
       if (r < GBM) {
         t_yl[r] = ypre[k] < 0 ? -1 : (int32_t)(ypre[k] - (g.col_base + n0));
-        if constexpr (MODE == GM_D) {
-          t_sp[r] = lpre[k];
-          t_sc[r] = cpre[k];
-        }
       }
     }
   }
@@ -459,8 +454,10 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   const int ncols = (int)(g.N - n0 < GBN ? g.N - n0 : GBN);
   const int lc0 = wn * WN + fr;  // tile-local column of acc[.][0]
   if constexpr (MODE == GM_LSE) {
-    float2* red = reinterpret_cast<float2*>(smem);  // [NWN][GBM]
+    float2* red = reinterpret_cast<float2*>(smem + kRedElem);  // [NWN][GBM]
     const int32_t* yl = t_yl;
+    const bool keepE = g.E != nullptr;
+    uint16_t* stg = smem + wave * (WM * WN);  // this wavefront's E stage
     // full tiles (the common case) compile without the column checks
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
@@ -519,9 +516,26 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
           // entry (the rounding of M*log2e scales the whole partial sum by one
           // factor 2^d, |d| <= 2^-24 |M| log2e)
           const float nb = kFull || mx[r] != -INFINITY ? -mx[r] * kL2E : 0.0f;
-          sm[r] = __builtin_amdgcn_exp2f(fmaf(acc[i][0][r], kL2E, nb));
+          // the exponentials replace the logits in acc (E below)
+          acc[i][0][r] = __builtin_amdgcn_exp2f(fmaf(acc[i][0][r], kL2E, nb));
+          sm[r] = acc[i][0][r];
 #pragma unroll
-          for (int j = 1; j < FN; ++j) sm[r] += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, nb));
+          for (int j = 1; j < FN; ++j) {
+            acc[i][j][r] = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, nb));
+            sm[r] += acc[i][j][r];
+          }
+        }
+        if (keepE) {
+          // binary16 pairs (nearest even) into this wavefront's stage
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            stage_pair(stg, lane, i, j, f16x2_bits(acc[i][j][0], acc[i][j][1]),
+                       f16x2_bits(acc[i][j][2], acc[i][j][3]));
+          if (fr == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (m0 + rt0 + r < M) g.wmax[(m0 + rt0 + r) * g.ldw + tn * NWN + wn] = mx[r];
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor1>(sm[r]);
@@ -542,6 +556,22 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     else
       body(BoolC<false>{});
     __syncthreads();
+    if (keepE) {
+      // rows up to the active count rounded up to kPad and columns up to the
+      // vocabulary rounded up to kPad are written (past the vocabulary the
+      // exponentials are exact zeros; rows past the active count are never
+      // read)
+      const int64_t mpad = (M + kPad - 1) / kPad * kPad;
+      const int64_t npad = (g.N + kPad - 1) / kPad * kPad;
+      const int nrows_w = (int)(mpad - m0 < GBM ? mpad - m0 : GBM);
+      const int ncols_w = (int)(npad - n0 < GBN ? npad - n0 : GBN);
+      const int rw0 = wm * WM, cw0 = wn * WN;
+      uint16_t* dst = g.E + (n0 + cw0) / 32 * g.lde + (m0 + rw0) * 32;
+      if (ncols_w == GBN && nrows_w == GBM)
+        store_staged_rows<true>(stg, lane, dst, 32, g.lde, WM, WN);
+      else
+        store_staged_rows<false>(stg, lane, dst, 32, g.lde, nrows_w - rw0, ncols_w - cw0);
+    }
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       if (row >= M) continue;
@@ -558,119 +588,11 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
       }
       g.part[row * g.ntn + tn] = make_float2(mx, sm);
     }
-  } else if constexpr (MODE == GM_D) {
-    // per-row tables
-    const float2* sp = t_sp;
-    const float* sc = t_sc;
-    const int32_t* yl = t_yl;
-    // rows up to the active count rounded up to kPad, columns up to the
-    // chunk width rounded up to kPad are written (zeros past the data), so
-    // the products over the chunk may read whole kPad blocks
-    const int64_t mpad = (M + kPad - 1) / kPad * kPad;
-    const int64_t npad = (g.N + kPad - 1) / kPad * kPad;
-    const int nrows_w = (int)(mpad - m0 < GBM ? mpad - m0 : GBM);
-    const int ncols_w = (int)(npad - n0 < GBN ? npad - n0 : GBN);
-    // Each wavefront stages its 128 x 64 block of dlogits in its own 16 KB of
-    // the (now idle) ring, column-major: row c of the stage holds column c of
-    // the block, 128 bfloat16 in 32 eight-byte quads, quad q stored at
-    // q ^ stage_swz(c).  Both stores then leave with 16-byte accesses.
-    uint16_t* stg = smem + wave * (WM * WN);
-    auto body = [&](auto full_tag) {
-      constexpr bool kFull = decltype(full_tag)::value;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int rt0 = wm * WM + i * 16 + rq;
-        const float4 pa = *reinterpret_cast<const float4*>(sp + rt0);
-        const float4 pb = *reinterpret_cast<const float4*>(sp + rt0 + 2);
-        const float4 c4 = *reinterpret_cast<const float4*>(sc + rt0);
-        const int4 y4 = *reinterpret_cast<const int4*>(yl + rt0);
-        const float mv[4] = {pa.x, pa.z, pb.x, pb.z};
-        const float lv[4] = {pa.y, pa.w, pb.y, pb.w};
-        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-        const int dy[4] = {y4.x - lc0, y4.y - lc0, y4.z - lc0, y4.w - lc0};
-        // Every entry but the sampled token's is coef * exp(x - lse) =
-        // sign(coef) * exp2(x*log2e + c) with c = log2|coef| - M*log2e - log2 S
-        // per row: one fused step and one exp per entry.  The rounding of c
-        // scales a row's entries by one factor 2^d, |d| <= 2^-24 |c|, far
-        // below the bfloat16 result's resolution; coef = 0 gives c = -inf and
-        // exact zeros.  The sign goes onto the packed bfloat16 bits.
-        float cr[4];
-        uint32_t sg[2];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          cr[r] = fmaf(-mv[r], kL2E, __builtin_amdgcn_logf(fabsf(cv[r])) - lv[r]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          sg[h] = ((__builtin_bit_cast(uint32_t, cv[2 * h]) >> 16) & 0x8000u) |
-                  (__builtin_bit_cast(uint32_t, cv[2 * h + 1]) & 0x80000000u);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const bool live = kFull || lc0 + j * 16 < ncols;
-          float e[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            e[r] = live ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kL2E, cr[r])) : 0.0f;
-          stage_pair(stg, lane, i, j, bf16x2_bits(e[0], e[1]) | sg[0],
-                     bf16x2_bits(e[2], e[3]) | sg[1]);
-        }
-        // the sampled token's entry, coef * (p - 1), is rewritten in the
-        // stage by the one lane holding it (a rare, divergent store after the
-        // lane's own quad write)
-        bool hit[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hit[r] = (unsigned)dy[r] < (unsigned)WN && (dy[r] & 15) == 0;
-        if (hit[0] || hit[1] || hit[2] || hit[3]) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (hit[r]) {
-              // a bitwise select (a variable index would send acc to scratch);
-              // each element is copied out first, since a bit cast of a vector
-              // element expression reads the vector's first element
-              uint32_t xb = 0;
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const float a = acc[i][j][r];
-                xb |= __builtin_bit_cast(uint32_t, a) & (dy[r] == 16 * j ? ~0u : 0u);
-              }
-              const float p =
-                  __builtin_amdgcn_exp2f(fmaf(__builtin_bit_cast(float, xb) - mv[r], kL2E, -lv[r]));
-              const int c = dy[r] + fr;  // column within the wavefront block
-              const int q = i * 4 + (lane >> 4);
-              stg[c * WM + 4 * (q ^ stage_swz(c)) + r] = bf16_bits(cv[r] * (p - 1.0f));
-            }
-          }
-        }
-      }
-      __syncthreads();
-      const int rw0 = wm * WM, cw0 = wn * WN;  // wavefront block within the tile
-      // (both are multiples of 32, so the block starts at a panel boundary)
-      store_staged_rows<kFull>(stg, lane, g.D + (n0 + cw0) / 32 * g.ldd + (m0 + rw0) * 32, 32,
-                               g.ldd, nrows_w - rw0, ncols_w - cw0);
-      // transposed: lane l takes column c = 16*cg + l%16 and its 8 rows
-      // 32*tp + 8*(l/16) .. +7, so one instruction writes the 64-byte records
-      // of 16 consecutive columns in one 32-row panel (a contiguous 1 KB
-      // block) and the 16 columns' distinct stage permutations keep the LDS
-      // reads free of bank conflicts
-      const int cl = lane & 15, q = lane >> 4;
-#pragma unroll
-      for (int sidx = 0; sidx < (WM / 32) * (WN / 16); ++sidx) {
-        const int tp = sidx % (WM / 32), c = 16 * (sidx / (WM / 32)) + cl;
-        const int t8 = 4 * tp + q;  // 8-row group within the block
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + c * WM + 4 * ((2 * t8) ^ stage_swz(c)));
-        if (kFull || (cw0 + c < ncols_w && rw0 + 8 * t8 < nrows_w))
-          __builtin_nontemporal_store(
-              v, reinterpret_cast<u32x4*>(g.Dt + ((m0 + rw0) / 32 + tp) * g.ldt +
-                                          (n0 + cw0 + c) * 32 + 8 * q));
-      }
-    };
-    if (ncols == GBN && nrows_w == GBM)
-      body(BoolC<true>{});
-    else
-      body(BoolC<false>{});
   } else {
     const int nrows = (int)(M - m0 < GBM ? M - m0 : GBM);
     const int ldc = (int)g.ldc;
-    // GM_STORE stages its bfloat16 block like the dlogits (see GM_D)
+    // GM_STORE stages its bfloat16 block through LDS like the forward's
+    // exponentials
     uint16_t* stg = smem + wave * (WM * WN);
     const int64_t base = (m0 + wm * WM + rq) * g.ldc + n0 + lc0;
     auto body = [&](auto full_tag) {
@@ -898,6 +820,115 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
   coef[k] = (float)tt.coef;
 }
 
+// dlogits of one vocabulary chunk from the forward product's exponentials.
+// For active token t and chunk column c (vocabulary id v = v0 + c), with m
+// the block maximum E[t, v] is relative to and lse_t = M_t + ln S_t:
+//   D[t, c] = coef_t exp(x - lse_t)
+//           = sign(coef_t) exp2((m - M_t) log2e + log2|coef_t| - log2 S_t) E[t, v]
+// except the sampled column, D[t, y_t] = coef_t (p - 1) with
+// p = exp2((x_y - M_t) log2e - log2 S_t) from the sampled logit x_y the
+// forward product kept.  Rows past the active count (up to kPad) are zeros.
+// Both layouts the gradient products read are written: D K-paneled over
+// the chunk's columns, Dt over tokens, each as 16-byte stores; the
+// transpose goes through LDS.  One workgroup per 64 tokens x 256 columns.
+constexpr int kDcTok = 64, kDcCol = 256;
+__global__ void __launch_bounds__(256)
+k_lm_dchunk(const uint16_t* __restrict__ E, int64_t lde, const float* __restrict__ wmax,
+            int64_t ldw, const float2* __restrict__ lsep, const float* __restrict__ coef,
+            const int32_t* __restrict__ ycol, const float* __restrict__ xy,
+            const int32_t* __restrict__ counts, int64_t v0, int64_t wv, int64_t nblk_c,
+            uint16_t* __restrict__ D, int64_t ldd, uint16_t* __restrict__ Dt, int64_t ldt) {
+  __shared__ float s_m[kDcTok], s_cl[kDcTok], s_dy[kDcTok];
+  __shared__ int32_t s_y[kDcTok];
+  __shared__ uint32_t s_sg[kDcTok];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kDcTok][kDcCol + 8];
+  const int64_t M = counts[0];
+  const int64_t mpad = (M + kPad - 1) / kPad * kPad;
+  const int64_t t0 = (int64_t)(blockIdx.x / nblk_c) * kDcTok;
+  const int64_t c0 = (int64_t)(blockIdx.x % nblk_c) * kDcCol;
+  if (t0 >= mpad) return;
+  const int64_t wpad = (wv + kPad - 1) / kPad * kPad;
+  const int tid = threadIdx.x;
+  if (tid < kDcTok) {
+    const int64_t t = t0 + tid;
+    float Mt = 0.0f, cl = -INFINITY, dy = 0.0f;
+    int32_t y = -1;
+    uint32_t sg = 0;
+    if (t < M) {
+      const float2 l = lsep[t];
+      const float cf = coef[t];
+      Mt = l.x;
+      // log2|coef| - log2 S: -inf for coef = 0 (a clip-cut gradient or a bad
+      // token id), which gives exact zeros
+      cl = __builtin_amdgcn_logf(fabsf(cf)) - l.y;
+      sg = __float_as_uint(cf) & 0x80000000u;
+      y = ycol[t];
+      if (y >= 0) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(xy[t] - Mt, kL2E, -l.y));
+        dy = cf * (pr - 1.0f);
+      }
+    }
+    s_m[tid] = Mt;
+    s_cl[tid] = cl;
+    s_dy[tid] = dy;
+    s_y[tid] = y;
+    s_sg[tid] = sg;
+  }
+  __syncthreads();
+  // D: per pass one 32-column panel of the 64 rows, 8 consecutive columns a
+  // thread (a contiguous 4 KB block of both E and D)
+  const int row = tid >> 2, quad = tid & 3;
+  const int64_t t = t0 + row;
+  const bool live_row = t < M;
+#pragma unroll
+  for (int p = 0; p < kDcCol / 32; ++p) {
+    const int64_t c = c0 + p * 32 + quad * 8;
+    if (c >= wpad) break;  // uniform across the workgroup
+    u32x4 out = u32x4{0u, 0u, 0u, 0u};
+    if (live_row) {
+      const u32x4 e = *reinterpret_cast<const u32x4*>(E + (c / 32) * lde + t * 32 + c % 32);
+      const int64_t v = v0 + c;
+      const float sc = __builtin_amdgcn_exp2f(fmaf(wmax[t * ldw + v / 64] - s_m[row], kL2E, s_cl[row]));
+      const uint32_t w[4] = {e.x, e.y, e.z, e.w};
+      uint32_t o[4];
+      const uint32_t sgm = s_sg[row] ? 0x80008000u : 0u;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f16x2 hv = __builtin_bit_cast(f16x2, w[h]);
+        o[h] = bf16x2_bits(sc * (float)hv.x, sc * (float)hv.y) ^ sgm;
+      }
+      const int64_t dyc = (int64_t)s_y[row] - v;  // the sampled column, if in these 8
+      if ((uint64_t)dyc < 8) {
+        const uint32_t bits = bf16_bits(s_dy[row]);
+        const int h = (int)dyc >> 1;
+        o[h] = (dyc & 1) ? ((o[h] & 0xFFFFu) | (bits << 16)) : ((o[h] & 0xFFFF0000u) | bits);
+      }
+      out = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    if (t < mpad) *reinterpret_cast<u32x4*>(D + (c / 32) * ldd + t * 32 + c % 32) = out;
+    *reinterpret_cast<u32x4*>(&tile[row][p * 32 + quad * 8]) = out;
+  }
+  __syncthreads();
+  // Dt: per pass 64 columns x 32 tokens of one token panel, 8 consecutive
+  // tokens a thread (a contiguous 4 KB block of Dt)
+  const int cl4 = tid >> 2;
+#pragma unroll
+  for (int pass = 0; pass < (kDcCol / 64) * (kDcTok / 32); ++pass) {
+    const int tp = pass / (kDcCol / 64);         // token panel within the block
+    const int cc = (pass % (kDcCol / 64)) * 64 + cl4;  // column within the block
+    const int64_t c = c0 + cc;
+    if (c >= wpad || t0 + tp * 32 >= mpad) continue;
+    uint32_t w4[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int r = tp * 32 + quad * 8 + 2 * h;
+      w4[h] = (uint32_t)tile[r][cc] | ((uint32_t)tile[r + 1][cc] << 16);
+    }
+    *reinterpret_cast<u32x4*>(Dt + ((t0 / 32) + tp) * ldt + c * 32 + quad * 8) =
+        u32x4{w4[0], w4[1], w4[2], w4[3]};
+  }
+}
+
 // dhidden rows: active tokens get their accumulator, others zero (NaN for a
 // bad token id at a counted position).
 __global__ void __launch_bounds__(256)
@@ -961,6 +992,8 @@ struct LmWs {
   uint16_t* Dc;      // [Tcap, kChunkV] dlogits chunk, K-paneled over its columns
   uint16_t* Dtc;     // [kChunkV, Tcap] the chunk transposed, K-paneled over tokens
   float* dH;         // [Tcap, H]
+  uint16_t* E;       // [Vpad, Tcap] binary16 exponentials, K-paneled over vocabulary
+  float* wmax;       // [Tcap, ntn * 4] their 64-column block maxima
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -998,6 +1031,8 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
   w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
+  w.E = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * round_up(V, kPad)));
+  w.wmax = reinterpret_cast<float*>(take(4 * (size_t)Tcap * ntn * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -1043,8 +1078,8 @@ int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_
   // token rows up to 2^24 keep every in-tile offset of the epilogues in 32 bits
   if (!mul_ok(N, C, T) || *T > (int64_t(1) << 24)) return DRGRPO_ERR_SHAPE;
   int64_t tmp;
-  if (!mul_ok(*T, (V + GBN - 1) / GBN * 8, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
-      !mul_ok(V, H * 2, &tmp))
+  if (!mul_ok(*T, (V + GBN - 1) / GBN * 16, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
+      !mul_ok(V, H * 2, &tmp) || !mul_ok(*T + kPad, (V + kPad) * 2, &tmp))
     return DRGRPO_ERR_SHAPE;
   return DRGRPO_OK;
 }
@@ -1058,15 +1093,17 @@ int launch_gemm(const GemmArgs& g, hipStream_t st, hipEvent_t ev_begin = nullptr
   const int64_t blocks = ntm * ntn;
   if (blocks <= 0) return DRGRPO_OK;
   if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
-  // 128 KB of LDS per workgroup (gfx950 has 160 KB per CU)
+  // 132 KB of LDS per workgroup, 140 KB for the forward product (gfx950 has
+  // 160 KB per CU)
+  const size_t lds = MODE == GM_LSE ? kGemmLdsLse : kGemmLds;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds) != hipSuccess)
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return DRGRPO_ERR_HIP;
   if (ev_begin || ev_end)
-    hipExtLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), kGemmLds, st, ev_begin,
+    hipExtLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), lds, st, ev_begin,
                           ev_end, 0, g);
   else
-    hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), kGemmLds, st, g);
+    hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), lds, st, g);
   return launch_status();
 }
 
@@ -1161,6 +1198,10 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   g.xy = w.xy;
   g.ycol = w.ycol;
   g.col_base = 0;
+  g.E = w.E;  // the exponentials the backward chunks turn into dlogits
+  g.lde = Tcap * 32;
+  g.wmax = w.wmax;
+  g.ldw = ntn * 4;
   if ((rc = launch_gemm<GM_LSE>(g, st, aux ? static_cast<hipEvent_t>(aux->fwd_event_begin) : nullptr,
                                 aux ? static_cast<hipEvent_t>(aux->fwd_event_end) : nullptr)) !=
       DRGRPO_OK)
@@ -1175,26 +1216,17 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   const int64_t vc_cap = V < kChunkV ? round_up(V, kPad) : kChunkV;
   for (int64_t v0 = 0; v0 < V; v0 += kChunkV) {
     const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
-    GemmArgs d = {};
-    d.A = w.Ha;
-    d.ar = 32;
-    d.ak = T * 32;
-    d.B = Wb + v0 * H;
-    d.br = H;
-    d.bk = 32;
-    d.M = T;
-    d.N = wv;
-    d.K = H;
-    d.M_dev = w.counts;
-    d.ycol = w.ycol;
-    d.col_base = v0;
-    d.lsep = w.lsep;
-    d.coef = w.coef;
-    d.D = w.Dc;
-    d.ldd = Tcap * 32;
-    d.Dt = w.Dtc;
-    d.ldt = vc_cap * 32;
-    if ((rc = launch_gemm<GM_D>(d, st)) != DRGRPO_OK) return rc;
+    // the chunk's dlogits from the forward product's exponentials, in both
+    // layouts the two products read
+    {
+      const int64_t nbc = (round_up(wv, kPad) + kDcCol - 1) / kDcCol;
+      const int64_t nbt = (Tcap + kDcTok - 1) / kDcTok;
+      hipLaunchKernelGGL(k_lm_dchunk, dim3((unsigned)(nbt * nbc)), dim3(256), 0, st,
+                         w.E + (v0 / 32) * (Tcap * 32), Tcap * 32, w.wmax, ntn * 4, w.lsep,
+                         w.coef, w.ycol, w.xy, w.counts, v0, wv, nbc, w.Dc, Tcap * 32, w.Dtc,
+                         vc_cap * 32);
+      if ((rc = launch_status()) != DRGRPO_OK) return rc;
+    }
 
     // the chunk of W transposed, [H, vc_cap] with zero columns past wv
     const int64_t wv_pad = round_up(wv, kPad);

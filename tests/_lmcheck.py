@@ -4,13 +4,16 @@ that a wrong part of the gradient fails them ("The Quiet Library", section
 gradients in the intended precision).
 
 What the GPU computes: every dlogits entry D[t, v] = coef_t (p_tv - [v = y_t])
-from binary32 logits, rounded to bfloat16; binary32 products
-dhidden = D . W and dW = D^T . hidden over those entries; bfloat16 results.
-Error model of one output element with oracle value R (binary64), from its
-terms D x (x = W[v, k] for dhidden, hidden[t, k] for dW):
+from binary32 logits (by way of exp(x - m) kept in binary16, relative
+rounding 2^-11), rounded to bfloat16; binary32 products dhidden = D . W and
+dW = D^T . hidden over those entries; bfloat16 results.  Error model of one
+output element with oracle value R (binary64), from its terms D x
+(x = W[v, k] for dhidden, hidden[t, k] for dW):
 
   * each D entry is rounded once to bfloat16: relative error <= u = 2^-8, zero
-    mean, RMS below u / sqrt(3) (round to nearest even);
+    mean, RMS below u / sqrt(3) (round to nearest even); the binary16
+    exponential adds at most 2^-11 = u / 8 before that rounding, inside the
+    slack of the bounds below;
   * binary32 logits and binary32 accumulation: relative error of order 2^-17
     of S = sum |D| |x| (the realised errors of both are ~1e-5 of S or less);
   * the result is rounded once to bfloat16: relative error <= u, RMS below
@@ -41,7 +44,7 @@ import numpy as np
 U = 2.0 ** -8            # bfloat16 unit roundoff
 E32 = 2.0 ** -17         # binary32 logits and accumulation, relative to S
 FROB_FACTOR = 3.0
-SLOPE_TOL = 3e-3         # parts whose reference is the gradient itself
+SLOPE_TOL = 4e-3         # parts whose reference is the gradient itself
 SLOPE_TOL_SOFTMAX = 5e-2  # dhidden's softmax part: ~2% of the row, its rounding noise is larger
 SOFTMAX_FROB_REL = 0.5   # ||err|| / ||softmax part|| over the whole part
 
@@ -131,9 +134,17 @@ def check_dW(got: np.ndarray, Dc: np.ndarray, Ha: np.ndarray, sampled: np.ndarra
     return res
 
 
+def round_rel(x: np.ndarray, bits: int) -> np.ndarray:
+    """x with its significand rounded to `bits` bits (nearest), any exponent:
+    the relative rounding of a binary16 value (bits = 11) without its range."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(m * 2.0 ** bits) / 2.0 ** bits, e)
+
+
 def emulate(D: np.ndarray, X: np.ndarray) -> np.ndarray:
-    """The GPU's precision path for D . X, emulated on the CPU: D rounded to
-    bfloat16, a binary32 product, the result rounded to bfloat16.  Only the
-    checker's own tests use it."""
-    Db = bf16_round(D).astype(np.float32)
+    """The GPU's precision path for D . X, emulated on the CPU: each D entry
+    carries the binary16 exponential's relative rounding (11 bits), is rounded
+    to bfloat16, enters a binary32 product, and the result is rounded to
+    bfloat16.  Only the checker's own tests use it."""
+    Db = bf16_round(round_rel(D, 11)).astype(np.float32)
     return bf16_round((Db @ X.astype(np.float32)).astype(np.float64))

@@ -111,7 +111,7 @@ def test_lmhead_full_size_sampled():
     assert abs(loss - t["loss"]) <= 2e-3 * abs(t["loss"])
     rng = np.random.default_rng(cfg.seed)
     tok = case.tokens.reshape(-1)
-    rows = np.unique(np.concatenate([rng.choice(active, 28, replace=False), active[:2],
+    rows = np.unique(np.concatenate([rng.choice(active, 60, replace=False), active[:2],
                                      active[-2:], [0]]))
     print(f"[{cfg.name}] oracle dlogits of {rows.size} token rows", flush=True)
     D = lmhead.dlogits_token_rows(h64, W64, tok, t, rows)
@@ -121,7 +121,7 @@ def test_lmhead_full_size_sampled():
     # (their gradient is the softmax part alone), and both ends
     samp_ids = np.unique(tok[active])
     others = np.setdiff1d(np.arange(cfg.V), samp_ids)
-    vs = np.unique(np.concatenate([rng.choice(samp_ids, 8, replace=False),
+    vs = np.unique(np.concatenate([rng.choice(samp_ids, 24, replace=False),
                                    rng.choice(others, 48, replace=False), [0, cfg.V - 1]]))
     print(f"[{cfg.name}] oracle dlogits columns of {vs.size} vocabulary rows", flush=True)
     Dc = lmhead.dlogits_vocab_cols(h64, W64, tok, t, vs)
