@@ -206,3 +206,38 @@ def test_lmhead_logprobs_full_size_sampled():
     print(f"[{cfg.name}] max |logp err| {err.max():.3g} (bound min {bound.min():.3g})", flush=True)
     assert (err <= bound).all()
     assert np.isfinite(got[counted]).all()
+
+
+def test_lmhead_bad_token_poisons_only_its_row():
+    """A counted token id outside [0, V) in a row with gradient: the loss is
+    NaN and the device status reports it; that token's dhidden row is NaN and
+    its dlogits row takes no part in the products, so every other dhidden row
+    and all of dW equal the oracle's gradients with that row removed."""
+    cfg, case, hb, Wb, old, ref, t = lm_case("lmhead_mini")
+    tok = case.tokens.copy()
+    coef = t["coef"].reshape(cfg.N, cfg.C)
+    i, tt = [(i, tt) for i in range(cfg.N) for tt in range(cfg.C)
+             if coef[i, tt] != 0 and tok[i, tt] != cfg.eos_id][3]
+    tok[i, tt] = cfg.V + 7
+    pos = i * cfg.C + tt
+    ws = torch.empty(dr.lmhead_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H, cfg.G),
+                     dtype=torch.uint8, device=DEV)
+    loss, dh, dW = dr.lmhead_loss_fwd_bwd(
+        _bits_to_dev(hb), _bits_to_dev(Wb), torch.from_numpy(tok).to(DEV), cfg.eos_id,
+        torch.from_numpy(case.rewards).to(DEV), torch.from_numpy(old).to(DEV),
+        None if ref is None else torch.from_numpy(ref).to(DEV), G=cfg.G, eps=cfg.eps,
+        beta=cfg.beta, norm_const=cfg.norm_const, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.isnan(float(loss.item()))
+    assert dr.device_status(ws) == dr.ERR_TOKEN_RANGE
+    got_h = _dev_to_f64(dh)
+    assert np.isnan(got_h[pos]).all()
+    keep = np.setdiff1d(np.arange(cfg.T), [pos])
+    D = t["dlogits"].copy()
+    D[pos] = 0.0
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    flat = case.tokens.reshape(-1)
+    check_dhidden(got_h[keep], D[keep], W64, t["coef"][keep], flat[keep])
+    act = np.setdiff1d(t["active_rows"], [pos])
+    check_dW(_dev_to_f64(dW), D[act], h64[act], np.isin(np.arange(cfg.V), flat[act]))
