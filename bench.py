@@ -97,6 +97,8 @@ def _ceil_lib():
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         L.ceiling_rows.argtypes = [P, P, I64, I64, I64, ctypes.c_int32, P, P, P, P, P]
         L.ceiling_rows.restype = ctypes.c_int
+        L.ceiling_rows_ticket.argtypes = [P, P, I64, I64, I64, P, P, I64, P, P, P, P]
+        L.ceiling_rows_ticket.restype = ctypes.c_int
         L.ceiling_device_info.restype = ctypes.c_int
         _ceil = L
     return _ceil
@@ -329,9 +331,11 @@ def measure_lmhead(cfg, case, steps, warmup):
     }
 
 
-def _timed_ceiling(mode, src, dst, rows, row_bytes, stride, row_read, sink, reps=5):
+def _timed_ceiling(mode, src, dst, rows, row_bytes, stride, row_read, sink, reps=5,
+                   ticket=None):
     """Median device time (HIP events stamped by the dispatch) of one
-    measurement-kernel launch on the current stream."""
+    measurement-kernel launch on the current stream; ticket = (class_rows,
+    n_read, counters) for the ticket order."""
     import numpy as np
     import torch
 
@@ -345,8 +349,13 @@ def _timed_ceiling(mode, src, dst, rows, row_bytes, stride, row_read, sink, reps
         e1.record()
     torch.cuda.synchronize()
     for e0, e1 in evs:  # the first launch is a warm-up
-        rc = L.ceiling_rows(ptr(src), ptr(dst), rows, row_bytes, stride, mode, ptr(row_read),
-                            ptr(sink), st, e0.cuda_event, e1.cuda_event)
+        if ticket is None:
+            rc = L.ceiling_rows(ptr(src), ptr(dst), rows, row_bytes, stride, mode, ptr(row_read),
+                                ptr(sink), st, e0.cuda_event, e1.cuda_event)
+        else:
+            rc = L.ceiling_rows_ticket(ptr(src), ptr(dst), rows, row_bytes, stride,
+                                       ptr(row_read), ptr(ticket[0]), ticket[1], ptr(ticket[2]),
+                                       st, e0.cuda_event, e1.cuda_event)
         if rc != 0:
             raise RuntimeError(f"ceiling_rows({mode}) returned {rc}")
     torch.cuda.synchronize()
@@ -444,7 +453,12 @@ def measure_loss(cfg, case, steps, warmup, ceilings=False):
         t_copy = _timed_ceiling(0, logits, dlogits, cfg.T, rb, 1, None, sink)
         t_fill = _timed_ceiling(1, None, dlogits, cfg.T, rb, 1, None, sink)
         t_read = _timed_ceiling(2, logits, dlogits, cfg.T, rb, 1, None, sink)
-        t_skel = _timed_ceiling(0, logits, dlogits, cfg.T, rb, stride, act_t, sink)
+        t_stride = _timed_ceiling(0, logits, dlogits, cfg.T, rb, stride, act_t, sink)
+        order = np.concatenate([np.flatnonzero(active), np.flatnonzero(active == 0)])
+        class_rows = torch.from_numpy(order.astype(np.int32)).to(dev)
+        counters = torch.zeros(65, dtype=torch.int32, device=dev)
+        t_skel = _timed_ceiling(0, logits, dlogits, cfg.T, rb, stride, act_t, sink,
+                                ticket=(class_rows, int(active.sum()), counters))
         skel_bytes = n_act * 2 * rb + n_inact * rb
         out["ceilings"] = {
             "how": "libceiling.so: one 1024-thread workgroup per row, every 16-byte load of a "
@@ -455,9 +469,13 @@ def measure_loss(cfg, case, steps, warmup, ceilings=False):
             "fill_gbps": cfg.T * rb / (t_fill / 1e3) / 1e9,
             "read_gbps": cfg.T * rb / (t_read / 1e3) / 1e9,
             "skeleton": {"what": "this batch's active rows copied and zero rows filled, in the "
-                                 "row kernel's order: its data movement alone",
+                                 "row kernel's ticket order: its data movement alone",
                          "ms": t_skel, "gbps": skel_bytes / (t_skel / 1e3) / 1e9,
                          "k_rows_frac_of_skeleton": t_skel / rows_avg},
+            "skeleton_stride_order": {
+                "what": "the same movement with workgroup b owning row (b * stride) mod T "
+                        "(the row kernel's earlier order)",
+                "ms": t_stride, "gbps": skel_bytes / (t_stride / 1e3) / 1e9},
             "k_rows_frac_of_copy": achieved / (full / (t_copy / 1e3) / 1e9),
         }
     del kw, aux, logits, dlogits, ws, old, ref

@@ -31,6 +31,21 @@ int ceiling_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes, in
                  int32_t mode, const uint8_t* row_read, uint32_t* sink, void* stream,
                  void* ev_begin, void* ev_end);
 
+/* The loss's active / zero row mix in its ticket order: as CEILING_COPY
+ * with row_read, but workgroup b takes the class (row_read flag) of row
+ * (b * row_stride) mod rows and then the next row of that class in memory
+ * order: class_rows ([rows] uint32, device) lists the n_read flagged rows in
+ * increasing order, then the others in increasing order; counters ([65]
+ * uint32, device) holds the two classes' tickets at [0] and [64], zeroed by
+ * the call on `stream` before the timed dispatch.  Flags, class_rows and
+ * n_read must agree (a workgroup whose ticket runs past its class does
+ * nothing).  Returns as ceiling_rows, -1 also for a NULL row_read,
+ * class_rows or counters and -2 for n_read outside [0, rows]. */
+int ceiling_rows_ticket(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                        int64_t row_stride, const uint8_t* row_read, const uint32_t* class_rows,
+                        int64_t n_read, uint32_t* counters, void* stream, void* ev_begin,
+                        void* ev_end);
+
 /* Properties of device `device` (hipGetDeviceProperties and the runtime's
  * versions).  Returns 0, -1 (NULL) or -7. */
 typedef struct ceiling_device_info {

@@ -134,7 +134,7 @@ int drgrpo_loss_fwd_bwd(const void* logits, const int64_t* tokens, int64_t eos_i
  *   - A device-side error (a token outside [0, V) at a mask=1 position)
  *     makes the loss NaN; the status word lives in the static array, so
  *     drgrpo_device_status does not apply to this call. */
-#define DRGRPO_NOALLOC_SCRATCH_BYTES (12u << 20)
+#define DRGRPO_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 int drgrpo_loss_fwd_bwd_noalloc(const void* logits, const int64_t* tokens, int64_t eos_id,
                                 const float* rewards, const float* logp_old,

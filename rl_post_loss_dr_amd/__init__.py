@@ -24,7 +24,7 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE = -1, -2, -3, -4
 ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_TOKEN_RANGE, ERR_ALIAS = -5, -6, -7, -8, -9
 ERR_SCRATCH_LIMIT = -10
-NOALLOC_SCRATCH_BYTES = 12 << 20  # DRGRPO_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 16 << 20  # DRGRPO_NOALLOC_SCRATCH_BYTES
 
 
 class DrGRPOError(RuntimeError):

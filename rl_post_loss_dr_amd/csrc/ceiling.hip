@@ -9,7 +9,8 @@
  * 16-byte nontemporal loads before using any, then stores 16-byte chunks
  * through a buffer descriptor bounded by the row with the same cache policy
  * (sc1 | nt).  Rows are visited in the order workgroup b -> row
- * (b * row_stride) mod rows.
+ * (b * row_stride) mod rows, or in the loss's ticket order (each class of
+ * rows in memory order, the classes mixed by that stride).
  */
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -30,12 +31,29 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // zeros), CEILING_READ (read the row; one word per row written so the loads
 // stay live).  With row_read set, rows whose flag is 0 are written as zeros
 // without a read and the others copied (the loss's active / zero-row mix).
+// With class_rows set (the ticket order): the workgroup takes the class
+// (flagged by row_read or not) of row (b * row_stride) mod rows, then the
+// next row of that class from class_rows (the n_read flagged rows in memory
+// order, then the others) by the class's counter in counters[0] / [64].
 __global__ void __launch_bounds__(kThreads)
 k_ceiling(const char* __restrict__ src, char* __restrict__ dst, uint32_t row_bytes, uint32_t rows,
           uint32_t row_stride, int mode, const uint8_t* __restrict__ row_read,
-          uint32_t* __restrict__ sink) {
-  const uint32_t row = (uint32_t)(((uint64_t)blockIdx.x * row_stride) % rows);
+          uint32_t* __restrict__ sink, const uint32_t* __restrict__ class_rows, uint32_t n_read,
+          uint32_t* __restrict__ counters) {
+  uint32_t row = (uint32_t)(((uint64_t)blockIdx.x * row_stride) % rows);
   const int tid = threadIdx.x;
+  if (class_rows) {
+    __shared__ uint32_t sh_row;
+    if (tid == 0) {
+      const bool r = row_read[row] != 0;
+      const uint32_t k = atomicAdd(counters + (r ? 0 : 64), 1u);
+      const uint32_t n = r ? n_read : rows - n_read;
+      sh_row = k < n ? class_rows[(r ? 0u : n_read) + k] : UINT32_MAX;
+    }
+    __syncthreads();
+    row = sh_row;
+    if (row >= rows) return;  // more tickets than rows of the class: inconsistent flags
+  }
   const uint32_t nchunks = row_bytes / 16;
   const uint32_t last = nchunks - 1;
   const u32x4* in = reinterpret_cast<const u32x4*>(src + (size_t)row * row_bytes);
@@ -69,11 +87,13 @@ k_ceiling(const char* __restrict__ src, char* __restrict__ dst, uint32_t row_byt
   }
 }
 
-}  // namespace
+__global__ void k_ceiling_reset(uint32_t* counters) {
+  counters[0] = 0u;
+  counters[64] = 0u;
+}
 
-extern "C" int ceiling_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes,
-                            int64_t row_stride, int32_t mode, const uint8_t* row_read,
-                            uint32_t* sink, void* stream, void* ev_begin, void* ev_end) {
+int check_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes, int64_t row_stride,
+               int32_t mode, uint32_t* sink) {
   // one 1024-thread workgroup per row: fewer than 2^32 work-items per dispatch
   if (rows <= 0 || rows > (int64_t)(UINT32_MAX / kThreads) || row_bytes <= 0 || row_bytes % 16 != 0 ||
       row_bytes > (int64_t)kNch * kThreads * 16 || row_stride <= 0 || row_stride > UINT32_MAX)
@@ -81,12 +101,42 @@ extern "C" int ceiling_rows(const void* src, void* dst, int64_t rows, int64_t ro
   if (mode != CEILING_COPY && mode != CEILING_FILL && mode != CEILING_READ) return -3;
   if (!dst || ((mode != CEILING_FILL) && !src) || (mode == CEILING_READ && !sink)) return -1;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0) return -6;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" int ceiling_rows(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                            int64_t row_stride, int32_t mode, const uint8_t* row_read,
+                            uint32_t* sink, void* stream, void* ev_begin, void* ev_end) {
+  const int rc = check_rows(src, dst, rows, row_bytes, row_stride, mode, sink);
+  if (rc != 0) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipExtLaunchKernelGGL(k_ceiling, dim3((unsigned)rows), dim3(kThreads), 0, st,
                         static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end), 0,
                         static_cast<const char*>(src), static_cast<char*>(dst),
                         (uint32_t)row_bytes, (uint32_t)rows, (uint32_t)row_stride, (int)mode,
-                        row_read, sink);
+                        row_read, sink, (const uint32_t*)nullptr, 0u, (uint32_t*)nullptr);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+extern "C" int ceiling_rows_ticket(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                                   int64_t row_stride, const uint8_t* row_read,
+                                   const uint32_t* class_rows, int64_t n_read,
+                                   uint32_t* counters, void* stream, void* ev_begin,
+                                   void* ev_end) {
+  const int rc = check_rows(src, dst, rows, row_bytes, row_stride, CEILING_COPY, nullptr);
+  if (rc != 0) return rc;
+  if (!row_read || !class_rows || !counters) return -1;
+  if (n_read < 0 || n_read > rows) return -2;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_ceiling_reset, dim3(1), dim3(1), 0, st, counters);
+  hipExtLaunchKernelGGL(k_ceiling, dim3((unsigned)rows), dim3(kThreads), 0, st,
+                        static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end), 0,
+                        static_cast<const char*>(src), static_cast<char*>(dst),
+                        (uint32_t)row_bytes, (uint32_t)rows, (uint32_t)row_stride,
+                        (int)CEILING_COPY, row_read, (uint32_t*)nullptr, class_rows,
+                        (uint32_t)n_read, counters);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

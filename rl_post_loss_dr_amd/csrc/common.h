@@ -71,14 +71,20 @@ __device__ inline TokenTerms token_terms(double logp, float old, float ref, floa
 // ------------------------------------------------------------------- k_prep
 // One wavefront per completion row i.
 // adv_mode: DRGRPO_ADV_CENTER or DRGRPO_ADV_ZSCORE (include/drgrpo.h).
+// zero2 (nullable): two words, [0] and [64], set to zero by completion 0
+// (the loss's ticket counters, ahead of the row kernel on the stream).
 __global__ void __launch_bounds__(64)
 k_prep(const int64_t* __restrict__ tokens, int64_t C, int64_t eos_id,
        const float* __restrict__ rewards, int64_t G, int adv_mode, int32_t* __restrict__ len,
        float* __restrict__ adv, uint8_t* __restrict__ row_flags, int32_t* __restrict__ aux_len,
        uint8_t* __restrict__ aux_mask, float* __restrict__ aux_adv,
-       int32_t* __restrict__ nocontrast_count) {
+       int32_t* __restrict__ nocontrast_count, uint32_t* __restrict__ zero2) {
   const int64_t i = blockIdx.x;
   const int lane = threadIdx.x;
+  if (zero2 && i == 0 && lane == 0) {
+    zero2[0] = 0u;
+    zero2[64] = 0u;
+  }
   int64_t first = C;
   if (tokens) {
     const int64_t* row = tokens + i * C;

@@ -4,10 +4,16 @@
  * Definitions are those of include/drgrpo.h ("Making Dr GRPO go brrr":
  * "The completion mask", "compute_logprobs", "PPO", "Dr. GRPO", "The loss").
  *
- * One call is three stream-ordered launches:
+ * One call is three (four) stream-ordered launches:
  *   k_prep    one wavefront per completion: first-EOS length (ballot over 64
- *             tokens at a time), group advantage, per-row flags.
- *   k_rows    one 1024-thread workgroup per token row: streams the row's V
+ *             tokens at a time), group advantage, per-row flags; zeroes the
+ *             row kernel's ticket counters.
+ *   k_plan    one workgroup, only for full-size rows at 256 or more
+ *             completions or for the token mean: prefix of active rows per
+ *             completion, counted tokens.
+ *   k_rows    one 1024-thread workgroup per token row (taken in the ticket
+ *             order of ticket_row: each class of rows, active or zero, in
+ *             memory order by an arrival counter): streams the row's V
  *             logits from HBM once with 16-byte loads, keeps them in
  *             registers (19 chunks of 16 B per lane covers a bf16 row of up
  *             to 155,648 entries), reduces max / sum-of-exp with wavefront
@@ -51,7 +57,16 @@ struct Ws {
   int64_t* total_len;  // [1] counted tokens (token-mean aggregation)
   double* tok_loss;    // [T] per-token term / row divisor
   uint8_t* tok_flags;  // [T]
+  uint32_t* plan;      // row plan of the ticket order: two counters and the
+                       // prefix of active rows per completion (kPlan* offsets)
 };
+
+// Offsets (in 32-bit words) into the row plan: the two ticket counters sit
+// 256 bytes apart, so their atomics do not share a cache line; the prefix
+// holds N + 1 entries.
+constexpr uint32_t kPlanActive = 0;
+constexpr uint32_t kPlanZero = 64;
+constexpr uint32_t kPlanPrefix = 128;
 
 size_t ws_carve(void* base, int64_t N, int64_t T, Ws* ws) {
   size_t off = 0;
@@ -69,6 +84,7 @@ size_t ws_carve(void* base, int64_t N, int64_t T, Ws* ws) {
   w.total_len = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.tok_loss = reinterpret_cast<double*>(take(sizeof(double) * T));
   w.tok_flags = reinterpret_cast<uint8_t*>(take(T));
+  w.plan = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (kPlanPrefix + N + 1)));
   if (ws) *ws = w;
   return off;
 }
@@ -253,9 +269,113 @@ struct RowArgs {
   float* aux_logp;
   float* aux_tok_loss;
   float* out_logp;  // forward-only mode: log-prob of every token
+  uint32_t* plan;   // row plan (k_plan) of the ticket order
   uint32_t row_stride;  // workgroup b handles row (b * row_stride) mod T; gcd(row_stride, T) = 1
   uint32_t T;
+  uint32_t N;
 };
+
+// The ticket order of the full-size rows.  Each row is of one of two
+// classes: active (counted token of a completion whose term is not
+// identically zero: it reads the row and writes its gradient) or zero (it
+// only writes zeros).  Workgroup b takes the class of row (b * row_stride)
+// mod T, so the workgroups in flight mix the classes in the batch's
+// proportion, and then the next row of that class in memory order from the
+// class's counter, so the rows in flight at once sit next to each other in
+// memory.  Against every workgroup owning row (b * row_stride) mod T this
+// measured 9-11% faster on the batch's data movement alone at 16K-64K rows
+// of 297 KB (3.7% at 128K rows).  The k-th active row lies in the completion
+// i with P[i] <= k < P[i+1] (P the exclusive prefix of active rows), the
+// k-th zero row in the completion with i*C - P[i] <= k < (i+1)*C - P[i+1]:
+// both keys are nondecreasing in i.  One wavefront finds i: for N < 256 the
+// whole prefix sits in its registers (4 entries a lane), formed while the
+// ticket is in flight, and i + 1 is the number of entries j <= N with
+// key(j) <= k; larger batches narrow [lo, hi) 63-fold per round.  Returns -1 for a ticket
+// past the class's rows (never, when len, adv and the prefix agree: they are
+// the same values).
+__device__ int64_t ticket_row(const RowArgs& a, int lane) {
+  const uint32_t C = (uint32_t)a.C, N = a.N;
+  const uint32_t r0 = (uint32_t)(((uint64_t)blockIdx.x * a.row_stride) % a.T);
+  const uint32_t i0 = r0 / C;
+  const bool act =
+      (int32_t)(r0 - i0 * C) < a.len[i0] && (a.adv[i0] != 0.0f || a.beta != 0.0f);
+  const uint32_t* P = a.plan + kPlanPrefix;
+  auto key = [&](uint32_t j, uint32_t p) { return act ? p : j * C - p; };
+  // N < 256: the wavefront forms P[j], j = lane*4 .. lane*4+3, itself from
+  // len and adv (the same values and test as the class above); larger
+  // batches read the prefix k_plan wrote
+  uint32_t pv[4];
+  uint32_t active_rows;
+  if (N < 256) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t j = (uint32_t)lane * 4u + u;
+      v[u] = (j < N && (a.adv[j] != 0.0f || a.beta != 0.0f)) ? (uint32_t)a.len[j] : 0u;
+    }
+    const uint32_t own = v[0] + v[1] + v[2] + v[3];
+    uint32_t incl = own;  // inclusive scan of the lanes' sums
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
+      if (lane >= off) incl += y;
+    }
+    uint32_t run = incl - own;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pv[u] = run;
+      run += v[u];
+    }
+    active_rows = (uint32_t)__shfl((int)incl, 63);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pv[u] = 0u;
+    active_rows = P[N];
+  }
+  uint32_t k = 0;
+  if (lane == 0) k = atomicAdd(a.plan + (act ? kPlanActive : kPlanZero), 1u);
+  k = __shfl(k, 0);
+  if (k >= (act ? active_rows : a.T - active_rows)) return -1;
+  uint32_t i, p0, p1;
+  if (N < 256) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t j = (uint32_t)lane * 4u + u;
+      n += (uint32_t)__popcll(__ballot(j <= N && key(j, pv[u]) <= k));
+    }
+    i = n - 1;  // key(0) = 0 <= k and key(N) > k: 0 <= i < N
+    auto pick = [&](uint32_t e) {
+      const uint32_t u = e & 3u;
+      const uint32_t v = u == 0 ? pv[0] : u == 1 ? pv[1] : u == 2 ? pv[2] : pv[3];
+      return (uint32_t)__shfl((int)v, (int)(e >> 2));
+    };
+    p0 = pick(i);
+    p1 = pick(i + 1);
+  } else {
+    uint32_t lo = 0, hi = N;  // key(lo) <= k < key(hi)
+    for (;;) {
+      // lanes 0..63 probe lo, lo + step, ... up to hi (loaded clamped to hi),
+      // so the lane after the last passing one holds the next entry
+      const uint32_t step = (hi - lo + 62) / 63;
+      const uint32_t j = lo + (uint32_t)lane * step;
+      const uint32_t p = P[min(j, hi)];
+      // keys are nondecreasing and the probe at lo passes: the passing lanes
+      // are a prefix, the last of them brackets the answer
+      const uint64_t m = __ballot(j < hi && key(j, p) <= k);
+      const int L = 63 - __clzll(m);
+      if (step == 1) {  // hi - lo <= 63: lane L holds P[i], lane L + 1 P[i + 1]
+        i = lo + (uint32_t)L;
+        p0 = (uint32_t)__shfl((int)p, L);
+        p1 = (uint32_t)__shfl((int)p, L + 1);
+        break;
+      }
+      lo += (uint32_t)L * step;
+      hi = min(lo + step, hi);
+    }
+  }
+  return (int64_t)i * C + (act ? k - p0 : (p1 - p0) + (k - (i * C - p0)));
+}
 
 // Merge one chunk of values into a lane's running (max, sum of exp(x - max)).
 template <int VEC>
@@ -353,8 +473,22 @@ __global__ void __launch_bounds__(NT) k_rows(RowArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   // consecutive workgroups take rows far apart, so the workgroups in flight
-  // mix rows of every reward group (active rows and zero rows interleave)
-  const int64_t row = (int64_t)(((uint64_t)blockIdx.x * a.row_stride) % a.T);
+  // mix rows of every reward group (active rows and zero rows interleave);
+  // the full-size rows of the loss go by the ticket order (ticket_row)
+  constexpr bool kTicket = !kFwdOnly && NT == kThreads;
+  int64_t row;
+  if constexpr (kTicket) {
+    __shared__ int64_t sh_row;
+    if (wave == 0) {
+      const int64_t r = ticket_row(a, lane);
+      if (lane == 0) sh_row = r;
+    }
+    __syncthreads();
+    row = sh_row;
+    if (row < 0) return;
+  } else {
+    row = (int64_t)(((uint64_t)blockIdx.x * a.row_stride) % a.T);
+  }
   const int64_t i = row / a.C;
   const int64_t t = row - i * a.C;
   const int64_t V = a.V;
@@ -501,6 +635,66 @@ __global__ void __launch_bounds__(NT) k_rows(RowArgs a) {
 }
 
 
+// Row plan of the ticket order for 256 or more completions (the row kernel
+// forms it itself below that), one workgroup: zeroes the two ticket
+// counters and writes P[i] = sum over completions j < i of their active rows
+// (len_j when adv_j != 0 or beta != 0, else 0), i = 0..N; with total_len
+// non-null also the batch's counted tokens (sum of len) for the token mean.
+// Integer sums: exact, order-free.
+__global__ void __launch_bounds__(1024)
+k_plan(const int32_t* __restrict__ len, const float* __restrict__ adv, float beta, int64_t N,
+       uint32_t* __restrict__ plan, int64_t* __restrict__ total_len) {
+  __shared__ uint32_t sh_w[16];
+  __shared__ long long sh_l[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* P = plan + kPlanPrefix;
+  if (tid == 0) {
+    plan[kPlanActive] = 0u;
+    plan[kPlanZero] = 0u;
+  }
+  uint32_t carry = 0;  // at most T < 2^31
+  long long lsum = 0;
+  for (int64_t base = 0; base < N; base += 1024) {
+    const int64_t i = base + tid;
+    uint32_t v = 0;
+    if (i < N) {
+      const int32_t L = len[i];
+      lsum += L;
+      v = (adv[i] != 0.0f || beta != 0.0f) ? (uint32_t)L : 0u;
+    }
+    uint32_t x = v;  // inclusive scan over the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) sh_w[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const uint32_t sw = sh_w[w];
+      before += w < wave ? sw : 0u;
+      chunk += sw;
+    }
+    if (i < N) P[i] = carry + before + x - v;
+    carry += chunk;
+    __syncthreads();  // sh_w is rewritten by the next chunk
+  }
+  if (tid == 0) P[N] = carry;
+  if (total_len) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+    if (lane == 0) sh_l[wave] = lsum;
+    __syncthreads();
+    if (tid == 0) {
+      long long t = 0;
+      for (int w = 0; w < 16; ++w) t += sh_l[w];
+      *total_len = (int64_t)t;
+    }
+  }
+}
+
 uint64_t gcd_u64(uint64_t a, uint64_t b) {
   while (b) {
     const uint64_t r = a % b;
@@ -530,10 +724,19 @@ bool vector_path(const void* logits, const void* dlogits, int64_t V, drgrpo_dtyp
          reinterpret_cast<uintptr_t>(dlogits) % 16 == 0;
 }
 
+// 256 threads when their register tile holds the whole row, else 1024.
+bool rows_fit_256(int64_t V, drgrpo_dtype_t dtype, bool vec) {
+  const int64_t nch = V / (dtype == DRGRPO_BF16 ? (vec ? 8 : 1) : (vec ? 4 : 1));
+  return nch <= (int64_t)kNch * 256;
+}
+
+// k_rows over T rows.  The loss's 1024-thread kernels go by the ticket order
+// and need a.plan written by k_plan earlier on the same stream.
 template <bool kFwdOnly>
 int launch_rows(RowArgs a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
                 hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
   a.T = (uint32_t)T;
+  a.N = (uint32_t)(T / a.C);
   a.row_stride = row_stride_for(T);
   const bool vec = vector_path(a.logits, kFwdOnly ? nullptr : a.dlogits, a.V, dtype);
   const dim3 grid((unsigned)T);
@@ -544,9 +747,8 @@ int launch_rows(RowArgs a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
     else
       hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
   };
-  // 256 threads when their register tile holds the whole row
-  const int64_t nch = a.V / (dtype == DRGRPO_BF16 ? (vec ? 8 : 1) : (vec ? 4 : 1));
-  const bool small = nch <= (int64_t)kNch * 256;
+  const bool small = rows_fit_256(a.V, dtype, vec);
+  if (!kFwdOnly && !small && !a.plan) return DRGRPO_ERR_PARAM;
   auto pick = [&](auto k256, auto k1024) {
     if (small)
       go(k256, 256);
@@ -646,11 +848,14 @@ int enqueue_loss(const void* logits, const int64_t* tokens, int64_t eos_id, cons
 
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
                      adv_mode, ws.len, ws.adv, ws.row_flags, x.len, x.mask, x.adv,
-                     (int32_t*)nullptr);
+                     (int32_t*)nullptr, ws.plan);
   int rc = launch_status();
   if (rc != DRGRPO_OK) return rc;
-  if (agg == DRGRPO_AGG_TOKEN_MEAN) {
-    hipLaunchKernelGGL(k_total_len, dim3(1), dim3(1024), 0, st, ws.len, N, ws.total_len);
+  const bool ticket = !rows_fit_256(V, dtype, vector_path(logits, out_dlogits, V, dtype));
+  // the row kernel forms the prefix itself below 256 completions
+  if ((ticket && N >= 256) || agg == DRGRPO_AGG_TOKEN_MEAN) {
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, ws.len, ws.adv, beta, N, ws.plan,
+                       agg == DRGRPO_AGG_TOKEN_MEAN ? ws.total_len : (int64_t*)nullptr);
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
   }
 
@@ -674,6 +879,7 @@ int enqueue_loss(const void* logits, const int64_t* tokens, int64_t eos_id, cons
   a.aux_logp = x.logp;
   a.aux_tok_loss = x.tok_loss;
   a.out_logp = nullptr;
+  a.plan = ticket ? ws.plan : nullptr;
   rc = launch_rows<false>(a, T, dtype, st, static_cast<hipEvent_t>(o.rows_event_begin),
                          static_cast<hipEvent_t>(o.rows_event_end));
   if (rc != DRGRPO_OK) return rc;
@@ -796,7 +1002,7 @@ extern "C" int drgrpo_completion_mask(const int64_t* tokens, int64_t N, int64_t 
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, static_cast<hipStream_t>(stream),
                      tokens, C, eos_id, (const float*)nullptr, (int64_t)1, 0, (int32_t*)nullptr,
                      (float*)nullptr, (uint8_t*)nullptr, out_len, out_mask, (float*)nullptr,
-                     (int32_t*)nullptr);
+                     (int32_t*)nullptr, (uint32_t*)nullptr);
   return launch_status();
 }
 
@@ -816,7 +1022,7 @@ extern "C" int drgrpo_group_advantage_ex(const float* rewards, int64_t N, int64_
                      (int64_t)1, (int64_t)0, rewards, G, (int)adv_mode, (int32_t*)nullptr,
                      (float*)nullptr,
                      (uint8_t*)nullptr, (int32_t*)nullptr, (uint8_t*)nullptr, out_adv,
-                     out_nocontrast);
+                     out_nocontrast, (uint32_t*)nullptr);
   return launch_status();
 }
 

@@ -1157,7 +1157,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   // mask, advantage, active-token list, gathered hidden rows and transposes
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id, rewards, G,
                      adv_mode, w.len, w.adv, w.row_flags, (int32_t*)nullptr, (uint8_t*)nullptr,
-                     (float*)nullptr, (int32_t*)nullptr);
+                     (float*)nullptr, (int32_t*)nullptr, (uint32_t*)nullptr);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   if (agg == DRGRPO_AGG_TOKEN_MEAN) {
     hipLaunchKernelGGL(k_total_len, dim3(1), dim3(1024), 0, st, w.len, N, w.total_len);
@@ -1318,7 +1318,8 @@ extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const i
   // counted tokens (first EOS inclusive), listed and gathered like the loss pass
   hipLaunchKernelGGL(k_prep, dim3((unsigned)N), dim3(64), 0, st, tokens, C, eos_id,
                      (const float*)nullptr, (int64_t)1, 0, w.len, (float*)nullptr, (uint8_t*)nullptr,
-                     (int32_t*)nullptr, (uint8_t*)nullptr, (float*)nullptr, (int32_t*)nullptr);
+                     (int32_t*)nullptr, (uint8_t*)nullptr, (float*)nullptr, (int32_t*)nullptr,
+                     (uint32_t*)nullptr);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_offsets, dim3(1), dim3(1024), 0, st, w.len, (const float*)nullptr, N,
                      0.0f, w.offs, w.counts);

@@ -32,6 +32,40 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_ceiling_library_exports_and_checks():
+    """libceiling.so (the benchmark's measurement kernels) exports every call
+    include/ceiling.h declares, and its calls reject bad arguments before
+    launching anything."""
+    from rl_post_loss_dr_amd.build import CEIL_LIB
+    if not os.path.exists(CEIL_LIB):
+        dr.build()
+    C = ctypes.CDLL(CEIL_LIB)
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ceiling.h")).read(),
+                 flags=re.S)
+    names = sorted(set(re.findall(r"\b(ceiling_[a-z0-9_]+)\s*\(", src)))
+    assert {"ceiling_rows", "ceiling_rows_ticket", "ceiling_device_info"} <= set(names)
+    for n in names:
+        assert hasattr(C, n), n
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    C.ceiling_rows.argtypes = [P, P, I64, I64, I64, ctypes.c_int32, P, P, P, P, P]
+    C.ceiling_rows_ticket.argtypes = [P, P, I64, I64, I64, P, P, I64, P, P, P, P]
+    F = 1 << 40
+    assert C.ceiling_rows(F, F, 0, 4096, 1, 0, None, None, None, None, None) == -2
+    assert C.ceiling_rows(F, F, 8, 4100, 1, 0, None, None, None, None, None) == -2
+    assert C.ceiling_rows(F, F, 8, 4096, 1, 7, None, None, None, None, None) == -3
+    assert C.ceiling_rows(None, F, 8, 4096, 1, 0, None, None, None, None, None) == -1
+    assert C.ceiling_rows(F + 8, F, 8, 4096, 1, 0, None, None, None, None, None) == -6
+    ok = [F, F, 8, 4096, 3, F, F, 4, F, None, None, None]
+    for idx in (5, 6, 8):  # row_read, class_rows, counters
+        bad = list(ok)
+        bad[idx] = None
+        assert C.ceiling_rows_ticket(*bad) == -1, idx
+    for n_read in (-1, 9):
+        bad = list(ok)
+        bad[7] = n_read
+        assert C.ceiling_rows_ticket(*bad) == -2, n_read
+
+
 def test_workspace_bytes(L):
     assert L.drgrpo_workspace_bytes(64, 256, 151936, 8) > 64 * 256 * 8
     # the dispatch limit: T x 1024 threads below 2^32 (V > 4864)
@@ -229,7 +263,7 @@ def test_noalloc_validates_before_touching_the_scratch(L):
     assert call({7: -1.0}) == dr.ERR_PARAM
     assert call({15: 4}) == dr.ERR_DTYPE
     assert call({8: 0.04}) == dr.ERR_NULL  # beta > 0 without logp_ref
-    # 2048 x 1024 token rows: a 19 MB workspace, beyond the 12 MiB array
+    # 2048 x 1024 token rows: a 19 MB workspace, beyond the 16 MiB array
     assert dr.workspace_bytes(2048, 1024, 8, 8) > dr.NOALLOC_SCRATCH_BYTES
     assert call({12: 2048, 13: 1024, 14: 8}) == dr.ERR_SCRATCH_LIMIT
     # the largest batch the header promises fits
