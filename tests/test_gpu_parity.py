@@ -176,6 +176,57 @@ def test_token_out_of_range_sets_status():
     assert dr.device_status(ws) == dr.OK
 
 
+def test_token_out_of_range_full_size_rows():
+    """The same rule on full-size rows (V = 151,936, the 1024-thread kernel and
+    its ticket order): an id outside [0, V) is ignored at a masked position,
+    and at a counted position, of a completion with or without reward
+    contrast, makes the loss NaN, that row NaN and the status word report it;
+    every other dlogits row is bit for bit the good call's."""
+    cfg, case, x, old, ref, res = small_case("mini_bf16")
+    logits = to_device_logits(x, cfg, DEV)
+    args = (torch.from_numpy(case.rewards).to(DEV), torch.from_numpy(old).to(DEV), None)
+    ws = dr.make_workspace(cfg.N, cfg.C, cfg.V, cfg.G, DEV)
+
+    def run(tok):
+        loss, d = dr.loss_fwd_bwd(logits, torch.from_numpy(tok).to(DEV), cfg.eos_id, *args,
+                                  G=cfg.G, workspace=ws)
+        torch.cuda.synchronize()
+        return float(loss.item()), d.reshape(-1, cfg.V).view(torch.int16).cpu().numpy(), \
+            dr.device_status(ws)
+
+    loss0, d0, st0 = run(case.tokens)
+    assert st0 == dr.OK
+    lens, adv = res.len, res.adv
+    # completions that end in an EOS with room before it: positions before the
+    # EOS are counted and replacing their id leaves every length unchanged
+    act_seq = [i for i in range(cfg.N) if adv[i] != 0 and 3 <= lens[i] < cfg.C]
+    zero_seq = [i for i in range(cfg.N) if adv[i] == 0 and 3 <= lens[i] < cfg.C]
+    assert act_seq and zero_seq
+    # masked position (past the EOS): ignored
+    i = act_seq[0]
+    tok = case.tokens.copy()
+    tok[i, lens[i]] = cfg.V + 5
+    loss, d, st = run(tok)
+    assert st == dr.OK and loss == loss0 and np.array_equal(d, d0)
+    # counted positions, with and without reward contrast, several bad ids
+    for i, tt, bad in ((act_seq[0], lens[act_seq[0]] - 2, -3), (act_seq[-1], 0, cfg.V),
+                       (zero_seq[0], 1, 1 << 40)):
+        tok = case.tokens.copy()
+        tok[i, tt] = bad
+        loss, d, st = run(tok)
+        row = i * cfg.C + tt
+        print(f"completion {i} position {tt} id {bad}", flush=True)
+        assert st == dr.ERR_TOKEN_RANGE
+        assert np.isnan(loss)
+        got_row = d[row].view(np.uint16)
+        assert ((got_row & 0x7F80) == 0x7F80).all() and ((got_row & 0x007F) != 0).all()
+        others = np.ones(d.shape[0], bool)
+        others[row] = False
+        assert np.array_equal(d[others], d0[others])
+    loss, d, st = run(case.tokens)
+    assert st == dr.OK and loss == loss0 and np.array_equal(d, d0)
+
+
 def test_nan_logits_propagate_only_from_counted_rows():
     cfg, case, x, old, ref, res = small_case("tiny_fp32")
     x2 = x.copy()
