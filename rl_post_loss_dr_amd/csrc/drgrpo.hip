@@ -282,17 +282,18 @@ struct RowArgs {
 // mod T, so the workgroups in flight mix the classes in the batch's
 // proportion, and then the next row of that class in memory order from the
 // class's counter, so the rows in flight at once sit next to each other in
-// memory.  Against every workgroup owning row (b * row_stride) mod T this
-// measured 9-11% faster on the batch's data movement alone at 16K-64K rows
-// of 297 KB (3.7% at 128K rows).  The k-th active row lies in the completion
-// i with P[i] <= k < P[i+1] (P the exclusive prefix of active rows), the
-// k-th zero row in the completion with i*C - P[i] <= k < (i+1)*C - P[i+1]:
-// both keys are nondecreasing in i.  One wavefront finds i: for N < 256 the
-// whole prefix sits in its registers (4 entries a lane), formed while the
-// ticket is in flight, and i + 1 is the number of entries j <= N with
-// key(j) <= k; larger batches narrow [lo, hi) 63-fold per round.  Returns -1 for a ticket
-// past the class's rows (never, when len, adv and the prefix agree: they are
-// the same values).
+// memory.  Against every workgroup owning row (b * row_stride) mod T, with
+// rows of 297 KB: 11% faster at 16K rows of which 30% are active, 9% with
+// all of them active, 2% at 64K rows (55% active), 3% slower at 128K rows
+// (two thirds active).  The k-th active row lies in the completion i with
+// P[i] <= k < P[i+1] (P the exclusive prefix of active rows), the k-th zero
+// row in the completion with i*C - P[i] <= k < (i+1)*C - P[i+1]: both keys
+// are nondecreasing in i.  One wavefront finds i: for N < 256 the whole
+// prefix sits in its registers (4 entries a lane), formed before the ticket
+// is taken, and i + 1 is the number of entries j <= N with key(j) <= k;
+// larger batches narrow [lo, hi) 63-fold per round.  Returns -1 for a
+// ticket past the class's rows (never, when len, adv and the prefix agree:
+// they are the same values).
 __device__ int64_t ticket_row(const RowArgs& a, int lane) {
   const uint32_t C = (uint32_t)a.C, N = a.N;
   const uint32_t r0 = (uint32_t)(((uint64_t)blockIdx.x * a.row_stride) % a.T);
