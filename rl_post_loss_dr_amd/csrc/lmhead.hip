@@ -37,6 +37,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256;                   // workgroup tile rows (A rows)
@@ -81,6 +82,21 @@ constexpr double kL2ED = 1.4426950408889634074;
 
 enum { GM_LSE = 0, GM_ACC = 2, GM_STORE = 3 };
 
+// Layout of the forward product's exponentials E, the accumulators' own
+// order: tile (tm, tn) of GBM x GBN at (tm * ntn + tn) * GBM * GBN; in it
+// wavefront (wm, wn)'s WM x WN block at (wm * NWN + wn) * WM * WN; in that
+// its 16 x 16 MFMA block (i, j) at (i * FN + j) * 256; in that lane l's four
+// rows 4 * (l / 16) + r, r = 0..3, of column l % 16 at l * 4 + r.  Each lane
+// stores its 4 values as one 8-byte store, so a wavefront's 16 x 16 block is
+// 512 contiguous bytes.  Element (t, v) lies at ebk_offset(t, v, ntn).
+__host__ __device__ inline int64_t ebk_offset(int64_t t, int64_t v, int64_t ntn) {
+  const int64_t tl = t % GBM, vl = v % GBN;
+  const int64_t wm = tl / WM, i = (tl % WM) / 16, q = (tl % 16) / 4, r = tl % 4;
+  const int64_t wn = vl / WN, j = (vl % WN) / 16, f = vl % 16;
+  return ((t / GBM) * ntn + v / GBN) * (GBM * GBN) + (wm * NWN + wn) * (WM * WN) +
+         (i * FN + j) * 256 + (q * 16 + f) * 4 + r;
+}
+
 
 struct GemmArgs {
   // Operands in bfloat16.  Element (r, k) of A sits at
@@ -101,10 +117,9 @@ struct GemmArgs {
   int64_t col_base;      // vocabulary id of column 0
   // GM_LSE, optional (NULL: not stored): E = exp(x - m) of every logit in
   // binary16, with m the maximum of its row over the 64 columns of one
-  // wavefront block, K-paneled over the vocabulary: (t, v) at
-  // E[(v / 32) * lde + t * 32 + v % 32]; the maxima at wmax[t * ldw + v / 64]
+  // wavefront block, in the accumulators' own order (see ebk_offset); the
+  // maxima at wmax[(v / 64) * ldw + t] (ldw: the rows rounded up to GBM)
   uint16_t* E;
-  int64_t lde;
   float* wmax;
   int64_t ldw;
   // GM_ACC / GM_STORE
@@ -457,7 +472,6 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     float2* red = reinterpret_cast<float2*>(smem + kRedElem);  // [NWN][GBM]
     const int32_t* yl = t_yl;
     const bool keepE = g.E != nullptr;
-    uint16_t* stg = smem + wave * (WM * WN);  // this wavefront's E stage
     // full tiles (the common case) compile without the column checks
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
@@ -526,16 +540,19 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
           }
         }
         if (keepE) {
-          // binary16 pairs (nearest even) into this wavefront's stage
+          // binary16 (nearest even), the lane's four rows of a column as one
+          // 8-byte store (ebk_offset); the block maxima of the four rows as
+          // one 16-byte store, the 16 rows of block i in 64 contiguous bytes
+          uint16_t* eb = g.E + ((int64_t)tm * ntn_t + tn) * (GBM * GBN) +
+                         (wm * NWN + wn) * (WM * WN) + lane * 4;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            stage_pair(stg, lane, i, j, f16x2_bits(acc[i][j][0], acc[i][j][1]),
-                       f16x2_bits(acc[i][j][2], acc[i][j][3]));
-          if (fr == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (m0 + rt0 + r < M) g.wmax[(m0 + rt0 + r) * g.ldw + tn * NWN + wn] = mx[r];
-          }
+            __builtin_nontemporal_store(
+                u32x2{f16x2_bits(acc[i][j][0], acc[i][j][1]), f16x2_bits(acc[i][j][2], acc[i][j][3])},
+                reinterpret_cast<u32x2*>(eb + (i * FN + j) * 256));
+          if (fr == 0)
+            *reinterpret_cast<float4*>(g.wmax + (tn * NWN + wn) * g.ldw + m0 + rt0) =
+                make_float4(mx[0], mx[1], mx[2], mx[3]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor1>(sm[r]);
@@ -556,22 +573,6 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     else
       body(BoolC<false>{});
     __syncthreads();
-    if (keepE) {
-      // rows up to the active count rounded up to kPad and columns up to the
-      // vocabulary rounded up to kPad are written (past the vocabulary the
-      // exponentials are exact zeros; rows past the active count are never
-      // read)
-      const int64_t mpad = (M + kPad - 1) / kPad * kPad;
-      const int64_t npad = (g.N + kPad - 1) / kPad * kPad;
-      const int nrows_w = (int)(mpad - m0 < GBM ? mpad - m0 : GBM);
-      const int ncols_w = (int)(npad - n0 < GBN ? npad - n0 : GBN);
-      const int rw0 = wm * WM, cw0 = wn * WN;
-      uint16_t* dst = g.E + (n0 + cw0) / 32 * g.lde + (m0 + rw0) * 32;
-      if (ncols_w == GBN && nrows_w == GBM)
-        store_staged_rows<true>(stg, lane, dst, 32, g.lde, WM, WN);
-      else
-        store_staged_rows<false>(stg, lane, dst, 32, g.lde, nrows_w - rw0, ncols_w - cw0);
-    }
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       if (row >= M) continue;
@@ -828,19 +829,22 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
 // except the sampled column, D[t, y_t] = coef_t (p - 1) with
 // p = exp2((x_y - M_t) log2e - log2 S_t) from the sampled logit x_y the
 // forward product kept.  Rows past the active count (up to kPad) are zeros.
-// Both layouts the gradient products read are written: D K-paneled over
-// the chunk's columns, Dt over tokens, each as 16-byte stores; the
-// transpose goes through LDS.  One workgroup per 64 tokens x 256 columns.
+// D is written K-paneled over the chunk's columns with 16-byte stores; the
+// transposed copy Dt over tokens, as both gradient products read them.  One
+// workgroup per 64 tokens x 256 columns: a quarter of one forward tile,
+// whose exponentials are 4 runs of 8 KB (ebk_offset), read with 16-byte
+// loads, scaled, and transposed through LDS.
 constexpr int kDcTok = 64, kDcCol = 256;
+static_assert(kDcCol == GBN && GBM % kDcTok == 0 && WM % kDcTok == 0, "a quarter tile");
 __global__ void __launch_bounds__(256)
-k_lm_dchunk(const uint16_t* __restrict__ E, int64_t lde, const float* __restrict__ wmax,
+k_lm_dchunk(const uint16_t* __restrict__ E, int64_t ntn, const float* __restrict__ wmax,
             int64_t ldw, const float2* __restrict__ lsep, const float* __restrict__ coef,
             const int32_t* __restrict__ ycol, const float* __restrict__ xy,
             const int32_t* __restrict__ counts, int64_t v0, int64_t wv, int64_t nblk_c,
             uint16_t* __restrict__ D, int64_t ldd, uint16_t* __restrict__ Dt, int64_t ldt) {
-  __shared__ float s_m[kDcTok], s_cl[kDcTok], s_dy[kDcTok];
+  __shared__ float s_sc[kDcTok][NWN];  // scale of row, 64-column block
+  __shared__ float s_dy[kDcTok];
   __shared__ int32_t s_y[kDcTok];
-  __shared__ uint32_t s_sg[kDcTok];
   __shared__ __attribute__((aligned(16))) uint16_t tile[kDcTok][kDcCol + 8];
   const int64_t M = counts[0];
   const int64_t mpad = (M + kPad - 1) / kPad * kPad;
@@ -849,69 +853,89 @@ k_lm_dchunk(const uint16_t* __restrict__ E, int64_t lde, const float* __restrict
   if (t0 >= mpad) return;
   const int64_t wpad = (wv + kPad - 1) / kPad * kPad;
   const int tid = threadIdx.x;
-  if (tid < kDcTok) {
-    const int64_t t = t0 + tid;
-    float Mt = 0.0f, cl = -INFINITY, dy = 0.0f;
+  {
+    // thread (row, block): the row's scale over that 64-column block; block 0
+    // also the row's sampled column and its entry
+    const int row = tid >> 2, blk = tid & 3;
+    const int64_t t = t0 + row;
+    float sc = 0.0f, dy = 0.0f;
     int32_t y = -1;
-    uint32_t sg = 0;
     if (t < M) {
       const float2 l = lsep[t];
       const float cf = coef[t];
-      Mt = l.x;
       // log2|coef| - log2 S: -inf for coef = 0 (a clip-cut gradient or a bad
-      // token id), which gives exact zeros
-      cl = __builtin_amdgcn_logf(fabsf(cf)) - l.y;
-      sg = __float_as_uint(cf) & 0x80000000u;
+      // token id), which gives exact zeros; the scale carries coef's sign
+      // (bfloat16 rounding is symmetric: the same bits as negating the result)
+      const float cl = __builtin_amdgcn_logf(fabsf(cf)) - l.y;
+      const float m = wmax[((v0 + c0) / 64 + blk) * ldw + t];
+      sc = __builtin_copysignf(__builtin_amdgcn_exp2f(fmaf(m - l.x, kL2E, cl)), cf);
       y = ycol[t];
       if (y >= 0) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(xy[t] - Mt, kL2E, -l.y));
+        const float pr = __builtin_amdgcn_exp2f(fmaf(xy[t] - l.x, kL2E, -l.y));
         dy = cf * (pr - 1.0f);
       }
     }
-    s_m[tid] = Mt;
-    s_cl[tid] = cl;
-    s_dy[tid] = dy;
-    s_y[tid] = y;
-    s_sg[tid] = sg;
+    s_sc[row][blk] = sc;
+    if (blk == 0) {
+      s_dy[row] = dy;
+      s_y[row] = y;
+    }
+  }
+  __syncthreads();
+  // the quarter tile: rows wm * WM + 16 * i0 .. +63 of forward tile (tm, tn),
+  // all its columns; in each wavefront block (wm, wn) the 16 MFMA blocks
+  // (i, j), i = i0 .. i0 + 3, are one contiguous 8 KB run
+  {
+    // element (t0, v0 + c0) opens the run of wavefront block (wm, 0)
+    const uint16_t* base = E + ebk_offset(t0, v0 + c0, ntn);
+#pragma unroll
+    for (int pass = 0; pass < 2 * NWN; ++pass) {
+      const int wn = pass >> 1;
+      const int bb = (pass & 1) * 8 + (tid >> 5);  // MFMA block of the run, 0..15
+      const int k = tid & 31;                       // 16-byte piece: lanes 2k, 2k + 1
+      const u32x4 e =
+          *reinterpret_cast<const u32x4*>(base + wn * (WM * WN) + bb * 256 + k * 8);
+      const int i = bb / FN, j = bb % FN;
+      const int l0 = 2 * k;                            // lanes l0, l0 + 1: same rows
+      const int rbase = i * 16 + 4 * (l0 >> 4);        // quarter-tile row of r = 0
+      const int col = wn * WN + j * 16 + (l0 & 15);    // columns col, col + 1
+      const uint32_t w[4] = {e.x, e.y, e.z, e.w};      // lane l0 rows 0-1, 2-3; l0+1 rows 0-1, 2-3
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rbase + r;
+        const bool live = t0 + row < M;
+        const float sc = s_sc[row][wn];
+        const f16x2 a = __builtin_bit_cast(f16x2, w[r >> 1]);
+        const f16x2 b = __builtin_bit_cast(f16x2, w[2 + (r >> 1)]);
+        const float ea = (float)((r & 1) ? a.y : a.x), eb = (float)((r & 1) ? b.y : b.x);
+        *reinterpret_cast<uint32_t*>(&tile[row][col]) =
+            live ? bf16x2_bits(sc * ea, sc * eb) : 0u;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kDcTok) {  // the sampled column of a row, when it is one of these
+    const int64_t dyc = (int64_t)s_y[tid] - (v0 + c0);
+    if (t0 + tid < M && (uint64_t)dyc < (uint64_t)kDcCol) tile[tid][dyc] = bf16_bits(s_dy[tid]);
   }
   __syncthreads();
   // D: per pass one 32-column panel of the 64 rows, 8 consecutive columns a
-  // thread (a contiguous 4 KB block of both E and D)
-  const int row = tid >> 2, quad = tid & 3;
-  const int64_t t = t0 + row;
-  const bool live_row = t < M;
+  // thread (a contiguous 4 KB block of D)
+  {
+    const int row = tid >> 2, quad = tid & 3;
+    const int64_t t = t0 + row;
 #pragma unroll
-  for (int p = 0; p < kDcCol / 32; ++p) {
-    const int64_t c = c0 + p * 32 + quad * 8;
-    if (c >= wpad) break;  // uniform across the workgroup
-    u32x4 out = u32x4{0u, 0u, 0u, 0u};
-    if (live_row) {
-      const u32x4 e = *reinterpret_cast<const u32x4*>(E + (c / 32) * lde + t * 32 + c % 32);
-      const int64_t v = v0 + c;
-      const float sc = __builtin_amdgcn_exp2f(fmaf(wmax[t * ldw + v / 64] - s_m[row], kL2E, s_cl[row]));
-      const uint32_t w[4] = {e.x, e.y, e.z, e.w};
-      uint32_t o[4];
-      const uint32_t sgm = s_sg[row] ? 0x80008000u : 0u;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const f16x2 hv = __builtin_bit_cast(f16x2, w[h]);
-        o[h] = bf16x2_bits(sc * (float)hv.x, sc * (float)hv.y) ^ sgm;
-      }
-      const int64_t dyc = (int64_t)s_y[row] - v;  // the sampled column, if in these 8
-      if ((uint64_t)dyc < 8) {
-        const uint32_t bits = bf16_bits(s_dy[row]);
-        const int h = (int)dyc >> 1;
-        o[h] = (dyc & 1) ? ((o[h] & 0xFFFFu) | (bits << 16)) : ((o[h] & 0xFFFF0000u) | bits);
-      }
-      out = u32x4{o[0], o[1], o[2], o[3]};
+    for (int p = 0; p < kDcCol / 32; ++p) {
+      const int64_t c = c0 + p * 32 + quad * 8;
+      if (c >= wpad) break;  // uniform across the workgroup
+      if (t < mpad)
+        *reinterpret_cast<u32x4*>(D + (c / 32) * ldd + t * 32 + c % 32) =
+            *reinterpret_cast<const u32x4*>(&tile[row][p * 32 + quad * 8]);
     }
-    if (t < mpad) *reinterpret_cast<u32x4*>(D + (c / 32) * ldd + t * 32 + c % 32) = out;
-    *reinterpret_cast<u32x4*>(&tile[row][p * 32 + quad * 8]) = out;
   }
-  __syncthreads();
   // Dt: per pass 64 columns x 32 tokens of one token panel, 8 consecutive
   // tokens a thread (a contiguous 4 KB block of Dt)
-  const int cl4 = tid >> 2;
+  const int cl4 = tid >> 2, quad = tid & 3;
 #pragma unroll
   for (int pass = 0; pass < (kDcCol / 64) * (kDcTok / 32); ++pass) {
     const int tp = pass / (kDcCol / 64);         // token panel within the block
@@ -992,8 +1016,8 @@ struct LmWs {
   uint16_t* Dc;      // [Tcap, kChunkV] dlogits chunk, K-paneled over its columns
   uint16_t* Dtc;     // [kChunkV, Tcap] the chunk transposed, K-paneled over tokens
   float* dH;         // [Tcap, H]
-  uint16_t* E;       // [Vpad, Tcap] binary16 exponentials, K-paneled over vocabulary
-  float* wmax;       // [Tcap, ntn * 4] their 64-column block maxima
+  uint16_t* E;       // binary16 exponentials of whole forward tiles (ebk_offset)
+  float* wmax;       // [ntn * NWN, round_up(T, GBM)] their 64-column block maxima
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -1031,8 +1055,9 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
   w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
-  w.E = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * round_up(V, kPad)));
-  w.wmax = reinterpret_cast<float*>(take(4 * (size_t)Tcap * ntn * 4));
+  // whole forward tiles (ebk_offset) and their 64-column block maxima
+  w.E = reinterpret_cast<uint16_t*>(take(2 * (size_t)round_up(T, GBM) * ntn * GBN));
+  w.wmax = reinterpret_cast<float*>(take(4 * (size_t)round_up(T, GBM) * ntn * NWN));
   if (ws) *ws = w;
   return off;
 }
@@ -1079,7 +1104,7 @@ int lm_check_shape(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G, int64_
   if (!mul_ok(N, C, T) || *T > (int64_t(1) << 24)) return DRGRPO_ERR_SHAPE;
   int64_t tmp;
   if (!mul_ok(*T, (V + GBN - 1) / GBN * 16, &tmp) || !mul_ok(*T, H * 4, &tmp) ||
-      !mul_ok(V, H * 2, &tmp) || !mul_ok(*T + kPad, (V + kPad) * 2, &tmp))
+      !mul_ok(V, H * 2, &tmp) || !mul_ok(*T + GBM, (V + GBN) * 2, &tmp))
     return DRGRPO_ERR_SHAPE;
   return DRGRPO_OK;
 }
@@ -1199,9 +1224,8 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   g.ycol = w.ycol;
   g.col_base = 0;
   g.E = w.E;  // the exponentials the backward chunks turn into dlogits
-  g.lde = Tcap * 32;
   g.wmax = w.wmax;
-  g.ldw = ntn * 4;
+  g.ldw = round_up(T, GBM);
   if ((rc = launch_gemm<GM_LSE>(g, st, aux ? static_cast<hipEvent_t>(aux->fwd_event_begin) : nullptr,
                                 aux ? static_cast<hipEvent_t>(aux->fwd_event_end) : nullptr)) !=
       DRGRPO_OK)
@@ -1221,10 +1245,9 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     {
       const int64_t nbc = (round_up(wv, kPad) + kDcCol - 1) / kDcCol;
       const int64_t nbt = (Tcap + kDcTok - 1) / kDcTok;
-      hipLaunchKernelGGL(k_lm_dchunk, dim3((unsigned)(nbt * nbc)), dim3(256), 0, st,
-                         w.E + (v0 / 32) * (Tcap * 32), Tcap * 32, w.wmax, ntn * 4, w.lsep,
-                         w.coef, w.ycol, w.xy, w.counts, v0, wv, nbc, w.Dc, Tcap * 32, w.Dtc,
-                         vc_cap * 32);
+      hipLaunchKernelGGL(k_lm_dchunk, dim3((unsigned)(nbt * nbc)), dim3(256), 0, st, w.E, ntn,
+                         w.wmax, round_up(T, GBM), w.lsep, w.coef, w.ycol, w.xy, w.counts, v0,
+                         wv, nbc, w.Dc, Tcap * 32, w.Dtc, vc_cap * 32);
       if ((rc = launch_status()) != DRGRPO_OK) return rc;
     }
 
