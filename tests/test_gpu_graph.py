@@ -3,7 +3,8 @@ replayed, as a training or rollout loop would issue them: every replay equals
 the eager call bit for bit, with eager work and synchronisations between
 replays and the outputs overwritten before each replay.  The library only
 launches kernels (no memset, no host synchronisation; the workspace state is
-cleared by its own kernels), which is what makes the capture valid."""
+cleared by its own kernels: the row kernel's ticket counters by k_prep, at
+320 completions also by k_plan), which is what makes the capture valid."""
 import numpy as np
 import pytest
 import torch
@@ -34,7 +35,7 @@ def _bits_to_dev(bits: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "mini_kl_bf16", "ragged_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "mini_kl_bf16", "ragged_bf16", "many_seq_bf16"])
 def test_loss_graph_replay(name):
     print(f"case {name}", flush=True)
     cfg, case, x, old, ref, _ = small_case(name)
