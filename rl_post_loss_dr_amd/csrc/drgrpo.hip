@@ -8,12 +8,13 @@
  *   k_prep    one wavefront per completion: first-EOS length (ballot over 64
  *             tokens at a time), group advantage, per-row flags; zeroes the
  *             row kernel's ticket counters.
- *   k_plan    one workgroup, only for full-size rows at 256 or more
+ *   k_plan    one workgroup, only for the ticket order at 256 or more
  *             completions or for the token mean: prefix of active rows per
  *             completion, counted tokens.
- *   k_rows    one 1024-thread workgroup per token row (taken in the ticket
- *             order of ticket_row: each class of rows, active or zero, in
- *             memory order by an arrival counter): streams the row's V
+ *   k_rows    one 1024-thread workgroup per token row (rows of at least
+ *             192 KB taken in the ticket order of ticket_row: each class of
+ *             rows, active or zero, in memory order by an arrival counter;
+ *             smaller ones by a fixed stride): streams the row's V
  *             logits from HBM once with 16-byte loads, keeps them in
  *             registers (19 chunks of 16 B per lane covers a bf16 row of up
  *             to 155,648 entries), reduces max / sum-of-exp with wavefront
@@ -466,8 +467,9 @@ __device__ __attribute__((always_inline)) inline void write_dlogits(
 // overlap their phases; 1024 otherwise.  (512 threads for rows up to twice
 // that measured 10-25% faster on an all-active batch but 5-17% slower on a
 // sparse one: not used.)
-template <int DT, int VEC, bool kFwdOnly, int NT>
+template <int DT, int VEC, bool kFwdOnly, int NT, bool kOrd = false>
 __global__ void __launch_bounds__(NT) k_rows(RowArgs a) {
+  static_assert(!kOrd || (!kFwdOnly && NT == kThreads), "the ticket order: the loss's 1024-thread rows");
   using IO = Io<DT, VEC>;
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
@@ -475,8 +477,9 @@ __global__ void __launch_bounds__(NT) k_rows(RowArgs a) {
   const int wave = tid >> 6;
   // consecutive workgroups take rows far apart, so the workgroups in flight
   // mix rows of every reward group (active rows and zero rows interleave);
-  // the full-size rows of the loss go by the ticket order (ticket_row)
-  constexpr bool kTicket = !kFwdOnly && NT == kThreads;
+  // the loss's rows of at least kTicketMinRowBytes go by the ticket order
+  // (ticket_row)
+  constexpr bool kTicket = kOrd;
   int64_t row;
   if constexpr (kTicket) {
     __shared__ int64_t sh_row;
@@ -731,8 +734,24 @@ bool rows_fit_256(int64_t V, drgrpo_dtype_t dtype, bool vec) {
   return nch <= (int64_t)kNch * 256;
 }
 
-// k_rows over T rows.  The loss's 1024-thread kernels go by the ticket order
-// and need a.plan written by k_plan earlier on the same stream.
+// The ticket order pays from rows of about 192 KB: a shorter-lived workgroup
+// spends relatively more on its start (the class, the prefix, the atomic).
+// k_rows on the B=8, G=8, C=256 batch (30% active rows / all active):
+// 128 KB rows 0.49 / 0.95 ms in the stride order against 0.58 / 0.97 in the
+// ticket order, 160 KB 0.58 / 1.12 against 0.65 / 1.11, 195 KB 0.75 / 1.39
+// against 0.74 / 1.30, 297 KB 1.16 / 2.05 against 1.03 / 1.82.
+constexpr int64_t kTicketMinRowBytes = 196608;
+
+// whether the loss's rows go by the ticket order (1024-thread rows of at
+// least kTicketMinRowBytes)
+bool rows_ticketed(int64_t V, drgrpo_dtype_t dtype, bool vec) {
+  return !rows_fit_256(V, dtype, vec) &&
+         V * (dtype == DRGRPO_BF16 ? 2 : 4) >= kTicketMinRowBytes;
+}
+
+// k_rows over T rows.  The loss's kernels in the ticket order need a.plan
+// written by k_plan, or its counters zeroed by k_prep, earlier on the same
+// stream.
 template <bool kFwdOnly>
 int launch_rows(RowArgs a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
                 hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
@@ -749,24 +768,31 @@ int launch_rows(RowArgs a, int64_t T, drgrpo_dtype_t dtype, hipStream_t st,
       hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
   };
   const bool small = rows_fit_256(a.V, dtype, vec);
-  if (!kFwdOnly && !small && !a.plan) return DRGRPO_ERR_PARAM;
-  auto pick = [&](auto k256, auto k1024) {
+  const bool ticket = !kFwdOnly && rows_ticketed(a.V, dtype, vec);
+  if (ticket && !a.plan) return DRGRPO_ERR_PARAM;
+  auto pick = [&](auto k256, auto k1024, auto k1024_ticket) {
     if (small)
       go(k256, 256);
+    else if (ticket)
+      go(k1024_ticket, kThreads);
     else
       go(k1024, kThreads);
   };
   constexpr bool F = kFwdOnly;
   if (dtype == DRGRPO_BF16) {
     if (vec)
-      pick(k_rows<DRGRPO_BF16, 8, F, 256>, k_rows<DRGRPO_BF16, 8, F, kThreads>);
+      pick(k_rows<DRGRPO_BF16, 8, F, 256>, k_rows<DRGRPO_BF16, 8, F, kThreads>,
+           k_rows<DRGRPO_BF16, 8, F, kThreads, !F>);
     else
-      pick(k_rows<DRGRPO_BF16, 1, F, 256>, k_rows<DRGRPO_BF16, 1, F, kThreads>);
+      pick(k_rows<DRGRPO_BF16, 1, F, 256>, k_rows<DRGRPO_BF16, 1, F, kThreads>,
+           k_rows<DRGRPO_BF16, 1, F, kThreads, !F>);
   } else {
     if (vec)
-      pick(k_rows<DRGRPO_F32, 4, F, 256>, k_rows<DRGRPO_F32, 4, F, kThreads>);
+      pick(k_rows<DRGRPO_F32, 4, F, 256>, k_rows<DRGRPO_F32, 4, F, kThreads>,
+           k_rows<DRGRPO_F32, 4, F, kThreads, !F>);
     else
-      pick(k_rows<DRGRPO_F32, 1, F, 256>, k_rows<DRGRPO_F32, 1, F, kThreads>);
+      pick(k_rows<DRGRPO_F32, 1, F, 256>, k_rows<DRGRPO_F32, 1, F, kThreads>,
+           k_rows<DRGRPO_F32, 1, F, kThreads, !F>);
   }
   return launch_status();
 }
@@ -852,7 +878,7 @@ int enqueue_loss(const void* logits, const int64_t* tokens, int64_t eos_id, cons
                      (int32_t*)nullptr, ws.plan);
   int rc = launch_status();
   if (rc != DRGRPO_OK) return rc;
-  const bool ticket = !rows_fit_256(V, dtype, vector_path(logits, out_dlogits, V, dtype));
+  const bool ticket = rows_ticketed(V, dtype, vector_path(logits, out_dlogits, V, dtype));
   // the row kernel forms the prefix itself below 256 completions
   if ((ticket && N >= 256) || agg == DRGRPO_AGG_TOKEN_MEAN) {
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, ws.len, ws.adv, beta, N, ws.plan,

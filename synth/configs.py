@@ -144,13 +144,13 @@ _add(Config(name="big_v_f32", B=2, G=2, C=3, V=200003, dtype="f32", logit_std=2.
 _add(Config(name="big_v_bf16", B=2, G=2, C=3, V=262144, logit_std=2.0, eos_id=QWEN_EOS,
             tok_lo=0, tok_hi=262144, eos_rows=2, reward="tiny", p=0.5, old_noise=0.05,
             seed=7009))
-# full-size-row kernel (V above one 256-thread register tile) at many
-# completions: 320 completions (the row search's multi-round path) and 4104
-# one-token completions (three rounds), groups with and without contrast
-_add(Config(name="many_seq_bf16", B=40, G=8, C=3, V=39008, logit_std=2.0, eos_id=3, tok_lo=0,
-            tok_hi=39008, eos_rows=200, eos_t0_rows=40, p=0.15, old_noise=0.05, seed=7015))
-_add(Config(name="many_seq_c1_bf16", B=513, G=8, C=1, V=39008, logit_std=2.0, eos_id=3,
-            tok_lo=0, tok_hi=39008, eos_rows=400, p=0.1, old_noise=0.05, seed=7016))
+# the row kernel's ticket order (rows of 192 KB: V = 98,304 in bfloat16) at
+# many completions: 320 completions (the row search's multi-round path) and
+# 4104 one-token completions (three rounds), groups with and without contrast
+_add(Config(name="many_seq_bf16", B=40, G=8, C=3, V=98304, logit_std=2.0, eos_id=3, tok_lo=0,
+            tok_hi=98304, eos_rows=200, eos_t0_rows=40, p=0.15, old_noise=0.05, seed=7015))
+_add(Config(name="many_seq_c1_bf16", B=513, G=8, C=1, V=98304, logit_std=2.0, eos_id=3,
+            tok_lo=0, tok_hi=98304, eos_rows=400, p=0.1, old_noise=0.05, seed=7016))
 _add(Config(name="no_eos_id", B=2, G=2, C=5, V=640, logit_std=1.0, eos_id=-1, tok_lo=0,
             tok_hi=640, eos_rows=0, reward="tiny", p=0.5, old_noise=0.05, seed=7010))
 _add(Config(name="lmhead_mini", B=2, G=4, C=32, V=4096, H=QWEN_H, eos_id=3, tok_lo=0,
