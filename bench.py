@@ -16,7 +16,7 @@ pattern with no arithmetic (copy, fill, read, and the batch's active / zero
 row mix) on the same buffers.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--headline-only]
+                       [--no-cpu-baseline] [--headline-only] [--no-eager]
 """
 from __future__ import annotations
 
@@ -257,6 +257,117 @@ def cpu_baseline(cfg, case, target_s: float = 15.0):
             "single_thread": single, "host": host}
 
 
+def _eager_terms(lp, tokens, eos_id, rewards, logp_old, logp_ref, G, eps, beta, kappa):
+    """The method's per-token terms in plain PyTorch from already computed
+    log-probs: mask through the first EOS, group-centred advantage, clipped
+    min-surrogate, optional k3 KL, token sum over the constant kappa."""
+    import torch
+
+    N, C = tokens.shape
+    is_eos = tokens == eos_id
+    first = torch.where(is_eos.any(1), is_eos.int().argmax(1), torch.full_like(tokens[:, 0], C))
+    mask = torch.arange(C, device=tokens.device)[None, :] <= first[:, None]
+    grp = rewards.view(-1, G)
+    adv = (grp - grp.mean(1, keepdim=True)).reshape(N, 1)
+    ratio = torch.exp(lp - logp_old)
+    surr = torch.minimum(ratio * adv, torch.clamp(ratio, 1 - eps, 1 + eps) * adv)
+    lam = -surr
+    if beta != 0.0:
+        d = logp_ref - lp
+        lam = lam + beta * (torch.exp(d) - d - 1)
+    return torch.where(mask, lam, torch.zeros_like(lam)).sum() / kappa
+
+
+def _time_eager(fn, reps=3):
+    """Median of `reps` timed calls of fn() after one untimed call."""
+    import numpy as np
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return float(np.median(ms)), ms
+
+
+def eager_loss(cfg, logits, tokens, rewards, old, ref, loss_ours, dlogits_ours):
+    """The same loss written the plain way in eager PyTorch on the same GPU and
+    inputs (log-softmax over V in float32, gather, autograd for dlogits), as
+    context for the fused call: its time, and its agreement with the fused
+    result."""
+    import torch
+
+    torch.cuda.reset_peak_memory_stats()
+
+    def step():
+        x = logits.detach().requires_grad_(True)
+        lp = torch.log_softmax(x.float(), dim=-1).gather(-1, tokens.unsqueeze(-1)).squeeze(-1)
+        loss = _eager_terms(lp, tokens, cfg.eos_id, rewards, old, ref, cfg.G, cfg.eps, cfg.beta,
+                            cfg.norm_const)
+        loss.backward()
+        return loss.detach(), x.grad
+
+    loss, grad = step()
+    gmax = float(dlogits_ours.float().abs().max().item())
+    diff = float((grad.float() - dlogits_ours.float()).abs().max().item())
+    lo = float(loss.item())
+    del loss, grad
+    med, ms = _time_eager(lambda: step())
+    peak = torch.cuda.max_memory_allocated() / 2 ** 30
+    torch.cuda.empty_cache()
+    return {"what": "the loss and dlogits written the plain way in eager PyTorch on the same "
+                    "inputs: float32 log-softmax over V, gather, clipped min-surrogate, token "
+                    "sum, autograd for dlogits",
+            "ms": med, "ms_all": ms, "speedup_of_fused_call": None,
+            "loss": lo, "loss_rel_diff": abs(lo - loss_ours) / max(abs(loss_ours), 1e-30),
+            "dlogits_max_abs_diff": diff, "dlogits_max_abs": gmax,
+            "peak_allocated_gib": round(peak, 1)}
+
+
+def eager_lmhead(cfg, hidden, W, tokens, rewards, old, loss_ours, dh_ours, dW_ours):
+    """The fused lm_head loss written the plain way in eager PyTorch on the same
+    GPU and inputs: the [T, V] logits materialised by a bf16 GEMM, float32
+    log-softmax, gather, autograd for dhidden and dW (context for the fused
+    call)."""
+    import torch
+
+    torch.cuda.reset_peak_memory_stats()
+    N, C = tokens.shape
+
+    def step():
+        h = hidden.detach().requires_grad_(True)
+        w = W.detach().requires_grad_(True)
+        logits = torch.nn.functional.linear(h, w)
+        lp = torch.log_softmax(logits.float(), dim=-1).gather(
+            -1, tokens.reshape(-1, 1)).reshape(N, C)
+        loss = _eager_terms(lp, tokens, cfg.eos_id, rewards, old, None, cfg.G, cfg.eps,
+                            cfg.beta, cfg.norm_const)
+        loss.backward()
+        return loss.detach(), h.grad, w.grad
+
+    loss, gh, gw = step()
+    rel = lambda a, b: float((a.float() - b.float()).abs().max().item()) / max(
+        float(b.float().abs().max().item()), 1e-30)
+    lo = float(loss.item())
+    res = {"dhidden_max_abs_diff_rel": rel(gh, dh_ours), "dW_max_abs_diff_rel": rel(gw, dW_ours)}
+    del loss, gh, gw
+    med, ms = _time_eager(lambda: step())
+    peak = torch.cuda.max_memory_allocated() / 2 ** 30
+    torch.cuda.empty_cache()
+    return {"what": "the loss, dhidden and dW written the plain way in eager PyTorch on the same "
+                    "inputs: [T, V] logits from a bf16 GEMM over all token rows, float32 "
+                    "log-softmax, gather, clipped min-surrogate, token sum, autograd",
+            "ms": med, "ms_all": ms, "speedup_of_fused_call": None, "loss": lo,
+            "loss_rel_diff": abs(lo - loss_ours) / max(abs(loss_ours), 1e-30), **res,
+            "peak_allocated_gib": round(peak, 1)}
+
+
 def _spread(xs):
     import numpy as np
 
@@ -265,10 +376,11 @@ def _spread(xs):
             "p90": float(np.percentile(a, 90)), "n": int(a.size)}
 
 
-def measure_lmhead(cfg, case, steps, warmup):
+def measure_lmhead(cfg, case, steps, warmup, eager=False):
     """Fused lm_head workload: hidden [T, H] and W [V, H] in, loss, dhidden,
     dW out.  Per call: whole-call time (events between calls) and the
-    forward product's time (events stamped by its dispatch)."""
+    forward product's time (events stamped by its dispatch); with eager, the
+    plain PyTorch formulation on the same inputs (context)."""
     import numpy as np
     import torch
 
@@ -320,6 +432,13 @@ def measure_lmhead(cfg, case, steps, warmup):
     med = float(np.median(call_ms))
     fwd_med = float(np.median(fwd_ms))
     req = 3 * per_gemm / (med / 1e3) / 1e12
+    eager_rec = None
+    if eager:
+        loss_t, _, _ = dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None,
+                                              **kw)
+        eager_rec = eager_lmhead(cfg, hidden, W, tokens, rewards, old, float(loss_t.item()), dh,
+                                 dW)
+        eager_rec["speedup_of_fused_call"] = eager_rec["ms"] / med
     del kw, hidden, W, dh, dW, ws
     torch.cuda.empty_cache()
     return {
@@ -336,8 +455,8 @@ def measure_lmhead(cfg, case, steps, warmup):
         "note": "required = logits, dhidden and dW products over the active tokens; executed "
                 "adds the MFMA work of padded tiles (256 x 256 tiles, hidden size 896 in four "
                 "256-column tiles); frac against 2.5 PFLOP/s dense bf16",
+        **({"torch_eager": eager_rec} if eager_rec else {}),
     }
-
 
 
 def _lmhead_executed_flops(n_act, V, H, tile=256, kpad=32, chunk=32768):
@@ -385,11 +504,12 @@ def _timed_ceiling(mode, src, dst, rows, row_bytes, stride, row_read, sink, reps
     return float(np.median([a.elapsed_time(b) for a, b in evs[1:]]))
 
 
-def measure_loss(cfg, case, steps, warmup, ceilings=False):
+def measure_loss(cfg, case, steps, warmup, ceilings=False, eager=False):
     """One loss workload: K timed calls after W warm-up calls; per call the
     whole call (events between calls) and the row kernel (events stamped by
     its dispatch).  With ceilings, the measurement kernels run afterwards on
-    the same buffers."""
+    the same buffers; with eager, the plain PyTorch formulation on the same
+    inputs (context, not the measurement)."""
     import numpy as np
     import torch
 
@@ -501,6 +621,11 @@ def measure_loss(cfg, case, steps, warmup, ceilings=False):
                 "ms": t_stride, "gbps": skel_bytes / (t_stride / 1e3) / 1e9},
             "k_rows_frac_of_copy": achieved / (full / (t_copy / 1e3) / 1e9),
         }
+    if eager:
+        loss_t, _ = dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, **kw)
+        e = eager_loss(cfg, logits, tokens, rewards, old, ref, float(loss_t.item()), dlogits)
+        e["speedup_of_fused_call"] = e["ms"] / float(np.median(call_ms))
+        out["torch_eager"] = e
     del kw, aux, logits, dlogits, ws, old, ref
     torch.cuda.empty_cache()
     return out
@@ -747,7 +872,9 @@ def main():
     ap.add_argument("--workload", default="qwen_b8g8c256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the other workloads and the ceilings")
+                    help="skip the other workloads, the ceilings and the eager PyTorch timing")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="skip timing the plain eager PyTorch formulation (context only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 4 GiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -781,7 +908,7 @@ def main():
     cfg = synth.get_config(args.workload)
     case = synth.make_case(cfg)
     if cfg.H is not None:
-        r = measure_lmhead(cfg, case, args.steps, args.warmup)
+        r = measure_lmhead(cfg, case, args.steps, args.warmup, eager=not args.no_eager)
         rec = {
             "metric": METRIC, "value": r["tokens_per_s"], "unit": "completion tokens/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -799,7 +926,8 @@ def main():
         print(json.dumps(rec), flush=True)
         return
 
-    head = measure_loss(cfg, case, args.steps, args.warmup, ceilings=not args.headline_only)
+    head = measure_loss(cfg, case, args.steps, args.warmup, ceilings=not args.headline_only,
+                        eager=not (args.headline_only or args.no_eager))
     rec = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -832,6 +960,8 @@ def main():
     }
     if "ceilings" in head:
         rec["ceilings"] = head["ceilings"]
+    if "torch_eager" in head:
+        rec["torch_eager"] = head["torch_eager"]
     rec["provenance"] = provenance(cfg.seed)
     if not args.headline_only and cfg.name == "qwen_b8g8c256":
         work = {}
@@ -844,7 +974,7 @@ def main():
             work[name] = r
         c = synth.get_config("lmhead_b8g8c512")
         print(f"[bench] {c.name}", file=sys.stderr, flush=True)
-        work[c.name] = measure_lmhead(c, synth.make_case(c), 5, 2)
+        work[c.name] = measure_lmhead(c, synth.make_case(c), 5, 2, eager=not args.no_eager)
         rec["workloads"] = work
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, case)
