@@ -165,6 +165,11 @@ _add(Config(name="lmhead_multi", B=2, G=2, C=7, V=20488, H=96, eos_id=3, tok_lo=
 _add(Config(name="lmhead_chunks3", B=2, G=2, C=4, V=70000, H=64, eos_id=3, tok_lo=0,
             tok_hi=70000, eos_rows=1, reward="tiny", p=0.5, old_noise=0.05, w_std=0.1,
             seed=7014))
+# a wide hidden size (Qwen2.5-7B's 3584: 112 reduction steps in the forward
+# and dhidden products) with a ragged last column tile
+_add(Config(name="lmhead_wide_h", B=2, G=2, C=16, V=8200, H=3584, eos_id=3, tok_lo=0,
+            tok_hi=8200, eos_rows=2, eos_t0_rows=1, reward="tiny", p=0.5, old_noise=0.05,
+            seed=7017))
 # tiny fp64-checkable shape for finite differences of the lm_head oracle
 _add(Config(name="lmhead_fd", B=2, G=2, C=3, V=48, H=32, eos_id=3, tok_lo=0, tok_hi=48,
             eos_rows=1, reward="tiny", p=0.5, old_noise=0.3, ref_noise=0.2, beta=0.04,

@@ -54,7 +54,8 @@ def check_small_grads(cfg, case, hb, Wb, t, dh, dW):
     print(f"[{cfg.name}] {r1} {r2}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3"])
+@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3",
+                                  "lmhead_wide_h"])
 def test_lmhead_small(name):
     print(f"case {name}", flush=True)
     cfg, case, hb, Wb, old, ref, t = lm_case(name)
@@ -145,7 +146,8 @@ def _logp_bound(h64, W64, rows):
     return 2 * gamma * a.max(axis=1) + 1e-5
 
 
-@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3"])
+@pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3",
+                                  "lmhead_wide_h"])
 def test_lmhead_logprobs_small(name):
     """Forward-only fused log-probs: every counted token against the oracle,
     zeros after the first EOS, and every token when no EOS id is given."""
