@@ -144,6 +144,14 @@ _add(Config(name="big_v_f32", B=2, G=2, C=3, V=200003, dtype="f32", logit_std=2.
 _add(Config(name="big_v_bf16", B=2, G=2, C=3, V=262144, logit_std=2.0, eos_id=QWEN_EOS,
             tok_lo=0, tok_hi=262144, eos_rows=2, reward="tiny", p=0.5, old_noise=0.05,
             seed=7009))
+# the ticket order's other two row paths: 16-byte binary32 chunks (256 KB rows)
+# and 2-byte bfloat16 elements (an odd vocabulary of 98,305 entries)
+_add(Config(name="ticket_v4_f32", B=2, G=3, C=4, V=65536, dtype="f32", logit_std=2.0, eos_id=5,
+            tok_lo=0, tok_hi=65536, eos_rows=3, eos_t0_rows=1, reward="tiny", p=0.5,
+            old_noise=0.05, seed=7018))
+_add(Config(name="ticket_odd_bf16", B=2, G=3, C=4, V=98305, logit_std=2.0, eos_id=5,
+            tok_lo=0, tok_hi=98305, eos_rows=3, eos_t0_rows=1, reward="tiny", p=0.5,
+            old_noise=0.05, ref_noise=0.1, beta=0.04, seed=7019))
 # the row kernel's ticket order (rows of 192 KB: V = 98,304 in bfloat16) at
 # many completions: 320 completions (the row search's multi-round path) and
 # 4104 one-token completions (three rounds), groups with and without contrast

@@ -17,7 +17,7 @@ DEV = torch.device("cuda:0")
 
 SMALL = ["tiny_fp32", "mini_bf16", "mini_kl_bf16", "ragged_bf16", "odd_v_f32", "odd_v_bf16",
          "clip_heavy_f32", "clip_heavy_bf16", "big_v_f32", "big_v_bf16", "no_eos_id",
-         "many_seq_bf16", "many_seq_c1_bf16"]
+         "many_seq_bf16", "many_seq_c1_bf16", "ticket_v4_f32", "ticket_odd_bf16"]
 
 
 def _run(cfg, case, x, old, ref, kappa=None, out=None, aux=None, logits=None):
