@@ -82,6 +82,22 @@ constexpr double kL2ED = 1.4426950408889634074;
 
 enum { GM_LSE = 0, GM_ACC = 2, GM_STORE = 3 };
 
+// Tile shape of each product.  The forward product's output width is the
+// vocabulary: 256 x 256 tiles, wavefronts of WM x WN = 128 x 64 in a 2 x 4
+// grid (the constants above).  The two gradient products' output width is
+// the hidden size, 896 = 4 x 224 at the Qwen2.5-0.5B shape: 256 x 224 tiles,
+// wavefronts of 64 x 112 in a 4 x 2 grid, so no column of a tile is padding
+// (256-column tiles spent 1/8 of their MFMAs on it).  Their LDS stages still
+// hold 256 rows of B, the last 32 unused: the direct loads are the forward
+// product's.
+template <int MODE>
+struct TileShape {
+  static constexpr bool kFwd = MODE == GM_LSE;
+  static constexpr int BN = kFwd ? GBN : 224;  // output columns of a workgroup
+  static constexpr int WM = kFwd ? 128 : 64;
+  static constexpr int WN = kFwd ? 64 : 112;
+};
+
 // Layout of the forward product's exponentials E, the accumulators' own
 // order: tile (tm, tn) of GBM x GBN at (tm * ntn + tn) * GBM * GBN; in it
 // wavefront (wm, wn)'s WM x WN block at (wm * NWN + wn) * WM * WN; in that
@@ -192,41 +208,50 @@ constexpr int kDppMirror = 0x140;
 // among 8 consecutive, and rows equal mod 4 among 16, get distinct values
 __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// quad permutation of row c of an epilogue stage: an even value, so 16-byte
-// pairs of quads stay in order; 16 consecutive rows get distinct values, and
-// 4 rows from a multiple of 4 distinct bits 2-3 (the transposing reads)
+// quad permutation of row c of an epilogue stage of kWM rows (kWM / 4
+// quads): an even value below kWM / 4; 16 consecutive rows get distinct
+// values (8 at kWM = 64), and 4 rows from a multiple of 4 distinct bits 2-3
+// (the transposing reads)
+template <int kWM>
 __device__ inline int stage_swz(int c) {
-  return 2 * (((c & 3) << 1) | ((c >> 2) & 1) | (((c >> 3) & 1) << 3));
+  static_assert(kWM == 128 || kWM == 64, "stage heights");
+  if constexpr (kWM == 128)
+    return 2 * (((c & 3) << 1) | ((c >> 2) & 1) | (((c >> 3) & 1) << 3));
+  else
+    return 2 * (((c & 3) << 1) | ((c >> 2) & 1));
 }
 
-// 16-byte stores of a wavefront's staged WM x WN bfloat16 block, element
+// 16-byte stores of a wavefront's staged kWM x kWN bfloat16 block, element
 // (t, c) to out[t * rs + (c / 32) * ps + c % 32] (row-major: rs = ld, ps = 32;
 // K-paneled over columns: rs = 32, ps = panel stride), for rows t < rows_lim
 // and 8-column groups c < cols_lim (cols_lim a multiple of 8).  One
 // instruction covers 16 rows x 32 columns: a contiguous 1 KB block when
-// paneled.  The transposing LDS read gives lane li of a 16-lane group 4
+// paneled (kWN = 112: the last covers 16 columns, the other lanes read a
+// column of the block and store nothing).  The transposing LDS read gives lane li of a 16-lane group 4
 // consecutive columns of row tb + li when lane 4e + q4 of the group points at
 // quad tb/4 + q4 of stage row (first column + e).  The stores are
 // nontemporal: a dlogits chunk and its transpose (1.9 GB at 32K columns) are
 // far larger than any cache, and the hint made the dlogits product 2-3%
 // faster without slowing the products that read the chunk back.
-template <bool kFull>
+template <bool kFull, int kWM, int kWN>
 __device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t* out, int64_t rs,
                                          int64_t ps, int rows_lim, int cols_lim) {
+  static_assert(kWN % 16 == 0, "whole 16-column groups");
   const int grp = lane >> 4, li = lane & 15;
   const int e = li >> 2, q4 = li & 3;
 #pragma unroll
-  for (int sidx = 0; sidx < (WN / 32) * (WM / 16); ++sidx) {
-    const int tb = 16 * (sidx % (WM / 16));
-    const int cb = 32 * (sidx / (WM / 16)) + 8 * grp;  // 8 columns of this group
+  for (int sidx = 0; sidx < ((kWN + 31) / 32) * (kWM / 16); ++sidx) {
+    const int tb = 16 * (sidx % (kWM / 16));
+    const int cb = 32 * (sidx / (kWM / 16)) + 8 * grp;  // 8 columns of this group
     const int qq = (tb >> 2) + q4;
-    const int ca = cb + e, cc = cb + 4 + e;
+    // columns past the block (the last group at kWN = 112) read its last column
+    const int ca = cb + e < kWN ? cb + e : kWN - 1, cc = cb + 4 + e < kWN ? cb + 4 + e : kWN - 1;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(stg + ca * WM + 4 * (qq ^ stage_swz(ca))));
+        (__attribute__((address_space(3))) s16x4*)(stg + ca * kWM + 4 * (qq ^ stage_swz<kWM>(ca))));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(stg + cc * WM + 4 * (qq ^ stage_swz(cc))));
+        (__attribute__((address_space(3))) s16x4*)(stg + cc * kWM + 4 * (qq ^ stage_swz<kWM>(cc))));
     const int t = tb + li;
-    if (kFull || (t < rows_lim && cb < cols_lim)) {
+    if ((kWN % 32 == 0 || cb < kWN) && (kFull || (t < rows_lim && cb < cols_lim))) {
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       __builtin_nontemporal_store(u32x4{l2.x, l2.y, h2.x, h2.y},
                                   reinterpret_cast<u32x4*>(out + t * rs + (cb / 32) * ps + cb % 32));
@@ -237,10 +262,11 @@ __device__ inline void store_staged_rows(const uint16_t* stg, int lane, uint16_t
 // Stage column c = j*16 + (lane % 16) of the wavefront block, rows
 // i*16 + 4*(lane/16) .. +3 (one MFMA accumulator quad, as bfloat16 bits:
 // rows 0-1 in lo, 2-3 in hi, the lower row in the low half).
+template <int kWM>
 __device__ inline void stage_pair(uint16_t* stg, int lane, int i, int j, uint32_t lo, uint32_t hi) {
   const int q = i * 4 + (lane >> 4);
   const int c = j * 16 + (lane & 15);
-  *reinterpret_cast<uint2*>(stg + c * WM + 4 * (q ^ stage_swz(c))) = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(stg + c * kWM + 4 * (q ^ stage_swz<kWM>(c))) = make_uint2(lo, hi);
 }
 
 // two wavefronts per SIMD: the register budget of 8 wavefronts per CU, whatever the
@@ -248,6 +274,14 @@ __device__ inline void stage_pair(uint16_t* stg, int lane, int i, int j, uint32_
 template <int MODE>
 __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // this product's tile shape (for the forward product the same values as
+  // the namespace constants these names hide)
+  constexpr int BN = TileShape<MODE>::BN;
+  constexpr int WM = TileShape<MODE>::WM, WN = TileShape<MODE>::WN;
+  constexpr int NWM = GBM / WM, NWN = BN / WN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  static_assert(NWM * NWN * 64 == GT && BN <= GBN, "eight wavefronts; B rows within a stage");
+  static_assert((GT / 64) * WM * WN <= kRingElems, "epilogue staging exceeds the ring");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -265,7 +299,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // (M read on the device) take part, spread evenly over the XCDs.
   // (32-bit index arithmetic: the host keeps the grid below 2^31 workgroups)
   const int ntm = (int)((M + GBM - 1) / GBM);
-  const int ntn_t = (int)((g.N + GBN - 1) / GBN);
+  const int ntn_t = (int)((g.N + BN - 1) / BN);
   const int total = ntm * ntn_t;
   const int b = blockIdx.x;
   if (b >= total) return;
@@ -284,7 +318,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     tn = v % ntn_t;
   }
   const int64_t m0 = (int64_t)tm * GBM;
-  const int64_t n0 = (int64_t)tn * GBN;
+  const int64_t n0 = (int64_t)tn * BN;
 
   // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
   // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled
@@ -420,26 +454,53 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
-      if (i < FN) fb[cur ^ 1][i] = frag_b(As + GBM * GBK, i);
+      if constexpr (FN <= FM) {
+        if (i < FN) fb[cur ^ 1][i] = frag_b(As + GBM * GBK, i);
+      } else {  // FN / FM of them after each row block (4 x 7: 1, 2, 2, 2)
+#pragma unroll
+        for (int jb = i * FN / FM; jb < (i + 1) * FN / FM; ++jb)
+          fb[cur ^ 1][jb] = frag_b(As + GBM * GBK, jb);
+      }
       fa[i] = frag_a(As, i);
     }
-    static_assert(FM == 8 && FN == 4, "scheduling groups below assume 8 x 4 MFMA blocks");
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    static_assert((FM == 8 && FN == 4) || (FM == 4 && FN == 7),
+                  "scheduling groups below assume 8 x 4 or 4 x 7 MFMA blocks");
+    if constexpr (FM == 4) {
+      // per row block 7 MFMAs and its 2 or 3 fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
   int64_t kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -466,7 +527,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   const int rq = 4 * (lane >> 4);
 
   // columns of this tile that exist (the rest of the tile is padding)
-  const int ncols = (int)(g.N - n0 < GBN ? g.N - n0 : GBN);
+  const int ncols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
   const int lc0 = wn * WN + fr;  // tile-local column of acc[.][0]
   if constexpr (MODE == GM_LSE) {
     float2* red = reinterpret_cast<float2*>(smem + kRedElem);  // [NWN][GBM]
@@ -568,7 +629,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
         }
       }
     };
-    if (ncols == GBN)
+    if (ncols == BN)
       body(BoolC<true>{});
     else
       body(BoolC<false>{});
@@ -620,17 +681,17 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
         } else {
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            stage_pair(stg, lane, i, j, bf16x2_bits(acc[i][j][0], acc[i][j][1]),
+            stage_pair<WM>(stg, lane, i, j, bf16x2_bits(acc[i][j][0], acc[i][j][1]),
                        bf16x2_bits(acc[i][j][2], acc[i][j][3]));
         }
       }
       if constexpr (MODE == GM_STORE) {
         __syncthreads();
-        store_staged_rows<kFull>(stg, lane, g.Cb + (m0 + wm * WM) * g.ldc + n0 + wn * WN, g.ldc,
+        store_staged_rows<kFull, WM, WN>(stg, lane, g.Cb + (m0 + wm * WM) * g.ldc + n0 + wn * WN, g.ldc,
                                  32, nrows - wm * WM, ncols - wn * WN);
       }
     };
-    if (ncols == GBN && nrows == GBM)
+    if (ncols == BN && nrows == GBM)
       body(BoolC<true>{});
     else
       body(BoolC<false>{});
@@ -1114,7 +1175,7 @@ template <int MODE>
 int launch_gemm(const GemmArgs& g, hipStream_t st, hipEvent_t ev_begin = nullptr,
                 hipEvent_t ev_end = nullptr) {
   const int64_t ntm = (g.M + GBM - 1) / GBM;
-  const int64_t ntn = (g.N + GBN - 1) / GBN;
+  const int64_t ntn = (g.N + TileShape<MODE>::BN - 1) / TileShape<MODE>::BN;
   const int64_t blocks = ntm * ntn;
   if (blocks <= 0) return DRGRPO_OK;
   if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
