@@ -453,23 +453,23 @@ def measure_lmhead(cfg, case, steps, warmup, eager=False):
         "call_tflops_required": req, "call_frac_required": req / 2500.0,
         "call_tflops_executed": executed / (med / 1e3) / 1e12,
         "note": "required = logits, dhidden and dW products over the active tokens; executed "
-                "adds the MFMA work of padded tiles (256 x 256 tiles, hidden size 896 in four "
-                "256-column tiles); frac against 2.5 PFLOP/s dense bf16",
+                "adds the MFMA work of padded tiles (256 x 256 forward tiles, 256 x 224 "
+                "gradient tiles); frac against 2.5 PFLOP/s dense bf16",
         **({"torch_eager": eager_rec} if eager_rec else {}),
     }
 
 
-def _lmhead_executed_flops(n_act, V, H, tile=256, kpad=32, chunk=32768):
+def _lmhead_executed_flops(n_act, V, H, tile=256, grad_cols=224, kpad=32, chunk=32768):
     """MFMA work of one fused lm_head call as launched: the forward product
-    over all V columns, then per vocabulary chunk the dhidden product
-    (reducing over the chunk's columns) and the dW product (reducing over the
-    active tokens, padded to 32), every product on whole 256 x 256 tiles."""
+    over all V columns on whole 256 x 256 tiles, then per vocabulary chunk the
+    dhidden product (reducing over the chunk's columns) and the dW product
+    (reducing over the active tokens, padded to 32) on whole 256 x 224 tiles."""
     ru = lambda x, m: (x + m - 1) // m * m
     f = 2.0 * ru(n_act, tile) * ru(V, tile) * H
     for v0 in range(0, V, chunk):
         wv = min(chunk, V - v0)
-        f += 2.0 * ru(n_act, tile) * ru(H, tile) * ru(wv, kpad)
-        f += 2.0 * ru(wv, tile) * ru(H, tile) * ru(n_act, kpad)
+        f += 2.0 * ru(n_act, tile) * ru(H, grad_cols) * ru(wv, kpad)
+        f += 2.0 * ru(wv, tile) * ru(H, grad_cols) * ru(n_act, kpad)
     return f
 
 
