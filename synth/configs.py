@@ -178,6 +178,11 @@ _add(Config(name="lmhead_chunks3", B=2, G=2, C=4, V=70000, H=64, eos_id=3, tok_l
 _add(Config(name="lmhead_wide_h", B=2, G=2, C=16, V=8200, H=3584, eos_id=3, tok_lo=0,
             tok_hi=8200, eos_rows=2, eos_t0_rows=1, reward="tiny", p=0.5, old_noise=0.05,
             seed=7017))
+# a hidden size that leaves the last 224-column gradient tile partly filled
+# (1536 = 6 x 224 + 192: its second wavefront column stores 80 of 112 columns)
+_add(Config(name="lmhead_h1536", B=2, G=2, C=12, V=5000, H=1536, eos_id=3, tok_lo=0,
+            tok_hi=5000, eos_rows=2, reward="tiny", p=0.5, old_noise=0.05, ref_noise=0.1,
+            beta=0.04, seed=7020))
 # tiny fp64-checkable shape for finite differences of the lm_head oracle
 _add(Config(name="lmhead_fd", B=2, G=2, C=3, V=48, H=32, eos_id=3, tok_lo=0, tok_hi=48,
             eos_rows=1, reward="tiny", p=0.5, old_noise=0.3, ref_noise=0.2, beta=0.04,

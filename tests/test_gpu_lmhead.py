@@ -55,7 +55,7 @@ def check_small_grads(cfg, case, hb, Wb, t, dh, dW):
 
 
 @pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3",
-                                  "lmhead_wide_h"])
+                                  "lmhead_wide_h", "lmhead_h1536"])
 def test_lmhead_small(name):
     print(f"case {name}", flush=True)
     cfg, case, hb, Wb, old, ref, t = lm_case(name)
@@ -147,7 +147,7 @@ def _logp_bound(h64, W64, rows):
 
 
 @pytest.mark.parametrize("name", ["lmhead_mini", "lmhead_multi", "lmhead_chunks3",
-                                  "lmhead_wide_h"])
+                                  "lmhead_wide_h", "lmhead_h1536"])
 def test_lmhead_logprobs_small(name):
     """Forward-only fused log-probs: every counted token against the oracle,
     zeros after the first EOS, and every token when no EOS id is given."""
