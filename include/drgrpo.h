@@ -54,8 +54,17 @@
 extern "C" {
 #endif
 
-/* Element type of logits and dlogits. */
-typedef enum { DRGRPO_F32 = 0, DRGRPO_BF16 = 1 } drgrpo_dtype_t;
+/* Element type of logits and dlogits.  The two range markers are no element
+ * type: they make every 32-bit value a value of the type, so a C caller's
+ * out-of-range value reaches the C++ implementation as a defined value and is
+ * rejected with DRGRPO_ERR_DTYPE (without them C++ only defines the values 0
+ * and 1 for this enumeration). */
+typedef enum {
+  DRGRPO_F32 = 0,
+  DRGRPO_BF16 = 1,
+  DRGRPO_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  DRGRPO_DTYPE_RANGE_MAX_ = 2147483647
+} drgrpo_dtype_t;
 
 /* Status codes (0 = success, negative = error). */
 enum {
