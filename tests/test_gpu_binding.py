@@ -1,7 +1,7 @@
 """The binding refuses caller-supplied outputs and workspaces it cannot hand to
 the kernels (a host tensor, a wrong element type or shape, a buffer on the
 host or of another type) before anything is launched: the outputs and the
-inputs are left untouched."""
+inputs are left untouched.  The Python example of README.md runs as written."""
 import pytest
 import torch
 
@@ -57,3 +57,35 @@ def test_loss_rejects_bad_workspace_and_devices():
     with pytest.raises(TypeError):
         dr.loss_fwd_bwd(logits, tokens, 0, rewards, old.cpu(), None, G=G)
     assert float(host_ws.sum()) == 0
+
+
+def test_readme_usage_runs():
+    """The Python example of README.md, run as written on small inputs: the
+    autograd form hands the logits the same dlogits as the direct call, and
+    the fused lm_head form returns finite gradients of the right shapes."""
+    import os
+    import re
+
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "README.md")).read()
+    code = re.search(r"```python\n(.*?)```", text, flags=re.S).group(1)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    B, G, C, V, H, eos_id = 2, 8, 8, 4096, 64, 3
+    N = B * G
+    logits = (torch.randn((N, C, V), generator=g) * 2).to(torch.bfloat16).to(DEV)
+    logits.requires_grad_(True)
+    tokens = torch.randint(4, V, (N, C), generator=g)
+    tokens[0, 2] = eos_id
+    tokens = tokens.to(DEV)
+    rewards = torch.tensor([1.0, 0.0] * (N // 2), device=DEV)
+    hidden = torch.randn((N * C, H), generator=g).to(torch.bfloat16).to(DEV)
+    W = (torch.randn((V, H), generator=g) * 0.1).to(torch.bfloat16).to(DEV)
+    ns = dict(logits=logits, tokens=tokens, eos_id=eos_id, rewards=rewards, hidden=hidden, W=W)
+    exec(compile(code, "README.md", "exec"), ns)
+    torch.cuda.synchronize()
+    _, dl_direct = dr.loss_fwd_bwd(logits.detach(), tokens, eos_id, rewards,
+                                   dr.logprobs(logits.detach(), tokens), G=8)
+    assert torch.equal(logits.grad, dl_direct)
+    assert torch.isfinite(ns["loss"]).item()
+    assert ns["dhidden"].shape == hidden.shape and ns["dW"].shape == W.shape
+    assert torch.isfinite(ns["dhidden"].float()).all() and torch.isfinite(ns["dW"].float()).all()
