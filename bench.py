@@ -368,6 +368,22 @@ def eager_lmhead(cfg, hidden, W, tokens, rewards, old, loss_ours, dh_ours, dW_ou
             "peak_allocated_gib": round(peak, 1)}
 
 
+def _timed_calls(fn, n=5):
+    """Median and spread of n calls of fn() after one untimed call, timed by
+    events recorded between the calls on the current stream."""
+    import torch
+
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        ev[k].record()
+        fn()
+    ev[n].record()
+    torch.cuda.synchronize()
+    return _spread([ev[k].elapsed_time(ev[k + 1]) for k in range(n)])
+
+
 def _spread(xs):
     import numpy as np
 
@@ -432,6 +448,19 @@ def measure_lmhead(cfg, case, steps, warmup, eager=False):
     med = float(np.median(call_ms))
     fwd_med = float(np.median(fwd_ms))
     req = 3 * per_gemm / (med / 1e3) / 1e12
+    # the forward-only fused log-prob pass (old / reference log-probs): one
+    # product over every counted token, its logits never stored
+    n_cnt = int((mask_rows != 0).sum().item())
+    ws_lp = torch.empty(dr.lmhead_logprobs_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H),
+                        dtype=torch.uint8, device=dev)
+    lp_ms = _timed_calls(lambda: dr.lmhead_logprobs(hidden, W, tokens, cfg.eos_id,
+                                                    workspace=ws_lp))
+    lp_flop = 2.0 * n_cnt * cfg.V * cfg.H
+    logprobs_rec = {"entry_point": "drgrpo_lmhead_logprobs", "counted_tokens": n_cnt,
+                    "ms": lp_ms, "tflop": lp_flop / 1e12,
+                    "tflops": lp_flop / (lp_ms["median"] / 1e3) / 1e12,
+                    "frac": lp_flop / (lp_ms["median"] / 1e3) / 1e12 / 2500.0}
+    del ws_lp
     eager_rec = None
     if eager:
         loss_t, _, _ = dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards, old, None,
@@ -455,6 +484,7 @@ def measure_lmhead(cfg, case, steps, warmup, eager=False):
         "note": "required = logits, dhidden and dW products over the active tokens; executed "
                 "adds the MFMA work of padded tiles (256 x 256 forward tiles, 256 x 224 "
                 "gradient tiles); frac against 2.5 PFLOP/s dense bf16",
+        "logprobs_pass": logprobs_rec,
         **({"torch_eager": eager_rec} if eager_rec else {}),
     }
 
@@ -621,6 +651,14 @@ def measure_loss(cfg, case, steps, warmup, ceilings=False, eager=False):
                 "ms": t_stride, "gbps": skel_bytes / (t_stride / 1e3) / 1e9},
             "k_rows_frac_of_copy": achieved / (full / (t_copy / 1e3) / 1e9),
         }
+    # the forward-only log-prob pass (old / reference log-probs) over the same
+    # logits: every row read once, one binary32 per row written
+    lp_ms = _timed_calls(lambda: dr.logprobs(logits, tokens))
+    lp_bytes = cfg.T * (cfg.V * logits.element_size() + 8 + 4)
+    out["logprobs_pass"] = {
+        "entry_point": "drgrpo_logprobs", "ms": lp_ms, "bytes_per_call": lp_bytes,
+        "gbps": lp_bytes / (lp_ms["median"] / 1e3) / 1e9,
+        "frac": lp_bytes / (lp_ms["median"] / 1e3) / 1e9 / HBM_PEAK_GBPS}
     if eager:
         loss_t, _ = dr.loss_fwd_bwd(logits, tokens, cfg.eos_id, rewards, old, ref, **kw)
         e = eager_loss(cfg, logits, tokens, rewards, old, ref, float(loss_t.item()), dlogits)
@@ -960,6 +998,7 @@ def main():
     }
     if "ceilings" in head:
         rec["ceilings"] = head["ceilings"]
+    rec["logprobs_pass"] = head["logprobs_pass"]
     if "torch_eager" in head:
         rec["torch_eager"] = head["torch_eager"]
     rec["provenance"] = provenance(cfg.seed)
