@@ -284,8 +284,8 @@ struct RowArgs {
 // proportion, and then the next row of that class in memory order from the
 // class's counter, so the rows in flight at once sit next to each other in
 // memory.  Against every workgroup owning row (b * row_stride) mod T, with
-// rows of 297 KB: 11% faster at 16K rows of which 30% are active, 9% with
-// all of them active, 2% at 64K rows (55% active), 3% slower at 128K rows
+// rows of 297 KB: 10% faster at 16K rows of which 30% are active, 8% with
+// all of them active, even at 64K rows (55% active), 1% faster at 128K rows
 // (two thirds active).  The k-th active row lies in the completion i with
 // P[i] <= k < P[i+1] (P the exclusive prefix of active rows), the k-th zero
 // row in the completion with i*C - P[i] <= k < (i+1)*C - P[i+1]: both keys
