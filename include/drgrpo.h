@@ -264,8 +264,7 @@ int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_
  * The workspace (drgrpo_lmhead_workspace_bytes) holds the active tokens'
  * hidden rows (and their transpose), those exponentials (2 bytes per token
  * row and vocabulary entry: 10 GB at N*C = 32768, V = 151936), one
- * vocabulary chunk of W transposed and one chunk of dlogits in both
- * layouts. */
+ * vocabulary chunk of W transposed and one chunk of dlogits. */
 size_t drgrpo_lmhead_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G);
 
 int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,

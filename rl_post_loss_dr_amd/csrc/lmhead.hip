@@ -18,10 +18,11 @@
  *   GM_STORE  dW_chunk = dlogits_chunk^T . H_a     (bfloat16 result)
  *
  * Between them, one vocabulary chunk at a time, k_lm_dchunk streams E into
- * dlogits = coef*(softmax - onehot) in bfloat16, row-major and transposed
- * (no product is computed twice).  Transposed copies of the compacted hidden
- * states and of each vocabulary chunk of W give every product its reduction
- * dimension contiguous.  No floating-point atomics: results are bitwise
+ * dlogits = coef*(softmax - onehot) in bfloat16 (no product is computed
+ * twice).  Transposed copies of the compacted hidden states and of each
+ * vocabulary chunk of W give the products their reduction dimension
+ * contiguous; the dW product reads the dlogits chunk, whose reduction
+ * dimension (tokens) is strided, through transposing LDS reads.  No floating-point atomics: results are bitwise
  * reproducible.
  */
 #include <hip/hip_ext.h>
@@ -119,6 +120,9 @@ struct GemmArgs {
   // A[r * ar + (k / 32) * ak + k % 32]: a row-major [M, ld] matrix has
   // ar = ld, ak = 32; a K-paneled one, stored as K/32 panels [rows][32],
   // has ar = 32, ak = rows * 32.  The same holds for B ([N, K]) with br, bk.
+  // GM_STORE's A is paneled over its rows instead (the dlogits chunk as the
+  // streaming kernel writes it, rows = vocabulary columns): (r, k) at
+  // A[(r / 32) * ar + k * 32 + r % 32], ar the panel stride, ak = 32 * 32.
   const uint16_t* A;
   const uint16_t* B;
   int64_t ar, ak, br, bk;
@@ -208,6 +212,12 @@ constexpr int kDppMirror = 0x140;
 // among 8 consecutive, and rows equal mod 4 among 16, get distinct values
 __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
+// chunk permutation of record k (one reduction index, 32 rows of 64 B) of
+// GM_STORE's A stage: records k and k + 8 use opposite chunk pairs, so the
+// transposing fragment reads of a half wavefront (4 records x 2 chunks for
+// each of its two 16-lane groups, records 8g + ..) touch every bank once
+__device__ inline int tsw(int k) { return 2 * ((k >> 3) & 1); }
+
 // quad permutation of row c of an epilogue stage of kWM rows (kWM / 4
 // quads): an even value below kWM / 4; 16 consecutive rows get distinct
 // values (8 at kWM = 64), and 4 rows from a multiple of 4 distinct bits 2-3
@@ -271,6 +281,33 @@ __device__ inline void stage_pair(uint16_t* stg, int lane, int i, int j, uint32_
 
 // two wavefronts per SIMD: the register budget of 8 wavefronts per CU, whatever the
 // workgroup size (with 4-wavefront workgroups, two workgroups share a CU)
+// GM_STORE's fragment reads within one step, in issue order: after the
+// MFMAs of row block i (of 4), B fragments b_cum(i) .. b_cum(i+1)-1 of the
+// next stage (all 7 within row blocks 0-2, so the last one has a row block of
+// MFMAs to land), then the two transposing reads of A fragment i.  A
+// wavefront's LDS reads complete in order, so "at most n outstanding" lands
+// every read with n or more issued after it; the counts below follow.
+namespace store_reads {
+constexpr int b_cum(int i) { return i <= 0 ? 0 : i == 1 ? 3 : i == 2 ? 5 : 7; }
+constexpr int n(int i) { return b_cum(i + 1) - b_cum(i) + 2; }
+constexpr int before(int i) { return i == 0 ? 0 : before(i - 1) + n(i - 1); }
+constexpr int a_end(int i) { return before(i) + n(i) - 1; }  // A fragment i's last read
+constexpr int b_last(int i) {                                   // the last B read
+  return b_cum(i + 1) > b_cum(i) ? before(i) + b_cum(i + 1) - b_cum(i) - 1 : b_last(i - 1);
+}
+constexpr int kTotal = before(4);
+// row block 0 needs every B fragment and A fragment 0 of the previous step
+constexpr int kLand0 = b_last(3) > a_end(0) ? b_last(3) : a_end(0);
+constexpr int kWait0 = kTotal - 1 - kLand0;
+constexpr bool landed0(int i) { return a_end(i) <= kLand0; }
+// A fragment i (not landed by then) before row block i: the previous step's
+// reads after it and this step's reads of row blocks 0 .. i-1
+constexpr int wait_a(int i) { return kTotal - 1 - a_end(i) + before(i); }
+static_assert(b_cum(4) == 7 && kTotal == 15 && kWait0 == 4 && landed0(1) && !landed0(2) &&
+                  wait_a(2) == 11 && wait_a(3) == 13,
+              "GM_STORE read order");
+}  // namespace store_reads
+
 template <int MODE>
 __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -333,20 +370,35 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // multiple of 32.  The four 16-byte chunks of a row are stored XOR-permuted
   // by swz(row % 16), so the fragment reads (16 rows, one chunk) spread over
   // all LDS banks.
+  // GM_STORE's A (paneled over its rows) lands as one [32 k][32 rows] block
+  // per row panel: wavefront wv loads panel wv of the tile (2 KB, two
+  // contiguous 1 KB halves of 16 k records); panels past the last valid row
+  // re-read the last valid one.  Record k's chunks are permuted by tsw(k),
+  // and its fragments come back through transposing LDS reads.
+  constexpr bool kAT = MODE == GM_STORE;
+  static_assert(!kAT || (kDmaA == 2 && GBM / 32 == GT / 64), "one row panel of A per wavefront");
   const int64_t nk = K / GBK;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int64_t nvA = M - m0 < GBM ? M - m0 : GBM;    // >= 1: the tile exists
   const int64_t nvB = g.N - n0 < GBN ? g.N - n0 : GBN;
-  const uint16_t* baseA = g.A + m0 * g.ar;
+  const int64_t plastA = (nvA - 1) >> 5;
+  const uint16_t* baseA =
+      kAT ? g.A + (m0 / 32 + (wv < plastA ? wv : plastA)) * g.ar : g.A + m0 * g.ar;
   const uint16_t* baseB = g.B + n0 * g.br;
-  const int pbA = (int)(((nvA - 1) * g.ar + GBK) * 2);  // the rows' span in one panel
+  // the span one stage's loads address: the rows' span in one panel
+  const int pbA = kAT ? GBK * 32 * 2 : (int)(((nvA - 1) * g.ar + GBK) * 2);
   const int pbB = (int)(((nvB - 1) * g.br + GBK) * 2);
   const int dchunk = 8 * ((lane & 3) ^ swz(lane >> 2));
   uint32_t voffA[kDmaA], voffB[kDmaB];
 #pragma unroll
   for (int p = 0; p < kDmaA; ++p) {
-    const int64_t r = (wv * kDmaA + p) * 16 + (lane >> 2);
-    voffA[p] = (uint32_t)(((r < nvA ? r : nvA - 1) * g.ar + dchunk) * 2);
+    if constexpr (kAT) {
+      const int k = 16 * p + (lane >> 2);
+      voffA[p] = (uint32_t)((k * 32 + 8 * ((lane & 3) ^ tsw(k))) * 2);
+    } else {
+      const int64_t r = (wv * kDmaA + p) * 16 + (lane >> 2);
+      voffA[p] = (uint32_t)(((r < nvA ? r : nvA - 1) * g.ar + dchunk) * 2);
+    }
   }
 #pragma unroll
   for (int p = 0; p < kDmaB; ++p) {
@@ -376,11 +428,64 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // A fragments are reloaded in place, row block by row block, as soon as the
   // MFMAs of that block have issued; B fragments are double-buffered
   bf16x8 fa[FM], fb[2][FN];
-  auto frag_a = [&](const uint16_t* As, int i) {
-    return *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
+  // GM_STORE reads every fragment through inline assembly: the compiler
+  // models the transposing read's builtin as possibly aliasing the direct
+  // loads in flight and would drain them all (vmcnt(0)) before each one.
+  // The reads then issue in program order and the step waits for them
+  // explicitly (lgkmcnt), naming the fragments as operands of the wait so no
+  // instruction that reads them can move above it.
+  auto lds_addr = [](const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
   };
-  auto frag_b = [&](const uint16_t* Bs, int j) {
-    return *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
+  // GM_STORE's A fragment i: rows wm*WM + i*16 + fr sit in panel
+  // pb = 2*wm + i/2 at rows rb = 16*(i%2).. of it.  Lane 4e + q of a 16-lane
+  // group points at record k = 8*(lane/16) + 4*hh + e, rows rb + 4q .. +3;
+  // the read hands lane fr of the group records k0 .. k0+3 of row rb + fr:
+  // two reads (hh = 0, 1) give its 8 reduction indices.  In bytes from the
+  // stage: 4096*wm + 2048*(i/2) + 64*k + 16*(chunk ^ tsw(k)) + 8*(q%2) with
+  // chunk = 2*(i%2) + q/2; all but 2048*(i/2) + 256*hh depend on the lane and
+  // the parity of i only, so each read is a base register plus an offset.
+  const uint32_t offA[2] = {
+      (uint32_t)(4096 * wm + 64 * (8 * (lane >> 4) + (fr >> 2)) +
+                 16 * ((2 * 0 + ((fr & 3) >> 1)) ^ tsw(8 * (lane >> 4))) + 8 * (fr & 1)),
+      (uint32_t)(4096 * wm + 64 * (8 * (lane >> 4) + (fr >> 2)) +
+                 16 * ((2 * 1 + ((fr & 3) >> 1)) ^ tsw(8 * (lane >> 4))) + 8 * (fr & 1))};
+  const uint32_t offB = (uint32_t)(2 * ((wn * WN + fr) * GBK + fk));
+  auto frag_a = [&](const uint16_t* As, int i) -> bf16x8 {
+    if constexpr (kAT) {
+      const uint32_t base = lds_addr(As) + offA[i & 1];
+      s16x4 t[2];
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(t[0]) : "v"(base), "i"(2048 * (i >> 1)) : "memory");
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(t[1]) : "v"(base), "i"(2048 * (i >> 1) + 256) : "memory");
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
+    }
+  };
+  // (GM_STORE: B fragment j at offB + 1024*j bytes from the stage's B rows)
+  auto frag_b = [&](const uint16_t* Bs, int j) -> bf16x8 {
+    if constexpr (kAT) {
+      bf16x8 v;
+      asm volatile("ds_read_b128 %0, %1 offset:%2"
+                   : "=v"(v) : "v"(lds_addr(Bs) + offB), "i"(1024 * j) : "memory");
+      return v;
+    } else {
+      return *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
+    }
+  };
+  // GM_STORE: every fragment read has landed; the fragments named stay in
+  // their registers until here
+  // (each empty statement after a wait keeps a fragment's readers below it)
+  auto settle_all = [&]() {
+    if constexpr (kAT) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[0][j]), "+v"(fb[1][j]));
+    }
   };
 
   f32x4 acc[FM][FN];
@@ -433,6 +538,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     for (int i = 0; i < FM; ++i) fa[i] = frag_a(smem, i);
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(smem + GBM * GBK, j);
+    settle_all();
   }
   // one step: stage kt's operands are in registers (fa, fb[cur]); make stage
   // kt+1 visible, refill the slot stage kt-1 used (its last fragments were
@@ -451,10 +557,30 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     const uint16_t* As = smem + ((kt + 1) % kStages) * kStageElems;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if constexpr (kAT) {
+        // the previous step's (or the prologue's, which waits for all) reads
+        // this row block needs, in the order store_reads describes
+        static_assert(FM == 4 && FN == 7, "store_reads");
+        if (i == 0) {
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(store_reads::kWait0) : "memory");
+#pragma unroll
+          for (int k = 0; k < FM; ++k)
+            if (store_reads::landed0(k)) asm volatile("" : "+v"(fa[k]));
+#pragma unroll
+          for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[cur][j]));
+        } else if (!store_reads::landed0(i)) {
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(store_reads::wait_a(i)) : "memory");
+          asm volatile("" : "+v"(fa[i]));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
-      if constexpr (FN <= FM) {
+      if constexpr (kAT) {
+#pragma unroll
+        for (int jb = store_reads::b_cum(i); jb < store_reads::b_cum(i + 1); ++jb)
+          fb[cur ^ 1][jb] = frag_b(As + GBM * GBK, jb);
+      } else if constexpr (FN <= FM) {
         if (i < FN) fb[cur ^ 1][i] = frag_b(As + GBM * GBK, i);
       } else {  // FN / FM of them after each row block (4 x 7: 1, 2, 2, 2)
 #pragma unroll
@@ -508,6 +634,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     step(kt + 1, 1);
   }
   if (kt < nk) step(kt, 0);
+  if (nk > 0) settle_all();  // the last step's reads (never used) are no longer in flight
   if constexpr (kTables) {
 #pragma unroll
     for (int k = 0; k < kYPer; ++k) {
@@ -890,9 +1017,9 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
 // except the sampled column, D[t, y_t] = coef_t (p - 1) with
 // p = exp2((x_y - M_t) log2e - log2 S_t) from the sampled logit x_y the
 // forward product kept.  Rows past the active count (up to kPad) are zeros.
-// D is written K-paneled over the chunk's columns with 16-byte stores; the
-// transposed copy Dt over tokens, as both gradient products read them.  One
-// workgroup per 64 tokens x 256 columns: a quarter of one forward tile,
+// D is written K-paneled over the chunk's columns with 16-byte stores, the
+// layout both gradient products read (the dW product through transposing LDS
+// reads).  One workgroup per 64 tokens x 256 columns: a quarter of one forward tile,
 // whose exponentials are 4 runs of 8 KB (ebk_offset), read with 16-byte
 // loads, scaled, and transposed through LDS.
 constexpr int kDcTok = 64, kDcCol = 256;
@@ -902,7 +1029,7 @@ k_lm_dchunk(const uint16_t* __restrict__ E, int64_t ntn, const float* __restrict
             int64_t ldw, const float2* __restrict__ lsep, const float* __restrict__ coef,
             const int32_t* __restrict__ ycol, const float* __restrict__ xy,
             const int32_t* __restrict__ counts, int64_t v0, int64_t wv, int64_t nblk_c,
-            uint16_t* __restrict__ D, int64_t ldd, uint16_t* __restrict__ Dt, int64_t ldt) {
+            uint16_t* __restrict__ D, int64_t ldd) {
   __shared__ float s_sc[kDcTok][NWN];  // scale of row, 64-column block
   __shared__ float s_dy[kDcTok];
   __shared__ int32_t s_y[kDcTok];
@@ -994,24 +1121,6 @@ k_lm_dchunk(const uint16_t* __restrict__ E, int64_t ntn, const float* __restrict
             *reinterpret_cast<const u32x4*>(&tile[row][p * 32 + quad * 8]);
     }
   }
-  // Dt: per pass 64 columns x 32 tokens of one token panel, 8 consecutive
-  // tokens a thread (a contiguous 4 KB block of Dt)
-  const int cl4 = tid >> 2, quad = tid & 3;
-#pragma unroll
-  for (int pass = 0; pass < (kDcCol / 64) * (kDcTok / 32); ++pass) {
-    const int tp = pass / (kDcCol / 64);         // token panel within the block
-    const int cc = (pass % (kDcCol / 64)) * 64 + cl4;  // column within the block
-    const int64_t c = c0 + cc;
-    if (c >= wpad || t0 + tp * 32 >= mpad) continue;
-    uint32_t w4[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int r = tp * 32 + quad * 8 + 2 * h;
-      w4[h] = (uint32_t)tile[r][cc] | ((uint32_t)tile[r + 1][cc] << 16);
-    }
-    *reinterpret_cast<u32x4*>(Dt + ((t0 / 32) + tp) * ldt + c * 32 + quad * 8) =
-        u32x4{w4[0], w4[1], w4[2], w4[3]};
-  }
 }
 
 // dhidden rows: active tokens get their accumulator, others zero (NaN for a
@@ -1075,7 +1184,6 @@ struct LmWs {
   uint16_t* Hat;     // [H, Tcap] K-paneled over tokens (Tcap/32 panels [H][32])
   uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W transposed, K-paneled over it
   uint16_t* Dc;      // [Tcap, kChunkV] dlogits chunk, K-paneled over its columns
-  uint16_t* Dtc;     // [kChunkV, Tcap] the chunk transposed, K-paneled over tokens
   float* dH;         // [Tcap, H]
   uint16_t* E;       // binary16 exponentials of whole forward tiles (ebk_offset)
   float* wmax;       // [ntn * NWN, round_up(T, GBM)] their 64-column block maxima
@@ -1114,7 +1222,6 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
   w.Wtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * vc));
   w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
-  w.Dtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)vc * Tcap));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
   // whole forward tiles (ebk_offset) and their 64-column block maxima
   w.E = reinterpret_cast<uint16_t*>(take(2 * (size_t)round_up(T, GBM) * ntn * GBN));
@@ -1254,8 +1361,9 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   // operand layouts: the gathered hidden rows Ha, K-paneled over H (panel
   // stride T * 32); their transpose Hat [H, Tcap], K-paneled over tokens;
-  // each dlogits chunk D, K-paneled over its vocabulary columns, and its
-  // transpose Dt over tokens; the W chunk transposed, Wtc, over vocabulary
+  // each dlogits chunk D, K-paneled over its vocabulary columns (the dW
+  // product reads it as paneled over its rows); the W chunk transposed, Wtc,
+  // over vocabulary
   hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)(N * ((C + kGatherTok - 1) / kGatherTok))),
                      dim3(256), 0, st, hid, H, tokens, C, V, w.len,
                      w.offs, w.act_pos, w.ycol, w.Ha, T * 32, w.tok_loss, w.tok_flags);
@@ -1298,21 +1406,19 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
   // backward, one vocabulary chunk at a time
-  const int64_t vc_cap = V < kChunkV ? round_up(V, kPad) : kChunkV;
   for (int64_t v0 = 0; v0 < V; v0 += kChunkV) {
     const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
-    // the chunk's dlogits from the forward product's exponentials, in both
-    // layouts the two products read
+    // the chunk's dlogits from the forward product's exponentials
     {
       const int64_t nbc = (round_up(wv, kPad) + kDcCol - 1) / kDcCol;
       const int64_t nbt = (Tcap + kDcTok - 1) / kDcTok;
       hipLaunchKernelGGL(k_lm_dchunk, dim3((unsigned)(nbt * nbc)), dim3(256), 0, st, w.E, ntn,
                          w.wmax, round_up(T, GBM), w.lsep, w.coef, w.ycol, w.xy, w.counts, v0,
-                         wv, nbc, w.Dc, Tcap * 32, w.Dtc, vc_cap * 32);
+                         wv, nbc, w.Dc, Tcap * 32);
       if ((rc = launch_status()) != DRGRPO_OK) return rc;
     }
 
-    // the chunk of W transposed, [H, vc_cap] with zero columns past wv
+    // the chunk of W transposed, [H, wv rounded up to 32] with zero columns past wv
     const int64_t wv_pad = round_up(wv, kPad);
     const int64_t tblocks = ((wv_pad + 63) / 64) * ((H + 63) / 64);
     hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb + v0 * H, H,
@@ -1335,10 +1441,10 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     a.accumulate = v0 > 0;
     if ((rc = launch_gemm<GM_ACC>(a, st)) != DRGRPO_OK) return rc;
 
-    GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a
-    s.A = w.Dtc;
-    s.ar = 32;
-    s.ak = vc_cap * 32;
+    GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a, A = D paneled over its rows
+    s.A = w.Dc;
+    s.ar = Tcap * 32;
+    s.ak = 32 * 32;
     s.B = w.Hat;
     s.br = 32;
     s.bk = H * 32;
