@@ -257,14 +257,18 @@ int drgrpo_logprobs(const void* logits, const int64_t* tokens, int64_t N, int64_
  *   N*C at most 2^24 (else DRGRPO_ERR_SHAPE); hidden, W and the outputs
  *   16-byte aligned (else DRGRPO_ERR_ALIGN).  Other arguments as for
  *   drgrpo_loss_fwd_bwd.  Logits accumulate in binary32 on the matrix cores;
- *   the forward keeps exp(logit - m) of every active token's logits in
- *   binary16 (m the maximum of its row over a 64-column block; relative
- *   rounding 2^-11), from which dlogits are formed and enter the two gradient
- *   products rounded to bfloat16, one vocabulary chunk at a time.
+ *   the forward keeps E = exp(logit - r) of every active token's logits in
+ *   bfloat16 (relative rounding 2^-8), r one reference per token (its sampled
+ *   token's logit; its largest logit when that lies more than 48 above, found
+ *   by a second pass of the forward product for such calls).  Each token's
+ *   dlogits are a factor s = coef exp(r - lse) times E (the sampled entry
+ *   adjusted), so the dhidden product reads E and scales its result rows by
+ *   s, and the dW product reads E against the hidden rows scaled by s and
+ *   rounded to bfloat16, one vocabulary chunk at a time.
  * The workspace (drgrpo_lmhead_workspace_bytes) holds the active tokens'
- * hidden rows (and their transpose), those exponentials (2 bytes per token
- * row and vocabulary entry: 10 GB at N*C = 32768, V = 151936), one
- * vocabulary chunk of W transposed and one chunk of dlogits. */
+ * hidden rows (and their scaled transpose), those exponentials (2 bytes per
+ * token row and vocabulary entry: 10 GB at N*C = 32768, V = 151936) and one
+ * vocabulary chunk of W transposed. */
 size_t drgrpo_lmhead_workspace_bytes(int64_t N, int64_t C, int64_t V, int64_t H, int64_t G);
 
 int drgrpo_lmhead_loss_fwd_bwd(const void* hidden, const void* W, const int64_t* tokens,

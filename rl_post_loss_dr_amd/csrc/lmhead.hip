@@ -6,24 +6,31 @@
  * Definitions are those of include/drgrpo.h with logits = hidden . W^T.
  * Only "active" tokens (counted, with a non-zero advantage or beta > 0)
  * have a non-zero gradient; they are compacted first and every GEMM runs over
- * them alone.  All products are C = A . B^T with both operands stored with
- * the reduction dimension contiguous ("NT"), computed by one MFMA kernel
+ * them alone.  All products are C = A . B^T computed by one MFMA kernel
  * (v_mfma_f32_16x16x32_bf16, binary32 accumulation) with three epilogues:
  *
  *   GM_LSE    logits tile of H_a . W^T -> per-token (max, sum exp) over the
- *             tile's vocabulary columns, the sampled token's logit, and
- *             E = exp(x - m) of every logit in binary16 (m the maximum of
- *             its row in a 64-column block)
- *   GM_ACC    dhidden += dlogits_chunk . W_chunk   (binary32 accumulator)
- *   GM_STORE  dW_chunk = dlogits_chunk^T . H_a     (bfloat16 result)
+ *             tile's vocabulary columns and the sampled token's logit (the
+ *             forward-only log-prob pass)
+ *   GM_LSE_E  the same product for the loss: sums of exp(x - r_t) relative to
+ *             a per-token reference r_t fixed before the product (the sampled
+ *             token's logit), and E = exp(x - r_t) of every logit in bfloat16
+ *   GM_ACC    dhidden += s_t * (E_chunk . W_chunk)      (binary32 accumulator)
+ *   GM_STORE  dW_chunk = E_chunk^T . (s . H_a)           (bfloat16 result)
  *
- * Between them, one vocabulary chunk at a time, k_lm_dchunk streams E into
- * dlogits = coef*(softmax - onehot) in bfloat16 (no product is computed
- * twice).  Transposed copies of the compacted hidden states and of each
- * vocabulary chunk of W give the products their reduction dimension
- * contiguous; the dW product reads the dlogits chunk, whose reduction
- * dimension (tokens) is strided, through transposing LDS reads.  No floating-point atomics: results are bitwise
- * reproducible.
+ * With one reference per token, every dlogits entry is a per-token factor
+ * times E: D[t, v] = s_t E[t, v] with s_t = coef_t exp(r_t - lse_t), once the
+ * sampled entry of E is replaced by exp(x_y - r_t) - exp(lse_t - r_t).  The
+ * gradient products therefore read E as it is (no dlogits array): dhidden
+ * applies s_t to its result rows, dW reads the hidden states scaled by s_t.
+ * A row whose logits exceed its reference by more than a fixed window (its
+ * exponentials would leave the binary32 range) flags the call; the forward
+ * product then runs again with that row's maximum as its reference.
+ * Transposed copies of the compacted hidden states and of each vocabulary
+ * chunk of W give the products their reduction dimension contiguous; the
+ * dhidden product reads E, whose reduction dimension (vocabulary) is strided
+ * in the forward's accumulator order, through transposing LDS reads.  No
+ * floating-point atomics: results are bitwise reproducible.
  */
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -80,8 +87,13 @@ constexpr int kPad = 32;                   // token counts and vocabulary chunks
 constexpr int kChunkV = 32768;
 constexpr float kL2E = 1.4426950408889634f;
 constexpr double kL2ED = 1.4426950408889634074;
+// How far (in nats) a token's logits may exceed its reference before the
+// forward product runs again for it: E stays below e^48 (bfloat16 and
+// binary32 hold up to e^88), its sum over any vocabulary below e^61 and the
+// gradient products' sums far inside the binary32 range.
+constexpr float kRefWindow = 48.0f;
 
-enum { GM_LSE = 0, GM_ACC = 2, GM_STORE = 3 };
+enum { GM_LSE = 0, GM_LSE_E = 1, GM_ACC = 2, GM_STORE = 3 };
 
 // Tile shape of each product.  The forward product's output width is the
 // vocabulary: 256 x 256 tiles, wavefronts of WM x WN = 128 x 64 in a 2 x 4
@@ -93,7 +105,7 @@ enum { GM_LSE = 0, GM_ACC = 2, GM_STORE = 3 };
 // product's.
 template <int MODE>
 struct TileShape {
-  static constexpr bool kFwd = MODE == GM_LSE;
+  static constexpr bool kFwd = MODE == GM_LSE || MODE == GM_LSE_E;
   static constexpr int BN = kFwd ? GBN : 224;  // output columns of a workgroup
   static constexpr int WM = kFwd ? 128 : 64;
   static constexpr int WN = kFwd ? 64 : 112;
@@ -106,6 +118,10 @@ struct TileShape {
 // rows 4 * (l / 16) + r, r = 0..3, of column l % 16 at l * 4 + r.  Each lane
 // stores its 4 values as one 8-byte store, so a wavefront's 16 x 16 block is
 // 512 contiguous bytes.  Element (t, v) lies at ebk_offset(t, v, ntn).
+// The gradient products read E in this order: for the dhidden product, 32
+// vocabulary columns of a tile's 256 tokens are 16 runs of 1 KB (blocks
+// j, j+1 of every (wm, i)); for the dW product, 32 tokens of its 256
+// vocabulary rows are 4 runs of 4 KB (blocks i, i+1 of every wn).
 __host__ __device__ inline int64_t ebk_offset(int64_t t, int64_t v, int64_t ntn) {
   const int64_t tl = t % GBM, vl = v % GBN;
   const int64_t wm = tl / WM, i = (tl % WM) / 16, q = (tl % 16) / 4, r = tl % 4;
@@ -120,33 +136,36 @@ struct GemmArgs {
   // A[r * ar + (k / 32) * ak + k % 32]: a row-major [M, ld] matrix has
   // ar = ld, ak = 32; a K-paneled one, stored as K/32 panels [rows][32],
   // has ar = 32, ak = rows * 32.  The same holds for B ([N, K]) with br, bk.
-  // GM_STORE's A is paneled over its rows instead (the dlogits chunk as the
-  // streaming kernel writes it, rows = vocabulary columns): (r, k) at
-  // A[(r / 32) * ar + k * 32 + r % 32], ar the panel stride, ak = 32 * 32.
+  // The gradient products' A is the forward product's E (ebk_offset order;
+  // ar and ak unused): GM_ACC's element (t, k) is E[t, col_base + k], GM_STORE's
+  // element (v, k) is E[k, col_base + v].
   const uint16_t* A;
   const uint16_t* B;
   int64_t ar, ak, br, bk;
   int64_t M, N, K;    // static bounds (grid); K a multiple of 8
   const int32_t* M_dev;  // if set: M = *M_dev (active-token count)
   const int32_t* K_dev;  // if set: K = *K_dev (padded active-token count)
-  // GM_LSE
-  float2* part;          // [rows, ntn] per-token (max, sum exp) of each column tile
-  int64_t ntn;
+  // GM_LSE / GM_LSE_E
+  float2* part;          // [rows, ntn] per-token (reference, sum exp) of each column tile
+  int64_t ntn;           // vocabulary tiles of the forward product (all products)
   float* xy;             // [rows] sampled token's logit
   const int32_t* ycol;   // [rows] sampled token id
-  int64_t col_base;      // vocabulary id of column 0
-  // GM_LSE, optional (NULL: not stored): E = exp(x - m) of every logit in
-  // binary16, with m the maximum of its row over the 64 columns of one
-  // wavefront block, in the accumulators' own order (see ebk_offset); the
-  // maxima at wmax[(v / 64) * ldw + t] (ldw: the rows rounded up to GBM)
+  int64_t col_base;      // vocabulary id of column 0 (the gradient products: of the chunk)
+  // GM_LSE_E: E = exp(x - r_t) of every logit in bfloat16, in the
+  // accumulators' own order (ebk_offset); r_t = mref[t]; a row whose logits
+  // in a tile exceed r_t by more than kRefWindow raises *flag and records
+  // the tile's maximum (order-preserving int image) in rowmax[t] (atomic max)
   uint16_t* E;
-  float* wmax;
-  int64_t ldw;
+  const float* mref;
+  int32_t* rowmax;
+  int32_t* flag;
+  const int32_t* run_if;  // the rerun kernel: does nothing unless *run_if != 0
   // GM_ACC / GM_STORE
   float* Cf;             // [M, ldc] binary32 accumulator
   uint16_t* Cb;          // [M, ldc] bfloat16 result
   int64_t ldc;
   int accumulate;        // GM_ACC: add to Cf (else overwrite)
+  const float* rscale;   // GM_ACC: row t's result is scaled by rscale[t]
 };
 
 template <bool B>
@@ -212,11 +231,17 @@ constexpr int kDppMirror = 0x140;
 // among 8 consecutive, and rows equal mod 4 among 16, get distinct values
 __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// chunk permutation of record k (one reduction index, 32 rows of 64 B) of
-// GM_STORE's A stage: records k and k + 8 use opposite chunk pairs, so the
-// transposing fragment reads of a half wavefront (4 records x 2 chunks for
-// each of its two 16-lane groups, records 8g + ..) touch every bank once
-__device__ inline int tsw(int k) { return 2 * ((k >> 3) & 1); }
+// chunk permutation within a 512-byte E block (one 16 x 16 MFMA block) of
+// GM_ACC's A stage: LDS chunk 8q + y (16 bytes) holds the block's chunk
+// 8q + (y ^ 2q), i.e. columns 2y', 2y'+1 of rows 4q .. 4q+3 with y' = y ^ 2q.
+// One transposing read of a 16-lane group takes 4 consecutive columns of all
+// four quads: 8 chunks that land on 8 distinct 16-byte positions of a
+// 128-byte bank row, so the group touches every bank once.  Its own inverse.
+__device__ inline int esw(int p) { return p ^ (2 * (p >> 3)); }
+
+// the forward product's wavefront grid, under names the products' own tile
+// shapes do not hide
+constexpr int WM_F = WM, WN_F = WN, NWN_F = NWN;
 
 // quad permutation of row c of an epilogue stage of kWM rows (kWM / 4
 // quads): an even value below kWM / 4; 16 consecutive rows get distinct
@@ -279,15 +304,13 @@ __device__ inline void stage_pair(uint16_t* stg, int lane, int i, int j, uint32_
   *reinterpret_cast<uint2*>(stg + c * kWM + 4 * (q ^ stage_swz<kWM>(c))) = make_uint2(lo, hi);
 }
 
-// two wavefronts per SIMD: the register budget of 8 wavefronts per CU, whatever the
-// workgroup size (with 4-wavefront workgroups, two workgroups share a CU)
-// GM_STORE's fragment reads within one step, in issue order: after the
+// GM_ACC's fragment reads within one step, in issue order: after the
 // MFMAs of row block i (of 4), B fragments b_cum(i) .. b_cum(i+1)-1 of the
 // next stage (all 7 within row blocks 0-2, so the last one has a row block of
 // MFMAs to land), then the two transposing reads of A fragment i.  A
 // wavefront's LDS reads complete in order, so "at most n outstanding" lands
 // every read with n or more issued after it; the counts below follow.
-namespace store_reads {
+namespace tr_reads {
 constexpr int b_cum(int i) { return i <= 0 ? 0 : i == 1 ? 3 : i == 2 ? 5 : 7; }
 constexpr int n(int i) { return b_cum(i + 1) - b_cum(i) + 2; }
 constexpr int before(int i) { return i == 0 ? 0 : before(i - 1) + n(i - 1); }
@@ -306,10 +329,12 @@ constexpr int wait_a(int i) { return kTotal - 1 - a_end(i) + before(i); }
 static_assert(b_cum(4) == 7 && kTotal == 15 && kWait0 == 4 && landed0(1) && !landed0(2) &&
                   wait_a(2) == 11 && wait_a(3) == 13,
               "GM_STORE read order");
-}  // namespace store_reads
+}  // namespace tr_reads
 
+// One output tile b of a product (the launch's workgroup id, or a tile a
+// workgroup of the rerun kernel walks to).
 template <int MODE>
-__global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_gemm(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   // this product's tile shape (for the forward product the same values as
   // the namespace constants these names hide)
@@ -338,7 +363,6 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   const int ntm = (int)((M + GBM - 1) / GBM);
   const int ntn_t = (int)((g.N + BN - 1) / BN);
   const int total = ntm * ntn_t;
-  const int b = blockIdx.x;
   if (b >= total) return;
   const int q8 = total / 8;
   const int v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
@@ -360,41 +384,47 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // ---- main loop: a ring of kStages LDS stages, each [A 256 x 32 | B 256 x 32]
   // bfloat16 (row r of A at r*32, of B at (256 + r)*32; 64-byte rows), filled
   // by direct global -> LDS loads issued kStages-1 stages ahead.  Each
-  // wavefront loads kDmaA 16-row groups of A and kDmaB of B, through buffer
-  // descriptors over the tile's rows of the current 32-wide reduction panel
+  // wavefront loads kDmaA 1 KB pieces of A and kDmaB of B, through buffer
+  // descriptors over the tile's part of the current 32-wide reduction step
   // (buffer loads: the compiler counts them on vmcnt alone, so the LDS
   // fragment reads keep fine-grained waits).
-  // One instruction moves 16 rows x 64 B (lane l: row l/4, chunk l%4): a
-  // single contiguous 1 KB block of a K-paneled operand.  Rows past M or N
+  // A paneled operand: one instruction moves 16 rows x 64 B (lane l: row
+  // l/4, chunk l%4), a single contiguous 1 KB block.  Rows past M or N
   // re-read the last valid row (their results are never used).  K is a
-  // multiple of 32.  The four 16-byte chunks of a row are stored XOR-permuted
-  // by swz(row % 16), so the fragment reads (16 rows, one chunk) spread over
-  // all LDS banks.
-  // GM_STORE's A (paneled over its rows) lands as one [32 k][32 rows] block
-  // per row panel: wavefront wv loads panel wv of the tile (2 KB, two
-  // contiguous 1 KB halves of 16 k records); panels past the last valid row
-  // re-read the last valid one.  Record k's chunks are permuted by tsw(k),
-  // and its fragments come back through transposing LDS reads.
-  constexpr bool kAT = MODE == GM_STORE;
-  static_assert(!kAT || (kDmaA == 2 && GBM / 32 == GT / 64), "one row panel of A per wavefront");
+  // multiple of 32.  The four 16-byte chunks of a row are stored
+  // XOR-permuted by swz(row % 16), so the fragment reads (16 rows, one chunk)
+  // spread over all LDS banks.
+  // The gradient products' A is E in the forward's order (ebk_offset): one
+  // instruction moves one 1 KB run, two 16 x 16 blocks.  GM_ACC (rows =
+  // tokens, reduction over vocabulary) stages run (wm, i) of the forward tile
+  // at 1 KB * (8 wm + i), its chunks permuted within each 512-byte block by
+  // esw, and reads its fragments through transposing LDS reads.  GM_STORE
+  // (rows = vocabulary, reduction over tokens) stages its four 4 KB runs
+  // (one per wn) in order and reads each fragment as two 8-byte reads.
+  constexpr bool kAT = MODE == GM_ACC;     // A through transposing reads
+  constexpr bool kEA = MODE == GM_ACC || MODE == GM_STORE;  // A is E
+  static_assert(!kEA || kDmaA == 2, "two E runs per wavefront and stage");
   const int64_t nk = K / GBK;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int64_t nvA = M - m0 < GBM ? M - m0 : GBM;    // >= 1: the tile exists
   const int64_t nvB = g.N - n0 < GBN ? g.N - n0 : GBN;
-  const int64_t plastA = (nvA - 1) >> 5;
-  const uint16_t* baseA =
-      kAT ? g.A + (m0 / 32 + (wv < plastA ? wv : plastA)) * g.ar : g.A + m0 * g.ar;
   const uint16_t* baseB = g.B + n0 * g.br;
-  // the span one stage's loads address: the rows' span in one panel
-  const int pbA = kAT ? GBK * 32 * 2 : (int)(((nvA - 1) * g.ar + GBK) * 2);
+  // the span one stage's loads address
+  const int pbA = MODE == GM_ACC     ? 2 * (32768 + 7 * 1024 + 512)
+                  : MODE == GM_STORE ? 2 * (3 * 8192 + 2048)
+                                     : (int)(((nvA - 1) * g.ar + GBK) * 2);
   const int pbB = (int)(((nvB - 1) * g.br + GBK) * 2);
   const int dchunk = 8 * ((lane & 3) ^ swz(lane >> 2));
   uint32_t voffA[kDmaA], voffB[kDmaB];
 #pragma unroll
   for (int p = 0; p < kDmaA; ++p) {
-    if constexpr (kAT) {
-      const int k = 16 * p + (lane >> 2);
-      voffA[p] = (uint32_t)((k * 32 + 8 * ((lane & 3) ^ tsw(k))) * 2);
+    if constexpr (MODE == GM_ACC) {
+      // run (wm, i) = (wv / 4, 2 (wv % 4) + p); lane l: chunk esw(l % 32) of block l / 32
+      voffA[p] = (uint32_t)(2 * ((wv >> 2) * 32768 + (2 * (wv & 3) + p) * 1024 +
+                                 (lane >> 5) * 256 + esw(lane & 31) * 8));
+    } else if constexpr (MODE == GM_STORE) {
+      // run wn = wv / 2, its half wv % 2, 1 KB piece p
+      voffA[p] = (uint32_t)(2 * ((wv >> 1) * 8192 + (wv & 1) * 1024 + p * 512 + lane * 8));
     } else {
       const int64_t r = (wv * kDmaA + p) * 16 + (lane >> 2);
       voffA[p] = (uint32_t)(((r < nvA ? r : nvA - 1) * g.ar + dchunk) * 2);
@@ -405,10 +435,25 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     const int64_t r = (wv * kDmaB + p) * 16 + (lane >> 2);
     voffB[p] = (uint32_t)(((r < nvB ? r : nvB - 1) * g.br + dchunk) * 2);
   }
+  // first element of stage kt's part of A
+  auto a_stage = [&](int64_t kt) -> const uint16_t* {
+    if constexpr (MODE == GM_ACC) {
+      const int64_t v = g.col_base + kt * GBK;  // the step's first vocabulary column
+      return g.A + ((int64_t)tm * g.ntn + v / GBN) * (GBM * GBN) + ((v % GBN) / WN_F) * (WM_F * WN_F) +
+             ((v % WN_F) / 32) * 512;
+    } else if constexpr (MODE == GM_STORE) {
+      // tokens 32 kt ..: forward row tile kt / 8, its wavefront row block
+      // (kt % 8) / 4, MFMA row blocks 2 (kt % 4), +1
+      return g.A + ((kt / 8) * g.ntn + (g.col_base + m0) / GBN) * (GBM * GBN) +
+             ((kt % 8) / 4) * (NWN_F * WM_F * WN_F) + (kt % 4) * 2048;
+    } else {
+      return g.A + m0 * g.ar + kt * g.ak;
+    }
+  };
   auto dma = [&](int64_t kt) {
     uint16_t* slot = smem + (kt % kStages) * kStageElems;
-    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(baseA + kt * g.ak), 0,
-                                                      pbA, 0x00020000);
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a_stage(kt)), 0, pbA,
+                                                      0x00020000);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(baseB + kt * g.bk), 0,
                                                       pbB, 0x00020000);
 #pragma unroll
@@ -428,7 +473,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // A fragments are reloaded in place, row block by row block, as soon as the
   // MFMAs of that block have issued; B fragments are double-buffered
   bf16x8 fa[FM], fb[2][FN];
-  // GM_STORE reads every fragment through inline assembly: the compiler
+  // GM_ACC reads every fragment through inline assembly: the compiler
   // models the transposing read's builtin as possibly aliasing the direct
   // loads in flight and would drain them all (vmcnt(0)) before each one.
   // The reads then issue in program order and the step waits for them
@@ -437,34 +482,45 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   auto lds_addr = [](const uint16_t* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
   };
-  // GM_STORE's A fragment i: rows wm*WM + i*16 + fr sit in panel
-  // pb = 2*wm + i/2 at rows rb = 16*(i%2).. of it.  Lane 4e + q of a 16-lane
-  // group points at record k = 8*(lane/16) + 4*hh + e, rows rb + 4q .. +3;
-  // the read hands lane fr of the group records k0 .. k0+3 of row rb + fr:
-  // two reads (hh = 0, 1) give its 8 reduction indices.  In bytes from the
-  // stage: 4096*wm + 2048*(i/2) + 64*k + 16*(chunk ^ tsw(k)) + 8*(q%2) with
-  // chunk = 2*(i%2) + q/2; all but 2048*(i/2) + 256*hh depend on the lane and
-  // the parity of i only, so each read is a base register plus an offset.
+  // GM_ACC's A fragment i: rows wm*WM + i*16 + fr are rows 4q + r of MFMA
+  // block i' = 4 (wm % 2) + i of forward wavefront row block wm / 2, staged
+  // as run 4 wm + i (1 KB each).  Lane 4e + q4 of 16-lane group g points at
+  // quad q4 (4 rows) of column f = 8 (g % 2) + 4 hh + e of block g / 2 of the
+  // run; the read hands lane fr of the group columns f - e .. +3 of row fr,
+  // and the two reads (hh = 0, 1) give its 8 reduction indices 8g .. 8g+7.
+  // Column f of quad q4 is chunk 8 q4 + f / 2 (half f % 2) of its block,
+  // staged at chunk esw(8 q4 + f / 2).  In bytes from the stage:
+  // 4096 wm + 1024 i + 512 (g / 2) + 16 esw(..) + 8 (e % 2): the lane- and
+  // hh-dependent part is one base register per hh, 1024 i an offset.
+  const int g4 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
   const uint32_t offA[2] = {
-      (uint32_t)(4096 * wm + 64 * (8 * (lane >> 4) + (fr >> 2)) +
-                 16 * ((2 * 0 + ((fr & 3) >> 1)) ^ tsw(8 * (lane >> 4))) + 8 * (fr & 1)),
-      (uint32_t)(4096 * wm + 64 * (8 * (lane >> 4) + (fr >> 2)) +
-                 16 * ((2 * 1 + ((fr & 3) >> 1)) ^ tsw(8 * (lane >> 4))) + 8 * (fr & 1))};
+      (uint32_t)(4096 * wm + 512 * (g4 >> 1) + 16 * esw(8 * q4 + 4 * (g4 & 1) + 0 + (e4 >> 1)) +
+                 8 * (e4 & 1)),
+      (uint32_t)(4096 * wm + 512 * (g4 >> 1) + 16 * esw(8 * q4 + 4 * (g4 & 1) + 2 + (e4 >> 1)) +
+                 8 * (e4 & 1))};
+  // GM_STORE's A fragment i: vocabulary rows wm*WM + i*16 + fr are column fr
+  // of MFMA block (i_l, j = i) of forward wavefront column block wn = wm;
+  // the lane's tokens 8 g4 .. +7 are quads 2 (g4 % 2), +1 of block i_l = g4 / 2,
+  // two 8-byte reads 128 bytes apart
+  const int offS = (4096 * wm + 2048 * (g4 >> 1) + 256 * (g4 & 1) + 8 * fr) / 2;
   const uint32_t offB = (uint32_t)(2 * ((wn * WN + fr) * GBK + fk));
   auto frag_a = [&](const uint16_t* As, int i) -> bf16x8 {
     if constexpr (kAT) {
-      const uint32_t base = lds_addr(As) + offA[i & 1];
       s16x4 t[2];
       asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                   : "=v"(t[0]) : "v"(base), "i"(2048 * (i >> 1)) : "memory");
+                   : "=v"(t[0]) : "v"(lds_addr(As) + offA[0]), "i"(1024 * i) : "memory");
       asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                   : "=v"(t[1]) : "v"(base), "i"(2048 * (i >> 1) + 256) : "memory");
+                   : "=v"(t[1]) : "v"(lds_addr(As) + offA[1]), "i"(1024 * i) : "memory");
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    } else if constexpr (MODE == GM_STORE) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(As + offS + 256 * i);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(As + offS + 256 * i + 64);
+      return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
     } else {
       return *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + fr) * GBK + fk);
     }
   };
-  // (GM_STORE: B fragment j at offB + 1024*j bytes from the stage's B rows)
+  // (GM_ACC: B fragment j at offB + 1024*j bytes from the stage's B rows)
   auto frag_b = [&](const uint16_t* Bs, int j) -> bf16x8 {
     if constexpr (kAT) {
       bf16x8 v;
@@ -475,7 +531,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
       return *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + j * 16 + fr) * GBK + fk);
     }
   };
-  // GM_STORE: every fragment read has landed; the fragments named stay in
+  // GM_ACC: every fragment read has landed; the fragments named stay in
   // their registers until here
   // (each empty statement after a wait keeps a fragment's readers below it)
   auto settle_all = [&]() {
@@ -513,19 +569,27 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // loaded into registers here, before the first stages' loads, and written
   // to LDS after the main loop, whose last wait has seen them land: the
   // loads cost no wait of their own.
-  //   GM_LSE: tile-local column of the row's sampled token (-1: none, or a
-  //           column of another tile, which never equals a local column)
+  //   GM_LSE, GM_LSE_E: tile-local column of the row's sampled token (-1:
+  //           none, or a column of another tile, which never equals a local
+  //           column)
+  //   GM_LSE_E: the row's reference r_t (rows past M: the last row's, whose
+  //           logits they repeat)
   int32_t* const t_yl = reinterpret_cast<int32_t*>(smem + kTableElem);  // [GBM]
-  constexpr bool kTables = MODE == GM_LSE;
+  float* const t_mr = reinterpret_cast<float*>(smem + kTableElem) + GBM;  // [GBM]
+  constexpr bool kTables = MODE == GM_LSE || MODE == GM_LSE_E;
+  constexpr bool kRef = MODE == GM_LSE_E;
   static_assert(!kTables || !kTablesInRing, "the epilogue tables are written while waves may still read the ring");
+  static_assert(2 * GBM * 4 <= kTableBytes, "two row tables");
   constexpr int kYPer = (GBM + GT - 1) / GT;
   int32_t ypre[kYPer];
+  float mrpre[kYPer];
   if constexpr (kTables) {
 #pragma unroll
     for (int k = 0; k < kYPer; ++k) {
       const int r = tid + k * GT;
       const bool ok = r < GBM && m0 + r < M;
       ypre[k] = ok ? g.ycol[m0 + r] : -1;
+      if constexpr (kRef) mrpre[k] = r < GBM ? g.mref[ok ? m0 + r : M - 1] : 0.0f;
     }
   }
   if (nk > 0)
@@ -559,17 +623,17 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
     for (int i = 0; i < FM; ++i) {
       if constexpr (kAT) {
         // the previous step's (or the prologue's, which waits for all) reads
-        // this row block needs, in the order store_reads describes
-        static_assert(FM == 4 && FN == 7, "store_reads");
+        // this row block needs, in the order tr_reads describes
+        static_assert(FM == 4 && FN == 7, "tr_reads");
         if (i == 0) {
-          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(store_reads::kWait0) : "memory");
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(tr_reads::kWait0) : "memory");
 #pragma unroll
           for (int k = 0; k < FM; ++k)
-            if (store_reads::landed0(k)) asm volatile("" : "+v"(fa[k]));
+            if (tr_reads::landed0(k)) asm volatile("" : "+v"(fa[k]));
 #pragma unroll
           for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[cur][j]));
-        } else if (!store_reads::landed0(i)) {
-          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(store_reads::wait_a(i)) : "memory");
+        } else if (!tr_reads::landed0(i)) {
+          asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(tr_reads::wait_a(i)) : "memory");
           asm volatile("" : "+v"(fa[i]));
         }
       }
@@ -578,7 +642,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
       if constexpr (kAT) {
 #pragma unroll
-        for (int jb = store_reads::b_cum(i); jb < store_reads::b_cum(i + 1); ++jb)
+        for (int jb = tr_reads::b_cum(i); jb < tr_reads::b_cum(i + 1); ++jb)
           fb[cur ^ 1][jb] = frag_b(As + GBM * GBK, jb);
       } else if constexpr (FN <= FM) {
         if (i < FN) fb[cur ^ 1][i] = frag_b(As + GBM * GBK, i);
@@ -641,6 +705,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
       const int r = tid + k * GT;
       if (r < GBM) {
         t_yl[r] = ypre[k] < 0 ? -1 : (int32_t)(ypre[k] - (g.col_base + n0));
+        if constexpr (kRef) t_mr[r] = mrpre[k];
       }
     }
   }
@@ -656,10 +721,9 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   // columns of this tile that exist (the rest of the tile is padding)
   const int ncols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
   const int lc0 = wn * WN + fr;  // tile-local column of acc[.][0]
-  if constexpr (MODE == GM_LSE) {
+  if constexpr (MODE == GM_LSE || MODE == GM_LSE_E) {
     float2* red = reinterpret_cast<float2*>(smem + kRedElem);  // [NWN][GBM]
     const int32_t* yl = t_yl;
-    const bool keepE = g.E != nullptr;
     // full tiles (the common case) compile without the column checks
     auto body = [&](auto full_tag) {
       constexpr bool kFull = decltype(full_tag)::value;
@@ -709,15 +773,22 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
         for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppHalfMirror>(mo[r]));
 #pragma unroll
         for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppMirror>(mo[r]));
-        float mx[4], sm[4];
+        float mx[4], sm[4], ref[4];
+        if constexpr (kRef) {
+          const float4 m4 = *reinterpret_cast<const float4*>(t_mr + rt0);
+          ref[0] = m4.x, ref[1] = m4.y, ref[2] = m4.z, ref[3] = m4.w;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           mx[r] = ord_f32(mo[r]);
-          // (a quarter tile past the last vocabulary column holds no value at
-          // all, only in a partial tile); exp(x - M) as exp2(x*log2e - M*log2e), one fused step per
-          // entry (the rounding of M*log2e scales the whole partial sum by one
-          // factor 2^d, |d| <= 2^-24 |M| log2e)
-          const float nb = kFull || mx[r] != -INFINITY ? -mx[r] * kL2E : 0.0f;
+          // exp(x - ref) as exp2(x*log2e - ref*log2e), one fused step per
+          // entry (the rounding of ref*log2e scales the whole partial sum by
+          // one factor 2^d, |d| <= 2^-24 |ref| log2e).  GM_LSE: ref = the
+          // row's maximum over the tile (a quarter tile past the last
+          // vocabulary column holds no value at all, only in a partial tile);
+          // GM_LSE_E: the row's reference, fixed for the whole call
+          if constexpr (!kRef) ref[r] = mx[r];
+          const float nb = kRef || kFull || ref[r] != -INFINITY ? -ref[r] * kL2E : 0.0f;
           // the exponentials replace the logits in acc (E below)
           acc[i][0][r] = __builtin_amdgcn_exp2f(fmaf(acc[i][0][r], kL2E, nb));
           sm[r] = acc[i][0][r];
@@ -727,20 +798,16 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
             sm[r] += acc[i][j][r];
           }
         }
-        if (keepE) {
-          // binary16 (nearest even), the lane's four rows of a column as one
-          // 8-byte store (ebk_offset); the block maxima of the four rows as
-          // one 16-byte store, the 16 rows of block i in 64 contiguous bytes
+        if constexpr (kRef) {
+          // bfloat16 (nearest even), the lane's four rows of a column as one
+          // 8-byte store (ebk_offset)
           uint16_t* eb = g.E + ((int64_t)tm * ntn_t + tn) * (GBM * GBN) +
                          (wm * NWN + wn) * (WM * WN) + lane * 4;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             __builtin_nontemporal_store(
-                u32x2{f16x2_bits(acc[i][j][0], acc[i][j][1]), f16x2_bits(acc[i][j][2], acc[i][j][3])},
+                u32x2{bf16x2_bits(acc[i][j][0], acc[i][j][1]), bf16x2_bits(acc[i][j][2], acc[i][j][3])},
                 reinterpret_cast<u32x2*>(eb + (i * FN + j) * 256));
-          if (fr == 0)
-            *reinterpret_cast<float4*>(g.wmax + (tn * NWN + wn) * g.ldw + m0 + rt0) =
-                make_float4(mx[0], mx[1], mx[2], mx[3]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppXor1>(sm[r]);
@@ -767,6 +834,21 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
       float mx = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NWN; ++w) mx = fmaxf(mx, red[w * GBM + r].x);
+      if constexpr (kRef) {
+        // the wavefronts' sums share the row's reference
+        const float ref = t_mr[r];
+        float sm = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWN; ++w) sm += red[w * GBM + r].y;
+        g.part[row * g.ntn + tn] = make_float2(ref, sm);
+        // logits beyond the reference's window: record the tile's maximum and
+        // flag the call (rare)
+        if (mx - ref > kRefWindow) {
+          atomicMax(g.rowmax + row, f32_ord(mx));
+          __hip_atomic_store(g.flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        continue;
+      }
       float sm = 0.0f;
       if (mx != -INFINITY) {
 #pragma unroll
@@ -792,6 +874,9 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
         auto ok = [&](int j, int r) { return kFull || (lc0 + j * 16 < ncols && rt0 + r < nrows); };
         if constexpr (MODE == GM_ACC) {
           float* c = g.Cf + base + i * 16 * ldc;
+          // the rows' dlogits factors (rscale holds the rows of whole tiles)
+          const float4 s4 = *reinterpret_cast<const float4*>(g.rscale + m0 + rt0);
+          const float sc[4] = {s4.x, s4.y, s4.z, s4.w};
           float old[FN][4] = {};
           if (g.accumulate) {
 #pragma unroll
@@ -804,7 +889,7 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
           for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (ok(j, r)) c[r * ldc + j * 16] = old[j][r] + acc[i][j][r];
+              if (ok(j, r)) c[r * ldc + j * 16] = fmaf(sc[r], acc[i][j][r], old[j][r]);
         } else {
 #pragma unroll
           for (int j = 0; j < FN; ++j)
@@ -822,6 +907,26 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
       body(BoolC<true>{});
     else
       body(BoolC<false>{});
+  }
+}
+
+// One workgroup per output tile; two wavefronts per SIMD (the register
+// budget of 8 wavefronts per CU).
+template <int MODE>
+__global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_gemm(GemmArgs g) {
+  gemm_tile<MODE>(g, (int)blockIdx.x);
+}
+
+// The loss's forward product once more, for a call whose first pass flagged
+// a row (its references updated in between): nothing happens unless
+// *run_if != 0, so it is launched on every call with one workgroup per CU,
+// and each workgroup walks tiles b, b + gridDim.x, .. below nblocks.
+__global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2)))
+k_gemm_rerun(GemmArgs g, int nblocks) {
+  if (__builtin_amdgcn_readfirstlane(*g.run_if) == 0) return;
+  for (int b = (int)blockIdx.x; b < nblocks; b += (int)gridDim.x) {
+    gemm_tile<GM_LSE_E>(g, b);
+    __syncthreads();  // the next tile's loads reuse the LDS this one's epilogue reads
   }
 }
 
@@ -913,11 +1018,12 @@ k_lm_gather(const uint16_t* __restrict__ hidden, int64_t H, const int64_t* __res
 // accesses on both sides (8 columns of a row in, 8 rows of a column out: a
 // quarter of a 64-byte panel record), so cols and the row counts are
 // multiples of 8 and every offset a multiple of 8 elements.  The grid covers
-// ceil(rows_pad / 64) x ceil(cols / 64) tiles.
+// ceil(rows_pad / 64) x ceil(cols / 64) tiles.  With rscale, source row r is
+// multiplied by rscale[r] (binary32) and rounded to bfloat16 on the way.
 __global__ void __launch_bounds__(256)
 k_transpose(const uint16_t* __restrict__ src, int64_t s_rs, int64_t s_ps, int64_t rows,
             int64_t rows_pad, int64_t cols, const int32_t* __restrict__ rows_dev,
-            uint16_t* __restrict__ dst, int64_t d_ps) {
+            const float* __restrict__ rscale, uint16_t* __restrict__ dst, int64_t d_ps) {
   constexpr int TS = 64, TP = TS + 8;  // tile, padded LDS row (16-byte aligned rows)
   __shared__ __attribute__((aligned(16))) uint16_t tile[TS][TP];
   const int64_t R = rows_dev ? (int64_t)*rows_dev : rows;
@@ -930,8 +1036,19 @@ k_transpose(const uint16_t* __restrict__ src, int64_t s_rs, int64_t s_ps, int64_
     const int k = e >> 3, cc = (e & 7) * 8;  // tile row, first of its 8 columns
     const int64_t r = r0 + k, c = c0 + cc;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (r < R && c < cols)
+    if (r < R && c < cols) {
       v = *reinterpret_cast<const u32x4*>(src + r * s_rs + (c / 32) * s_ps + c % 32);
+      if (rscale) {
+        const float sc = rscale[r];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[u] = bf16x2_bits(sc * __builtin_bit_cast(float, w[u] << 16),
+                             sc * __builtin_bit_cast(float, w[u] & 0xFFFF0000u));
+        v = u32x4{o[0], o[1], o[2], o[3]};
+      }
+    }
     *reinterpret_cast<u32x4*>(&tile[k][cc]) = v;
   }
   __syncthreads();
@@ -983,8 +1100,8 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
              const int32_t* __restrict__ ycol, int64_t C, const float* __restrict__ adv,
              const int32_t* __restrict__ len, const float* __restrict__ logp_old,
              const float* __restrict__ logp_ref, float eps, float beta, double kappa, int agg,
-             const int64_t* __restrict__ total_len, float2* __restrict__ lsep,
-             float* __restrict__ coef, double* __restrict__ tok_loss,
+             const int64_t* __restrict__ total_len, const float* __restrict__ mref,
+             uint16_t* __restrict__ E, float* __restrict__ rscale, double* __restrict__ tok_loss,
              uint8_t* __restrict__ tok_flags) {
   const int lane = threadIdx.x & 63;
   const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -994,9 +1111,9 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
   if (lane != 0) return;
   const int64_t pos = act_pos[k];
   const int64_t i = pos / C;
-  if (ycol[k] < 0) {  // bad token id: excluded from the gradient, poisons the loss
-    lsep[k] = make_float2(0.0f, INFINITY);
-    coef[k] = 0.0f;
+  const int32_t y = ycol[k];
+  if (y < 0) {  // bad token id: excluded from the gradient, poisons the loss
+    rscale[k] = 0.0f;
     return;
   }
   const double logp = (double)xy[k] - lse;
@@ -1005,121 +1122,66 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
                                     adv[i], eps, beta, div);
   tok_loss[pos] = tt.lam / div;
   tok_flags[pos] = tt.flags;
-  lsep[k] = make_float2(ls.M, (float)log2(ls.S));
-  coef[k] = (float)tt.coef;
+  // dlogits of the row: D[t, v] = coef (p_v - [v = y]) = s E[t, v] with
+  // E = exp(x - r) (r the row's reference) and s = coef exp(r - lse), once
+  // the sampled entry of E holds exp(x_y - r) - exp(lse - r); coef = 0 (a
+  // clip-cut gradient) gives s = 0, exact zero rows
+  const double r = (double)mref[k];
+  const float cf = (float)tt.coef;
+  rscale[k] = (float)((double)cf * exp(r - lse));
+  E[ebk_offset(k, y, ntn)] = bf16_bits((float)(exp((double)xy[k] - r) - exp(lse - r)));
 }
 
-// dlogits of one vocabulary chunk from the forward product's exponentials.
-// For active token t and chunk column c (vocabulary id v = v0 + c), with m
-// the block maximum E[t, v] is relative to and lse_t = M_t + ln S_t:
-//   D[t, c] = coef_t exp(x - lse_t)
-//           = sign(coef_t) exp2((m - M_t) log2e + log2|coef_t| - log2 S_t) E[t, v]
-// except the sampled column, D[t, y_t] = coef_t (p - 1) with
-// p = exp2((x_y - M_t) log2e - log2 S_t) from the sampled logit x_y the
-// forward product kept.  Rows past the active count (up to kPad) are zeros.
-// D is written K-paneled over the chunk's columns with 16-byte stores, the
-// layout both gradient products read (the dW product through transposing LDS
-// reads).  One workgroup per 64 tokens x 256 columns: a quarter of one forward tile,
-// whose exponentials are 4 runs of 8 KB (ebk_offset), read with 16-byte
-// loads, scaled, and transposed through LDS.
-constexpr int kDcTok = 64, kDcCol = 256;
-static_assert(kDcCol == GBN && GBM % kDcTok == 0 && WM % kDcTok == 0, "a quarter tile");
+// Each active token's reference r_t for the loss's forward product: its
+// sampled token's logit hidden_t . W[y_t] (binary32 sum of bfloat16
+// products, one wavefront per token; 0 for a bad token id).  Any value would
+// do as long as E = exp(x - r_t) stays in range: the sampled token's logit is
+// at most the row's maximum, and a row whose maximum lies more than
+// kRefWindow above it is detected and redone.  Also clears the call's flag
+// and the rows' recorded maxima.
 __global__ void __launch_bounds__(256)
-k_lm_dchunk(const uint16_t* __restrict__ E, int64_t ntn, const float* __restrict__ wmax,
-            int64_t ldw, const float2* __restrict__ lsep, const float* __restrict__ coef,
-            const int32_t* __restrict__ ycol, const float* __restrict__ xy,
-            const int32_t* __restrict__ counts, int64_t v0, int64_t wv, int64_t nblk_c,
-            uint16_t* __restrict__ D, int64_t ldd) {
-  __shared__ float s_sc[kDcTok][NWN];  // scale of row, 64-column block
-  __shared__ float s_dy[kDcTok];
-  __shared__ int32_t s_y[kDcTok];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kDcTok][kDcCol + 8];
-  const int64_t M = counts[0];
-  const int64_t mpad = (M + kPad - 1) / kPad * kPad;
-  const int64_t t0 = (int64_t)(blockIdx.x / nblk_c) * kDcTok;
-  const int64_t c0 = (int64_t)(blockIdx.x % nblk_c) * kDcCol;
-  if (t0 >= mpad) return;
-  const int64_t wpad = (wv + kPad - 1) / kPad * kPad;
-  const int tid = threadIdx.x;
-  {
-    // thread (row, block): the row's scale over that 64-column block; block 0
-    // also the row's sampled column and its entry
-    const int row = tid >> 2, blk = tid & 3;
-    const int64_t t = t0 + row;
-    float sc = 0.0f, dy = 0.0f;
-    int32_t y = -1;
-    if (t < M) {
-      const float2 l = lsep[t];
-      const float cf = coef[t];
-      // log2|coef| - log2 S: -inf for coef = 0 (a clip-cut gradient or a bad
-      // token id), which gives exact zeros; the scale carries coef's sign
-      // (bfloat16 rounding is symmetric: the same bits as negating the result)
-      const float cl = __builtin_amdgcn_logf(fabsf(cf)) - l.y;
-      const float m = wmax[((v0 + c0) / 64 + blk) * ldw + t];
-      sc = __builtin_copysignf(__builtin_amdgcn_exp2f(fmaf(m - l.x, kL2E, cl)), cf);
-      y = ycol[t];
-      if (y >= 0) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(xy[t] - l.x, kL2E, -l.y));
-        dy = cf * (pr - 1.0f);
-      }
-    }
-    s_sc[row][blk] = sc;
-    if (blk == 0) {
-      s_dy[row] = dy;
-      s_y[row] = y;
-    }
-  }
-  __syncthreads();
-  // the quarter tile: rows wm * WM + 16 * i0 .. +63 of forward tile (tm, tn),
-  // all its columns; in each wavefront block (wm, wn) the 16 MFMA blocks
-  // (i, j), i = i0 .. i0 + 3, are one contiguous 8 KB run
-  {
-    // element (t0, v0 + c0) opens the run of wavefront block (wm, 0)
-    const uint16_t* base = E + ebk_offset(t0, v0 + c0, ntn);
+k_lm_mref(const uint16_t* __restrict__ Ha, int64_t ha_ps, const uint16_t* __restrict__ W, int64_t H,
+          const int32_t* __restrict__ counts, const int32_t* __restrict__ ycol,
+          float* __restrict__ mref, int32_t* __restrict__ rowmax, int32_t* __restrict__ flag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 0;
+  if (k >= counts[0]) return;
+  const int32_t y = ycol[k];
+  float acc = 0.0f;
+  if (y >= 0) {
+    for (int64_t h = 8 * lane; h < H; h += 8 * 64) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(Ha + (h / 32) * ha_ps + k * 32 + h % 32);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)y * H + h);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int pass = 0; pass < 2 * NWN; ++pass) {
-      const int wn = pass >> 1;
-      const int bb = (pass & 1) * 8 + (tid >> 5);  // MFMA block of the run, 0..15
-      const int k = tid & 31;                       // 16-byte piece: lanes 2k, 2k + 1
-      const u32x4 e =
-          *reinterpret_cast<const u32x4*>(base + wn * (WM * WN) + bb * 256 + k * 8);
-      const int i = bb / FN, j = bb % FN;
-      const int l0 = 2 * k;                            // lanes l0, l0 + 1: same rows
-      const int rbase = i * 16 + 4 * (l0 >> 4);        // quarter-tile row of r = 0
-      const int col = wn * WN + j * 16 + (l0 & 15);    // columns col, col + 1
-      const uint32_t w[4] = {e.x, e.y, e.z, e.w};      // lane l0 rows 0-1, 2-3; l0+1 rows 0-1, 2-3
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rbase + r;
-        const bool live = t0 + row < M;
-        const float sc = s_sc[row][wn];
-        const f16x2 a = __builtin_bit_cast(f16x2, w[r >> 1]);
-        const f16x2 b = __builtin_bit_cast(f16x2, w[2 + (r >> 1)]);
-        const float ea = (float)((r & 1) ? a.y : a.x), eb = (float)((r & 1) ? b.y : b.x);
-        *reinterpret_cast<uint32_t*>(&tile[row][col]) =
-            live ? bf16x2_bits(sc * ea, sc * eb) : 0u;
+      for (int u = 0; u < 4; ++u) {
+        acc = fmaf(__builtin_bit_cast(float, av[u] << 16), __builtin_bit_cast(float, wv[u] << 16), acc);
+        acc = fmaf(__builtin_bit_cast(float, av[u] & 0xFFFF0000u),
+                   __builtin_bit_cast(float, wv[u] & 0xFFFF0000u), acc);
       }
     }
   }
-  __syncthreads();
-  if (tid < kDcTok) {  // the sampled column of a row, when it is one of these
-    const int64_t dyc = (int64_t)s_y[tid] - (v0 + c0);
-    if (t0 + tid < M && (uint64_t)dyc < (uint64_t)kDcCol) tile[tid][dyc] = bf16_bits(s_dy[tid]);
-  }
-  __syncthreads();
-  // D: per pass one 32-column panel of the 64 rows, 8 consecutive columns a
-  // thread (a contiguous 4 KB block of D)
-  {
-    const int row = tid >> 2, quad = tid & 3;
-    const int64_t t = t0 + row;
 #pragma unroll
-    for (int p = 0; p < kDcCol / 32; ++p) {
-      const int64_t c = c0 + p * 32 + quad * 8;
-      if (c >= wpad) break;  // uniform across the workgroup
-      if (t < mpad)
-        *reinterpret_cast<u32x4*>(D + (c / 32) * ldd + t * 32 + c % 32) =
-            *reinterpret_cast<const u32x4*>(&tile[row][p * 32 + quad * 8]);
-    }
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) {
+    mref[k] = acc;
+    rowmax[k] = INT32_MIN;
+  }
+}
+
+// After a flagged forward pass: each row that exceeded its reference takes
+// its maximum over the vocabulary as the new reference (the largest value
+// recorded, since only tiles beyond the window record).  Nothing unless
+// flagged.
+__global__ void __launch_bounds__(256)
+k_lm_mref_fix(const int32_t* __restrict__ counts, const int32_t* __restrict__ flag,
+              const int32_t* __restrict__ rowmax, float* __restrict__ mref) {
+  if (*flag == 0) return;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < counts[0];
+       k += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t m = rowmax[k];
+    if (m != INT32_MIN) mref[k] = ord_f32(m);
   }
 }
 
@@ -1176,17 +1238,17 @@ struct LmWs {
   int32_t* ycol;     // [T]
   double* tok_loss;  // [T]
   uint8_t* tok_flags;
-  float2* part;      // [T, ntn]
+  float2* part;      // [T, ntn] (reference, sum exp) of each vocabulary tile
   float* xy;         // [T]
-  float2* lsep;      // [T] (M, log2 S) of each active token's log-sum-exp
-  float* coef;       // [T]
+  float* mref;       // [round_up(T, GBM)] each active token's reference r_t
+  int32_t* rowmax;   // [T] maxima recorded for rows beyond their reference
+  int32_t* flag;     // [1] some row was beyond its reference
+  float* rscale;     // [round_up(T, GBM)] each active token's dlogits factor s_t
   uint16_t* Ha;      // [T, H] K-paneled over H (H/32 panels [T][32])
-  uint16_t* Hat;     // [H, Tcap] K-paneled over tokens (Tcap/32 panels [H][32])
+  uint16_t* Hs;      // [H, Tcap] s_t * hidden_t, K-paneled over tokens (Tcap/32 panels [H][32])
   uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W transposed, K-paneled over it
-  uint16_t* Dc;      // [Tcap, kChunkV] dlogits chunk, K-paneled over its columns
   float* dH;         // [Tcap, H]
-  uint16_t* E;       // binary16 exponentials of whole forward tiles (ebk_offset)
-  float* wmax;       // [ntn * NWN, round_up(T, GBM)] their 64-column block maxima
+  uint16_t* E;       // bfloat16 exponentials of whole forward tiles (ebk_offset)
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -1216,16 +1278,16 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.tok_flags = reinterpret_cast<uint8_t*>(take(T));
   w.part = reinterpret_cast<float2*>(take(8 * (size_t)T * ntn));
   w.xy = reinterpret_cast<float*>(take(4 * T));
-  w.lsep = reinterpret_cast<float2*>(take(8 * T));
-  w.coef = reinterpret_cast<float*>(take(4 * T));
+  w.mref = reinterpret_cast<float*>(take(4 * round_up(T, GBM)));
+  w.rowmax = reinterpret_cast<int32_t*>(take(4 * T));
+  w.flag = reinterpret_cast<int32_t*>(take(4));
+  w.rscale = reinterpret_cast<float*>(take(4 * round_up(T, GBM)));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
-  w.Hat = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
+  w.Hs = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
   w.Wtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * vc));
-  w.Dc = reinterpret_cast<uint16_t*>(take(2 * (size_t)Tcap * vc));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
-  // whole forward tiles (ebk_offset) and their 64-column block maxima
+  // whole forward tiles (ebk_offset)
   w.E = reinterpret_cast<uint16_t*>(take(2 * (size_t)round_up(T, GBM) * ntn * GBN));
-  w.wmax = reinterpret_cast<float*>(take(4 * (size_t)round_up(T, GBM) * ntn * NWN));
   if (ws) *ws = w;
   return off;
 }
@@ -1288,7 +1350,7 @@ int launch_gemm(const GemmArgs& g, hipStream_t st, hipEvent_t ev_begin = nullptr
   if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
   // 132 KB of LDS per workgroup, 140 KB for the forward product (gfx950 has
   // 160 KB per CU)
-  const size_t lds = MODE == GM_LSE ? kGemmLdsLse : kGemmLds;
+  const size_t lds = TileShape<MODE>::kFwd ? kGemmLdsLse : kGemmLds;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<MODE>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return DRGRPO_ERR_HIP;
@@ -1297,6 +1359,20 @@ int launch_gemm(const GemmArgs& g, hipStream_t st, hipEvent_t ev_begin = nullptr
                           ev_end, 0, g);
   else
     hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)blocks), dim3(GT), lds, st, g);
+  return launch_status();
+}
+
+// The loss's forward product again when *g.run_if is set: one workgroup per
+// CU (256 on gfx950) over the same tiles.
+constexpr int kRerunGrid = 256;
+int launch_rerun(const GemmArgs& g, hipStream_t st) {
+  const int64_t blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+  if (blocks <= 0) return DRGRPO_OK;
+  if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_rerun),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLdsLse) != hipSuccess)
+    return DRGRPO_ERR_HIP;
+  hipLaunchKernelGGL(k_gemm_rerun, dim3(kRerunGrid), dim3(GT), kGemmLdsLse, st, g, (int)blocks);
   return launch_status();
 }
 
@@ -1360,22 +1436,19 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
                      w.counts);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   // operand layouts: the gathered hidden rows Ha, K-paneled over H (panel
-  // stride T * 32); their transpose Hat [H, Tcap], K-paneled over tokens;
-  // each dlogits chunk D, K-paneled over its vocabulary columns (the dW
-  // product reads it as paneled over its rows); the W chunk transposed, Wtc,
-  // over vocabulary
+  // stride T * 32); the scaled transpose Hs [H, Tcap], K-paneled over
+  // tokens; the W chunk transposed, Wtc, over vocabulary; E in the forward
+  // product's accumulator order (ebk_offset)
   hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)(N * ((C + kGatherTok - 1) / kGatherTok))),
                      dim3(256), 0, st, hid, H, tokens, C, V, w.len,
                      w.offs, w.act_pos, w.ycol, w.Ha, T * 32, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
-  {
-    const int64_t blocks2 = ((Tcap + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, (int64_t)32,
-                       T * 32, T, Tcap, H, w.counts, w.Hat, H * 32);
-    if ((rc = launch_status()) != DRGRPO_OK) return rc;
-  }
+  hipLaunchKernelGGL(k_lm_mref, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.Ha, T * 32, Wb,
+                     H, w.counts, w.ycol, w.mref, w.rowmax, w.flag);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
-  // forward: per-token log-sum-exp over the vocabulary, logits never stored
+  // forward: per-token sums of exp(x - r_t) over the vocabulary and E; the
+  // logits are never stored
   GemmArgs g = {};
   g.A = w.Ha;
   g.ar = 32;
@@ -1392,60 +1465,65 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   g.xy = w.xy;
   g.ycol = w.ycol;
   g.col_base = 0;
-  g.E = w.E;  // the exponentials the backward chunks turn into dlogits
-  g.wmax = w.wmax;
-  g.ldw = round_up(T, GBM);
-  if ((rc = launch_gemm<GM_LSE>(g, st, aux ? static_cast<hipEvent_t>(aux->fwd_event_begin) : nullptr,
-                                aux ? static_cast<hipEvent_t>(aux->fwd_event_end) : nullptr)) !=
+  g.E = w.E;
+  g.mref = w.mref;
+  g.rowmax = w.rowmax;
+  g.flag = w.flag;
+  g.run_if = w.flag;
+  if ((rc = launch_gemm<GM_LSE_E>(g, st, aux ? static_cast<hipEvent_t>(aux->fwd_event_begin) : nullptr,
+                                  aux ? static_cast<hipEvent_t>(aux->fwd_event_end) : nullptr)) !=
       DRGRPO_OK)
     return rc;
+  // rows beyond their reference (if any): new references, the product again
+  hipLaunchKernelGGL(k_lm_mref_fix, dim3(64), dim3(256), 0, st, w.counts, w.flag, w.rowmax, w.mref);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  if ((rc = launch_rerun(g, st)) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
                      w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, w.len, logp_old, logp_ref, eps,
-                     beta, (double)norm_const, agg, w.total_len, w.lsep, w.coef, w.tok_loss,
+                     beta, (double)norm_const, agg, w.total_len, w.mref, w.E, w.rscale, w.tok_loss,
                      w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  {
+    // Hs = s_t * hidden_t, transposed (zero rows past the active count)
+    const int64_t blocks2 = ((Tcap + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)blocks2), dim3(256), 0, st, w.Ha, (int64_t)32,
+                       T * 32, T, Tcap, H, w.counts, (const float*)w.rscale, w.Hs, H * 32);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  }
 
   // backward, one vocabulary chunk at a time
   for (int64_t v0 = 0; v0 < V; v0 += kChunkV) {
     const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
-    // the chunk's dlogits from the forward product's exponentials
-    {
-      const int64_t nbc = (round_up(wv, kPad) + kDcCol - 1) / kDcCol;
-      const int64_t nbt = (Tcap + kDcTok - 1) / kDcTok;
-      hipLaunchKernelGGL(k_lm_dchunk, dim3((unsigned)(nbt * nbc)), dim3(256), 0, st, w.E, ntn,
-                         w.wmax, round_up(T, GBM), w.lsep, w.coef, w.ycol, w.xy, w.counts, v0,
-                         wv, nbc, w.Dc, Tcap * 32);
-      if ((rc = launch_status()) != DRGRPO_OK) return rc;
-    }
-
     // the chunk of W transposed, [H, wv rounded up to 32] with zero columns past wv
     const int64_t wv_pad = round_up(wv, kPad);
     const int64_t tblocks = ((wv_pad + 63) / 64) * ((H + 63) / 64);
     hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb + v0 * H, H,
-                       (int64_t)32, wv, wv_pad, H, (const int32_t*)nullptr, w.Wtc, H * 32);
+                       (int64_t)32, wv, wv_pad, H, (const int32_t*)nullptr, (const float*)nullptr,
+                       w.Wtc, H * 32);
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
-    GemmArgs a = {};  // dhidden += D_chunk . W_chunk
-    a.A = w.Dc;
-    a.ar = 32;
-    a.ak = Tcap * 32;
+    GemmArgs a = {};  // dhidden += s . (E_chunk . W_chunk)
+    a.A = w.E;
+    a.ntn = ntn;
+    a.col_base = v0;
     a.B = w.Wtc;
     a.br = 32;
     a.bk = H * 32;
     a.M = T;
     a.N = H;
-    a.K = round_up(wv, kPad);
+    a.K = wv_pad;
     a.M_dev = w.counts;
     a.Cf = w.dH;
     a.ldc = H;
     a.accumulate = v0 > 0;
+    a.rscale = w.rscale;
     if ((rc = launch_gemm<GM_ACC>(a, st)) != DRGRPO_OK) return rc;
 
-    GemmArgs s = {};  // dW_chunk = D_chunk^T . H_a, A = D paneled over its rows
-    s.A = w.Dc;
-    s.ar = Tcap * 32;
-    s.ak = 32 * 32;
-    s.B = w.Hat;
+    GemmArgs s = {};  // dW_chunk = E_chunk^T . Hs
+    s.A = w.E;
+    s.ntn = ntn;
+    s.col_base = v0;
+    s.B = w.Hs;
     s.br = 32;
     s.bk = H * 32;
     s.M = wv;

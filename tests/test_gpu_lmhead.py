@@ -74,6 +74,46 @@ def test_lmhead_deterministic():
     assert l1 == l2 and torch.equal(dh1, dh2) and torch.equal(dW1, dW2)
 
 
+def _scaled_bf16(bits: np.ndarray, rows: np.ndarray, factor: float) -> np.ndarray:
+    """bfloat16 bits with the given rows multiplied by a power of two (exact)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32).copy()
+    f[rows] *= np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_lmhead_rows_far_above_their_reference():
+    """The forward product keeps exp(x - r) with r the sampled token's logit;
+    rows whose largest logit lies more than 48 above it (here: every other
+    token's hidden row scaled by 32, logits up to ~170: the first pass even
+    overflows binary32 for some) make the
+    call run the forward product again with those rows' maxima.  Loss and
+    every gradient entry still match the oracle, and the result is the same
+    on a second call."""
+    cfg, case, _, Wb, _, _, _ = lm_case("lmhead_multi")
+    hb = _scaled_bf16(case.hidden(), np.arange(0, cfg.T, 2), 32.0)
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    tok = case.tokens.reshape(-1)
+    x = h64 @ W64.T
+    gap = x.max(axis=1) - x[np.arange(cfg.T), tok]
+    _, logp = lmhead.token_rows(h64, W64, tok, np.arange(cfg.T))
+    logp = logp.reshape(cfg.N, cfg.C)
+    old = synth.perturb(logp, case.old_noise)
+    ref = synth.perturb(logp, case.ref_noise)
+    t = lmhead.full(hb, Wb, case.tokens, cfg.eos_id, case.rewards, old, ref, cfg.G,
+                    f32(cfg.eps), f32(cfg.beta), f32(cfg.norm_const))
+    act = t["active_rows"]
+    far = act[gap[act] > 48.0]
+    print(f"{far.size} of {act.size} active rows beyond the window (max gap {gap[act].max():.1f})",
+          flush=True)
+    assert far.size >= 4 and far.size < act.size
+    loss, dh, dW = _run(cfg, case, hb, Wb, old, ref)
+    assert abs(loss - t["loss"]) <= 2e-3 * abs(t["loss"]), (loss, t["loss"])
+    check_small_grads(cfg, case, hb, Wb, t, dh, dW)
+    l2, dh2, dW2 = _run(cfg, case, hb, Wb, old, ref)
+    assert l2 == loss and torch.equal(dh, dh2) and torch.equal(dW, dW2)
+
+
 def test_lmhead_no_active_tokens():
     """All groups uniform and beta = 0: zero loss, zero gradients."""
     cfg, case, hb, Wb, old, ref, t = lm_case("lmhead_mini")

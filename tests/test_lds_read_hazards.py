@@ -1,6 +1,6 @@
 """Static check of LDS-read completion in the library's gfx950 assembly (CPU).
 
-The dW product of the fused lm_head issues its LDS fragment reads as inline
+The dhidden product of the fused lm_head issues its LDS fragment reads as inline
 assembly (the transposing read's builtin would make the compiler drain every
 direct global->LDS load in flight before each read), so the compiler does not
 know their results arrive late.  Its explicit lgkmcnt waits name the
@@ -148,11 +148,11 @@ def test_every_kernel_waits_for_its_lds_reads(device_asm):
     assert checked >= 10
 
 
-def test_dw_product_reads_are_inline_transposing_reads(device_asm):
-    """The dW product (k_gemm<3>) is the one the check exists for: its main
-    loop reads A through ds_read_b64_tr_b16 and has explicit waits."""
+def test_dhidden_product_reads_are_inline_transposing_reads(device_asm):
+    """The dhidden product (k_gemm<2>) is the one the check exists for: its
+    main loop reads A through ds_read_b64_tr_b16 and has explicit waits."""
     text = device_asm["lmhead.hip"]
-    sym = next(s for s in _kernels(text) if "k_gemmILi3E" in s)
+    sym = next(s for s in _kernels(text) if "k_gemmILi2E" in s)
     body = text[text.index(sym + ":"):]
     body = body[:body.index(".Lfunc_end")]
     assert body.count("ds_read_b64_tr_b16") >= 16

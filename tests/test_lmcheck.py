@@ -1,6 +1,8 @@
 """The fused lm_head gradient checker can fail: it accepts the oracle's
-gradients carried through the GPU's precision path (bfloat16 dlogits,
-binary32 products, bfloat16 results, emulated on the CPU) and rejects the
+gradients carried through the GPU's precision path (dlogits as bfloat16
+exponentials times a per-token factor, for dW the hidden rows scaled and
+rounded to bfloat16, binary32 products, bfloat16 results, emulated on the
+CPU) and rejects the
 same arrays with one part of the gradient wrong - the vocabulary rows of dW
 that no active token sampled zeroed or scaled by 1.01, one such row zeroed,
 dhidden's softmax part dropped or scaled, the sampled dW rows or dhidden
@@ -32,7 +34,7 @@ def _pieces(name):
 def test_checker_accepts_gpu_precision(name):
     cfg, h64, W64, tok, D, Dc, Ha, sampled, t = _pieces(name)
     dh = emulate(D, W64)
-    dW = emulate(Dc.T, Ha)
+    dW = emulate(Dc.T, Ha, t["coef"][t["active_rows"]])
     r1 = check_dhidden(dh, D, W64, t["coef"], tok)
     r2 = check_dW(dW, Dc, Ha, sampled)
     print(name, r1, r2)
@@ -43,7 +45,7 @@ def test_checker_accepts_gpu_precision(name):
 @pytest.mark.parametrize("name", CASES)
 def test_checker_rejects_wrong_dW_parts(name):
     cfg, h64, W64, tok, D, Dc, Ha, sampled, t = _pieces(name)
-    dW = emulate(Dc.T, Ha)
+    dW = emulate(Dc.T, Ha, t["coef"][t["active_rows"]])
     uns = np.flatnonzero(~sampled)
     samp = np.flatnonzero(sampled)
     # nonzero unsampled rows: the ones a wrong kernel could silently zero
