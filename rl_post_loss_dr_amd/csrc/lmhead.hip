@@ -122,12 +122,16 @@ struct TileShape {
 // vocabulary columns of a tile's 256 tokens are 16 runs of 1 KB (blocks
 // j, j+1 of every (wm, i)); for the dW product, 32 tokens of its 256
 // vocabulary rows are 4 runs of 4 KB (blocks i, i+1 of every wn).
+// first element of E tile (tm, tn), ntn tiles along the vocabulary
+__host__ __device__ inline int64_t etile(int64_t tm, int64_t tn, int64_t ntn) {
+  return (tm * ntn + tn) * (GBM * GBN);
+}
 __host__ __device__ inline int64_t ebk_offset(int64_t t, int64_t v, int64_t ntn) {
   const int64_t tl = t % GBM, vl = v % GBN;
   const int64_t wm = tl / WM, i = (tl % WM) / 16, q = (tl % 16) / 4, r = tl % 4;
   const int64_t wn = vl / WN, j = (vl % WN) / 16, f = vl % 16;
-  return ((t / GBM) * ntn + v / GBN) * (GBM * GBN) + (wm * NWN + wn) * (WM * WN) +
-         (i * FN + j) * 256 + (q * 16 + f) * 4 + r;
+  return etile(t / GBM, v / GBN, ntn) + (wm * NWN + wn) * (WM * WN) + (i * FN + j) * 256 +
+         (q * 16 + f) * 4 + r;
 }
 
 
@@ -367,7 +371,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
   const int q8 = total / 8;
   const int v = b < 8 * q8 ? (b % 8) * q8 + b / 8 : b;
   int tm, tn;
-  if constexpr (MODE == GM_LSE) {
+  if constexpr (TileShape<MODE>::kFwd) {
     constexpr int kColGroup = 8;
     const int grouped = (ntn_t / kColGroup) * kColGroup * ntm;
     const int gw = v < grouped ? kColGroup : ntn_t % kColGroup;  // width of v's group
@@ -439,12 +443,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
   auto a_stage = [&](int64_t kt) -> const uint16_t* {
     if constexpr (MODE == GM_ACC) {
       const int64_t v = g.col_base + kt * GBK;  // the step's first vocabulary column
-      return g.A + ((int64_t)tm * g.ntn + v / GBN) * (GBM * GBN) + ((v % GBN) / WN_F) * (WM_F * WN_F) +
+      return g.A + etile(tm, v / GBN, g.ntn) + ((v % GBN) / WN_F) * (WM_F * WN_F) +
              ((v % WN_F) / 32) * 512;
     } else if constexpr (MODE == GM_STORE) {
       // tokens 32 kt ..: forward row tile kt / 8, its wavefront row block
       // (kt % 8) / 4, MFMA row blocks 2 (kt % 4), +1
-      return g.A + ((kt / 8) * g.ntn + (g.col_base + m0) / GBN) * (GBM * GBN) +
+      return g.A + etile(kt / 8, (g.col_base + m0) / GBN, g.ntn) +
              ((kt % 8) / 4) * (NWN_F * WM_F * WN_F) + (kt % 4) * 2048;
     } else {
       return g.A + m0 * g.ar + kt * g.ak;
@@ -801,7 +805,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
         if constexpr (kRef) {
           // bfloat16 (nearest even), the lane's four rows of a column as one
           // 8-byte store (ebk_offset)
-          uint16_t* eb = g.E + ((int64_t)tm * ntn_t + tn) * (GBM * GBN) +
+          uint16_t* eb = g.E + etile(tm, tn, ntn_t) +
                          (wm * NWN + wn) * (WM * WN) + lane * 4;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
