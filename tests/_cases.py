@@ -163,3 +163,10 @@ def lm_case(name: str):
     terms = lmhead.full(hb, Wb, case.tokens, cfg.eos_id, case.rewards, old, ref, cfg.G,
                         f32(cfg.eps), f32(cfg.beta), f32(cfg.norm_const))
     return cfg, case, hb, Wb, old, ref, terms
+
+
+def scaled_bf16_rows(bits: np.ndarray, rows: np.ndarray, factor: float) -> np.ndarray:
+    """bfloat16 bits with the given rows multiplied by a power of two (exact)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32).copy()
+    f[rows] *= np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import rl_post_loss_dr_amd as dr
-from _cases import lm_case, small_case, to_device_logits
+from _cases import lm_case, scaled_bf16_rows, small_case, to_device_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -107,3 +107,57 @@ def test_lmhead_graph_replay():
         dr.lmhead_loss_fwd_bwd(hidden, W, tokens, cfg.eos_id, rewards.flip(0).contiguous(), lo,
                                lr, workspace=ws, **kw)
         torch.cuda.synchronize()
+
+
+def test_lmhead_graph_replay_rows_beyond_reference():
+    """The fused lm_head's flagged-row pass inside a captured graph: one graph
+    replayed while its hidden states alternate, in place, between inputs that
+    put 9 of 20 active rows beyond their reference (every other token's row
+    scaled by 32) and inputs that put none there; every replay equals the
+    eager call on the same inputs bit for bit, so the flag and the recorded
+    maxima are cleared by the library's own kernels on every call."""
+    import synth
+    from oracle import lmhead
+
+    cfg, case, hb, Wb, _, _, _ = lm_case("lmhead_multi")
+    hb_far = scaled_bf16_rows(hb, np.arange(0, cfg.T, 2), 32.0)
+    W = _bits_to_dev(Wb)
+    tokens = torch.from_numpy(case.tokens).to(DEV)
+    rewards = torch.from_numpy(case.rewards).to(DEV)
+    kw = dict(G=cfg.G, eps=cfg.eps, beta=cfg.beta, norm_const=cfg.norm_const)
+    ws_bytes = dr.lmhead_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H, cfg.G)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    inputs = {}
+    for k, bits in (("near", hb), ("far", hb_far)):
+        # old / reference log-probs near each input's own (the policy's)
+        _, lp = lmhead.token_rows(lmhead.bf16_to_f64(bits), lmhead.bf16_to_f64(Wb),
+                                  case.tokens.reshape(-1), np.arange(cfg.T))
+        lp = lp.reshape(cfg.N, cfg.C)
+        inputs[k] = (_bits_to_dev(bits), torch.from_numpy(synth.perturb(lp, case.old_noise)).to(DEV),
+                     torch.from_numpy(synth.perturb(lp, case.ref_noise)).to(DEV))
+    want = {}
+    for k, (h, lo, lr) in inputs.items():
+        l, dh, dW = dr.lmhead_loss_fwd_bwd(h, W, tokens, cfg.eos_id, rewards, lo, lr, workspace=ws,
+                                           **kw)
+        torch.cuda.synchronize()
+        assert torch.isfinite(l) and bool(torch.isfinite(dh.float()).all()), k
+        want[k] = (l.clone(), dh.clone(), dW.clone())
+    assert not torch.equal(want["near"][2], want["far"][2])
+    hidden, lo, lr = (x.clone() for x in inputs["near"])
+    dh_g, dW_g = torch.empty_like(hidden), torch.empty_like(W)
+    ws_g = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    graph, (loss_g, _, _) = _capture(lambda: dr.lmhead_loss_fwd_bwd(
+        hidden, W, tokens, cfg.eos_id, rewards, lo, lr, out_dhidden=dh_g, out_dW=dW_g,
+        workspace=ws_g, **kw))
+    for k in ["far", "near", "far", "near", "far"]:
+        for dst, src in zip((hidden, lo, lr), inputs[k]):
+            dst.copy_(src)
+        dh_g.fill_(1.0)
+        dW_g.fill_(1.0)
+        loss_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        l, dh, dW = want[k]
+        assert torch.equal(loss_g, l), k
+        assert torch.equal(dh_g, dh) and torch.equal(dW_g, dW), k

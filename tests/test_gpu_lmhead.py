@@ -17,7 +17,7 @@ import oracle
 import synth
 import rl_post_loss_dr_amd as dr
 from oracle import lmhead
-from _cases import f32, lm_case
+from _cases import f32, lm_case, scaled_bf16_rows
 from _lmcheck import check_dW, check_dhidden
 
 pytestmark = pytest.mark.gpu
@@ -74,13 +74,6 @@ def test_lmhead_deterministic():
     assert l1 == l2 and torch.equal(dh1, dh2) and torch.equal(dW1, dW2)
 
 
-def _scaled_bf16(bits: np.ndarray, rows: np.ndarray, factor: float) -> np.ndarray:
-    """bfloat16 bits with the given rows multiplied by a power of two (exact)."""
-    f = (bits.astype(np.uint32) << 16).view(np.float32).copy()
-    f[rows] *= np.float32(factor)
-    return (f.view(np.uint32) >> 16).astype(np.uint16)
-
-
 def test_lmhead_rows_far_above_their_reference():
     """The forward product keeps exp(x - r) with r the sampled token's logit;
     rows whose largest logit lies more than 48 above it (here: every other
@@ -90,7 +83,7 @@ def test_lmhead_rows_far_above_their_reference():
     every gradient entry still match the oracle, and the result is the same
     on a second call."""
     cfg, case, _, Wb, _, _, _ = lm_case("lmhead_multi")
-    hb = _scaled_bf16(case.hidden(), np.arange(0, cfg.T, 2), 32.0)
+    hb = scaled_bf16_rows(case.hidden(), np.arange(0, cfg.T, 2), 32.0)
     h64 = lmhead.bf16_to_f64(hb)
     W64 = lmhead.bf16_to_f64(Wb)
     tok = case.tokens.reshape(-1)
