@@ -197,11 +197,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-// the same in binary16 (one v_cvt_pk_f16_f32, nearest even)
-__device__ inline uint32_t f16x2_bits(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
-}
 
 // Cross-lane moves within a DPP row of 16 lanes (lanes sharing l / 16).  A
 // max or sum over the row takes four steps: swaps within quads (xor 1, xor 2),
