@@ -15,8 +15,8 @@
  *   GM_LSE_E  the same product for the loss: sums of exp(x - r_t) relative to
  *             a per-token reference r_t fixed before the product (the sampled
  *             token's logit), and E = exp(x - r_t) of every logit in bfloat16
- *   GM_ACC    dhidden += s_t * (E_chunk . W_chunk)      (binary32 accumulator)
- *   GM_STORE  dW_chunk = E_chunk^T . (s . H_a)           (bfloat16 result)
+ *   GM_ACC    dhidden = s_t * (E . W) over the whole vocabulary   (binary32)
+ *   GM_STORE  dW_chunk = E_chunk^T . (s . H_a)                     (bfloat16)
  *
  * With one reference per token, every dlogits entry is a per-token factor
  * times E: D[t, v] = s_t E[t, v] with s_t = coef_t exp(r_t - lse_t), once the
@@ -26,8 +26,8 @@
  * A row whose logits exceed its reference by more than a fixed window (its
  * exponentials would leave the binary32 range) flags the call; the forward
  * product then runs again with that row's maximum as its reference.
- * Transposed copies of the compacted hidden states and of each vocabulary
- * chunk of W give the products their reduction dimension contiguous; the
+ * Transposed copies of the compacted hidden states and of W give the
+ * products their reduction dimension contiguous; the
  * dhidden product reads E, whose reduction dimension (vocabulary) is strided
  * in the forward's accumulator order, through transposing LDS reads.  No
  * floating-point atomics: results are bitwise reproducible.
@@ -80,10 +80,9 @@ static_assert(kGemmLdsLse <= (size_t)kLdsMax, "forward product's LDS");
 static_assert(!kTablesInRing || kRingElems - kTableBytes / 2 >= (GT / 64) * WM * WN,
               "epilogue staging overlaps the tables");
 static_assert((GT / 64) * WM * WN <= kRingElems, "epilogue staging exceeds the ring");
-constexpr int kPad = 32;                   // token counts and vocabulary chunks are padded to this
-// vocabulary columns per backward chunk: 128 dW row tiles (two full rounds
-// on 256 CUs); measured against 8K, 16K and 24K columns, at twice the 16K
-// chunk buffers
+constexpr int kPad = 32;                   // token and vocabulary counts are padded to this
+// vocabulary rows per dW launch: 128 row tiles (two full rounds on 256 CUs;
+// measured against 8K, 16K and 24K)
 constexpr int kChunkV = 32768;
 constexpr float kL2E = 1.4426950408889634f;
 constexpr double kL2ED = 1.4426950408889634074;
@@ -1245,7 +1244,7 @@ struct LmWs {
   float* rscale;     // [round_up(T, GBM)] each active token's dlogits factor s_t
   uint16_t* Ha;      // [T, H] K-paneled over H (H/32 panels [T][32])
   uint16_t* Hs;      // [H, Tcap] s_t * hidden_t, K-paneled over tokens (Tcap/32 panels [H][32])
-  uint16_t* Wtc;     // [H, kChunkV] one vocabulary chunk of W transposed, K-paneled over it
+  uint16_t* Wt;      // [H, V rounded up to 32] W transposed, K-paneled over the vocabulary
   float* dH;         // [Tcap, H]
   uint16_t* E;       // bfloat16 exponentials of whole forward tiles (ebk_offset)
 };
@@ -1255,7 +1254,6 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws) {
   const int64_t Tcap = round_up(T, kPad);
   const int64_t ntn = (V + GBN - 1) / GBN;
-  const int64_t vc = V < kChunkV ? round_up(V, kPad) : kChunkV;
   size_t off = 0;
   char* b = static_cast<char*>(base);
   auto take = [&](size_t bytes) {
@@ -1283,7 +1281,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.rscale = reinterpret_cast<float*>(take(4 * round_up(T, GBM)));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
   w.Hs = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * Tcap));
-  w.Wtc = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * vc));
+  w.Wt = reinterpret_cast<uint16_t*>(take(2 * (size_t)H * round_up(V, kPad)));
   w.dH = reinterpret_cast<float*>(take(4 * (size_t)Tcap * H));
   // whole forward tiles (ebk_offset)
   w.E = reinterpret_cast<uint16_t*>(take(2 * (size_t)round_up(T, GBM) * ntn * GBN));
@@ -1436,7 +1434,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   // operand layouts: the gathered hidden rows Ha, K-paneled over H (panel
   // stride T * 32); the scaled transpose Hs [H, Tcap], K-paneled over
-  // tokens; the W chunk transposed, Wtc, over vocabulary; E in the forward
+  // tokens; W transposed, Wt, over vocabulary; E in the forward
   // product's accumulator order (ebk_offset)
   hipLaunchKernelGGL(k_lm_gather, dim3((unsigned)(N * ((C + kGatherTok - 1) / kGatherTok))),
                      dim3(256), 0, st, hid, H, tokens, C, V, w.len,
@@ -1490,35 +1488,38 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
     if ((rc = launch_status()) != DRGRPO_OK) return rc;
   }
 
-  // backward, one vocabulary chunk at a time
+  // dhidden = s . (E . W) over the whole vocabulary in one product: W
+  // transposed, [H, V rounded up to 32] with zero columns past V
+  const int64_t Vpad = round_up(V, kPad);
+  {
+    const int64_t tblocks = ((Vpad + 63) / 64) * ((H + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb, H,
+                       (int64_t)32, V, Vpad, H, (const int32_t*)nullptr, (const float*)nullptr,
+                       w.Wt, H * 32);
+    if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  }
+  GemmArgs a = {};
+  a.A = w.E;
+  a.ntn = ntn;
+  a.col_base = 0;
+  a.B = w.Wt;
+  a.br = 32;
+  a.bk = H * 32;
+  a.M = T;
+  a.N = H;
+  a.K = Vpad;
+  a.M_dev = w.counts;
+  a.Cf = w.dH;
+  a.ldc = H;
+  a.accumulate = 0;
+  a.rscale = w.rscale;
+  if ((rc = launch_gemm<GM_ACC>(a, st)) != DRGRPO_OK) return rc;
+
+  // dW = E^T . Hs, one vocabulary chunk of 32,768 rows at a time (128 row
+  // tiles: two full rounds on 256 CUs)
   for (int64_t v0 = 0; v0 < V; v0 += kChunkV) {
     const int64_t wv = V - v0 < kChunkV ? V - v0 : kChunkV;
-    // the chunk of W transposed, [H, wv rounded up to 32] with zero columns past wv
-    const int64_t wv_pad = round_up(wv, kPad);
-    const int64_t tblocks = ((wv_pad + 63) / 64) * ((H + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tblocks), dim3(256), 0, st, Wb + v0 * H, H,
-                       (int64_t)32, wv, wv_pad, H, (const int32_t*)nullptr, (const float*)nullptr,
-                       w.Wtc, H * 32);
-    if ((rc = launch_status()) != DRGRPO_OK) return rc;
-
-    GemmArgs a = {};  // dhidden += s . (E_chunk . W_chunk)
-    a.A = w.E;
-    a.ntn = ntn;
-    a.col_base = v0;
-    a.B = w.Wtc;
-    a.br = 32;
-    a.bk = H * 32;
-    a.M = T;
-    a.N = H;
-    a.K = wv_pad;
-    a.M_dev = w.counts;
-    a.Cf = w.dH;
-    a.ldc = H;
-    a.accumulate = v0 > 0;
-    a.rscale = w.rscale;
-    if ((rc = launch_gemm<GM_ACC>(a, st)) != DRGRPO_OK) return rc;
-
-    GemmArgs s = {};  // dW_chunk = E_chunk^T . Hs
+    GemmArgs s = {};
     s.A = w.E;
     s.ntn = ntn;
     s.col_base = v0;
