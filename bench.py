@@ -491,9 +491,11 @@ def measure_lmhead(cfg, case, steps, warmup, eager=False):
 
 def _lmhead_executed_flops(n_act, V, H, tile=256, grad_cols=224, kpad=32, chunk=32768):
     """MFMA work of one fused lm_head call as launched: the forward product
-    over all V columns on whole 256 x 256 tiles, then per vocabulary chunk the
-    dhidden product (reducing over the chunk's columns) and the dW product
-    (reducing over the active tokens, padded to 32) on whole 256 x 224 tiles."""
+    over all V columns on whole 256 x 256 tiles, the dhidden product (reducing
+    over V rounded up to 32) and, per vocabulary chunk, the dW product
+    (reducing over the active tokens, padded to 32) on whole 256 x 224 tiles.
+    The dhidden term is summed per chunk: the chunks are multiples of 32, so
+    the sum equals the one product over V rounded up to 32."""
     ru = lambda x, m: (x + m - 1) // m * m
     f = 2.0 * ru(n_act, tile) * ru(V, tile) * H
     for v0 in range(0, V, chunk):
