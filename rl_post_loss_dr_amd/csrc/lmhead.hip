@@ -91,6 +91,7 @@ constexpr double kL2ED = 1.4426950408889634074;
 // binary32 hold up to e^88), its sum over any vocabulary below e^61 and the
 // gradient products' sums far inside the binary32 range.
 constexpr float kRefWindow = 48.0f;
+constexpr float kRefSumMax = 7.0167e20f;  // e^48 (rounded down)
 
 enum { GM_LSE = 0, GM_LSE_E = 1, GM_ACC = 2, GM_STORE = 3 };
 
@@ -154,13 +155,13 @@ struct GemmArgs {
   float* xy;             // [rows] sampled token's logit
   const int32_t* ycol;   // [rows] sampled token id
   int64_t col_base;      // vocabulary id of column 0 (the gradient products: of the chunk)
-  // GM_LSE_E: E = exp(x - r_t) of every logit in bfloat16, in the
-  // accumulators' own order (ebk_offset); r_t = mref[t]; a row whose logits
-  // in a tile exceed r_t by more than kRefWindow raises *flag and records
-  // the tile's maximum (order-preserving int image) in rowmax[t] (atomic max)
+  // GM_LSE_E: partial sums of exp(x - r_t), r_t = mref[t], and (E != NULL)
+  // E = exp(x - r_t) of every logit in bfloat16, in the accumulators' own
+  // order (ebk_offset); a row whose tile sum exceeds e^kRefWindow sets
+  // rowmark[t] = 1 and raises *flag
   uint16_t* E;
   const float* mref;
-  int32_t* rowmax;
+  int32_t* rowmark;
   int32_t* flag;
   const int32_t* run_if;  // the rerun kernel: does nothing unless *run_if != 0
   // GM_ACC / GM_STORE
@@ -752,25 +753,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
             if (hit[r]) g.xy[m0 + rt0 + r] = __builtin_bit_cast(float, xb);
           }
         }
+        // GM_LSE: the row's maximum over the wavefront's columns (in-lane,
+        // then across the 16 lanes of its DPP row); GM_LSE_E needs none
         int mo[4];
+        if constexpr (kRef) {
+          if constexpr (!kFull) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float m = -INFINITY;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            if (!kFull && lc0 + j * 16 >= ncols) acc[i][j][r] = -INFINITY;
-            m = fmaxf(m, acc[i][j][r]);
+              for (int j = 0; j < FN; ++j)
+                if (lc0 + j * 16 >= ncols) acc[i][j][r] = -INFINITY;
           }
-          mo[r] = f32_ord(m);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              if (!kFull && lc0 + j * 16 >= ncols) acc[i][j][r] = -INFINITY;
+              m = fmaxf(m, acc[i][j][r]);
+            }
+            mo[r] = f32_ord(m);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppXor1>(mo[r]));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppXor2>(mo[r]));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppHalfMirror>(mo[r]));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppMirror>(mo[r]));
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppXor1>(mo[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppXor2>(mo[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppHalfMirror>(mo[r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mo[r] = max(mo[r], dpp_i32<kDppMirror>(mo[r]));
         float mx[4], sm[4], ref[4];
         if constexpr (kRef) {
           const float4 m4 = *reinterpret_cast<const float4*>(t_mr + rt0);
@@ -778,7 +791,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          mx[r] = ord_f32(mo[r]);
+          if constexpr (!kRef) mx[r] = ord_f32(mo[r]);
           // exp(x - ref) as exp2(x*log2e - ref*log2e), one fused step per
           // entry (the rounding of ref*log2e scales the whole partial sum by
           // one factor 2^d, |d| <= 2^-24 |ref| log2e).  GM_LSE: ref = the
@@ -796,7 +809,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
             sm[r] += acc[i][j][r];
           }
         }
-        if constexpr (kRef) {
+        if (kRef && g.E) {
           // bfloat16 (nearest even), the lane's four rows of a column as one
           // 8-byte store (ebk_offset)
           uint16_t* eb = g.E + etile(tm, tn, ntn_t) +
@@ -817,7 +830,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
         for (int r = 0; r < 4; ++r) sm[r] += dpp_f32<kDppMirror>(sm[r]);
         if (fr == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) red[wn * GBM + rt0 + r] = make_float2(mx[r], sm[r]);
+          for (int r = 0; r < 4; ++r) red[wn * GBM + rt0 + r] = make_float2(kRef ? ref[r] : mx[r], sm[r]);
         }
       }
     };
@@ -829,24 +842,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int b) {
     for (int r = tid; r < GBM; r += GT) {
       const int64_t row = m0 + r;
       if (row >= M) continue;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NWN; ++w) mx = fmaxf(mx, red[w * GBM + r].x);
       if constexpr (kRef) {
         // the wavefronts' sums share the row's reference
-        const float ref = t_mr[r];
         float sm = 0.0f;
 #pragma unroll
         for (int w = 0; w < NWN; ++w) sm += red[w * GBM + r].y;
-        g.part[row * g.ntn + tn] = make_float2(ref, sm);
-        // logits beyond the reference's window: record the tile's maximum and
-        // flag the call (rare)
-        if (mx - ref > kRefWindow) {
-          atomicMax(g.rowmax + row, f32_ord(mx));
+        g.part[row * g.ntn + tn] = make_float2(t_mr[r], sm);
+        // every exponential of the tile's row is at most its sum: a sum
+        // beyond e^kRefWindow (or not a number) marks the row and flags the
+        // call (rare)
+        if (!(sm <= kRefSumMax)) {
+          g.rowmark[row] = 1;
           __hip_atomic_store(g.flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         continue;
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWN; ++w) mx = fmaxf(mx, red[w * GBM + r].x);
       float sm = 0.0f;
       if (mx != -INFINITY) {
 #pragma unroll
@@ -915,15 +928,17 @@ __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2))) k_
   gemm_tile<MODE>(g, (int)blockIdx.x);
 }
 
-// The loss's forward product once more, for a call whose first pass flagged
-// a row (its references updated in between): nothing happens unless
+// A forward product once more, for a call whose first pass flagged a row
+// (GM_LSE: the per-tile maxima the flagged rows' new references come from;
+// GM_LSE_E: the exponentials with those references): nothing happens unless
 // *run_if != 0, so it is launched on every call with one workgroup per CU,
 // and each workgroup walks tiles b, b + gridDim.x, .. below nblocks.
+template <int MODE>
 __global__ void __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(2)))
 k_gemm_rerun(GemmArgs g, int nblocks) {
   if (__builtin_amdgcn_readfirstlane(*g.run_if) == 0) return;
   for (int b = (int)blockIdx.x; b < nblocks; b += (int)gridDim.x) {
-    gemm_tile<GM_LSE_E>(g, b);
+    gemm_tile<MODE>(g, b);
     __syncthreads();  // the next tile's loads reuse the LDS this one's epilogue reads
   }
 }
@@ -1130,17 +1145,16 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
   E[ebk_offset(k, y, ntn)] = bf16_bits((float)(exp((double)xy[k] - r) - exp(lse - r)));
 }
 
-// Each active token's reference r_t for the loss's forward product: its
-// sampled token's logit hidden_t . W[y_t] (binary32 sum of bfloat16
-// products, one wavefront per token; 0 for a bad token id).  Any value would
-// do as long as E = exp(x - r_t) stays in range: the sampled token's logit is
-// at most the row's maximum, and a row whose maximum lies more than
-// kRefWindow above it is detected and redone.  Also clears the call's flag
-// and the rows' recorded maxima.
+// Each listed token's reference r_t for a forward product: its sampled
+// token's logit hidden_t . W[y_t] (binary32 sum of bfloat16 products, one
+// wavefront per token; 0 for a bad token id).  Any value would do as long as
+// exp(x - r_t) stays in range: the sampled token's logit is at most the row's
+// maximum, and a row whose maximum lies more than kRefWindow above it is
+// detected and redone.  Also clears the call's flag and the rows' marks.
 __global__ void __launch_bounds__(256)
 k_lm_mref(const uint16_t* __restrict__ Ha, int64_t ha_ps, const uint16_t* __restrict__ W, int64_t H,
           const int32_t* __restrict__ counts, const int32_t* __restrict__ ycol,
-          float* __restrict__ mref, int32_t* __restrict__ rowmax, int32_t* __restrict__ flag) {
+          float* __restrict__ mref, int32_t* __restrict__ rowmark, int32_t* __restrict__ flag) {
   const int lane = threadIdx.x & 63;
   const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 0;
@@ -1164,22 +1178,24 @@ k_lm_mref(const uint16_t* __restrict__ Ha, int64_t ha_ps, const uint16_t* __rest
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
   if (lane == 0) {
     mref[k] = acc;
-    rowmax[k] = INT32_MIN;
+    rowmark[k] = 0;
   }
 }
 
-// After a flagged forward pass: each row that exceeded its reference takes
-// its maximum over the vocabulary as the new reference (the largest value
-// recorded, since only tiles beyond the window record).  Nothing unless
-// flagged.
+// After a flagged forward pass and the max-relative pass over the same
+// tiles: each marked row takes its maximum over the vocabulary (the largest
+// of its per-tile maxima) as the new reference.  Nothing unless flagged.
 __global__ void __launch_bounds__(256)
 k_lm_mref_fix(const int32_t* __restrict__ counts, const int32_t* __restrict__ flag,
-              const int32_t* __restrict__ rowmax, float* __restrict__ mref) {
+              const int32_t* __restrict__ rowmark, const float2* __restrict__ part, int64_t ntn,
+              float* __restrict__ mref) {
   if (*flag == 0) return;
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < counts[0];
        k += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t m = rowmax[k];
-    if (m != INT32_MIN) mref[k] = ord_f32(m);
+    if (rowmark[k] == 0) continue;
+    float m = -INFINITY;
+    for (int64_t j = 0; j < ntn; ++j) m = fmaxf(m, part[k * ntn + j].x);
+    mref[k] = m;
   }
 }
 
@@ -1239,7 +1255,7 @@ struct LmWs {
   float2* part;      // [T, ntn] (reference, sum exp) of each vocabulary tile
   float* xy;         // [T]
   float* mref;       // [round_up(T, GBM)] each active token's reference r_t
-  int32_t* rowmax;   // [T] maxima recorded for rows beyond their reference
+  int32_t* rowmark;  // [T] rows beyond their reference (1)
   int32_t* flag;     // [1] some row was beyond its reference
   float* rscale;     // [round_up(T, GBM)] each active token's dlogits factor s_t
   uint16_t* Ha;      // [T, H] K-paneled over H (H/32 panels [T][32])
@@ -1276,7 +1292,7 @@ size_t lm_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LmWs* ws
   w.part = reinterpret_cast<float2*>(take(8 * (size_t)T * ntn));
   w.xy = reinterpret_cast<float*>(take(4 * T));
   w.mref = reinterpret_cast<float*>(take(4 * round_up(T, GBM)));
-  w.rowmax = reinterpret_cast<int32_t*>(take(4 * T));
+  w.rowmark = reinterpret_cast<int32_t*>(take(4 * T));
   w.flag = reinterpret_cast<int32_t*>(take(4));
   w.rscale = reinterpret_cast<float*>(take(4 * round_up(T, GBM)));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
@@ -1299,6 +1315,9 @@ struct LpWs {
   int32_t* ycol;     // [T]
   float2* part;      // [T, ntn]
   float* xy;         // [T]
+  float* mref;       // [T] each counted token's reference
+  int32_t* rowmark;  // [T] rows beyond their reference (1)
+  int32_t* flag;     // [1]
   uint16_t* Ha;      // [T, H] K-paneled over H (H/32 panels [T][32])
 };
 
@@ -1319,6 +1338,9 @@ size_t lp_carve(void* base, int64_t N, int64_t T, int64_t V, int64_t H, LpWs* ws
   w.ycol = reinterpret_cast<int32_t*>(take(4 * T));
   w.part = reinterpret_cast<float2*>(take(8 * (size_t)T * ntn));
   w.xy = reinterpret_cast<float*>(take(4 * T));
+  w.mref = reinterpret_cast<float*>(take(4 * T));
+  w.rowmark = reinterpret_cast<int32_t*>(take(4 * T));
+  w.flag = reinterpret_cast<int32_t*>(take(4));
   w.Ha = reinterpret_cast<uint16_t*>(take(2 * (size_t)T * H));
   if (ws) *ws = w;
   return off;
@@ -1362,14 +1384,16 @@ int launch_gemm(const GemmArgs& g, hipStream_t st, hipEvent_t ev_begin = nullptr
 // The loss's forward product again when *g.run_if is set: one workgroup per
 // CU (256 on gfx950) over the same tiles.
 constexpr int kRerunGrid = 256;
+template <int MODE>
 int launch_rerun(const GemmArgs& g, hipStream_t st) {
+  static_assert(TileShape<MODE>::kFwd, "forward products only");
   const int64_t blocks = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
   if (blocks <= 0) return DRGRPO_OK;
   if (blocks > INT32_MAX) return DRGRPO_ERR_SHAPE;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_rerun),
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_rerun<MODE>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLdsLse) != hipSuccess)
     return DRGRPO_ERR_HIP;
-  hipLaunchKernelGGL(k_gemm_rerun, dim3(kRerunGrid), dim3(GT), kGemmLdsLse, st, g, (int)blocks);
+  hipLaunchKernelGGL(k_gemm_rerun<MODE>, dim3(kRerunGrid), dim3(GT), kGemmLdsLse, st, g, (int)blocks);
   return launch_status();
 }
 
@@ -1441,7 +1465,7 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
                      w.offs, w.act_pos, w.ycol, w.Ha, T * 32, w.tok_loss, w.tok_flags);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_mref, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.Ha, T * 32, Wb,
-                     H, w.counts, w.ycol, w.mref, w.rowmax, w.flag);
+                     H, w.counts, w.ycol, w.mref, w.rowmark, w.flag);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
 
   // forward: per-token sums of exp(x - r_t) over the vocabulary and E; the
@@ -1464,17 +1488,20 @@ extern "C" int drgrpo_lmhead_loss_fwd_bwd_ex(const void* hidden, const void* W,
   g.col_base = 0;
   g.E = w.E;
   g.mref = w.mref;
-  g.rowmax = w.rowmax;
+  g.rowmark = w.rowmark;
   g.flag = w.flag;
   g.run_if = w.flag;
   if ((rc = launch_gemm<GM_LSE_E>(g, st, aux ? static_cast<hipEvent_t>(aux->fwd_event_begin) : nullptr,
                                   aux ? static_cast<hipEvent_t>(aux->fwd_event_end) : nullptr)) !=
       DRGRPO_OK)
     return rc;
-  // rows beyond their reference (if any): new references, the product again
-  hipLaunchKernelGGL(k_lm_mref_fix, dim3(64), dim3(256), 0, st, w.counts, w.flag, w.rowmax, w.mref);
+  // rows beyond their reference (if any): their maxima from a max-relative
+  // pass, those as new references, the product again
+  if ((rc = launch_rerun<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
+  hipLaunchKernelGGL(k_lm_mref_fix, dim3(64), dim3(256), 0, st, w.counts, w.flag, w.rowmark,
+                     w.part, ntn, w.mref);
   if ((rc = launch_status()) != DRGRPO_OK) return rc;
-  if ((rc = launch_rerun(g, st)) != DRGRPO_OK) return rc;
+  if ((rc = launch_rerun<GM_LSE_E>(g, st)) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
                      w.xy, w.counts, w.act_pos, w.ycol, C, w.adv, w.len, logp_old, logp_ref, eps,
                      beta, (double)norm_const, agg, w.total_len, w.mref, w.E, w.rscale, w.tok_loss,
@@ -1615,7 +1642,19 @@ extern "C" int drgrpo_lmhead_logprobs(const void* hidden, const void* W, const i
   g.xy = w.xy;
   g.ycol = w.ycol;
   g.col_base = 0;
-  if ((rc = launch_gemm<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
+  // sums relative to each token's sampled logit (no exponentials kept); a
+  // call with a row beyond that reference's window redoes every tile
+  // relative to its maxima
+  hipLaunchKernelGGL(k_lm_mref, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.Ha, T * 32,
+                     static_cast<const uint16_t*>(W), H, w.counts, w.ycol, w.mref, w.rowmark,
+                     w.flag);
+  if ((rc = launch_status()) != DRGRPO_OK) return rc;
+  g.mref = w.mref;
+  g.rowmark = w.rowmark;
+  g.flag = w.flag;
+  g.run_if = w.flag;
+  if ((rc = launch_gemm<GM_LSE_E>(g, st)) != DRGRPO_OK) return rc;
+  if ((rc = launch_rerun<GM_LSE>(g, st)) != DRGRPO_OK) return rc;
   hipLaunchKernelGGL(k_lm_logp, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, w.part, ntn,
                      w.xy, w.counts, w.act_pos, w.ycol, out_logp);
   return launch_status();

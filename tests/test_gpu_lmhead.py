@@ -204,6 +204,33 @@ def test_lmhead_logprobs_small(name):
     assert np.array_equal(got_all[counted], got[counted])
 
 
+def test_lmhead_logprobs_rows_far_above_their_reference():
+    """The forward-only pass sums exp(x - r) with r the sampled token's logit;
+    rows whose largest logit lies more than 48 above it (every other token's
+    hidden row scaled by 32) make the call redo every tile relative to the
+    rows' maxima; every counted log-prob still matches the oracle, with and
+    without an EOS id."""
+    cfg, case, _, Wb, _, _, _ = lm_case("lmhead_multi")
+    hb = scaled_bf16_rows(case.hidden(), np.arange(0, cfg.T, 2), 32.0)
+    h64 = lmhead.bf16_to_f64(hb)
+    W64 = lmhead.bf16_to_f64(Wb)
+    tok = case.tokens.reshape(-1)
+    x = h64 @ W64.T
+    gap = x.max(axis=1) - x[np.arange(cfg.T), tok]
+    lens = oracle.completion_len(case.tokens, cfg.eos_id)
+    counted = (np.arange(cfg.C)[None, :] < lens[:, None]).reshape(-1)
+    assert (gap[counted] > 48.0).sum() >= 4
+    _, want = lmhead.token_rows(h64, W64, tok, np.arange(cfg.T))
+    bound = _logp_bound(h64, W64, np.arange(cfg.T))
+    hd, Wd, td = _bits_to_dev(hb), _bits_to_dev(Wb), torch.from_numpy(case.tokens).to(DEV)
+    got = dr.lmhead_logprobs(hd, Wd, td, cfg.eos_id).cpu().numpy().astype(np.float64).reshape(-1)
+    err = np.abs(got - want)
+    assert (err[counted] <= bound[counted]).all(), float(err[counted].max())
+    assert (got[~counted] == 0.0).all()
+    got_all = dr.lmhead_logprobs(hd, Wd, td, -1).cpu().numpy().astype(np.float64).reshape(-1)
+    assert (np.abs(got_all - want) <= bound).all()
+
+
 def test_lmhead_logprobs_bad_token_is_nan():
     cfg, case, hb, Wb, old, ref, t = lm_case("lmhead_mini")
     tokens = case.tokens.copy()
