@@ -110,12 +110,13 @@ def test_lmhead_graph_replay():
 
 
 def test_lmhead_graph_replay_rows_beyond_reference():
-    """The fused lm_head's flagged-row pass inside a captured graph: one graph
-    replayed while its hidden states alternate, in place, between inputs that
-    put 9 of 20 active rows beyond their reference (every other token's row
-    scaled by 32) and inputs that put none there; every replay equals the
-    eager call on the same inputs bit for bit, so the flag and the recorded
-    maxima are cleared by the library's own kernels on every call."""
+    """The fused lm_head's flagged-row pass inside captured graphs (the loss
+    and the forward-only log-probs): each graph replayed while its hidden
+    states alternate, in place, between inputs that put 9 of 20 active rows
+    beyond their reference (every other token's row scaled by 32) and inputs
+    that put none there; every replay equals the eager call on the same
+    inputs bit for bit, so the flag and the row marks are cleared by the
+    library's own kernels on every call."""
     import synth
     from oracle import lmhead
 
@@ -149,9 +150,22 @@ def test_lmhead_graph_replay_rows_beyond_reference():
     graph, (loss_g, _, _) = _capture(lambda: dr.lmhead_loss_fwd_bwd(
         hidden, W, tokens, cfg.eos_id, rewards, lo, lr, out_dhidden=dh_g, out_dW=dW_g,
         workspace=ws_g, **kw))
+    # the forward-only log-probs of the same inputs, also from a graph
+    lp_want = {k: dr.lmhead_logprobs(h, W, tokens, cfg.eos_id).clone() for k, (h, _, _) in
+               inputs.items()}
+    torch.cuda.synchronize()
+    ws_lp = torch.empty(dr.lmhead_logprobs_workspace_bytes(cfg.N, cfg.C, cfg.V, cfg.H),
+                        dtype=torch.uint8, device=DEV)
+    graph_lp, lp_g = _capture(lambda: dr.lmhead_logprobs(hidden, W, tokens, cfg.eos_id,
+                                                         workspace=ws_lp))
     for k in ["far", "near", "far", "near", "far"]:
         for dst, src in zip((hidden, lo, lr), inputs[k]):
             dst.copy_(src)
+        lp_g.fill_(1.0)
+        torch.cuda.synchronize()
+        graph_lp.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lp_g, lp_want[k]), k
         dh_g.fill_(1.0)
         dW_g.fill_(1.0)
         loss_g.fill_(float("nan"))
