@@ -91,7 +91,8 @@ constexpr double kL2ED = 1.4426950408889634074;
 // binary32 hold up to e^88), its sum over any vocabulary below e^61 and the
 // gradient products' sums far inside the binary32 range.
 constexpr float kRefWindow = 48.0f;
-constexpr float kRefSumMax = 7.0167e20f;  // e^48 (rounded down)
+constexpr float kRefSumMax = 7.0167e20f;  // e^kRefWindow (rounded down)
+static_assert(kRefWindow == 48.0f, "kRefSumMax is e^48");
 
 enum { GM_LSE = 0, GM_LSE_E = 1, GM_ACC = 2, GM_STORE = 3 };
 
@@ -1149,8 +1150,8 @@ k_lm_combine(const float2* __restrict__ part, int64_t ntn, const float* __restri
 // token's logit hidden_t . W[y_t] (binary32 sum of bfloat16 products, one
 // wavefront per token; 0 for a bad token id).  Any value would do as long as
 // exp(x - r_t) stays in range: the sampled token's logit is at most the row's
-// maximum, and a row whose maximum lies more than kRefWindow above it is
-// detected and redone.  Also clears the call's flag and the rows' marks.
+// maximum, and a row whose exponentials sum beyond e^kRefWindow in some tile
+// is detected and redone.  Also clears the call's flag and the rows' marks.
 __global__ void __launch_bounds__(256)
 k_lm_mref(const uint16_t* __restrict__ Ha, int64_t ha_ps, const uint16_t* __restrict__ W, int64_t H,
           const int32_t* __restrict__ counts, const int32_t* __restrict__ ycol,
